@@ -1,0 +1,263 @@
+/*
+ * k2.h -- C ABI of libk2.so: the batch-1 decode hot path of a dense
+ * decoder-only LLM (and the routed-expert GEMV of a latent-MoE layer) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [k2-burn]      README of k2-burn, the K2-Horizon port: "Model shape",
+ *                  "Working end to end" (GroupedRMSNorm, split-half RoPE, GQA,
+ *                  SwiGLU MLP; "prefill + single-token decode" over "a
+ *                  preallocated per-layer KV cache"), "KV cache storage"
+ *                  (int8 with a per-head_dim-block scale; a prompt that does
+ *                  not fit is rejected), "Quantization" (fp8 E4M3 Linear
+ *                  weights), "Limitations" (effective batch size 1; plain
+ *                  SDPA with the softmax in fp32).
+ *   [k3_run.c]     kimi-k3-in-c src/cli/k3_run.c: header comment (token ids
+ *                  in, token ids out; routed experts multiplied straight out
+ *                  of MXFP4), real_cfg_hardcoded() (latent MoE: 896 experts,
+ *                  top-16, 2 shared, latent 3584, inter 3072, routed_scale,
+ *                  renorm, latent_norm), forward() (on failure the logits are
+ *                  left untouched and the caller must check), the request
+ *                  validation in main() (refuse rather than clamp), argmax_()
+ *                  (first maximum wins).
+ *   [cpu_weights.rs] avarok_core kimi_k3 cpu_weights.rs: MoeWeights (down, up,
+ *                  norm, router, bias, experts (w1, w2, w3), shared).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers are DEVICE pointers unless a comment says "host".  Every call
+ *   only enqueues work on `stream` (a hipStream_t passed as void*; NULL is the
+ *   null stream) and returns without synchronizing.
+ * - The caller owns and allocates every buffer (weights, caches, activations,
+ *   workspaces).  The library allocates no device memory, keeps no pointer
+ *   after returning, and holds no mutable global state.  Calls on different
+ *   streams with disjoint buffers may run concurrently.
+ * - Activations are fp32.  bf16 values travel as uint16_t bit patterns; fp8
+ *   is OCP E4M3FN (uint8_t codes); MXFP4 is OCP E2M1 elements packed two per
+ *   byte, low nibble = even column, with one E8M0 scale byte per 32
+ *   consecutive columns of a row.
+ * - Matrices are row-major [N out][K in].
+ * - Errors: every int-returning call returns a k2_status.  Arguments are
+ *   validated on the host (scalars and pointer alignment only, no device
+ *   sync).  On K2_EINVAL / K2_ERANGE / K2_EUNSUPPORTED nothing is enqueued and
+ *   every output buffer is left untouched.  K2_EHIP (a launch error reported
+ *   by the HIP runtime) is the only status after which outputs are undefined.
+ * - Alignment: weight, cache and activation pointers must be 16-byte
+ *   aligned (the kernels use 128-bit loads); K2_EINVAL otherwise.
+ */
+#ifndef K2_H
+#define K2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define K2_ABI_VERSION 1
+
+typedef enum {
+    K2_OK = 0,
+    K2_EINVAL = -1,        /* null / misaligned pointer, non-positive size */
+    K2_ERANGE = -2,        /* token, position or length out of range */
+    K2_EUNSUPPORTED = -3,  /* a shape or dtype this build does not handle */
+    K2_EHIP = -4           /* the HIP runtime reported a launch error */
+} k2_status;
+
+typedef enum {
+    K2_F32 = 0,
+    K2_BF16 = 1,
+    K2_FP8E4M3 = 2,
+    K2_MXFP4 = 3,
+    K2_I8 = 4
+} k2_dtype;
+
+int k2_abi_version(void);
+/* Host string for a status code (static storage). */
+const char *k2_status_str(int status);
+
+/* ------------------------------------------------------------------------
+ * Weight preparation ([k2-burn] "Quantization": only Linear weights are
+ * quantized; [k3_run.c] header: experts in MXFP4).  Input is the bf16 draw.
+ * ---------------------------------------------------------------------- */
+
+/* fp8 E4M3FN with one fp32 scale per output row:
+ *   row_scale[n] = fp32(max_k |W[n][k]| / 448),
+ *   codes[n][k]  = E4M3FN round-to-nearest-even, saturating at +-448, of
+ *                  fp32(W[n][k] / row_scale[n]); an all-zero row has scale 0
+ *                  and codes 0.  The sign of a zero result is kept.
+ * W: uint16 bf16 [N][K]; codes: uint8 [N][K]; row_scale: float [N].
+ * K2_EINVAL if K % 16 or any pointer is null/misaligned. */
+int k2_quantize_fp8_rows(const uint16_t *W, uint8_t *codes, float *row_scale,
+                         int N, int K, void *stream);
+
+/* MXFP4 (OCP Microscaling: E2M1 elements, blocks of 32, E8M0 scale):
+ *   e_b  = clamp(unbiased exponent field of fp32 amax_b - 2, -127, 127),
+ *   e8m0[n][b] = e_b + 127,
+ *   code = E2M1 round-to-nearest-even, saturating at +-6, of W * 2^-e_b.
+ * W: uint16 bf16 [N][K]; q: uint8 [N][K/2]; e8m0: uint8 [N][K/32].
+ * K2_EUNSUPPORTED if K % 32 != 0. */
+int k2_quantize_mxfp4(const uint16_t *W, uint8_t *q, uint8_t *e8m0, int N, int K,
+                      void *stream);
+
+/* ------------------------------------------------------------------------
+ * Step operations
+ * ---------------------------------------------------------------------- */
+
+/* GroupedRMSNorm ([k2-burn] "Model shape": layernorm_num_groups).  For each
+ * of `rows` vectors of length `hidden`, cut into `groups` equal contiguous
+ * groups: y = x / sqrt(mean over the group of x^2 + eps) * gamma (gamma over
+ * the full hidden size).  x, y: [rows][hidden] (may alias); gamma: [hidden].
+ * K2_EUNSUPPORTED if hidden % groups != 0 or hidden / groups > 16384. */
+int k2_rmsnorm_grouped(const float *x, const float *gamma, float *y, int rows, int hidden,
+                       int groups, float eps, void *stream);
+
+/* Dequantizing GEMV, y[b][n] = sum_k W_hat[n][k] * x[b][k] (+ residual[b][n]),
+ * fp32 accumulation, for B activation vectors (1 <= B <= 8).
+ *   qbf16:  W uint16 bf16 [N][K]
+ *   qfp8:   W uint8 E4M3FN [N][K], row_scale float [N] (applied after the sum)
+ *   qmxfp4: Wq uint8 [N][K/2], We8m0 uint8 [N][K/32] (per-block scale
+ *           applied to each 32-column partial sum)
+ *   f32:    W float [N][K]
+ * x: [B][K]; y: [B][N]; residual (nullable): [B][N], may alias y.
+ * K2_EUNSUPPORTED if K % 32 != 0 or B * K > 12288. */
+int k2_gemv_qbf16(const uint16_t *W, const float *x, float *y, const float *residual,
+                  int N, int K, int B, void *stream);
+int k2_gemv_qfp8(const uint8_t *W, const float *row_scale, const float *x, float *y,
+                 const float *residual, int N, int K, int B, void *stream);
+int k2_gemv_qmxfp4(const uint8_t *Wq, const uint8_t *We8m0, const float *x, float *y,
+                   const float *residual, int N, int K, int B, void *stream);
+int k2_gemv_f32(const float *W, const float *x, float *y, const float *residual, int N,
+                int K, int B, void *stream);
+
+/* RoPE table for split-half rotary embedding ([k2-burn] "Working end to
+ * end"; the table is sized by the context window, "KV cache storage"):
+ * cos_sin[p][i][0] = cos(p * theta^(-2i/head_dim)), [1] = sin(...), for
+ * p < cap, i < head_dim/2, computed in fp64 on the device and stored fp32. */
+int k2_rope_table(float *cos_sin, int cap, int head_dim, double theta, void *stream);
+
+/* Split-half RoPE in place on n_qh query heads q [n_qh][hd] and n_kv key heads
+ * k [n_kv][hd] at position pos: element i pairs with i + hd/2,
+ *   u_i <- a cos - b sin,  u_{i+hd/2} <- a sin + b cos.
+ * K2_ERANGE if pos >= cap; K2_EUNSUPPORTED unless hd is 16, 32, 64 or 128. */
+int k2_rope(float *q, float *k, const float *cos_sin, int n_qh, int n_kv, int head_dim,
+            int pos, int cap, void *stream);
+
+/* Store one position of K and V ([k2-burn] "KV cache storage").  Caches are
+ * [n_kv][cap][hd]; k, v are fp32 [n_kv][hd].
+ *   k2_kv_append:      kvdt K2_F32 (stored as is) or K2_BF16 (round to
+ *                      nearest even).
+ *   k2_kv_append_int8: symmetric int8 per (kv head, position) block:
+ *                      s = fp32(max|x| / 127), code = clamp(rint(fp32(x / s)),
+ *                      -127, 127); max|x| = 0 gives s = 0 and codes 0.
+ *                      Scales ks, vs: [n_kv][cap] fp32.
+ * K2_ERANGE if pos >= cap. */
+int k2_kv_append(k2_dtype kvdt, const float *k, const float *v, void *kc, void *vc,
+                 int n_kv, int head_dim, int cap, int pos, void *stream);
+int k2_kv_append_int8(const float *k, const float *v, int8_t *kc, int8_t *vc, float *ks,
+                      float *vs, int n_kv, int head_dim, int cap, int pos, void *stream);
+
+/* GQA decode attention ([k2-burn] "Model shape": 4x KV repeat; "Limitations":
+ * plain SDPA with the softmax in fp32).  For query head h the key/value head
+ * is h / (n_qh / n_kv); out[h] = softmax(q_h . K[0..len) * scale) V[0..len).
+ * Split over positions with an online fp32 softmax and a fixed-order combine
+ * (run-to-run deterministic).  kvdt: K2_F32, K2_BF16 or K2_I8 (ks, vs
+ * required).  q: [n_qh][hd] (already rotated); out: [n_qh][hd].
+ * ws: workspace of k2_attn_workspace_bytes(n_qh, n_kv, head_dim, cap) bytes,
+ * zero-filled by the caller before its first use (the kernels leave it zeroed
+ * again on exit).  K2_ERANGE unless 1 <= len <= cap; K2_EUNSUPPORTED unless
+ * hd is 16/32/64/128 and n_qh / n_kv is 1, 2, 4 or 8. */
+size_t k2_attn_workspace_bytes(int n_qh, int n_kv, int head_dim, int cap);
+int k2_gqa_decode_attn(k2_dtype kvdt, const float *q, const void *kc, const void *vc,
+                       const float *ks, const float *vs, float *out, int n_qh, int n_kv,
+                       int head_dim, int cap, int len, float scale, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* Fused step used by k2_decode_step: from the raw QKV projection
+ * qkv = [q (n_qh*hd); k (n_kv*hd); v (n_kv*hd)], rotate q and k at `pos`,
+ * store k and v at slot `pos` of the cache (kvdt as above), then attend over
+ * slots [0, pos] with scale 1/sqrt(hd).  The stored values are the ones
+ * attended to.  out: [n_qh][hd].  Same workspace as k2_gqa_decode_attn. */
+int k2_rope_append_attn(k2_dtype kvdt, const float *qkv, const float *cos_sin, void *kc,
+                        void *vc, float *ks, float *vs, float *out, int n_qh, int n_kv,
+                        int head_dim, int cap, int pos, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/* First-maximum argmax of x[0..n) ([k3_run.c] argmax_()): out_idx[0] is the
+ * lowest index holding the largest value.  ws: k2_argmax_workspace_bytes(n)
+ * bytes, zero-filled before first use (left zeroed on exit). */
+size_t k2_argmax_workspace_bytes(int n);
+int k2_argmax(const float *x, int n, int32_t *out_idx, void *ws, size_t ws_bytes,
+              void *stream);
+
+/* ------------------------------------------------------------------------
+ * Whole decode step of a dense decoder ([k2-burn] "Project layout": model.rs
+ * embed -> layers -> norm -> lm_head; layer.rs norm + attention residual,
+ * norm + MLP residual; mlp.rs SwiGLU)
+ * ---------------------------------------------------------------------- */
+
+typedef struct {
+    int hidden, n_layers, n_qh, n_kv, head_dim, inter, vocab, groups, cap;
+    float eps;
+    double rope_theta;
+    k2_dtype wdt;    /* projections + lm_head: K2_F32, K2_BF16, K2_FP8E4M3, K2_MXFP4 */
+    k2_dtype kvdt;   /* K2_F32, K2_BF16, K2_I8 */
+    k2_dtype embdt;  /* K2_F32 or K2_BF16 */
+} k2_config;
+
+/* One layer (host struct of device pointers).  qkv stacks the q rows, then k,
+ * then v; gu stacks the gate rows, then the up rows.  *_s: fp32 row scales
+ * (fp8), E8M0 bytes (MXFP4), NULL otherwise. */
+typedef struct {
+    const void *qkv, *qkv_s;    /* [(n_qh + 2 n_kv) hd][hidden] */
+    const void *o, *o_s;        /* [hidden][n_qh hd] */
+    const void *gu, *gu_s;      /* [2 inter][hidden] */
+    const void *down, *down_s;  /* [hidden][inter] */
+    const float *g_in, *g_post; /* [hidden] */
+    void *kc, *vc;              /* [n_kv][cap][hd] of kvdt */
+    float *ks, *vs;             /* [n_kv][cap] (int8 only) */
+} k2_layer;
+
+typedef struct {
+    k2_config cfg;
+    const void *embed;          /* [vocab][hidden] of embdt */
+    const void *lm, *lm_s;      /* [vocab][hidden] of wdt (+ scales) */
+    const float *g_final;       /* [hidden] */
+    const float *rope;          /* k2_rope_table(cap, head_dim, rope_theta) */
+    const k2_layer *layers;     /* HOST array [n_layers] */
+    void *ws;                   /* k2_decode_workspace_bytes(&cfg), zero-filled
+                                   before first use */
+    size_t ws_bytes;
+} k2_model;
+
+size_t k2_decode_workspace_bytes(const k2_config *cfg);
+
+/* Validate a model description (sizes, dtypes, pointers, alignment). */
+int k2_model_check(const k2_model *m);
+
+/* One decode position: embed `token` (host int), run every layer at `pos`
+ * (its K and V are stored at slot pos before attending), then, when `logits`
+ * is non-NULL, the final norm, the lm_head and the argmax.  logits: [vocab]
+ * fp32 (nullable: prefill positions skip the head); next_token: device int32
+ * (nullable), the first-maximum argmax.  K2_ERANGE if token is outside
+ * [0, vocab) or pos outside [0, cap): refuse rather than clamp ([k3_run.c]
+ * main()), nothing enqueued. */
+int k2_decode_step(const k2_model *m, int token, int pos, float *logits, int32_t *next_token,
+                   void *stream);
+
+/* Same step with the token read from device memory (d_token), so that a
+ * greedy loop can feed next_token back without a host round trip
+ * (d_token may equal the previous step's next_token).  A token outside
+ * [0, vocab) is caught on the device: *d_err (device int32, nullable) is set
+ * to K2_ERANGE, and the step runs on token 0 so that every kernel still
+ * completes; the caller must check d_err before trusting the outputs
+ * ([k3_run.c] forward(): the caller must check). */
+int k2_decode_step_dev(const k2_model *m, const int32_t *d_token, int pos, float *logits,
+                       int32_t *next_token, int32_t *d_err, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* K2_H */

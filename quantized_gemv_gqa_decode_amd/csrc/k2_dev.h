@@ -1,0 +1,135 @@
+// k2_dev.h -- device helpers shared by the gfx950 kernels of libk2.
+//
+// CDNA4 specifics used here: 64-lane wavefronts, 128-bit global loads
+// (16 bytes per lane = 1 KiB per wave instruction), the gfx950 hardware
+// converters v_cvt_pk_f32_fp8 (OCP E4M3FN -> fp32, two values) and
+// v_cvt_scalef32_pk_f32_fp4 (OCP E2M1 -> fp32, two values), and LDS for
+// staging activation vectors.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/k2.h"
+
+#define K2_WAVE 64
+#define K2_BLOCK 256
+#define K2_WAVES_PER_BLOCK (K2_BLOCK / K2_WAVE)
+
+typedef float k2_f2 __attribute__((ext_vector_type(2)));
+typedef uint32_t k2_u4 __attribute__((ext_vector_type(4)));
+
+namespace k2 {
+
+// ------------------------------------------------------------- reductions --
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, K2_WAVE);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, K2_WAVE));
+    return v;
+}
+
+// Sum across aligned groups of `W` lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, K2_WAVE);
+    return v;
+}
+
+// ---------------------------------------------------------------- codecs --
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Two OCP E4M3FN bytes (bytes 0,1 or 2,3 of a dword) -> two fp32.
+__device__ __forceinline__ k2_f2 fp8x2_lo(uint32_t u) { return __builtin_amdgcn_cvt_pk_f32_fp8(u, false); }
+__device__ __forceinline__ k2_f2 fp8x2_hi(uint32_t u) { return __builtin_amdgcn_cvt_pk_f32_fp8(u, true); }
+
+// Two E2M1 nibbles of byte `SEL` of a dword -> two fp32 (low nibble first).
+template <int SEL>
+__device__ __forceinline__ k2_f2 fp4x2(uint32_t u)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, SEL);
+}
+
+// E8M0 scale byte -> 2^(b - 127) as fp32 (b = 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b)
+{
+    return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
+// fp32 -> OCP E4M3FN code, round to nearest even, saturating at +-448; the
+// sign bit of the input is kept.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float t)
+{
+    uint32_t sign = (__float_as_uint(t) >> 31) << 7;
+    float a = fabsf(t);
+    uint32_t code;
+    if (a >= 448.0f) {
+        code = 0x7E;
+    } else if (a < 0.015625f) {                    // below 2^-6: subnormal step 2^-9
+        float q = rintf(a * 512.0f);               // exact scaling, RNE
+        code = (uint32_t)q;                        // 8 means 2^-6 = exponent 1, mantissa 0
+    } else {
+        int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;   // a in [2^e, 2^(e+1))
+        float q = rintf(ldexpf(a, 3 - e));         // in [8, 16]
+        uint32_t qi = (uint32_t)q;
+        if (qi == 16) { e += 1; qi = 8; }
+        code = ((uint32_t)(e + 7) << 3) | (qi - 8);
+        if (code > 0x7E) code = 0x7E;
+    }
+    return (uint8_t)(code | sign);
+}
+
+// fp32 -> E2M1 code (4 bits), round to nearest even, saturating at +-6; sign kept.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float t)
+{
+    uint32_t sign = (__float_as_uint(t) >> 31) << 3;
+    float a = fabsf(t);
+    uint32_t code;
+    if (a >= 6.0f) {
+        code = 7;
+    } else if (a < 1.0f) {                         // step 0.5 (subnormal + 1.0)
+        code = (uint32_t)rintf(a * 2.0f);          // 0 -> 0, 1 -> 0.5, 2 -> 1.0 (= 0b010)
+    } else {
+        int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;   // 0, 1 or 2
+        uint32_t q = (uint32_t)rintf(ldexpf(a, 1 - e));          // in [2, 4]
+        if (q == 4) { e += 1; q = 2; }
+        code = ((uint32_t)(e + 1) << 1) | (q - 2);
+    }
+    return code | sign;
+}
+
+}  // namespace k2
+
+// ------------------------------------------------------------ host helpers --
+
+#define K2_CHECK_LAUNCH()                                    \
+    do {                                                     \
+        hipError_t e_ = hipGetLastError();                   \
+        if (e_ != hipSuccess) return K2_EHIP;                \
+    } while (0)
+
+static inline bool k2_aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+static inline bool k2_ptr_ok(const void *p) { return p != nullptr && k2_aligned16(p); }
+static inline hipStream_t k2_stream(void *s) { return (hipStream_t)s; }
+static inline size_t k2_align256(size_t n) { return (n + 255) & ~(size_t)255; }

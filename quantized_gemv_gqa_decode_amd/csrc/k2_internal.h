@@ -1,0 +1,157 @@
+// k2_internal.h -- argument blocks and launchers shared between the
+// translation units of libk2 (not part of the C ABI).
+#pragma once
+
+#include "k2_dev.h"
+
+#define K2_MAX_GROUPS 8
+#define K2_MAX_LDS_FLOATS 12288          // 48 KiB of staged activations
+#define K2_GEMV_MAX_BLOCKS 4096
+#define K2_ATTN_MAX_CHUNK 1024           // positions per attention block
+#define K2_ATTN_MIN_CHUNK 32
+#define K2_ATTN_TARGET_BLOCKS 512
+#define K2_ARGMAX_MAX_BLOCKS K2_GEMV_MAX_BLOCKS
+
+namespace k2 {
+
+enum { PRO_NONE = 0, PRO_NORM = 1 };
+enum { EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2 };
+
+// Cross-block argmax: every block writes its (value, index) candidate, the
+// last block to arrive reduces them in block order and resets the counter.
+struct ArgmaxArgs {
+    float *part_v;
+    int *part_i;
+    unsigned *counter;
+    int32_t *out_idx;
+    int n_blocks;
+};
+
+struct GemvArgs {
+    const void *W;
+    const float *Sf;           // fp8 row scales
+    const uint8_t *S8;         // MXFP4 E8M0 scales
+    const float *x;            // [B][K] (or h for PRO_NORM)
+    const float *gamma;        // PRO_NORM
+    float eps;                 // PRO_NORM
+    int groups;                // PRO_NORM
+    float *y;
+    const float *residual;     // nullable, [B][N]
+    int N, K, B;
+    int n_out;                 // EPI_SWIGLU: inter (N = 2 * inter)
+    int64_t n_units;
+    ArgmaxArgs am;             // EPI_ARGMAX
+};
+
+int gemv_dispatch(int wdt, const GemvArgs &a, int pro, int epi, hipStream_t st);
+
+// ------------------------------------------------------------- attention --
+
+struct AttnArgs {
+    const float *q;            // rotated q [n_qh][hd]  (unfused)
+    const float *qkv;          // raw projection (fused)
+    const float *cos_sin;      // [cap][hd/2][2] (fused)
+    void *kc, *vc;
+    float *ks, *vs;
+    float *out;                // [n_qh][hd]
+    float *part;               // [n_kv][S][rep][hd]
+    float *part_ml;            // [n_kv][S][rep][2]
+    unsigned *counter;         // [n_kv]
+    int n_qh, n_kv, cap, len, pos, chunk, S;
+    float scale;
+};
+
+size_t attn_ws_bytes(int n_qh, int n_kv, int hd, int cap);
+int attn_splits(int n_kv, int len, int *chunk);
+int attn_launch(int kvdt, int hd, int rep, bool fused, const AttnArgs &a, hipStream_t st);
+void attn_ws_carve(void *ws, int n_qh, int n_kv, int hd, int cap, AttnArgs &a);
+
+// --------------------------------------------------------------- argmax --
+
+size_t argmax_ws_bytes();
+void argmax_ws_carve(void *ws, ArgmaxArgs &am);
+
+// ------------------------------------------------------------------- misc --
+
+int embed_launch(int embdt, const void *E, int H, int vocab, int token, const int32_t *d_token,
+                 int32_t *d_err, float *h, unsigned *zero_a, int zero_a_n, unsigned *zero_b,
+                 int zero_b_n, hipStream_t st);
+
+// ------------------------------------------------------ device functions --
+
+__device__ __forceinline__ void argmax_pair_max(float &v, int &i, float ov, int oi)
+{
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+}
+
+__device__ __forceinline__ void argmax_wave(float &v, int &i)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(v, o, K2_WAVE);
+        const int oi = __shfl_xor(i, o, K2_WAVE);
+        argmax_pair_max(v, i, ov, oi);
+    }
+}
+
+// Block-level (value, index) reduction; result valid in thread 0.
+__device__ __forceinline__ void argmax_block(float &v, int &i)
+{
+    __shared__ float sv[K2_WAVES_PER_BLOCK];
+    __shared__ int si[K2_WAVES_PER_BLOCK];
+    argmax_wave(v, i);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) { sv[wave] = v; si[wave] = i; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < K2_WAVES_PER_BLOCK; ++w) argmax_pair_max(v, i, sv[w], si[w]);
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void store_agent(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(int *p, int v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_agent(const int *p)
+{
+    return __hip_atomic_load(const_cast<int *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Publish this block's candidate; the last block reduces all of them in
+// block order (a fixed order, so the result does not depend on timing),
+// writes the index and re-zeroes the counter for the next use.
+__device__ __forceinline__ void argmax_block_finish(float v, int i, const ArgmaxArgs &am)
+{
+    __shared__ int is_last;
+    argmax_block(v, i);
+    if (threadIdx.x == 0) {
+        store_agent(am.part_v + blockIdx.x, v);
+        store_agent(am.part_i + blockIdx.x, i);
+        __threadfence();
+        const unsigned prev = atomicAdd(am.counter, 1u);
+        is_last = (prev == (unsigned)am.n_blocks - 1u);
+    }
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int b = threadIdx.x; b < am.n_blocks; b += K2_BLOCK)
+        argmax_pair_max(bv, bi, load_agent(am.part_v + b), load_agent(am.part_i + b));
+    argmax_block(bv, bi);
+    if (threadIdx.x == 0) {
+        *am.out_idx = bi;
+        atomicExch(am.counter, 0u);
+    }
+}
+
+}  // namespace k2

@@ -1,0 +1,277 @@
+// misc.hip -- the small kernels of the decode step and the weight quantizers.
+#include <math.h>
+
+#include "k2_dev.h"
+#include "k2_internal.h"
+
+namespace k2 {
+
+// ---------------------------------------------------------------- RMSNorm --
+// GroupedRMSNorm ([k2-burn] "Model shape": layernorm_num_groups): one block per
+// (row, group); y = x / sqrt(mean(x^2) + eps) * gamma.
+__global__ __launch_bounds__(K2_BLOCK) void rmsnorm_grouped_kernel(const float *x, const float *gamma,
+                                                                   float *y, int hidden, int groups,
+                                                                   float eps)
+{
+    __shared__ float red[K2_WAVES_PER_BLOCK];
+    const int row = blockIdx.x / groups, g = blockIdx.x % groups, gs = hidden / groups;
+    const float *xr = x + (int64_t)row * hidden + (int64_t)g * gs;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < gs; i += K2_BLOCK) ss += xr[i] * xr[i];
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < K2_WAVES_PER_BLOCK; ++w) t += red[w];
+    const float r = 1.0f / sqrtf(t / (float)gs + eps);
+    float *yr = y + (int64_t)row * hidden + (int64_t)g * gs;
+    const float *gm = gamma + (int64_t)g * gs;
+    for (int i = threadIdx.x; i < gs; i += K2_BLOCK) yr[i] = xr[i] * r * gm[i];
+}
+
+// ------------------------------------------------------------------- RoPE --
+// cos/sin of pos * theta^(-2i/hd), computed in fp64 and stored as fp32.
+__global__ void rope_table_kernel(float *cs, int cap, int hd, double theta)
+{
+    const int half = hd / 2;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)cap * half) return;
+    const int p = (int)(t / half), i = (int)(t % half);
+    const double inv = pow(theta, -2.0 * (double)i / (double)hd);
+    const double ang = (double)p * inv;
+    cs[t * 2] = (float)cos(ang);
+    cs[t * 2 + 1] = (float)sin(ang);
+}
+
+// split-half rotation of n_heads heads of size hd, in place; one thread per pair
+__global__ void rope_kernel(float *q, float *k, const float *cs, int n_qh, int n_kv, int hd, int pos)
+{
+    const int half = hd / 2;
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (n_qh + n_kv) * half) return;
+    const int h = t / half, i = t % half;
+    float *u = (h < n_qh) ? q + (int64_t)h * hd : k + (int64_t)(h - n_qh) * hd;
+    const float c = cs[((int64_t)pos * half + i) * 2], s = cs[((int64_t)pos * half + i) * 2 + 1];
+    const float a = u[i], b = u[i + half];
+    u[i] = a * c - b * s;
+    u[i + half] = a * s + b * c;
+}
+
+// ------------------------------------------------------------------ embed --
+// h = fp32(E[token]); the token comes from the host (token >= 0) or from
+// device memory (d_token).  A device token outside [0, vocab) sets *d_err and
+// is replaced by 0 so that every later kernel still runs to completion.
+// The same launch re-zeroes the arrival counters of the step's workspace.
+__global__ void embed_kernel(int embdt, const void *E, int H, int vocab, int token,
+                             const int32_t *d_token, int32_t *d_err, float *h, unsigned *za,
+                             int za_n, unsigned *zb, int zb_n)
+{
+    int tok = token;
+    if (d_token) {
+        tok = *d_token;
+        if (tok < 0 || tok >= vocab) {
+            if (d_err && threadIdx.x == 0 && blockIdx.x == 0) *d_err = K2_ERANGE;
+            tok = 0;
+        }
+    }
+    const int64_t base = (int64_t)tok * H;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < H; i += gridDim.x * blockDim.x)
+        h[i] = embdt == K2_BF16 ? bf16_to_f32(((const uint16_t *)E)[base + i])
+                                : ((const float *)E)[base + i];
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < za_n; i += blockDim.x) za[i] = 0u;
+        for (int i = threadIdx.x; i < zb_n; i += blockDim.x) zb[i] = 0u;
+    }
+}
+
+int embed_launch(int embdt, const void *E, int H, int vocab, int token, const int32_t *d_token,
+                 int32_t *d_err, float *h, unsigned *za, int za_n, unsigned *zb, int zb_n,
+                 hipStream_t st)
+{
+    int blocks = (H + K2_BLOCK - 1) / K2_BLOCK;
+    if (blocks > 64) blocks = 64;
+    hipLaunchKernelGGL(embed_kernel, dim3(blocks), dim3(K2_BLOCK), 0, st, embdt, E, H, vocab, token,
+                       d_token, d_err, h, za, za_n, zb, zb_n);
+    K2_CHECK_LAUNCH();
+    return K2_OK;
+}
+
+// ------------------------------------------------------------- quantizers --
+// fp8 E4M3FN per output row ([k2-burn] "Quantization"): one block per row.
+__global__ __launch_bounds__(K2_BLOCK) void quant_fp8_rows_kernel(const uint16_t *W, uint8_t *codes,
+                                                                  float *scale, int K)
+{
+    __shared__ float red[K2_WAVES_PER_BLOCK];
+    const int64_t n = blockIdx.x;
+    const uint16_t *row = W + n * K;
+    float m = 0.f;
+    for (int k = threadIdx.x; k < K; k += K2_BLOCK) m = fmaxf(m, fabsf(bf16_to_f32(row[k])));
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    float amax = 0.f;
+#pragma unroll
+    for (int w = 0; w < K2_WAVES_PER_BLOCK; ++w) amax = fmaxf(amax, red[w]);
+    const float s = amax / 448.0f;                 // IEEE fp32 division
+    if (threadIdx.x == 0) scale[n] = s;
+    for (int k = threadIdx.x; k < K; k += K2_BLOCK) {
+        uint8_t c = 0;
+        if (amax != 0.f) c = f32_to_e4m3(bf16_to_f32(row[k]) / s);
+        codes[n * K + k] = c;
+    }
+}
+
+// MXFP4 (OCP Microscaling: E2M1, 32-column blocks, E8M0): one thread per block.
+__global__ void quant_mxfp4_kernel(const uint16_t *W, uint8_t *q, uint8_t *e8m0, int64_t n_blocks,
+                                   int K)
+{
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= n_blocks) return;
+    const int64_t nb_row = K / 32;
+    const int64_t n = b / nb_row, bb = b % nb_row;
+    const uint16_t *src = W + n * K + bb * 32;
+    float v[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        v[i] = bf16_to_f32(src[i]);
+        amax = fmaxf(amax, fabsf(v[i]));
+    }
+    int E = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;
+    int eb = E - 2;
+    eb = eb < -127 ? -127 : (eb > 127 ? 127 : eb);
+    e8m0[b] = (uint8_t)(eb + 127);
+    uint8_t *dst = q + n * (K / 2) + bb * 16;
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) {
+        const uint32_t c0 = f32_to_e2m1(ldexpf(v[i], -eb));
+        const uint32_t c1 = f32_to_e2m1(ldexpf(v[i + 1], -eb));
+        dst[i / 2] = (uint8_t)(c0 | (c1 << 4));
+    }
+}
+
+// ----------------------------------------------------------------- argmax --
+__global__ __launch_bounds__(K2_BLOCK) void argmax_kernel(const float *x, int n, ArgmaxArgs am)
+{
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int i = blockIdx.x * K2_BLOCK + threadIdx.x; i < n; i += gridDim.x * K2_BLOCK)
+        argmax_pair_max(bv, bi, x[i], i);
+    argmax_block_finish(bv, bi, am);
+}
+
+size_t argmax_ws_bytes()
+{
+    return k2_align256((size_t)K2_ARGMAX_MAX_BLOCKS * 4) * 2 + 256;
+}
+
+void argmax_ws_carve(void *ws, ArgmaxArgs &am)
+{
+    char *p = (char *)ws;
+    am.part_v = (float *)p;
+    p += k2_align256((size_t)K2_ARGMAX_MAX_BLOCKS * 4);
+    am.part_i = (int *)p;
+    p += k2_align256((size_t)K2_ARGMAX_MAX_BLOCKS * 4);
+    am.counter = (unsigned *)p;
+}
+
+}  // namespace k2
+
+using namespace k2;
+
+// ---------------------------------------------------------------- C ABI --
+
+extern "C" int k2_abi_version(void) { return K2_ABI_VERSION; }
+
+extern "C" const char *k2_status_str(int status)
+{
+    switch (status) {
+    case K2_OK: return "ok";
+    case K2_EINVAL: return "invalid argument (null or misaligned pointer, bad size)";
+    case K2_ERANGE: return "out of range (token, position or length)";
+    case K2_EUNSUPPORTED: return "unsupported shape or dtype";
+    case K2_EHIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+extern "C" int k2_rmsnorm_grouped(const float *x, const float *gamma, float *y, int rows, int hidden,
+                                  int groups, float eps, void *stream)
+{
+    if (!k2_ptr_ok(x) || !k2_ptr_ok(gamma) || !k2_ptr_ok(y)) return K2_EINVAL;
+    if (rows <= 0 || hidden <= 0 || groups <= 0) return K2_EINVAL;
+    if (hidden % groups) return K2_EUNSUPPORTED;
+    hipLaunchKernelGGL(rmsnorm_grouped_kernel, dim3(rows * groups), dim3(K2_BLOCK), 0,
+                       k2_stream(stream), x, gamma, y, hidden, groups, eps);
+    K2_CHECK_LAUNCH();
+    return K2_OK;
+}
+
+extern "C" int k2_rope_table(float *cos_sin, int cap, int head_dim, double theta, void *stream)
+{
+    if (!k2_ptr_ok(cos_sin)) return K2_EINVAL;
+    if (cap <= 0 || head_dim <= 0 || head_dim % 2 || !(theta > 0)) return K2_EINVAL;
+    const int64_t n = (int64_t)cap * (head_dim / 2);
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       k2_stream(stream), cos_sin, cap, head_dim, theta);
+    K2_CHECK_LAUNCH();
+    return K2_OK;
+}
+
+extern "C" int k2_rope(float *q, float *k, const float *cos_sin, int n_qh, int n_kv, int head_dim,
+                       int pos, int cap, void *stream)
+{
+    if (!k2_ptr_ok(q) || !k2_ptr_ok(k) || !k2_ptr_ok(cos_sin)) return K2_EINVAL;
+    if (n_qh <= 0 || n_kv <= 0 || cap <= 0) return K2_EINVAL;
+    if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128) return K2_EUNSUPPORTED;
+    if (pos < 0 || pos >= cap) return K2_ERANGE;
+    const int n = (n_qh + n_kv) * (head_dim / 2);
+    hipLaunchKernelGGL(rope_kernel, dim3((n + 255) / 256), dim3(256), 0, k2_stream(stream), q, k,
+                       cos_sin, n_qh, n_kv, head_dim, pos);
+    K2_CHECK_LAUNCH();
+    return K2_OK;
+}
+
+extern "C" int k2_quantize_fp8_rows(const uint16_t *W, uint8_t *codes, float *row_scale, int N, int K,
+                                    void *stream)
+{
+    if (!k2_ptr_ok(W) || !k2_ptr_ok(codes) || !k2_ptr_ok(row_scale)) return K2_EINVAL;
+    if (N <= 0 || K <= 0 || K % 16) return K2_EINVAL;
+    hipLaunchKernelGGL(quant_fp8_rows_kernel, dim3(N), dim3(K2_BLOCK), 0, k2_stream(stream), W, codes,
+                       row_scale, K);
+    K2_CHECK_LAUNCH();
+    return K2_OK;
+}
+
+extern "C" int k2_quantize_mxfp4(const uint16_t *W, uint8_t *q, uint8_t *e8m0, int N, int K,
+                                 void *stream)
+{
+    if (!k2_ptr_ok(W) || !k2_ptr_ok(q) || !e8m0) return K2_EINVAL;
+    if (N <= 0 || K <= 0) return K2_EINVAL;
+    if (K % 32) return K2_EUNSUPPORTED;
+    const int64_t nb = (int64_t)N * (K / 32);
+    hipLaunchKernelGGL(quant_mxfp4_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0,
+                       k2_stream(stream), W, q, e8m0, nb, K);
+    K2_CHECK_LAUNCH();
+    return K2_OK;
+}
+
+extern "C" size_t k2_argmax_workspace_bytes(int n) { return n > 0 ? argmax_ws_bytes() : 0; }
+
+extern "C" int k2_argmax(const float *x, int n, int32_t *out_idx, void *ws, size_t ws_bytes,
+                         void *stream)
+{
+    if (!k2_ptr_ok(x) || !out_idx || !ws || ((uintptr_t)ws & 255u)) return K2_EINVAL;
+    if (n <= 0) return K2_EINVAL;
+    if (ws_bytes < argmax_ws_bytes()) return K2_EINVAL;
+    ArgmaxArgs am{};
+    argmax_ws_carve(ws, am);
+    am.out_idx = out_idx;
+    int blocks = (n + K2_BLOCK - 1) / K2_BLOCK;
+    if (blocks > 1024) blocks = 1024;
+    am.n_blocks = blocks;
+    hipLaunchKernelGGL(argmax_kernel, dim3(blocks), dim3(K2_BLOCK), 0, k2_stream(stream), x, n, am);
+    K2_CHECK_LAUNCH();
+    return K2_OK;
+}

@@ -1,0 +1,167 @@
+"""Device-resident decoder for the C ABI's ``k2_decode_step``.
+
+PyTorch only allocates device memory here; weights are uploaded from the
+seeded draws of ``synth`` and quantized on the device by the library's own
+``k2_quantize_*`` kernels; every step of the decode runs in libk2.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import k2
+
+_NP_TORCH = {np.float32: torch.float32, np.uint16: torch.int16, np.uint8: torch.uint8,
+             np.int8: torch.int8}
+
+
+def upload(a: np.ndarray, device) -> torch.Tensor:
+    """Copy a host array to the device, keeping its bytes (uint16 -> int16)."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class DeviceMat:
+    """A projection matrix in the library's storage format on the device."""
+
+    def __init__(self, wdt: str, draw: np.ndarray, device, stream=None):
+        N, K = draw.shape
+        self.wdt, self.N, self.K = wdt, N, K
+        self.s = None
+        if wdt in ("f32", "bf16"):
+            self.w = upload(draw, device)
+        else:
+            src = upload(draw, device)
+            if wdt == "fp8":
+                self.w = torch.empty((N, K), dtype=torch.uint8, device=device)
+                self.s = torch.empty(N, dtype=torch.float32, device=device)
+                k2.check(k2.k2_quantize_fp8_rows(src, self.w, self.s, N, K, stream))
+            elif wdt == "mxfp4":
+                self.w = torch.empty((N, K // 2), dtype=torch.uint8, device=device)
+                self.s = torch.empty((N, K // 32), dtype=torch.uint8, device=device)
+                k2.check(k2.k2_quantize_mxfp4(src, self.w, self.s, N, K, stream))
+            else:
+                raise ValueError(wdt)
+            torch.cuda.current_stream().synchronize()
+            del src
+
+    @property
+    def nbytes(self) -> int:
+        return self.w.numel() * self.w.element_size() + (
+            0 if self.s is None else self.s.numel() * self.s.element_size())
+
+
+def kv_cache(kvdt: str, n_kv: int, cap: int, hd: int, device):
+    dt = {"f32": torch.float32, "bf16": torch.int16, "i8": torch.int8}[kvdt]
+    kc = torch.zeros((n_kv, cap, hd), dtype=dt, device=device)
+    vc = torch.zeros((n_kv, cap, hd), dtype=dt, device=device)
+    if kvdt == "i8":
+        ks = torch.zeros((n_kv, cap), dtype=torch.float32, device=device)
+        vs = torch.zeros((n_kv, cap), dtype=torch.float32, device=device)
+    else:
+        ks = vs = None
+    return kc, vc, ks, vs
+
+
+class DecodeModel:
+    """All buffers of one dense decoder (a ``synth.DecoderConfig``) on the GPU,
+    plus the ``k2_model`` struct that points at them."""
+
+    def __init__(self, cfg, device="cuda", n_layers: Optional[int] = None):
+        import synth
+        if n_layers is not None:
+            cfg = cfg.replace(n_layers=n_layers)
+        self.cfg = cfg
+        self.device = torch.device(device)
+        H = cfg.hidden
+        self.embed = upload(synth.embed_weight(cfg), self.device)
+        self.lm = DeviceMat(cfg.wdt, synth.lm_head_weight(cfg), self.device)
+        self.g_final = upload(synth.norm_gain(cfg), self.device)
+        self.layers = []
+        for l in range(cfg.n_layers):
+            mats = {w: DeviceMat(cfg.wdt, synth.layer_weight(cfg, l, w), self.device)
+                    for w in ("wqkv", "wo", "wgu", "wd")}
+            kc, vc, ks, vs = kv_cache(cfg.kvdt, cfg.n_kv, cfg.cap, cfg.head_dim, self.device)
+            self.layers.append(dict(mats=mats, g_in=upload(synth.norm_gain(cfg), self.device),
+                                    g_post=upload(synth.norm_gain(cfg), self.device),
+                                    kc=kc, vc=vc, ks=ks, vs=vs))
+        self.rope = torch.empty((cfg.cap, cfg.head_dim // 2, 2), dtype=torch.float32,
+                                device=self.device)
+        k2.check(k2.k2_rope_table(self.rope, cfg.cap, cfg.head_dim, cfg.theta))
+        self._build()
+
+    def _build(self):
+        cfg = self.cfg
+        c = k2.k2_config(cfg.hidden, cfg.n_layers, cfg.n_qh, cfg.n_kv, cfg.head_dim, cfg.inter,
+                         cfg.vocab, cfg.groups, cfg.cap, cfg.eps, cfg.theta, k2.DTYPES[cfg.wdt],
+                         k2.DTYPES[cfg.kvdt], k2.DTYPES[cfg.embed_dt])
+        ws_bytes = k2.k2_decode_workspace_bytes(c)
+        if ws_bytes == 0:
+            raise k2.K2Error(k2.K2_EUNSUPPORTED)
+        self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=self.device)
+        arr = (k2.k2_layer * cfg.n_layers)()
+        for i, L in enumerate(self.layers):
+            m = L["mats"]
+            arr[i] = k2.k2_layer(
+                k2.ptr(m["wqkv"].w), k2.ptr(m["wqkv"].s), k2.ptr(m["wo"].w), k2.ptr(m["wo"].s),
+                k2.ptr(m["wgu"].w), k2.ptr(m["wgu"].s), k2.ptr(m["wd"].w), k2.ptr(m["wd"].s),
+                k2.ptr(L["g_in"]), k2.ptr(L["g_post"]), k2.ptr(L["kc"]), k2.ptr(L["vc"]),
+                k2.ptr(L["ks"]), k2.ptr(L["vs"]))
+        self._layers_arr = arr
+        self.model = k2.k2_model(c, k2.ptr(self.embed), k2.ptr(self.lm.w), k2.ptr(self.lm.s),
+                                 k2.ptr(self.g_final), k2.ptr(self.rope),
+                                 C.cast(arr, C.POINTER(k2.k2_layer)), k2.ptr(self.ws), ws_bytes)
+        k2.check(k2.k2_model_check(self.model))
+        self.logits = torch.zeros(cfg.vocab, dtype=torch.float32, device=self.device)
+        self.next = torch.zeros(1, dtype=torch.int32, device=self.device)
+
+    # ------------------------------------------------------------------
+    def weight_bytes(self) -> int:
+        """Bytes of projection and lm_head weights read by one full step."""
+        n = self.lm.nbytes
+        for L in self.layers:
+            n += sum(m.nbytes for m in L["mats"].values())
+        return n
+
+    def step(self, token: int, pos: int, want_logits: bool = True, stream=None):
+        """Enqueue one position (host token).  Returns the device tensors
+        (logits, next) when want_logits, else (None, None)."""
+        lg = self.logits if want_logits else None
+        nx = self.next if want_logits else None
+        k2.check(k2.k2_decode_step(self.model, token, pos, lg, nx, stream))
+        return lg, nx
+
+    def step_dev(self, d_token: torch.Tensor, pos: int, d_next: torch.Tensor,
+                 d_err: Optional[torch.Tensor] = None, want_logits: bool = True, stream=None):
+        lg = self.logits if want_logits else None
+        k2.check(k2.k2_decode_step_dev(self.model, d_token, pos, lg, d_next, d_err, stream))
+        return lg
+
+    def generate(self, prompt, n_decode: int, teacher=None, collect_logits: bool = True):
+        """Greedy run on the device: the prompt positions skip the head, the
+        last prompt position and every decode position emit an argmax.  With
+        ``teacher`` the fed tokens come from it (teacher forcing).  Returns
+        (tokens, [logits as CPU fp32 arrays])."""
+        cfg = self.cfg
+        P = len(prompt)
+        n_decode = min(n_decode, cfg.cap - P)
+        toks, lgs = [], []
+        for p, t in enumerate(prompt):
+            last = p == P - 1
+            self.step(int(t), p, want_logits=last)
+        torch.cuda.synchronize()
+        toks.append(int(self.next.item()))
+        if collect_logits:
+            lgs.append(self.logits.cpu().numpy().copy())
+        for i in range(n_decode - 1):
+            feed = toks[-1] if teacher is None else int(teacher[i])
+            self.step(feed, P + i)
+            torch.cuda.synchronize()
+            toks.append(int(self.next.item()))
+            if collect_logits:
+                lgs.append(self.logits.cpu().numpy().copy())
+        return toks, lgs

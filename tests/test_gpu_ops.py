@@ -1,0 +1,354 @@
+"""GPU parity of every single operation of libk2 against the CPU oracle, on
+the same seeded inputs.  Integer work (quantizer codes, scales, KV-cache
+codes, argmax indices) must be bit-exact; fp32 arithmetic must fall inside
+bounds derived from fp32 accumulation against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+from helpers import DEV, GPU, bf16_draw, say, sumabs_bound, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+if GPU:
+    from quantized_gemv_gqa_decode_amd import k2
+    from quantized_gemv_gqa_decode_amd.k2 import check
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------- quantizers ---
+
+@pytest.mark.parametrize("N,K", [(1, 32), (37, 96), (130, 2560), (6144, 2560)])
+def test_quantize_fp8_rows_bit_exact(N, K):
+    say(f"fp8 quantizer N={N} K={K}")
+    w = bf16_draw((N, K), seed=N + K)
+    if N > 3:
+        w[3] = 0                                 # zero row
+        w[2, 5] = 0x8000                         # -0.0
+    codes_o, s_o = oracle.quant_fp8_rows(w)
+    W = to_dev(w)
+    codes = torch.empty((N, K), dtype=torch.uint8, device=DEV)
+    s = torch.empty(N, dtype=torch.float32, device=DEV)
+    check(k2.k2_quantize_fp8_rows(W, codes, s, N, K))
+    sync()
+    assert np.array_equal(to_host(s).view(np.uint32), s_o.view(np.uint32))
+    assert np.array_equal(to_host(codes), codes_o)
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (37, 96), (130, 2560), (512, 3584)])
+def test_quantize_mxfp4_bit_exact(N, K):
+    say(f"mxfp4 quantizer N={N} K={K}")
+    w = bf16_draw((N, K), seed=3 * N + K)
+    if N > 3:
+        w[2, 32:64] = 0                          # zero block
+        w[3, 7] = 0x8000                         # -0.0
+        w[1, 0:32] = bf16_draw((1, 32), std=40.0, seed=9)[0]   # large block
+    q_o, e_o = oracle.quant_mxfp4(w)
+    W = to_dev(w)
+    q = torch.empty((N, K // 2), dtype=torch.uint8, device=DEV)
+    e = torch.empty((N, K // 32), dtype=torch.uint8, device=DEV)
+    check(k2.k2_quantize_mxfp4(W, q, e, N, K))
+    sync()
+    assert np.array_equal(to_host(e), e_o)
+    assert np.array_equal(to_host(q), q_o)
+
+
+# --------------------------------------------------- decoders (lane layout) ---
+
+def test_fp8_decode_every_code_via_gemv():
+    """A one-hot x reads one column of the dequantized matrix exactly: every
+    finite E4M3FN code in every column position of a 16-byte chunk."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    K = 256
+    row = np.zeros(K, np.uint8)
+    row[:codes.size] = codes
+    N = 4
+    W = np.stack([np.roll(row, 16 * i) for i in range(N)])
+    scale = np.array([1.0, 0.5, 3.0, 2.0 ** -9], np.float32)
+    Wd, Sd = to_dev(W), to_dev(scale)
+    y = torch.empty(N, dtype=torch.float32, device=DEV)
+    for k in range(K):
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        check(k2.k2_gemv_qfp8(Wd, Sd, to_dev(x), y, None, N, K, 1))
+        got = to_host(y)
+        want = np.array([np.float32(oracle.fp8_value(W[n, k])[()] * scale[n]) for n in range(N)])
+        assert np.array_equal(got, want), (k, got, want)
+
+
+def test_mxfp4_decode_every_nibble_via_gemv():
+    K = 512
+    byts = np.arange(256, dtype=np.uint8)                    # every (low, high) nibble pair
+    q = np.stack([byts, np.roll(byts, 7)])                   # 2 rows x 256 bytes = 512 columns
+    e = np.array([[127, 120, 130, 1, 200, 127, 100, 127, 127, 127, 127, 127, 127, 127, 127, 127],
+                  [126] * 16], np.uint8)
+    N = 2
+    Qd, Ed = to_dev(q), to_dev(e)
+    y = torch.empty(N, dtype=torch.float32, device=DEV)
+    for k in range(0, K, 3):
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        check(k2.k2_gemv_qmxfp4(Qd, Ed, to_dev(x), y, None, N, K, 1))
+        got = to_host(y)
+        for n in range(N):
+            b = q[n, k // 2]
+            nib = (b >> 4) if (k & 1) else (b & 15)
+            want = oracle.e2m1_value(nib)[()] * oracle.e8m0_value(e[n, k // 32])[()]
+            assert got[n] == np.float32(want), (n, k, got[n], want)
+
+
+# -------------------------------------------------------------------- GEMV ---
+
+def _mat_and_dense(wdt, N, K, seed):
+    draw = bf16_draw((N, K), seed=seed) if wdt != "f32" else \
+        (np.random.default_rng(seed).standard_normal((N, K)) * 0.02).astype(np.float32)
+    m = oracle.Mat.from_draw(wdt, draw)
+    # dense dequantized weights from torch's own decoders (for the error bound)
+    dense = brute.dequant(m.dtype, m.w, m.s).numpy()
+    return m, dense
+
+
+def _gemv_call(wdt, m, X, Y, R, N, K, B):
+    if wdt == "f32":
+        return k2.k2_gemv_f32(to_dev(m.w), X, Y, R, N, K, B)
+    if wdt == "bf16":
+        return k2.k2_gemv_qbf16(to_dev(m.w), X, Y, R, N, K, B)
+    if wdt == "fp8":
+        return k2.k2_gemv_qfp8(to_dev(m.w), to_dev(m.s), X, Y, R, N, K, B)
+    return k2.k2_gemv_qmxfp4(to_dev(m.w), to_dev(m.s), X, Y, R, N, K, B)
+
+
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("N,K,B", [(1, 32, 1), (37, 96, 1), (131, 640, 1), (517, 2560, 1),
+                                   (70, 4096, 1), (33, 10240, 1), (45, 320, 2), (19, 1024, 4),
+                                   (23, 1536, 8)])
+def test_gemv_matches_oracle(wdt, N, K, B):
+    say(f"gemv {wdt} N={N} K={K} B={B}")
+    m, dense = _mat_and_dense(wdt, N, K, seed=N * 31 + K)
+    rng = np.random.default_rng(K + B)
+    x = rng.standard_normal((B, K)).astype(np.float32)
+    res = rng.standard_normal((B, N)).astype(np.float32)
+    X = to_dev(x)
+    Y = torch.full((B, N), float("nan"), dtype=torch.float32, device=DEV)
+    check(_gemv_call(wdt, m, X, Y, None, N, K, B))
+    Yr = to_dev(res)
+    check(_gemv_call(wdt, m, X, Yr, Yr, N, K, B))         # in-place residual
+    sync()
+    got, got_r = to_host(Y), to_host(Yr)
+    for b in range(B):
+        ref = m.matvec(x[b].astype(np.float64))
+        tol = sumabs_bound(dense, x[b].astype(np.float64))
+        assert np.all(np.abs(got[b] - ref) <= tol), (b, np.abs(got[b] - ref).max())
+        assert np.all(np.abs(got_r[b] - (ref + res[b])) <= tol + 2.0 ** -23 * np.abs(ref + res[b]))
+
+
+def test_gemv_rejects_bad_args_without_writing():
+    N, K = 8, 64
+    W = torch.zeros((N, K), dtype=torch.int16, device=DEV)
+    x = torch.zeros(K, dtype=torch.float32, device=DEV)
+    y = torch.full((N,), 7.0, device=DEV)
+    assert k2.k2_gemv_qbf16(W, x, y, None, N, 48, 1) == k2.K2_EUNSUPPORTED
+    assert k2.k2_gemv_qbf16(W, x, y, None, 0, K, 1) == k2.K2_EINVAL
+    assert k2.k2_gemv_qbf16(W, x, y, None, N, K, 3) == k2.K2_EUNSUPPORTED
+    assert k2.k2_gemv_qbf16(k2.ptr(W) + 2, x, y, None, N, K, 1) == k2.K2_EINVAL
+    assert k2.k2_gemv_qfp8(W, None, x, y, None, N, K, 1) == k2.K2_EINVAL
+    sync()
+    assert torch.all(y == 7.0)
+
+
+# ---------------------------------------------------------------- RMSNorm ---
+
+@pytest.mark.parametrize("rows,H,G", [(1, 64, 2), (3, 2560, 2), (2, 3584, 1), (1, 96, 3)])
+def test_rmsnorm_grouped(rows, H, G):
+    rng = np.random.default_rng(H)
+    x = rng.standard_normal((rows, H)).astype(np.float32) * 3
+    g = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    y = torch.empty((rows, H), dtype=torch.float32, device=DEV)
+    check(k2.k2_rmsnorm_grouped(to_dev(x), to_dev(g), y, rows, H, G, 1e-6))
+    sync()
+    got = to_host(y)
+    for r in range(rows):
+        ref = oracle.rmsnorm_grouped(x[r], g, G, 1e-6)
+        assert np.allclose(got[r], ref, rtol=2e-6, atol=1e-6)
+
+
+# ------------------------------------------------------------------- RoPE ---
+
+@pytest.mark.parametrize("hd,cap", [(16, 64), (128, 32768)])
+def test_rope_table_and_rotation(hd, cap):
+    cs = torch.empty((cap, hd // 2, 2), dtype=torch.float32, device=DEV)
+    check(k2.k2_rope_table(cs, cap, hd, 1e4))
+    sync()
+    t = to_host(cs)
+    for p in (0, 1, cap // 3, cap - 1):
+        ang = p * 1e4 ** (-2.0 * np.arange(hd // 2) / hd)
+        assert np.allclose(t[p, :, 0], np.cos(ang), atol=2e-7, rtol=0)
+        assert np.allclose(t[p, :, 1], np.sin(ang), atol=2e-7, rtol=0)
+    nq, nkv = 8, 2
+    rng = np.random.default_rng(hd)
+    q = rng.standard_normal(nq * hd).astype(np.float32)
+    k = rng.standard_normal(nkv * hd).astype(np.float32)
+    for pos in (0, 5, cap - 1):
+        Q, Kt = to_dev(q), to_dev(k)
+        check(k2.k2_rope(Q, Kt, cs, nq, nkv, hd, pos, cap))
+        sync()
+        rq = oracle.rope(q.astype(np.float64), nq, hd, pos, 1e4)
+        rk = oracle.rope(k.astype(np.float64), nkv, hd, pos, 1e4)
+        # table entries within 2^-24 plus fp32 arithmetic; angle rounded once in fp64
+        assert np.allclose(to_host(Q), rq, atol=3e-6 * (1 + np.abs(q).max()), rtol=0)
+        assert np.allclose(to_host(Kt), rk, atol=3e-6 * (1 + np.abs(k).max()), rtol=0)
+    assert k2.k2_rope(Q, Kt, cs, nq, nkv, hd, cap, cap) == k2.K2_ERANGE
+
+
+# --------------------------------------------------------------- KV append ---
+
+@pytest.mark.parametrize("kvdt", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("hd", [16, 128])
+def test_kv_append_bit_exact(kvdt, hd):
+    n_kv, cap = 4, 50
+    rng = np.random.default_rng(hd)
+    oc = oracle.KVCache(kvdt, n_kv, cap, hd)
+    dt = {"f32": torch.float32, "bf16": torch.int16, "i8": torch.int8}[kvdt]
+    kc = torch.zeros((n_kv, cap, hd), dtype=dt, device=DEV)
+    vc = torch.zeros((n_kv, cap, hd), dtype=dt, device=DEV)
+    ks = torch.zeros((n_kv, cap), dtype=torch.float32, device=DEV)
+    vs = torch.zeros((n_kv, cap), dtype=torch.float32, device=DEV)
+    for pos in (0, 1, 17, cap - 1):
+        k = (rng.standard_normal(n_kv * hd) * 2).astype(np.float32)
+        v = (rng.standard_normal(n_kv * hd) * 0.5).astype(np.float32)
+        if pos == 17:
+            v[:hd] = 0.0                          # an all-zero block
+            k[3] = np.float32(127 / 64)           # hand value
+        oc.store(k.astype(np.float64), v.astype(np.float64), pos)
+        if kvdt == "i8":
+            check(k2.k2_kv_append_int8(to_dev(k), to_dev(v), kc, vc, ks, vs, n_kv, hd, cap, pos))
+        else:
+            check(k2.k2_kv_append(k2.DTYPES[kvdt], to_dev(k), to_dev(v), kc, vc, n_kv, hd, cap, pos))
+    sync()
+    view = np.uint16 if kvdt == "bf16" else None
+    assert np.array_equal(to_host(kc, view).view(oc.k.dtype), oc.k)
+    assert np.array_equal(to_host(vc, view).view(oc.v.dtype), oc.v)
+    if kvdt == "i8":
+        assert np.array_equal(to_host(ks).view(np.uint32), oc.ks.view(np.uint32))
+        assert np.array_equal(to_host(vs).view(np.uint32), oc.vs.view(np.uint32))
+    assert k2.k2_kv_append(k2.K2_F32, to_dev(k), to_dev(v), kc, vc, n_kv, hd, cap, cap) == k2.K2_ERANGE
+
+
+# --------------------------------------------------------------- attention ---
+
+def _filled_cache(kvdt, n_kv, cap, hd, L, seed):
+    rng = np.random.default_rng(seed)
+    oc = oracle.KVCache(kvdt, n_kv, cap, hd)
+    if kvdt == "i8":
+        oc.k[:, :L] = rng.integers(-127, 128, (n_kv, L, hd))
+        oc.v[:, :L] = rng.integers(-127, 128, (n_kv, L, hd))
+        oc.ks[:, :L] = np.abs(rng.standard_normal((n_kv, L)) * 0.05).astype(np.float32)
+        oc.vs[:, :L] = np.abs(rng.standard_normal((n_kv, L)) * 0.05).astype(np.float32)
+    else:
+        kk = rng.standard_normal((n_kv, L, hd))
+        vv = rng.standard_normal((n_kv, L, hd))
+        if kvdt == "f32":
+            oc.k[:, :L] = kk
+            oc.v[:, :L] = vv
+        else:
+            oc.k[:, :L] = torch.from_numpy(kk).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            oc.v[:, :L] = torch.from_numpy(vv).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return oc
+
+
+def _dev_cache(oc):
+    return to_dev(oc.k), to_dev(oc.v), to_dev(oc.ks), to_dev(oc.vs)
+
+
+@pytest.mark.parametrize("kvdt", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("hd,n_qh,n_kv", [(128, 32, 8), (16, 4, 2), (128, 8, 8), (64, 16, 2)])
+@pytest.mark.parametrize("L", [1, 5, 33, 100, 777, 5000])
+def test_gqa_decode_attn_matches_oracle(kvdt, hd, n_qh, n_kv, L):
+    say(f"attn {kvdt} hd={hd} {n_qh}/{n_kv} L={L}")
+    cap = max(L, 8) + 3
+    oc = _filled_cache(kvdt, n_kv, cap, hd, L, seed=L + hd)
+    rng = np.random.default_rng(L)
+    q = rng.standard_normal(n_qh * hd).astype(np.float32) * 2
+    ref = oracle.attention(q.astype(np.float64), oc, n_qh, L)
+    ws_b = k2.k2_attn_workspace_bytes(n_qh, n_kv, hd, cap)
+    ws = torch.zeros(ws_b, dtype=torch.uint8, device=DEV)
+    out = torch.empty(n_qh * hd, dtype=torch.float32, device=DEV)
+    kc, vc, ks, vs = _dev_cache(oc)
+    for rep in range(2):                                     # the workspace stays reusable
+        check(k2.k2_gqa_decode_attn(k2.DTYPES[kvdt], to_dev(q), kc, vc, ks, vs, out, n_qh, n_kv,
+                                    hd, cap, L, 1.0 / math.sqrt(hd), ws, ws_b))
+        sync()
+        got = to_host(out)
+        vmax = np.abs(oc.dequant("v", L)).max()
+        assert np.abs(got - ref).max() <= 2e-5 * vmax + 1e-6, np.abs(got - ref).max()
+
+
+@pytest.mark.parametrize("kvdt", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("hd,n_qh,n_kv", [(128, 32, 8), (16, 4, 2)])
+@pytest.mark.parametrize("pos", [0, 31, 32, 700])
+def test_rope_append_attn_matches_oracle(kvdt, hd, n_qh, n_kv, pos):
+    say(f"fused attn {kvdt} hd={hd} pos={pos}")
+    cap = pos + 5
+    oc = _filled_cache(kvdt, n_kv, cap, hd, pos, seed=pos + 7)
+    rng = np.random.default_rng(pos)
+    qkv = (rng.standard_normal((n_qh + 2 * n_kv) * hd) * 1.5).astype(np.float32)
+    cs = torch.empty((cap, hd // 2, 2), dtype=torch.float32, device=DEV)
+    check(k2.k2_rope_table(cs, cap, hd, 1e4))
+    # oracle: rotate in fp64, store, attend
+    q = oracle.rope(qkv[: n_qh * hd].astype(np.float64), n_qh, hd, pos, 1e4)
+    k = oracle.rope(qkv[n_qh * hd:(n_qh + n_kv) * hd].astype(np.float64), n_kv, hd, pos, 1e4)
+    v = qkv[(n_qh + n_kv) * hd:].astype(np.float64)
+    kc, vc, ks, vs = _dev_cache(oc)
+    oc.store(k, v, pos)
+    ref = oracle.attention(q, oc, n_qh, pos + 1)
+    ws_b = k2.k2_attn_workspace_bytes(n_qh, n_kv, hd, cap)
+    ws = torch.zeros(ws_b, dtype=torch.uint8, device=DEV)
+    out = torch.empty(n_qh * hd, dtype=torch.float32, device=DEV)
+    check(k2.k2_rope_append_attn(k2.DTYPES[kvdt], to_dev(qkv), cs, kc, vc, ks, vs, out, n_qh,
+                                 n_kv, hd, cap, pos, ws, ws_b))
+    sync()
+    got = to_host(out)
+    vmax = np.abs(oc.dequant("v", pos + 1)).max()
+    # int8 codes of the new position may differ by one step where fp32 vs fp64
+    # rotation lands on a rounding boundary: allow one code step there
+    step = (np.abs(v).max() / 127) if kvdt == "i8" else 0.0
+    assert np.abs(got - ref).max() <= 5e-5 * vmax + 2 * step + 1e-5, np.abs(got - ref).max()
+    # the stored new position: same format, values within one storage step
+    view = np.uint16 if kvdt == "bf16" else None
+    gk = to_host(kc, view).view(oc.k.dtype)
+    gv = to_host(vc, view).view(oc.v.dtype)
+    assert np.array_equal(gk[:, :pos], oc.k[:, :pos]) and np.array_equal(gv[:, :pos], oc.v[:, :pos])
+    if kvdt == "i8":
+        assert np.abs(gk[:, pos].astype(int) - oc.k[:, pos].astype(int)).max() <= 1
+        assert np.array_equal(gv[:, pos], oc.v[:, pos])        # v is not rotated: same fp32 input
+    elif kvdt == "f32":
+        assert np.allclose(gk[:, pos], oc.k[:, pos], rtol=1e-5, atol=1e-5)
+        assert np.array_equal(gv[:, pos], oc.v[:, pos])
+    else:
+        a = (gk[:, pos].astype(np.uint32) << 16).view(np.float32)
+        b = (oc.k[:, pos].astype(np.uint32) << 16).view(np.float32)
+        assert np.allclose(a, b, rtol=2 ** -7, atol=1e-6)
+        assert np.array_equal(gv[:, pos], oc.v[:, pos])
+
+
+# ------------------------------------------------------------------ argmax ---
+
+@pytest.mark.parametrize("n", [1, 7, 255, 256, 257, 250624])
+def test_argmax_first_max(n):
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal(n).astype(np.float32)
+    if n > 10:
+        x[n // 3] = x[n - 2] = x.max() + 1.0                 # a tie: lowest index wins
+    ws_b = k2.k2_argmax_workspace_bytes(n)
+    ws = torch.zeros(ws_b, dtype=torch.uint8, device=DEV)
+    out = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    for _ in range(2):
+        check(k2.k2_argmax(to_dev(x), n, out, ws, ws_b))
+        sync()
+        assert int(out.item()) == oracle.argmax(x.astype(np.float64))
