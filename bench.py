@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Batch-1 greedy decode throughput on one MI355X, with the roofline of the
+dominant kernel and the fp64 CPU oracle timed beside it.
+
+Default workload: the K2-Horizon-3.7B-shaped dense decoder (hidden 2560,
+36 layers, 32 q / 8 kv heads, head_dim 128, SwiGLU 10240, vocab 250624,
+untied lm_head) with seeded random bf16 weights 0.02*N(0,1), a bf16 KV cache
+of context 4096 and a 512-token uniform-random prompt.  One step is one
+decode position: embedding, 36 layers (norm + QKV, RoPE + KV append + GQA
+attention, O + residual, norm + gate/up + SwiGLU, down + residual), final
+norm, lm_head and argmax, with the argmax fed back on the device.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def step_bytes(cfg, L: int, weight_bytes: int) -> int:
+    """Algorithmic HBM bytes of one decode position at prefix length L:
+    every projection and the lm_head once, the KV prefix of every layer once,
+    the new K/V row, the embedding row, the norm gains and the logits."""
+    kv_elem = {"f32": 4, "bf16": 2, "i8": 1}[cfg.kvdt]
+    kv_row = 2 * cfg.n_kv * cfg.head_dim * kv_elem + (2 * cfg.n_kv * 4 if cfg.kvdt == "i8" else 0)
+    emb = cfg.hidden * (4 if cfg.embed_dt == "f32" else 2)
+    gains = (2 * cfg.n_layers + 1) * cfg.hidden * 4
+    return (weight_bytes + cfg.n_layers * kv_row * L + emb + gains + cfg.vocab * 4)
+
+
+def time_kernel(fn, n_launch: int, stream) -> float:
+    """Average duration (ms) of `n_launch` back-to-back launches issued by fn(i).
+
+    The launches are captured once into a HIP graph so that host issue cost
+    does not enter the measurement; the replay is bracketed by HIP events on
+    the stream it runs on."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.graph(g, stream=cap):
+        for i in range(n_launch):
+            fn(i)
+    stream.wait_stream(cap)
+    with torch.cuda.stream(stream):
+        g.replay()                                   # warm
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record(stream)
+        g.replay()
+        e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e) / n_launch
+
+
+def kernel_table(gm, stream, reps: int):
+    """Per-kernel average duration and algorithmic bytes for the projection
+    kernels of the step, launched exactly as k2_decode_step launches them,
+    rotating over the layers so no launch finds its weights in a cache."""
+    import torch
+    from quantized_gemv_gqa_decode_amd import k2
+    cfg = gm.cfg
+    dev = gm.device
+    H, I = cfg.hidden, cfg.inter
+    qd = cfg.n_qh * cfg.head_dim
+    wdt = k2.DTYPES[cfg.wdt]
+    h = torch.randn(H, device=dev) * 0.5
+    hb = torch.empty_like(h)
+    x_o = torch.randn(qd, device=dev)
+    x_d = torch.randn(I, device=dev)
+    qkv = torch.empty(cfg.qkv_rows, device=dev)
+    act = torch.empty(I, device=dev)
+    logits = torch.empty(cfg.vocab, device=dev)
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    am_b = k2.k2_argmax_workspace_bytes(cfg.vocab)
+    am_ws = torch.zeros(am_b, dtype=torch.uint8, device=dev)
+    Ls = gm.layers
+    nl = len(Ls)
+
+    def mats(i, name):
+        m = Ls[i % nl]["mats"][name]
+        return m.w, m.s, m.nbytes
+
+    def gemv_plain(m, x, y, N, K):
+        w, s, _ = m
+        if cfg.wdt == "bf16":
+            return k2.k2_gemv_qbf16(w, x, y, y, N, K, 1)
+        if cfg.wdt == "f32":
+            return k2.k2_gemv_f32(w, x, y, y, N, K, 1)
+        if cfg.wdt == "fp8":
+            return k2.k2_gemv_qfp8(w, s, x, y, y, N, K, 1)
+        return k2.k2_gemv_qmxfp4(w, s, x, y, y, N, K, 1)
+
+    n = reps * nl
+    out = {}
+    ms = time_kernel(lambda i: k2.k2_norm_gemv(wdt, mats(i, "wqkv")[0], mats(i, "wqkv")[1], h,
+                                               Ls[i % nl]["g_in"], cfg.groups, cfg.eps, qkv,
+                                               cfg.qkv_rows, H), n, stream)
+    out["qkv_norm_gemv"] = (ms, mats(0, "wqkv")[2] + 2 * H * 4 + cfg.qkv_rows * 4)
+    ms = time_kernel(lambda i: gemv_plain(mats(i, "wo"), x_o, hb, H, qd), n, stream)
+    out["o_gemv_residual"] = (ms, mats(0, "wo")[2] + qd * 4 + 2 * H * 4)
+    ms = time_kernel(lambda i: k2.k2_norm_gemv_swiglu(wdt, mats(i, "wgu")[0], mats(i, "wgu")[1], h,
+                                                      Ls[i % nl]["g_post"], cfg.groups, cfg.eps,
+                                                      act, I, H), n, stream)
+    out["gate_up_norm_gemv_swiglu"] = (ms, mats(0, "wgu")[2] + 2 * H * 4 + I * 4)
+    ms = time_kernel(lambda i: gemv_plain(mats(i, "wd"), x_d, hb, H, I), n, stream)
+    out["down_gemv_residual"] = (ms, mats(0, "wd")[2] + I * 4 + 2 * H * 4)
+    nlm = max(4, reps)
+    ms = time_kernel(lambda i: k2.k2_norm_gemv_argmax(wdt, gm.lm.w, gm.lm.s, h, gm.g_final,
+                                                      cfg.groups, cfg.eps, logits, cfg.vocab, H,
+                                                      nxt, am_ws, am_b), nlm, stream)
+    out["lm_head_norm_gemv_argmax"] = (ms, gm.lm.nbytes + 2 * H * 4 + cfg.vocab * 4)
+    torch.cuda.synchronize()
+    return out
+
+
+def cpu_baseline(cfg, budget_s: float):
+    """The oracle as it stands (fp64, OpenMP over rows) on this host's cores,
+    on a bounded sample of the same workload: full decode positions 0..n-1 of
+    the whole model, n chosen so the sample takes about budget_s seconds."""
+    import numpy as np
+    import oracle
+    import synth
+    log("cpu baseline: drawing oracle weights")
+    dec = oracle.Decoder.from_synth(cfg)
+    pr = synth.prompt(cfg)
+    t0 = time.perf_counter()
+    dec.step(int(pr[0]), 0, want_logits=True)
+    t1 = time.perf_counter() - t0
+    n = int(max(1, min(16, budget_s / max(t1, 1e-6))))
+    t0 = time.perf_counter()
+    for p in range(1, n + 1):
+        dec.step(int(pr[p]), p, want_logits=True)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} full decode positions (1..{n}) of the whole model incl. lm_head, "
+                      f"fp64 oracle, after one untimed position; {dt:.1f} s",
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", default="k2h-3.7b-bf16-kvbf16-ctx4096")
+    ap.add_argument("--prompt-len", type=int, default=None)
+    ap.add_argument("--kernel-reps", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs the decode path on one GPU only; "
+                                   "--gpus must be 1 (multi-GPU sharding is a design note)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from quantized_gemv_gqa_decode_amd import k2
+    from quantized_gemv_gqa_decode_amd.model import DecodeModel
+
+    cfg = synth.CONFIGS[args.config]
+    P = cfg.prompt_len if args.prompt_len is None else args.prompt_len
+    W, K = args.warmup, args.steps
+    if P + W + K > cfg.cap:
+        sys.exit(f"prompt {P} + warmup {W} + steps {K} exceeds the context {cfg.cap}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    k2.load(build_if_missing=False)
+
+    log(f"building {cfg.name} on {torch.cuda.get_device_name(dev)}")
+    t0 = time.perf_counter()
+    gm = DecodeModel(cfg, dev)
+    torch.cuda.synchronize()
+    log(f"model ready in {time.perf_counter() - t0:.1f} s, weights {gm.weight_bytes() / 1e9:.3f} GB")
+    stream = torch.cuda.current_stream()
+
+    prompt = synth.prompt(cfg, P)
+    t0 = time.perf_counter()
+    for p, t in enumerate(prompt):
+        gm.step(int(t), p, want_logits=(p == P - 1))
+    torch.cuda.synchronize()
+    log(f"prefill of {P} positions (as decode steps) in {time.perf_counter() - t0:.2f} s")
+
+    hist = torch.zeros(W + K + 1, dtype=torch.int32, device=dev)
+    hist[0:1].copy_(gm.next)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    for j in range(W):
+        gm.step_dev(hist[j:j + 1], P + j, hist[j + 1:j + 2], err)
+    torch.cuda.synchronize()
+
+    ev_s = torch.cuda.Event(enable_timing=True)
+    ev_e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev_s.record(stream)
+    for j in range(W, W + K):
+        gm.step_dev(hist[j:j + 1], P + j, hist[j + 1:j + 2], err)
+    ev_e.record(stream)
+    ev_e.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev_s.elapsed_time(ev_e)
+    ms_step = ms_total / K
+    if int(err.item()) != 0:
+        sys.exit(f"device error flag {int(err.item())}")
+    toks = hist.cpu().numpy().tolist()
+    log(f"{K} steps: {ms_step * 1000:.1f} us/step (events), wall {wall / K * 1e6:.1f} us/step")
+
+    Lavg = P + W + (K + 1) / 2.0
+    wb = gm.weight_bytes()
+    sb = step_bytes(cfg, int(round(Lavg)), wb)
+    step_gbps = sb / (ms_step * 1e-3) / 1e9
+
+    log("per-kernel timing")
+    kt = kernel_table(gm, stream, args.kernel_reps)
+    per_step_share = {
+        "qkv_norm_gemv": cfg.n_layers, "o_gemv_residual": cfg.n_layers,
+        "gate_up_norm_gemv_swiglu": cfg.n_layers, "down_gemv_residual": cfg.n_layers,
+        "lm_head_norm_gemv_argmax": 1}
+    kernels = {}
+    for name, (ms, nbytes) in kt.items():
+        kernels[name] = {"us": round(ms * 1000, 2), "bytes": nbytes,
+                         "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                         "us_per_step": round(ms * 1000 * per_step_share[name], 1)}
+    dom = max(kernels, key=lambda k: kernels[k]["us_per_step"])
+    d = kernels[dom]
+    achieved = d["GBps"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        try:
+            cpu = cpu_baseline(cfg, args.cpu_budget)
+        except MemoryError as e:  # pragma: no cover
+            cpu = {"error": str(e)}
+
+    out = {
+        "metric": "decode tokens/s at batch 1 (3.7B-shaped) + achieved HBM GB/s vs peak",
+        "value": round(1000.0 / ms_step, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "weights": cfg.wdt, "kv_cache": cfg.kvdt,
+                   "prompt_len": P, "context": cfg.cap, "layers": cfg.n_layers,
+                   "hidden": cfg.hidden, "vocab": cfg.vocab, "batch": 1,
+                   "prefix_len_mean": Lavg},
+        "step_bytes": sb,
+        "step_GBps": round(step_gbps, 1),
+        "step_frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "bytes_per_launch": d["bytes"], "us_per_launch": d["us"], "traffic": None},
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "tokens_head": toks[:8],
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -131,6 +131,25 @@ int k2_gemv_qmxfp4(const uint8_t *Wq, const uint8_t *We8m0, const float *x, floa
 int k2_gemv_f32(const float *W, const float *x, float *y, const float *residual, int N,
                 int K, int B, void *stream);
 
+/* Fused projection forms used by k2_decode_step (one kernel each), with
+ * x = GroupedRMSNorm(h; gamma, groups, eps) computed in the prologue:
+ *   k2_norm_gemv:        y = W_hat x                       (QKV projection)
+ *   k2_norm_gemv_swiglu: act = silu(W_hat[0:inter] x) * W_hat[inter:2 inter] x
+ *                        ([k2-burn] SwiGLU MLP: gate rows, then up rows)
+ *   k2_norm_gemv_argmax: logits = W_hat x and out_idx = first-maximum argmax
+ *                        (final norm + untied lm_head); ws as k2_argmax.
+ * W/S in the formats of the k2_gemv_* calls (S: row scales for fp8, E8M0 for
+ * MXFP4, NULL otherwise).  h: [K]; K % 32 == 0, K <= 12288, groups <= 8,
+ * K % (4 groups) == 0. */
+int k2_norm_gemv(k2_dtype wdt, const void *W, const void *S, const float *h, const float *gamma,
+                 int groups, float eps, float *y, int N, int K, void *stream);
+int k2_norm_gemv_swiglu(k2_dtype wdt, const void *W, const void *S, const float *h,
+                        const float *gamma, int groups, float eps, float *act, int inter, int K,
+                        void *stream);
+int k2_norm_gemv_argmax(k2_dtype wdt, const void *W, const void *S, const float *h,
+                        const float *gamma, int groups, float eps, float *logits, int N, int K,
+                        int32_t *out_idx, void *ws, size_t ws_bytes, void *stream);
+
 /* RoPE table for split-half rotary embedding ([k2-burn] "Working end to
  * end"; the table is sized by the context window, "KV cache storage"):
  * cos_sin[p][i][0] = cos(p * theta^(-2i/head_dim)), [1] = sin(...), for

@@ -373,3 +373,68 @@ extern "C" int k2_gemv_f32(const float *W, const float *x, float *y, const float
 {
     return gemv_entry(K2_F32, W, nullptr, x, y, residual, N, K, B, stream);
 }
+
+// Fused projection forms of the decode step, x = GroupedRMSNorm(h).
+static int norm_gemv_check(int wdt, const void *W, const void *S, const float *h, const float *gamma,
+                           int groups, const float *y, int N, int K)
+{
+    if (!k2_ptr_ok(W) || !k2_ptr_ok(h) || !k2_ptr_ok(gamma) || !k2_ptr_ok(y)) return K2_EINVAL;
+    if ((wdt == K2_FP8E4M3 || wdt == K2_MXFP4) && !S) return K2_EINVAL;
+    if (N <= 0 || K <= 0 || groups <= 0) return K2_EINVAL;
+    if (wdt != K2_F32 && wdt != K2_BF16 && wdt != K2_FP8E4M3 && wdt != K2_MXFP4) return K2_EUNSUPPORTED;
+    if (K % 32 || K > K2_MAX_LDS_FLOATS || groups > K2_MAX_GROUPS || K % (4 * groups))
+        return K2_EUNSUPPORTED;
+    return K2_OK;
+}
+
+static GemvArgs norm_args(const void *W, const void *S, const float *h, const float *gamma, int groups,
+                          float eps, float *y, int N, int K)
+{
+    GemvArgs a{};
+    a.W = W;
+    a.Sf = (const float *)S;
+    a.S8 = (const uint8_t *)S;
+    a.x = h;
+    a.gamma = gamma;
+    a.groups = groups;
+    a.eps = eps;
+    a.y = y;
+    a.N = N;
+    a.K = K;
+    a.B = 1;
+    return a;
+}
+
+extern "C" int k2_norm_gemv(k2_dtype wdt, const void *W, const void *S, const float *h,
+                            const float *gamma, int groups, float eps, float *y, int N, int K,
+                            void *stream)
+{
+    int rc = norm_gemv_check(wdt, W, S, h, gamma, groups, y, N, K);
+    if (rc) return rc;
+    return gemv_dispatch(wdt, norm_args(W, S, h, gamma, groups, eps, y, N, K), PRO_NORM, EPI_PLAIN,
+                         k2_stream(stream));
+}
+
+extern "C" int k2_norm_gemv_swiglu(k2_dtype wdt, const void *W, const void *S, const float *h,
+                                   const float *gamma, int groups, float eps, float *act, int inter,
+                                   int K, void *stream)
+{
+    int rc = norm_gemv_check(wdt, W, S, h, gamma, groups, act, 2 * inter, K);
+    if (rc) return rc;
+    GemvArgs a = norm_args(W, S, h, gamma, groups, eps, act, 2 * inter, K);
+    a.n_out = inter;
+    return gemv_dispatch(wdt, a, PRO_NORM, EPI_SWIGLU, k2_stream(stream));
+}
+
+extern "C" int k2_norm_gemv_argmax(k2_dtype wdt, const void *W, const void *S, const float *h,
+                                   const float *gamma, int groups, float eps, float *logits, int N,
+                                   int K, int32_t *out_idx, void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = norm_gemv_check(wdt, W, S, h, gamma, groups, logits, N, K);
+    if (rc) return rc;
+    if (!out_idx || !ws || ((uintptr_t)ws & 255u) || ws_bytes < argmax_ws_bytes()) return K2_EINVAL;
+    GemvArgs a = norm_args(W, S, h, gamma, groups, eps, logits, N, K);
+    argmax_ws_carve(ws, a.am);
+    a.am.out_idx = out_idx;
+    return gemv_dispatch(wdt, a, PRO_NORM, EPI_ARGMAX, k2_stream(stream));
+}

@@ -59,6 +59,9 @@ SIGNATURES = {
     "k2_gemv_qfp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "k2_gemv_qmxfp4": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "k2_gemv_f32": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
+    "k2_norm_gemv": (_i, [_i, _vp, _vp, _vp, _vp, _i, _f, _vp, _i, _i, _vp]),
+    "k2_norm_gemv_swiglu": (_i, [_i, _vp, _vp, _vp, _vp, _i, _f, _vp, _i, _i, _vp]),
+    "k2_norm_gemv_argmax": (_i, [_i, _vp, _vp, _vp, _vp, _i, _f, _vp, _i, _i, _vp, _vp, _sz, _vp]),
     "k2_rope_table": (_i, [_vp, _i, _i, _d, _vp]),
     "k2_rope": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "k2_kv_append": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
@@ -145,6 +148,23 @@ def k2_gemv_qmxfp4(Wq, We8m0, x, y, residual, N, K, B, stream=None):
 
 def k2_gemv_f32(W, x, y, residual, N, K, B, stream=None):
     return load().k2_gemv_f32(ptr(W), ptr(x), ptr(y), ptr(residual), N, K, B, stream_handle(stream))
+
+
+def k2_norm_gemv(wdt, W, S, h, gamma, groups, eps, y, N, K, stream=None):
+    return load().k2_norm_gemv(wdt, ptr(W), ptr(S), ptr(h), ptr(gamma), groups, eps, ptr(y), N, K,
+                               stream_handle(stream))
+
+
+def k2_norm_gemv_swiglu(wdt, W, S, h, gamma, groups, eps, act, inter, K, stream=None):
+    return load().k2_norm_gemv_swiglu(wdt, ptr(W), ptr(S), ptr(h), ptr(gamma), groups, eps, ptr(act),
+                                      inter, K, stream_handle(stream))
+
+
+def k2_norm_gemv_argmax(wdt, W, S, h, gamma, groups, eps, logits, N, K, out_idx, ws, ws_bytes,
+                        stream=None):
+    return load().k2_norm_gemv_argmax(wdt, ptr(W), ptr(S), ptr(h), ptr(gamma), groups, eps,
+                                      ptr(logits), N, K, ptr(out_idx), ptr(ws), ws_bytes,
+                                      stream_handle(stream))
 
 
 def k2_rope_table(cos_sin, cap, head_dim, theta, stream=None):
