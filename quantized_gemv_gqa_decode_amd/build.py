@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libk2.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["gemv.hip", "attn.hip", "misc.hip", "decode.hip", "moe.hip"]
+SOURCES = ["gemv.hip", "gemv_f32.hip", "gemv_bf16.hip", "gemv_fp8.hip", "gemv_mxfp4.hip",
+           "attn.hip", "misc.hip", "decode.hip", "moe.hip"]
 ARCH = "gfx950"
 
 

@@ -11,16 +11,17 @@
 // positions [s*chunk, min(len, (s+1)*chunk)) for the rep query heads of kv
 // head g:
 //   1. the rep query heads are rotated (fused form) and scaled into LDS;
-//   2. scores: a K row of head_dim values is split over LPP lanes that each
-//      load 16 bytes, so one wave instruction covers 64/LPP positions; the
-//      int8 per-position scale multiplies the finished dot product;
-//   3. an fp32 softmax over the block's positions (max-subtracted);
-//   4. P V with the int8 value scale folded into the probability;
-//   5. with one split the normalised output is written directly; otherwise
-//      every block publishes (max, sum, unnormalised o) and the last block of
-//      the kv head to finish combines the S partials in split order (fixed
-//      order: the result is run-to-run deterministic) and re-zeroes the
-//      arrival counter.
+//   2. each wave streams its positions: a K (and V) row of head_dim values is
+//      split over LPP lanes that each load 16 bytes, so one wave instruction
+//      covers 64/LPP positions; the K and V loads of NL such slots are issued
+//      together before any arithmetic; the int8 per-position scale multiplies
+//      the finished dot product and is folded into the probability for V;
+//   3. each wave keeps an online fp32 softmax (running max, rescaled sum and
+//      accumulator); the four waves are merged through LDS;
+//   4. with one split the normalised output is written directly; otherwise
+//      every block publishes (max, sum, unnormalised o) and a second small
+//      kernel combines the S partials of each kv head in split order (fixed
+//      order: the result is run-to-run deterministic).
 // Fused form: the block holding the new position `pos` also rotates k, stores
 // k and v at slot pos in the cache format, and uses the stored (dequantized)
 // values for that position from LDS.
@@ -116,37 +117,53 @@ __device__ __forceinline__ float kv_store_head(float val, void *kc, void *vc, fl
     return stored;
 }
 
-template <int KVDT, int HD, int REP, bool FUSED>
-__global__ __launch_bounds__(K2_BLOCK) void attn_kernel(const AttnArgs a)
+template <int KVDT, int HD, int REP, bool FUSED, int WPB>
+__global__ __launch_bounds__(WPB * K2_WAVE) void attn_kernel(const AttnArgs a)
 {
     using T = typename KVT<KVDT>::T;
     constexpr int EPC = KVT<KVDT>::EPC;
     constexpr int LPP = HD / EPC;                  // lanes per position
-    constexpr int PPI = K2_WAVE / LPP;             // positions per wave instruction
-    constexpr int PPB = PPI * K2_WAVES_PER_BLOCK;  // positions per block sweep
-    constexpr int UN = 4;                          // sweeps in flight per wave
+    constexpr int PPI = K2_WAVE / LPP;             // positions per wave slot
+    constexpr int NL = EPC >= 16 ? 2 : 4;          // slots per wave per iteration
+    constexpr int NT = WPB * K2_WAVE;              // threads per block
     static_assert(LPP >= 1 && LPP <= K2_WAVE, "head_dim / dtype");
 
     __shared__ float qs[REP][HD];
-    __shared__ float sc[REP][K2_ATTN_MAX_CHUNK];
     __shared__ float newkv[2][HD];
-    __shared__ float red[K2_WAVES_PER_BLOCK][REP][HD];
-    __shared__ float ml[REP][2];
-    __shared__ float tmp4[K2_WAVES_PER_BLOCK];
-    __shared__ int is_last;
+    __shared__ float red_o[WPB][REP][HD];
+    __shared__ float red_ml[WPB][REP][2];
+    __shared__ float tmp4[WPB];
 
     const int g = blockIdx.y, s = blockIdx.x, S = gridDim.x;
     const int len = a.len;
     const int j0 = s * a.chunk;
     const int j1 = min(len, j0 + a.chunk);
-    const int n = j1 - j0;
     const bool holds_new = FUSED && (j1 == len);
     const int jc = holds_new ? j1 - 1 : j1;        // positions read from the cache
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int sub = lane / LPP, cl = lane % LPP;
 
+    const T *__restrict__ kbase = reinterpret_cast<const T *>(a.kc) + (int64_t)g * a.cap * HD;
+    const T *__restrict__ vbase = reinterpret_cast<const T *>(a.vc) + (int64_t)g * a.cap * HD;
+    // The K and V rows of the first iteration do not depend on q: issue them
+    // first (unconditionally, at a clamped valid position) so that they are in
+    // flight while q is rotated and the new position is appended.
+    k2_u4 kw[NL], vw[NL];
+    int jn[NL];
+    auto issue_kv = [&](int base) {
+#pragma unroll
+        for (int n = 0; n < NL; ++n) {
+            const int j = base + (n * WPB + wave) * PPI + sub;
+            jn[n] = j;
+            const int jj = j < jc ? j : j0;
+            kw[n] = *reinterpret_cast<const k2_u4 *>(kbase + (int64_t)jj * HD + cl * EPC);
+            vw[n] = *reinterpret_cast<const k2_u4 *>(vbase + (int64_t)jj * HD + cl * EPC);
+        }
+    };
+    issue_kv(j0);
+
     // 1. query heads of this kv head, rotated (fused) and pre-scaled
-    for (int t = tid; t < REP * HD; t += K2_BLOCK) {
+    for (int t = tid; t < REP * HD; t += NT) {
         const int hl = t / HD, d = t % HD, h = g * REP + hl;
         float val;
         if constexpr (FUSED) {
@@ -183,177 +200,201 @@ __global__ __launch_bounds__(K2_BLOCK) void attn_kernel(const AttnArgs a)
     }
     __syncthreads();
 
-    const T *__restrict__ kbase = reinterpret_cast<const T *>(a.kc) + (int64_t)g * a.cap * HD;
-    const T *__restrict__ vbase = reinterpret_cast<const T *>(a.vc) + (int64_t)g * a.cap * HD;
     const float *__restrict__ ksb = a.ks + (int64_t)g * a.cap;
     const float *__restrict__ vsb = a.vs + (int64_t)g * a.cap;
 
-    // 3. scores
-    {
-        float qv[REP][EPC];
+    // q slice of this lane: in registers when small, else read from LDS at use
+    constexpr bool QREG = REP * EPC <= 32;
+    float qv[QREG ? REP : 1][QREG ? EPC : 1];
+    if constexpr (QREG) {
 #pragma unroll
         for (int h = 0; h < REP; ++h)
 #pragma unroll
             for (int e = 0; e < EPC; ++e) qv[h][e] = qs[h][cl * EPC + e];
-        for (int jb = j0 + wave * PPI; jb < jc; jb += PPB * UN) {
-            k2_u4 w[UN];
-#pragma unroll
-            for (int u = 0; u < UN; ++u) {
-                const int j = jb + u * PPB + sub;
-                w[u] = (j < jc) ? *reinterpret_cast<const k2_u4 *>(kbase + (int64_t)j * HD + cl * EPC)
-                                : k2_u4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int u = 0; u < UN; ++u) {
-                const int j = jb + u * PPB + sub;
-                float kv[EPC];
-                kv_decode<KVDT>(w[u], kv);
-                float part[REP];
-#pragma unroll
-                for (int h = 0; h < REP; ++h) {
-                    float p = 0.f;
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e) p += qv[h][e] * kv[e];
-                    part[h] = group_sum<LPP>(p);
-                }
-                if (cl == 0 && j < jc) {
-                    const float ksc = (KVDT == K2_I8) ? ksb[j] : 1.0f;
-#pragma unroll
-                    for (int h = 0; h < REP; ++h) sc[h][j - j0] = part[h] * ksc;
-                }
-            }
-        }
-        if (holds_new) {
-            // score of the new position from the stored values in LDS
-            for (int h = wave; h < REP; h += K2_WAVES_PER_BLOCK) {
-                float p = 0.f;
-                for (int d = lane; d < HD; d += K2_WAVE) p += qs[h][d] * newkv[0][d];
-                p = wave_sum(p);
-                if (lane == 0) sc[h][n - 1] = p;
-            }
-        }
     }
-    __syncthreads();
 
-    // 4. softmax over the block's positions, one wave per head
-    for (int h = wave; h < REP; h += K2_WAVES_PER_BLOCK) {
-        float m = -INFINITY;
-        for (int j = lane; j < n; j += K2_WAVE) m = fmaxf(m, sc[h][j]);
-        m = wave_max(m);
-        float l = 0.f;
-        for (int j = lane; j < n; j += K2_WAVE) {
-            const float p = expf(sc[h][j] - m);
-            sc[h][j] = p;
-            l += p;
-        }
-        l = wave_sum(l);
-        if (lane == 0) { ml[h][0] = m; ml[h][1] = l; }
+    // 3. per-wave online softmax over the slots of this wave: slot n of
+    //    iteration it covers positions j0 + ((it*NL + n)*WPB + wave)*PPI + [0, PPI)
+    float m[REP], l[REP], acc[REP][EPC];
+#pragma unroll
+    for (int h = 0; h < REP; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
     }
-    __syncthreads();
-
-    // 5. P V
-    {
-        float acc[REP][EPC];
+    for (int base = j0; base < jc; base += NL * WPB * PPI) {
+        // take this iteration's rows, then put the next iteration's loads in
+        // flight before any arithmetic (double buffering)
+        k2_u4 kcur[NL], vcur[NL];
+        int jcur[NL];
 #pragma unroll
-        for (int h = 0; h < REP; ++h)
+        for (int n = 0; n < NL; ++n) { kcur[n] = kw[n]; vcur[n] = vw[n]; jcur[n] = jn[n]; }
+        if (base + NL * WPB * PPI < jc) issue_kv(base + NL * WPB * PPI);
+        float sc[NL][REP];
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
-        for (int jb = j0 + wave * PPI; jb < jc; jb += PPB * UN) {
-            k2_u4 w[UN];
-#pragma unroll
-            for (int u = 0; u < UN; ++u) {
-                const int j = jb + u * PPB + sub;
-                w[u] = (j < jc) ? *reinterpret_cast<const k2_u4 *>(vbase + (int64_t)j * HD + cl * EPC)
-                                : k2_u4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int u = 0; u < UN; ++u) {
-                const int j = jb + u * PPB + sub;
-                if (j < jc) {
-                    float vv[EPC];
-                    kv_decode<KVDT>(w[u], vv);
-                    const float vsc = (KVDT == K2_I8) ? vsb[j] : 1.0f;
-#pragma unroll
-                    for (int h = 0; h < REP; ++h) {
-                        const float p = sc[h][j - j0] * vsc;
-#pragma unroll
-                        for (int e = 0; e < EPC; ++e) acc[h][e] += p * vv[e];
-                    }
-                }
-            }
-        }
-        if (holds_new && wave == 0 && sub == 0) {
+        for (int n = 0; n < NL; ++n) {
+            float kv[EPC];
+            kv_decode<KVDT>(kcur[n], kv);
+            const bool valid = jcur[n] < jc;
+            const float ksc = (KVDT == K2_I8 && valid) ? ksb[jcur[n]] : 1.0f;
 #pragma unroll
             for (int h = 0; h < REP; ++h) {
-                const float p = sc[h][n - 1];
+                float p = 0.f;
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) acc[h][e] += p * newkv[1][cl * EPC + e];
+                for (int e = 0; e < EPC; ++e) {
+                    if constexpr (QREG) p += qv[h][e] * kv[e];
+                    else p += qs[h][cl * EPC + e] * kv[e];
+                }
+                p = group_sum<LPP>(p) * ksc;
+                sc[n][h] = valid ? p : -INFINITY;
             }
         }
-        // reduce over the position sub-groups of the wave
+#pragma unroll
+        for (int h = 0; h < REP; ++h) {
+            float mx = sc[0][h];
+#pragma unroll
+            for (int n = 1; n < NL; ++n) mx = fmaxf(mx, sc[n][h]);
+            mx = wave_max(mx);
+            const float mn = fmaxf(m[h], mx);
+            // mn is finite here: the first iteration of every wave that runs
+            // holds at least one valid position (base < jc for slot 0 of wave 0;
+            // other waves may see none, handled below)
+            const float corr = (mn == -INFINITY) ? 1.0f : expf(m[h] - mn);
+            l[h] *= corr;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[h][e] *= corr;
+            m[h] = mn;
+        }
+#pragma unroll
+        for (int n = 0; n < NL; ++n) {
+            if (jcur[n] < jc) {
+                float vv[EPC];
+                kv_decode<KVDT>(vcur[n], vv);
+                const float vsc = (KVDT == K2_I8) ? vsb[jcur[n]] : 1.0f;
+#pragma unroll
+                for (int h = 0; h < REP; ++h) {
+                    const float p = expf(sc[n][h] - m[h]);
+                    l[h] += p;
+                    const float pv = p * vsc;
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) acc[h][e] += pv * vv[e];
+                }
+            }
+        }
+    }
+    // the new position (fused): wave 0, values from LDS
+    if (holds_new && wave == 0) {
+#pragma unroll
+        for (int h = 0; h < REP; ++h) {
+            float p = 0.f;
+            for (int d = lane; d < HD; d += K2_WAVE) p += qs[h][d] * newkv[0][d];
+            const float snew = wave_sum(p);
+            const float mn = fmaxf(m[h], snew);
+            const float corr = expf(m[h] - mn);          // m = -inf gives 0
+            const float pn = expf(snew - mn);
+            l[h] = l[h] * corr + (sub == 0 ? pn : 0.f);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+                acc[h][e] = acc[h][e] * corr + (sub == 0 ? pn * newkv[1][cl * EPC + e] : 0.f);
+            m[h] = mn;
+        }
+    }
+    // 4. sum over the position sub-groups of the wave (same m across the wave)
+#pragma unroll
+    for (int h = 0; h < REP; ++h) {
+#pragma unroll
+        for (int o = LPP; o < K2_WAVE; o <<= 1) l[h] += __shfl_xor(l[h], o, K2_WAVE);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+            float v = acc[h][e];
+#pragma unroll
+            for (int o = LPP; o < K2_WAVE; o <<= 1) v += __shfl_xor(v, o, K2_WAVE);
+            acc[h][e] = v;
+        }
+    }
+    if (sub == 0) {
 #pragma unroll
         for (int h = 0; h < REP; ++h)
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                float v = acc[h][e];
+            for (int e = 0; e < EPC; ++e) red_o[wave][h][cl * EPC + e] = acc[h][e];
+    }
+    if (lane == 0) {
 #pragma unroll
-                for (int o = LPP; o < K2_WAVE; o <<= 1) v += __shfl_xor(v, o, K2_WAVE);
-                acc[h][e] = v;
-            }
-        if (sub == 0) {
-#pragma unroll
-            for (int h = 0; h < REP; ++h)
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) red[wave][h][cl * EPC + e] = acc[h][e];
-        }
+        for (int h = 0; h < REP; ++h) { red_ml[wave][h][0] = m[h]; red_ml[wave][h][1] = l[h]; }
     }
     __syncthreads();
 
-    // 6. output or partial
-    if (S == 1) {
-        for (int t = tid; t < REP * HD; t += K2_BLOCK) {
-            const int h = t / HD, d = t % HD;
-            float o = 0.f;
-#pragma unroll
-            for (int w = 0; w < K2_WAVES_PER_BLOCK; ++w) o += red[w][h][d];
-            a.out[(int64_t)(g * REP + h) * HD + d] = o / ml[h][1];
-        }
-        return;
-    }
+    // 5. combine the waves; output directly (one split) or publish a partial
     const int64_t pbase = ((int64_t)g * S + s) * REP;
-    for (int t = tid; t < REP * HD; t += K2_BLOCK) {
-        const int h = t / HD, d = t % HD;
-        float o = 0.f;
-#pragma unroll
-        for (int w = 0; w < K2_WAVES_PER_BLOCK; ++w) o += red[w][h][d];
-        store_agent(a.part + (pbase + h) * HD + d, o);
-    }
-    if (tid < REP * 2) store_agent(a.part_ml + pbase * 2 + tid, ml[tid / 2][tid % 2]);
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned prev = atomicAdd(a.counter + g, 1u);
-        is_last = (prev == (unsigned)S - 1u);
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    // 7. combine the S partials of kv head g in split order
-    for (int t = tid; t < REP * HD; t += K2_BLOCK) {
+    for (int t = tid; t < REP * HD; t += NT) {
         const int h = t / HD, d = t % HD;
         float M = -INFINITY;
-        for (int q = 0; q < S; ++q)
-            M = fmaxf(M, load_agent(a.part_ml + (((int64_t)g * S + q) * REP + h) * 2));
+#pragma unroll
+        for (int w = 0; w < WPB; ++w) M = fmaxf(M, red_ml[w][h][0]);
         float L = 0.f, o = 0.f;
-        for (int q = 0; q < S; ++q) {
-            const int64_t pb = ((int64_t)g * S + q) * REP + h;
-            const float f = expf(load_agent(a.part_ml + pb * 2) - M);
-            L += f * load_agent(a.part_ml + pb * 2 + 1);
-            o += f * load_agent(a.part + pb * HD + d);
+#pragma unroll
+        for (int w = 0; w < WPB; ++w) {
+            const float mw = red_ml[w][h][0];
+            const float f = (mw == -INFINITY) ? 0.f : expf(mw - M);
+            L += f * red_ml[w][h][1];
+            o += f * red_o[w][h][d];
         }
-        a.out[(int64_t)(g * REP + h) * HD + d] = o / L;
+        if (S == 1) {
+            a.out[(int64_t)(g * REP + h) * HD + d] = o / L;
+        } else {
+            a.part[(pbase + h) * HD + d] = o;
+            if (d == 0) {
+                a.part_ml[(pbase + h) * 2] = M;
+                a.part_ml[(pbase + h) * 2 + 1] = L;
+            }
+        }
     }
-    if (tid == 0) atomicExch(a.counter + g, 0u);
+}
+
+// Combine the S split partials of every query head in split order (a fixed
+// order: run-to-run deterministic): M = max_s m_s, L = sum_s l_s e^(m_s - M),
+// out = sum_s o_s e^(m_s - M) / L.  Grid = n_kv blocks.  A separate launch: the
+// kernel boundary makes every block's partials visible, with no
+// cross-block synchronisation inside a kernel.
+template <int HD, int REP>
+__global__ __launch_bounds__(K2_BLOCK) void attn_combine_kernel(const AttnArgs a)
+{
+    __shared__ float f[K2_ATTN_MAX_SPLITS][REP];
+    __shared__ float Mh[REP], Linv[REP];
+    const int g = blockIdx.x, S = a.S, tid = threadIdx.x;
+    const float *ml = a.part_ml + (int64_t)g * S * REP * 2;
+    for (int t = tid; t < S * REP; t += K2_BLOCK) f[t / REP][t % REP] = ml[(int64_t)t * 2];
+    __syncthreads();
+    if (tid < REP) {
+        float M = -INFINITY;
+        for (int q = 0; q < S; ++q) M = fmaxf(M, f[q][tid]);
+        Mh[tid] = M;
+    }
+    __syncthreads();
+    for (int t = tid; t < S * REP; t += K2_BLOCK) f[t / REP][t % REP] = expf(f[t / REP][t % REP] - Mh[t % REP]);
+    __syncthreads();
+    if (tid < REP) {
+        float L = 0.f;
+        for (int q = 0; q < S; ++q) L += f[q][tid] * ml[((int64_t)q * REP + tid) * 2 + 1];
+        Linv[tid] = 1.0f / L;
+    }
+    __syncthreads();
+    for (int t = tid; t < REP * HD; t += K2_BLOCK) {
+        const int h = t / HD, d = t % HD;
+        const float *po = a.part + ((int64_t)g * S * REP + h) * HD + d;
+        float o = 0.f;
+        int q = 0;
+        for (; q + 8 <= S; q += 8) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = po[(int64_t)(q + i) * REP * HD];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o += f[q + i][h] * v[i];
+        }
+        for (; q < S; ++q) o += f[q][h] * po[(int64_t)q * REP * HD];
+        a.out[(int64_t)(g * REP + h) * HD + d] = o * Linv[h];
+    }
 }
 
 // Standalone store of one position (k, v already rotated), grid = n_kv.
@@ -395,8 +436,7 @@ size_t attn_ws_bytes(int n_qh, int n_kv, int hd, int cap)
 {
     const size_t S = (size_t)attn_max_splits(n_kv, cap);
     const size_t rep = (size_t)(n_qh / n_kv);
-    return k2_align256((size_t)n_kv * S * rep * hd * 4) + k2_align256((size_t)n_kv * S * rep * 2 * 4) +
-           k2_align256((size_t)n_kv * 4);
+    return k2_align256((size_t)n_kv * S * rep * hd * 4) + k2_align256((size_t)n_kv * S * rep * 2 * 4);
 }
 
 void attn_ws_carve(void *ws, int n_qh, int n_kv, int hd, int cap, AttnArgs &a)
@@ -408,15 +448,18 @@ void attn_ws_carve(void *ws, int n_qh, int n_kv, int hd, int cap, AttnArgs &a)
     p += k2_align256((size_t)n_kv * S * rep * hd * 4);
     a.part_ml = (float *)p;
     p += k2_align256((size_t)n_kv * S * rep * 2 * 4);
-    a.counter = (unsigned *)p;
 }
 
 template <int KVDT, int HD, int REP, bool FUSED>
 static int attn_go(const AttnArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL((attn_kernel<KVDT, HD, REP, FUSED>), dim3(a.S, a.n_kv), dim3(K2_BLOCK), 0, st,
-                       a);
+    hipLaunchKernelGGL((attn_kernel<KVDT, HD, REP, FUSED, K2_WAVES_PER_BLOCK>), dim3(a.S, a.n_kv),
+                       dim3(K2_BLOCK), 0, st, a);
     K2_CHECK_LAUNCH();
+    if (a.S > 1) {
+        hipLaunchKernelGGL((attn_combine_kernel<HD, REP>), dim3(a.n_kv), dim3(K2_BLOCK), 0, st, a);
+        K2_CHECK_LAUNCH();
+    }
     return K2_OK;
 }
 
@@ -536,6 +579,7 @@ static int attn_common_check(k2_dtype kvdt, const void *kc, const void *vc, cons
     if (n_qh <= 0 || n_kv <= 0 || cap <= 0) return K2_EINVAL;
     if (kvdt != K2_F32 && kvdt != K2_BF16 && kvdt != K2_I8) return K2_EUNSUPPORTED;
     if (!hd_ok(head_dim) || !rep_ok(n_qh, n_kv)) return K2_EUNSUPPORTED;
+    if (cap > K2_ATTN_MAX_SPLITS * K2_ATTN_MAX_CHUNK) return K2_EUNSUPPORTED;
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < attn_ws_bytes(n_qh, n_kv, head_dim, cap))
         return K2_EINVAL;
     return K2_OK;

@@ -80,6 +80,7 @@ static int config_check(const k2_config *c)
         return K2_EUNSUPPORTED;
     if (c->kvdt != K2_F32 && c->kvdt != K2_BF16 && c->kvdt != K2_I8) return K2_EUNSUPPORTED;
     if (c->embdt != K2_F32 && c->embdt != K2_BF16) return K2_EUNSUPPORTED;
+    if (c->cap > K2_ATTN_MAX_SPLITS * K2_ATTN_MAX_CHUNK) return K2_EUNSUPPORTED;
     return K2_OK;
 }
 
@@ -126,8 +127,7 @@ static int decode_impl(const k2_model *m, int token, const int32_t *d_token, int
     const int H = c->hidden, hd = c->head_dim, wdt = c->wdt;
     const int qkv_rows = (c->n_qh + 2 * c->n_kv) * hd;
 
-    rc = embed_launch(c->embdt, m->embed, H, c->vocab, d_token ? -1 : token, d_token, d_err, w.h,
-                      at.counter, c->n_kv, am.counter, 1, st);
+    rc = embed_launch(c->embdt, m->embed, H, c->vocab, d_token ? -1 : token, d_token, d_err, w.h, st);
     if (rc) return rc;
 
     at.qkv = w.qkv;

@@ -23,26 +23,60 @@ namespace k2 {
 
 // ------------------------------------------------------------- reductions --
 
+// DPP lane moves (gfx9 encodings): quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror.  bound_ctrl keeps every lane's own value.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each row of 16 lanes, result in all 16 lanes (4 DPP adds).
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);   // row_half_mirror
+    v += dpp<0x140>(v);   // row_mirror
+    return v;
+}
+
+// Sum over the 64 lanes of the wave, result in every lane: DPP within rows of
+// 16, then the four row sums through readlane (uniform scalars).
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, K2_WAVE);
-    return v;
+    v = row16_sum(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, K2_WAVE));
-    return v;
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-// Sum across aligned groups of `W` lanes (W a power of two <= 64).
+// Sum across aligned groups of `W` lanes (W a power of two <= 64), result in
+// every lane of the group: DPP inside rows of 16, lane shuffles above.
 template <int W>
 __device__ __forceinline__ float group_sum(float v)
 {
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, K2_WAVE);
+    if constexpr (W >= 2) v += dpp<0xB1>(v);      // pairs
+    if constexpr (W >= 4) v += dpp<0x4E>(v);      // quads
+    if constexpr (W >= 8) v += dpp<0x141>(v);     // half rows
+    if constexpr (W >= 16) v += dpp<0x140>(v);    // rows
+    if constexpr (W >= 32) v += __shfl_xor(v, 16, K2_WAVE);
+    if constexpr (W >= 64) v += __shfl_xor(v, 32, K2_WAVE);
     return v;
 }
 

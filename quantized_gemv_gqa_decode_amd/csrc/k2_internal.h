@@ -8,8 +8,9 @@
 #define K2_MAX_LDS_FLOATS 12288          // 48 KiB of staged activations
 #define K2_GEMV_MAX_BLOCKS 4096
 #define K2_ATTN_MAX_CHUNK 1024           // positions per attention block
-#define K2_ATTN_MIN_CHUNK 32
-#define K2_ATTN_TARGET_BLOCKS 512
+#define K2_ATTN_MIN_CHUNK 64
+#define K2_ATTN_TARGET_BLOCKS 256
+#define K2_ATTN_MAX_SPLITS 512           // combine LDS bound: >= max splits
 #define K2_ARGMAX_MAX_BLOCKS K2_GEMV_MAX_BLOCKS
 
 namespace k2 {
@@ -17,12 +18,13 @@ namespace k2 {
 enum { PRO_NONE = 0, PRO_NORM = 1 };
 enum { EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2 };
 
-// Cross-block argmax: every block writes its (value, index) candidate, the
-// last block to arrive reduces them in block order and resets the counter.
+// Cross-block argmax: every block of the producing kernel writes its
+// (value, index) candidate; argmax_final_kernel reduces them in block order
+// (a fixed order, so the result does not depend on timing).  The kernel
+// boundary orders the two: no cross-block synchronisation inside a kernel.
 struct ArgmaxArgs {
     float *part_v;
     int *part_i;
-    unsigned *counter;
     int32_t *out_idx;
     int n_blocks;
 };
@@ -56,7 +58,6 @@ struct AttnArgs {
     float *out;                // [n_qh][hd]
     float *part;               // [n_kv][S][rep][hd]
     float *part_ml;            // [n_kv][S][rep][2]
-    unsigned *counter;         // [n_kv]
     int n_qh, n_kv, cap, len, pos, chunk, S;
     float scale;
 };
@@ -74,8 +75,8 @@ void argmax_ws_carve(void *ws, ArgmaxArgs &am);
 // ------------------------------------------------------------------- misc --
 
 int embed_launch(int embdt, const void *E, int H, int vocab, int token, const int32_t *d_token,
-                 int32_t *d_err, float *h, unsigned *zero_a, int zero_a_n, unsigned *zero_b,
-                 int zero_b_n, hipStream_t st);
+                 int32_t *d_err, float *h, hipStream_t st);
+int argmax_final_launch(const ArgmaxArgs &am, int n_blocks, hipStream_t st);
 
 // ------------------------------------------------------ device functions --
 
@@ -107,51 +108,6 @@ __device__ __forceinline__ void argmax_block(float &v, int &i)
         for (int w = 1; w < K2_WAVES_PER_BLOCK; ++w) argmax_pair_max(v, i, sv[w], si[w]);
     }
     __syncthreads();
-}
-
-__device__ __forceinline__ void store_agent(float *p, float v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_agent(int *p, int v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float *p)
-{
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int load_agent(const int *p)
-{
-    return __hip_atomic_load(const_cast<int *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Publish this block's candidate; the last block reduces all of them in
-// block order (a fixed order, so the result does not depend on timing),
-// writes the index and re-zeroes the counter for the next use.
-__device__ __forceinline__ void argmax_block_finish(float v, int i, const ArgmaxArgs &am)
-{
-    __shared__ int is_last;
-    argmax_block(v, i);
-    if (threadIdx.x == 0) {
-        store_agent(am.part_v + blockIdx.x, v);
-        store_agent(am.part_i + blockIdx.x, i);
-        __threadfence();
-        const unsigned prev = atomicAdd(am.counter, 1u);
-        is_last = (prev == (unsigned)am.n_blocks - 1u);
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-    for (int b = threadIdx.x; b < am.n_blocks; b += K2_BLOCK)
-        argmax_pair_max(bv, bi, load_agent(am.part_v + b), load_agent(am.part_i + b));
-    argmax_block(bv, bi);
-    if (threadIdx.x == 0) {
-        *am.out_idx = bi;
-        atomicExch(am.counter, 0u);
-    }
 }
 
 }  // namespace k2

@@ -62,10 +62,8 @@ __global__ void rope_kernel(float *q, float *k, const float *cs, int n_qh, int n
 // h = fp32(E[token]); the token comes from the host (token >= 0) or from
 // device memory (d_token).  A device token outside [0, vocab) sets *d_err and
 // is replaced by 0 so that every later kernel still runs to completion.
-// The same launch re-zeroes the arrival counters of the step's workspace.
 __global__ void embed_kernel(int embdt, const void *E, int H, int vocab, int token,
-                             const int32_t *d_token, int32_t *d_err, float *h, unsigned *za,
-                             int za_n, unsigned *zb, int zb_n)
+                             const int32_t *d_token, int32_t *d_err, float *h)
 {
     int tok = token;
     if (d_token) {
@@ -79,20 +77,15 @@ __global__ void embed_kernel(int embdt, const void *E, int H, int vocab, int tok
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < H; i += gridDim.x * blockDim.x)
         h[i] = embdt == K2_BF16 ? bf16_to_f32(((const uint16_t *)E)[base + i])
                                 : ((const float *)E)[base + i];
-    if (blockIdx.x == 0) {
-        for (int i = threadIdx.x; i < za_n; i += blockDim.x) za[i] = 0u;
-        for (int i = threadIdx.x; i < zb_n; i += blockDim.x) zb[i] = 0u;
-    }
 }
 
 int embed_launch(int embdt, const void *E, int H, int vocab, int token, const int32_t *d_token,
-                 int32_t *d_err, float *h, unsigned *za, int za_n, unsigned *zb, int zb_n,
-                 hipStream_t st)
+                 int32_t *d_err, float *h, hipStream_t st)
 {
     int blocks = (H + K2_BLOCK - 1) / K2_BLOCK;
     if (blocks > 64) blocks = 64;
     hipLaunchKernelGGL(embed_kernel, dim3(blocks), dim3(K2_BLOCK), 0, st, embdt, E, H, vocab, token,
-                       d_token, d_err, h, za, za_n, zb, zb_n);
+                       d_token, d_err, h);
     K2_CHECK_LAUNCH();
     return K2_OK;
 }
@@ -152,18 +145,40 @@ __global__ void quant_mxfp4_kernel(const uint16_t *W, uint8_t *q, uint8_t *e8m0,
 }
 
 // ----------------------------------------------------------------- argmax --
+// Candidates of a grid-stride pass over x, one per block.
 __global__ __launch_bounds__(K2_BLOCK) void argmax_kernel(const float *x, int n, ArgmaxArgs am)
 {
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
     for (int i = blockIdx.x * K2_BLOCK + threadIdx.x; i < n; i += gridDim.x * K2_BLOCK)
         argmax_pair_max(bv, bi, x[i], i);
-    argmax_block_finish(bv, bi, am);
+    argmax_block(bv, bi);
+    if (threadIdx.x == 0) {
+        am.part_v[blockIdx.x] = bv;
+        am.part_i[blockIdx.x] = bi;
+    }
+}
+
+// First maximum over the per-block candidates (value, then lowest index).
+__global__ __launch_bounds__(K2_BLOCK) void argmax_final_kernel(ArgmaxArgs am, int n_blocks)
+{
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int b = threadIdx.x; b < n_blocks; b += K2_BLOCK) argmax_pair_max(bv, bi, am.part_v[b], am.part_i[b]);
+    argmax_block(bv, bi);
+    if (threadIdx.x == 0) *am.out_idx = bi;
+}
+
+int argmax_final_launch(const ArgmaxArgs &am, int n_blocks, hipStream_t st)
+{
+    hipLaunchKernelGGL(argmax_final_kernel, dim3(1), dim3(K2_BLOCK), 0, st, am, n_blocks);
+    K2_CHECK_LAUNCH();
+    return K2_OK;
 }
 
 size_t argmax_ws_bytes()
 {
-    return k2_align256((size_t)K2_ARGMAX_MAX_BLOCKS * 4) * 2 + 256;
+    return k2_align256((size_t)K2_ARGMAX_MAX_BLOCKS * 4) * 2;
 }
 
 void argmax_ws_carve(void *ws, ArgmaxArgs &am)
@@ -172,8 +187,6 @@ void argmax_ws_carve(void *ws, ArgmaxArgs &am)
     am.part_v = (float *)p;
     p += k2_align256((size_t)K2_ARGMAX_MAX_BLOCKS * 4);
     am.part_i = (int *)p;
-    p += k2_align256((size_t)K2_ARGMAX_MAX_BLOCKS * 4);
-    am.counter = (unsigned *)p;
 }
 
 }  // namespace k2
@@ -273,5 +286,5 @@ extern "C" int k2_argmax(const float *x, int n, int32_t *out_idx, void *ws, size
     am.n_blocks = blocks;
     hipLaunchKernelGGL(argmax_kernel, dim3(blocks), dim3(K2_BLOCK), 0, k2_stream(stream), x, n, am);
     K2_CHECK_LAUNCH();
-    return K2_OK;
+    return argmax_final_launch(am, blocks, k2_stream(stream));
 }

@@ -1,0 +1,144 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* libk2.so loads and exports every function that include/k2.h declares.
+* Size queries and status strings work on the host.
+* Argument validation refuses bad calls with the documented status before
+  anything is launched: fake (but aligned) device addresses are passed, so a
+  call that got past validation would try to launch and fail with K2_EHIP on
+  this GPU-less host instead of returning the expected status.
+* The Python binding raises instead of falling back when the library is absent.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from quantized_gemv_gqa_decode_amd import k2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "k2.h")
+FAKE = 0x10000          # aligned, never dereferenced on the host
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(k2_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(n for n in names))
+
+
+def test_every_declared_symbol_is_exported():
+    L = k2.load()
+    names = declared_functions()
+    assert len(names) >= 20
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    # and the binding declares a signature for every one of them
+    assert not [n for n in names if n not in k2.SIGNATURES], \
+        [n for n in names if n not in k2.SIGNATURES]
+
+
+def test_version_and_status_strings():
+    assert k2.k2_abi_version() == 1
+    for rc in (0, -1, -2, -3, -4):
+        assert k2.k2_status_str(rc)
+    assert "unknown" in k2.k2_status_str(7)
+
+
+def test_workspace_sizes():
+    assert k2.k2_attn_workspace_bytes(32, 8, 128, 4096) > 0
+    assert k2.k2_attn_workspace_bytes(32, 7, 128, 4096) == 0          # n_qh % n_kv
+    assert k2.k2_argmax_workspace_bytes(250624) > 0
+    assert k2.k2_argmax_workspace_bytes(0) == 0
+    c = k2.k2_config(2560, 36, 32, 8, 128, 10240, 250624, 2, 4096, 1e-6, 1e4, k2.K2_BF16,
+                     k2.K2_BF16, k2.K2_BF16)
+    assert k2.k2_decode_workspace_bytes(c) > 0
+    bad = k2.k2_config(2560, 36, 32, 8, 96, 10240, 250624, 2, 4096, 1e-6, 1e4, k2.K2_BF16,
+                       k2.K2_BF16, k2.K2_BF16)
+    assert k2.k2_decode_workspace_bytes(bad) == 0                       # head_dim 96
+
+
+def test_gemv_validation():
+    L = k2.load()
+    st = None
+    assert L.k2_gemv_qbf16(None, FAKE, FAKE, None, 8, 64, 1, st) == k2.K2_EINVAL
+    assert L.k2_gemv_qbf16(FAKE + 2, FAKE, FAKE, None, 8, 64, 1, st) == k2.K2_EINVAL
+    assert L.k2_gemv_qbf16(FAKE, FAKE, FAKE, None, 0, 64, 1, st) == k2.K2_EINVAL
+    assert L.k2_gemv_qbf16(FAKE, FAKE, FAKE, None, 8, 48, 1, st) == k2.K2_EUNSUPPORTED
+    assert L.k2_gemv_qbf16(FAKE, FAKE, FAKE, None, 8, 64, 3, st) == k2.K2_EUNSUPPORTED
+    assert L.k2_gemv_qbf16(FAKE, FAKE, FAKE, None, 8, 12288 + 32, 1, st) == k2.K2_EUNSUPPORTED
+    assert L.k2_gemv_qfp8(FAKE, None, FAKE, FAKE, None, 8, 64, 1, st) == k2.K2_EINVAL
+    assert L.k2_gemv_qmxfp4(FAKE, None, FAKE, FAKE, None, 8, 64, 1, st) == k2.K2_EINVAL
+    assert L.k2_quantize_mxfp4(FAKE, FAKE, FAKE, 8, 48, st) == k2.K2_EUNSUPPORTED
+    assert L.k2_quantize_fp8_rows(FAKE, FAKE, FAKE, 8, 40, st) == k2.K2_EINVAL
+
+
+def test_rope_append_attention_validation():
+    L = k2.load()
+    st = None
+    assert L.k2_rope(FAKE, FAKE, FAKE, 32, 8, 128, 4096, 4096, st) == k2.K2_ERANGE
+    assert L.k2_rope(FAKE, FAKE, FAKE, 32, 8, 96, 0, 4096, st) == k2.K2_EUNSUPPORTED
+    assert L.k2_kv_append(k2.K2_BF16, FAKE, FAKE, FAKE, FAKE, 8, 128, 4096, -1, st) == k2.K2_ERANGE
+    assert L.k2_kv_append(k2.K2_I8, FAKE, FAKE, FAKE, FAKE, 8, 128, 4096, 0, st) == k2.K2_EUNSUPPORTED
+    assert L.k2_kv_append_int8(FAKE, FAKE, FAKE, FAKE, None, FAKE, 8, 128, 4096, 0, st) == k2.K2_EINVAL
+    wsb = k2.k2_attn_workspace_bytes(32, 8, 128, 4096)
+    ws = 0x100000
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 8, 128, 4096)
+    assert L.k2_gqa_decode_attn(k2.K2_BF16, *args, 0, 0.1, ws, wsb, st) == k2.K2_ERANGE
+    assert L.k2_gqa_decode_attn(k2.K2_BF16, *args, 4097, 0.1, ws, wsb, st) == k2.K2_ERANGE
+    assert L.k2_gqa_decode_attn(k2.K2_BF16, *args, 10, 0.1, ws, wsb - 4, st) == k2.K2_EINVAL
+    assert L.k2_gqa_decode_attn(k2.K2_BF16, *args, 10, 0.1, ws + 16, wsb, st) == k2.K2_EINVAL
+    assert L.k2_gqa_decode_attn(k2.K2_FP8E4M3, *args, 10, 0.1, ws, wsb, st) == k2.K2_EUNSUPPORTED
+    assert L.k2_gqa_decode_attn(k2.K2_I8, FAKE, FAKE, FAKE, None, None, FAKE, 32, 8, 128, 4096,
+                                10, 0.1, ws, wsb, st) == k2.K2_EINVAL
+    assert L.k2_rope_append_attn(k2.K2_BF16, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 32, 8, 128,
+                                 4096, 4096, ws, wsb, st) == k2.K2_ERANGE
+    assert L.k2_argmax(FAKE, 100, FAKE, ws, 16, st) == k2.K2_EINVAL
+
+
+def _fake_model(cfg_kw=None):
+    c = dict(hidden=64, n_layers=2, n_qh=4, n_kv=2, head_dim=16, inter=256, vocab=512, groups=2,
+             cap=32, eps=1e-6, rope_theta=1e4, wdt=k2.K2_F32, kvdt=k2.K2_F32, embdt=k2.K2_F32)
+    c.update(cfg_kw or {})
+    cfg = k2.k2_config(**c)
+    arr = (k2.k2_layer * c["n_layers"])()
+    for i in range(c["n_layers"]):
+        arr[i] = k2.k2_layer(*([FAKE] * 14))
+    ws_b = k2.k2_decode_workspace_bytes(cfg)
+    m = k2.k2_model(cfg, FAKE, FAKE, FAKE, FAKE, FAKE, C.cast(arr, C.POINTER(k2.k2_layer)),
+                    0x100000, ws_b)
+    m._keep = arr
+    return m
+
+
+def test_decode_step_refuses_before_launch():
+    m = _fake_model()
+    assert k2.k2_model_check(m) == k2.K2_OK
+    L = k2.load()
+    adr = C.addressof(m)
+    assert L.k2_decode_step(adr, 512, 0, FAKE, FAKE, None) == k2.K2_ERANGE
+    assert L.k2_decode_step(adr, -1, 0, FAKE, FAKE, None) == k2.K2_ERANGE
+    assert L.k2_decode_step(adr, 0, 32, FAKE, FAKE, None) == k2.K2_ERANGE
+    assert L.k2_decode_step(adr, 0, -1, FAKE, FAKE, None) == k2.K2_ERANGE
+    assert L.k2_decode_step(adr, 0, 0, FAKE + 4, FAKE, None) == k2.K2_EINVAL
+    assert L.k2_decode_step_dev(adr, None, 0, FAKE, FAKE, None, None) == k2.K2_EINVAL
+    m.ws_bytes -= 256
+    assert L.k2_decode_step(adr, 0, 0, FAKE, FAKE, None) == k2.K2_EINVAL
+    assert L.k2_decode_step(None, 0, 0, FAKE, FAKE, None) == k2.K2_EINVAL
+
+
+@pytest.mark.parametrize("change,rc", [(dict(head_dim=96), -3), (dict(n_kv=3), -3),
+                                       (dict(groups=3), -3), (dict(hidden=48), -3),
+                                       (dict(wdt=k2.K2_I8), -3), (dict(kvdt=k2.K2_MXFP4), -3),
+                                       (dict(vocab=0), -1), (dict(eps=-1.0), -1)])
+def test_model_check_rejects_bad_configs(change, rc):
+    m = _fake_model(change)
+    assert k2.k2_model_check(m) == rc
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(k2, "_lib", None)
+    monkeypatch.setattr(k2, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        k2.load(build_if_missing=False)

@@ -291,7 +291,7 @@ def test_gqa_decode_attn_matches_oracle(kvdt, hd, n_qh, n_kv, L):
 
 @pytest.mark.parametrize("kvdt", ["f32", "bf16", "i8"])
 @pytest.mark.parametrize("hd,n_qh,n_kv", [(128, 32, 8), (16, 4, 2)])
-@pytest.mark.parametrize("pos", [0, 31, 32, 700])
+@pytest.mark.parametrize("pos", [0, 31, 32, 700, 1024, 2000])
 def test_rope_append_attn_matches_oracle(kvdt, hd, n_qh, n_kv, pos):
     say(f"fused attn {kvdt} hd={hd} pos={pos}")
     cap = pos + 5
