@@ -122,6 +122,21 @@ def kernel_table(gm, stream, reps: int):
     out["gate_up_norm_gemv_swiglu"] = (ms, mats(0, "wgu")[2] + 2 * H * 4 + I * 4)
     ms = time_kernel(lambda i: gemv_plain(mats(i, "wd"), x_d, hb, H, I), n, stream)
     out["down_gemv_residual"] = (ms, mats(0, "wd")[2] + I * 4 + 2 * H * 4)
+    # fused RoPE + KV append + attention at the next free position (the slot it
+    # writes is the one the next decode step would write anyway)
+    pos = gm.bench_next_pos
+    L = pos + 1
+    qkvb = torch.randn(cfg.qkv_rows, device=dev)
+    ob = torch.empty(qd, device=dev)
+    awb = k2.k2_attn_workspace_bytes(cfg.n_qh, cfg.n_kv, cfg.head_dim, cfg.cap)
+    aws = torch.zeros(awb, dtype=torch.uint8, device=dev)
+    kvdt = k2.DTYPES[cfg.kvdt]
+    ms = time_kernel(lambda i: k2.k2_rope_append_attn(
+        kvdt, qkvb, gm.rope, Ls[i % nl]["kc"], Ls[i % nl]["vc"], Ls[i % nl]["ks"], Ls[i % nl]["vs"],
+        ob, cfg.n_qh, cfg.n_kv, cfg.head_dim, cfg.cap, pos, aws, awb), n, stream)
+    elem = {"f32": 4, "bf16": 2, "i8": 1}[cfg.kvdt]
+    kv_bytes = 2 * cfg.n_kv * cfg.head_dim * elem * L + (2 * cfg.n_kv * 4 * L if cfg.kvdt == "i8" else 0)
+    out["attention_rope_append"] = (ms, kv_bytes + cfg.qkv_rows * 4 + qd * 4)
     nlm = max(4, reps)
     ms = time_kernel(lambda i: k2.k2_norm_gemv_argmax(wdt, gm.lm.w, gm.lm.s, h, gm.g_final,
                                                       cfg.groups, cfg.eps, logits, cfg.vocab, H,
@@ -131,27 +146,32 @@ def kernel_table(gm, stream, reps: int):
     return out
 
 
-def cpu_baseline(cfg, budget_s: float):
+def cpu_baseline(cfg, budget_s: float, prefix: int = 0):
     """The oracle as it stands (fp64, OpenMP over rows) on this host's cores,
-    on a bounded sample of the same workload: full decode positions 0..n-1 of
-    the whole model, n chosen so the sample takes about budget_s seconds."""
+    on a bounded sample of the same workload: n full decode positions of the
+    whole model (after the same synthetic int8 history when one is used), n
+    chosen so the sample takes about budget_s seconds."""
     import numpy as np
     import oracle
     import synth
     log("cpu baseline: drawing oracle weights")
     dec = oracle.Decoder.from_synth(cfg)
+    if prefix:
+        dec.load_int8_prefix(prefix)
     pr = synth.prompt(cfg)
     t0 = time.perf_counter()
-    dec.step(int(pr[0]), 0, want_logits=True)
+    dec.step(int(pr[0]), prefix, want_logits=True)
     t1 = time.perf_counter() - t0
     n = int(max(1, min(16, budget_s / max(t1, 1e-6))))
     t0 = time.perf_counter()
     for p in range(1, n + 1):
-        dec.step(int(pr[p]), p, want_logits=True)
+        dec.step(int(pr[p]), prefix + p, want_logits=True)
     dt = time.perf_counter() - t0
+    where = f"positions {prefix + 1}..{prefix + n}" + (
+        f" after a synthetic int8 history of {prefix}" if prefix else "")
     return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{n} full decode positions (1..{n}) of the whole model incl. lm_head, "
-                      f"fp64 oracle, after one untimed position; {dt:.1f} s",
+            "sample": f"{n} full decode steps ({where}) of the whole model incl. lm_head, "
+                      f"fp64 oracle, after one untimed step; {dt:.1f} s",
             "cpu": platform.processor() or platform.machine()}
 
 
@@ -162,6 +182,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--config", default="k2h-3.7b-bf16-kvbf16-ctx4096")
     ap.add_argument("--prompt-len", type=int, default=None)
+    ap.add_argument("--prefix", type=int, default=0,
+                    help="int8 KV only: start from a seeded synthetic history of this many "
+                         "positions in every layer instead of a prompt prefill")
     ap.add_argument("--kernel-reps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -183,6 +206,8 @@ def main():
     cfg = synth.CONFIGS[args.config]
     P = cfg.prompt_len if args.prompt_len is None else args.prompt_len
     W, K = args.warmup, args.steps
+    if args.prefix:
+        P = args.prefix + 1
     if P + W + K > cfg.cap:
         sys.exit(f"prompt {P} + warmup {W} + steps {K} exceeds the context {cfg.cap}")
     dev = torch.device("cuda:0")
@@ -196,12 +221,23 @@ def main():
     log(f"model ready in {time.perf_counter() - t0:.1f} s, weights {gm.weight_bytes() / 1e9:.3f} GB")
     stream = torch.cuda.current_stream()
 
-    prompt = synth.prompt(cfg, P)
-    t0 = time.perf_counter()
-    for p, t in enumerate(prompt):
-        gm.step(int(t), p, want_logits=(p == P - 1))
-    torch.cuda.synchronize()
-    log(f"prefill of {P} positions (as decode steps) in {time.perf_counter() - t0:.2f} s")
+    if args.prefix:
+        if cfg.kvdt != "i8":
+            sys.exit("--prefix needs an int8 KV cache")
+        t0 = time.perf_counter()
+        gm.load_int8_prefix(args.prefix)
+        gm.step(int(synth.prompt(cfg, 1)[0]), args.prefix, want_logits=True)
+        torch.cuda.synchronize()
+        P = args.prefix + 1
+        log(f"synthetic int8 history of {args.prefix} positions loaded in "
+            f"{time.perf_counter() - t0:.1f} s")
+    else:
+        prompt = synth.prompt(cfg, P)
+        t0 = time.perf_counter()
+        for p, t in enumerate(prompt):
+            gm.step(int(t), p, want_logits=(p == P - 1))
+        torch.cuda.synchronize()
+        log(f"prefill of {P} positions (as decode steps) in {time.perf_counter() - t0:.2f} s")
 
     hist = torch.zeros(W + K + 1, dtype=torch.int32, device=dev)
     hist[0:1].copy_(gm.next)
@@ -233,9 +269,11 @@ def main():
     sb = step_bytes(cfg, int(round(Lavg)), wb)
     step_gbps = sb / (ms_step * 1e-3) / 1e9
 
+    gm.bench_next_pos = P + W + K
     log("per-kernel timing")
     kt = kernel_table(gm, stream, args.kernel_reps)
     per_step_share = {
+        "attention_rope_append": cfg.n_layers,
         "qkv_norm_gemv": cfg.n_layers, "o_gemv_residual": cfg.n_layers,
         "gate_up_norm_gemv_swiglu": cfg.n_layers, "down_gemv_residual": cfg.n_layers,
         "lm_head_norm_gemv_argmax": 1}
@@ -251,7 +289,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         try:
-            cpu = cpu_baseline(cfg, args.cpu_budget)
+            cpu = cpu_baseline(cfg, args.cpu_budget, args.prefix)
         except MemoryError as e:  # pragma: no cover
             cpu = {"error": str(e)}
 
@@ -269,7 +307,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "weights": cfg.wdt, "kv_cache": cfg.kvdt,
-                   "prompt_len": P, "context": cfg.cap, "layers": cfg.n_layers,
+                   "prompt_len": 0 if args.prefix else P, "synthetic_int8_history": args.prefix,
+                   "context": cfg.cap, "layers": cfg.n_layers,
                    "hidden": cfg.hidden, "vocab": cfg.vocab, "batch": 1,
                    "prefix_len_mean": Lavg},
         "step_bytes": sb,

@@ -350,6 +350,17 @@ class Decoder:
         lm = Mat.from_draw(cfg.wdt, synth.lm_head_weight(cfg))
         return cls(cfg, synth.embed_weight(cfg), lm, layers, gi, gp, synth.norm_gain(cfg))
 
+    def load_int8_prefix(self, length: int):
+        """Fill cache slots [0, length) of every layer with the seeded int8
+        history of ``synth.int8_kv_prefix`` (the same bytes the GPU side gets)."""
+        import synth
+        for l, c in enumerate(self.caches):
+            kc, vc, ks, vs = synth.int8_kv_prefix(self.cfg, l, length)
+            c.k[:, :length] = kc
+            c.v[:, :length] = vc
+            c.ks[:, :length] = ks
+            c.vs[:, :length] = vs
+
     def step(self, token: int, pos: int, want_logits: bool = True):
         """Run one position; returns (argmax, fp64 logits) or (-1, None)."""
         if not (0 <= token < self.cfg.vocab) or not (0 <= pos < self.cfg.cap):

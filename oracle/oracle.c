@@ -372,7 +372,7 @@ ORC_EXPORT void orc_kv_store(int kvdt, const double *u, void *c, float *sc, int 
 }
 
 /* GQA decode attention for one new query position over cache slots
- * [0, len).  Query head h reads kv head floor(h / (n_qh / n_kv)) (contiguous
+ * [0, len); query heads are independent (OpenMP over heads).  Query head h reads kv head floor(h / (n_qh / n_kv)) (contiguous
  * groups: the 4x repeat of [k2-burn] "Model shape").  Scores are scaled by
  * 1/sqrt(hd); the softmax subtracts the row maximum; all in fp64.
  * probs (nullable) receives [n_qh][len]. */
@@ -382,8 +382,9 @@ ORC_EXPORT void orc_attention(int kvdt, const double *q, const void *kc, const v
 {
     int rep = n_qh / n_kv;
     double scale = 1.0 / sqrt((double)hd);
-    double *s = (double *)malloc(sizeof(double) * (size_t)len);
+    #pragma omp parallel for schedule(static)
     for (int h = 0; h < n_qh; ++h) {
+        double *s = (double *)malloc(sizeof(double) * (size_t)len);
         int g = h / rep;
         const double *qh = q + (int64_t)h * hd;
         double mx = -INFINITY;
@@ -406,8 +407,8 @@ ORC_EXPORT void orc_attention(int kvdt, const double *q, const void *kc, const v
             for (int d = 0; d < hd; ++d)
                 oh[d] += s[j] * kv_read(kvdt, vc, vs, base + d, (int64_t)g * cap + j);
         }
+        free(s);
     }
-    free(s);
 }
 
 /* argmax with the first maximum winning ([k3_run.c] argmax_(): a later entry

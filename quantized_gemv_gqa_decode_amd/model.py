@@ -120,6 +120,20 @@ class DecodeModel:
         self.next = torch.zeros(1, dtype=torch.int32, device=self.device)
 
     # ------------------------------------------------------------------
+    def load_int8_prefix(self, length: int):
+        """Fill cache slots [0, length) of every layer with the seeded int8
+        history of ``synth.int8_kv_prefix`` (a stand-in for a long prefill)."""
+        import synth
+        if self.cfg.kvdt != "i8":
+            raise ValueError("the synthetic prefix is an int8 KV history")
+        for l, L in enumerate(self.layers):
+            kc, vc, ks, vs = synth.int8_kv_prefix(self.cfg, l, length)
+            L["kc"][:, :length].copy_(torch.from_numpy(kc))
+            L["vc"][:, :length].copy_(torch.from_numpy(vc))
+            L["ks"][:, :length].copy_(torch.from_numpy(ks))
+            L["vs"][:, :length].copy_(torch.from_numpy(vs))
+        torch.cuda.synchronize()
+
     def weight_bytes(self) -> int:
         """Bytes of projection and lm_head weights read by one full step."""
         n = self.lm.nbytes

@@ -125,3 +125,42 @@ def test_k2h_bf16_full_depth_teacher_forced():
     cfg = synth.K2H_BF16
     pr = synth.prompt(cfg, 6)
     run_parity(cfg, pr, 3, free_running=False)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["k2h-3.7b-fp8-kvi8-ctx4096", "k2h-3.7b-mxfp4-kvi8-ctx4096"])
+def test_k2h_quantized_full_depth_teacher_forced(name):
+    """fp8 E4M3 + row scale and MXFP4 weights quantized on the device from the
+    bf16 draw (bit-exact with the oracle's quantizers, pinned elsewhere), int8
+    KV, full depth and vocab."""
+    cfg = synth.CONFIGS[name]
+    run_parity(cfg, synth.prompt(cfg, 6), 3, free_running=False)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("prefix", [1024, 8192, 32760])
+def test_k2h_int8_long_context(prefix):
+    """int8 KV at long context: every layer starts from the same seeded int8
+    history on both sides, then two decode positions run at full depth."""
+    cfg = synth.K2H_BF16_I8_LONG
+    say(f"oracle: int8 history {prefix}")
+    dec = oracle.Decoder.from_synth(cfg)
+    dec.load_int8_prefix(prefix)
+    tok0 = int(synth.prompt(cfg, 1)[0])
+    ref = [dec.step(tok0, prefix)]
+    ref.append(dec.step(ref[0][0], prefix + 1))
+    say("gpu")
+    gm = DecodeModel(cfg, DEV)
+    gm.load_int8_prefix(prefix)
+    worst = 0.0
+    feed = tok0
+    for i, (rt, rl) in enumerate(ref):
+        lg, nx = gm.step(feed, prefix + i)
+        torch.cuda.synchronize()
+        g = to_host(lg).astype(np.float64)
+        err = float(np.abs(g - rl).max())
+        worst = max(worst, err)
+        assert err <= 5e-2, (i, err)
+        assert near_tie_ok(int(nx.item()), rl)
+        feed = rt                                    # teacher-forced on the oracle's token
+    say(f"int8 history {prefix}: max|dlogit| = {worst:.3g}")
