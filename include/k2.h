@@ -275,6 +275,81 @@ int k2_decode_step(const k2_model *m, int token, int pos, float *logits, int32_t
 int k2_decode_step_dev(const k2_model *m, const int32_t *d_token, int pos, float *logits,
                        int32_t *next_token, int32_t *d_err, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Latent-MoE layer ([k3_run.c] real_cfg_hardcoded(): n_experts 896, top-16,
+ * 2 shared experts, latent 3584, moe inter 3072, routed_scale, renorm,
+ * latent_norm; [cpu_weights.rs] MoeWeights: down, up, norm, router, bias,
+ * experts (w1, w2, w3), shared).  T token rows are independent.
+ * ---------------------------------------------------------------------- */
+
+/* Router: logits = W_r x (bf16 [n_experts][hidden]), sigma = sigmoid(logits);
+ * topk_idx[t] = the top_k experts by sigma + bias (bias: fp32 [n_experts],
+ * nullable = zeros; it affects the selection only), in descending order with
+ * the lower expert id first on equal scores; topk_w[t][j] = routed_scale *
+ * sigma_j / (sum of the selected sigma).  x: [T][hidden]; outputs [T][top_k]
+ * (int32 and fp32).  hidden % 32 == 0, hidden <= 12288, n_experts <= 1024,
+ * top_k <= min(32, n_experts).  ws: k2_moe_route_workspace_bytes(T,
+ * n_experts) bytes, 256-byte aligned. */
+size_t k2_moe_route_workspace_bytes(int T, int n_experts);
+int k2_moe_route(const uint16_t *Wr, const float *bias, const float *x, int T, int hidden,
+                 int n_experts, int top_k, float routed_scale, int32_t *topk_idx, float *topk_w,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/* Routed experts, gathered by expert ([k3_run.c]: routed experts multiplied
+ * directly from MXFP4):
+ *   r[t] = sum over j < top_k, in slot order, of
+ *          topk_w[t][j] * W2_e (silu(W1_e z[t]) * (W3_e z[t])),  e = topk_idx[t][j].
+ * z: [T][latent] fp32; r: [T][latent] fp32, overwritten.  Expert weights are
+ * MXFP4 (format above) for all n_experts experts back to back:
+ *   w13q [n_experts][2 inter][latent/2], w13s [n_experts][2 inter][latent/32]
+ *        (rows 0..inter-1 are W1 (gate), rows inter..2 inter-1 are W3 (up)),
+ *   w2q  [n_experts][latent][inter/2],   w2s  [n_experts][latent][inter/32].
+ * Only the selected experts are read.  An expert id outside [0, n_experts)
+ * is detected on the device: *d_err (device int32, nullable) is set to
+ * K2_ERANGE and that slot contributes nothing.  A token may select an expert
+ * more than once (each slot counts).  latent, inter: multiples of 32, at most
+ * 4096; T * top_k <= 1024; top_k <= 32; n_experts <= 1024.
+ * ws: k2_moe_workspace_bytes(T, top_k, latent, inter) bytes, 256-byte
+ * aligned.  The result does not depend on timing (fixed summation order). */
+size_t k2_moe_workspace_bytes(int T, int top_k, int latent, int inter);
+int k2_moe_expert_gemv(const float *z, int T, int latent, int inter, const int32_t *topk_idx,
+                       const float *topk_w, int top_k, int n_experts, const uint8_t *w13q,
+                       const uint8_t *w13s, const uint8_t *w2q, const uint8_t *w2s, float *r,
+                       int32_t *d_err, void *ws, size_t ws_bytes, void *stream);
+
+typedef struct {
+    int hidden, latent, inter, n_experts, top_k, n_shared;
+    float routed_scale;
+    float eps;                    /* latent RMSNorm */
+} k2_moe_config;
+
+/* Weights of one latent-MoE layer (host struct of device pointers). */
+typedef struct {
+    k2_moe_config cfg;
+    const uint16_t *w_router;     /* bf16 [n_experts][hidden] */
+    const float *router_bias;     /* fp32 [n_experts], nullable = zeros */
+    const uint16_t *w_down;       /* bf16 [latent][hidden] */
+    const float *latent_gamma;    /* fp32 [latent] */
+    const uint16_t *w_up;         /* bf16 [hidden][latent] */
+    const uint8_t *w13q, *w13s;   /* routed experts, layout of k2_moe_expert_gemv */
+    const uint8_t *w2q, *w2s;
+    const uint16_t *sh_w13;       /* bf16 [n_shared][2 inter][hidden]: W1 rows, then W3 rows */
+    const uint16_t *sh_w2;        /* bf16 [n_shared][hidden][inter] */
+} k2_moe_layer_weights;
+
+/* The whole layer on x [T][hidden] fp32:
+ *   route (k2_moe_route on x), z = RMSNorm(W_dn x) * latent_gamma (one group,
+ *   eps), r = k2_moe_expert_gemv(z), y = W_up r + sum_s W2_s(silu(W1_s x) *
+ *   (W3_s x)).
+ * y: [T][hidden], overwritten.  topk_idx_out / topk_w_out ([T][top_k],
+ * nullable) receive the routing.  d_err as in k2_moe_expert_gemv.  Limits:
+ * those of k2_moe_route and k2_moe_expert_gemv.  ws:
+ * k2_moe_layer_workspace_bytes(&cfg, T) bytes, 256-byte aligned. */
+size_t k2_moe_layer_workspace_bytes(const k2_moe_config *cfg, int T);
+int k2_moe_layer(const k2_moe_layer_weights *w, const float *x, int T, float *y,
+                 int32_t *topk_idx_out, float *topk_w_out, int32_t *d_err, void *ws,
+                 size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,7 @@ def lib():
         L.orc_decode_step.argtypes = [_vp, C.c_int, C.c_int, _vp]
         L.orc_moe_route.argtypes = [_vp, _vp, _vp, C.c_int, C.c_int, C.c_int, C.c_double,
                                     _vp, _vp]
+        L.orc_swiglu_expert.argtypes = [_vp, _vp, _vp, C.c_int, C.c_int, C.c_int, _vp]
         L.orc_moe_apply.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int, _vp, C.c_int,
                                     C.c_int, C.c_int, C.c_double, _vp, _vp, C.c_int, _vp]
         L.orc_num_threads.restype = C.c_int
@@ -401,6 +402,18 @@ def moe_route(wr: Mat, bias: np.ndarray, x: np.ndarray, top_k: int, routed_scale
     lib().orc_moe_route(C.addressof(wr.c), _p(b), _p(xx), H, E, top_k, routed_scale,
                         _p(sel), _p(gate))
     return sel, gate
+
+
+def swiglu_expert(w13: Mat, w2: Mat, u: np.ndarray) -> np.ndarray:
+    """One SwiGLU expert W2 (silu(W1 u) * (W3 u)); W13 stacks W1 then W3."""
+    inter = w13.shape[0] // 2
+    out_dim = w2.shape[0]
+    uu = np.ascontiguousarray(u, np.float64)
+    assert uu.size == w13.shape[1] and w2.shape[1] == inter
+    out = np.empty(out_dim, np.float64)
+    lib().orc_swiglu_expert(C.addressof(w13.c), C.addressof(w2.c), _p(uu), uu.size, inter,
+                            out_dim, _p(out))
+    return out
 
 
 def moe_apply(wdn: Mat, wup: Mat, experts13: Dict[int, Mat], experts2: Dict[int, Mat],

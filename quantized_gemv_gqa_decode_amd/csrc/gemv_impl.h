@@ -13,49 +13,104 @@ template <> struct WT<K2_BF16>    { static constexpr int EPC = 8;  };
 template <> struct WT<K2_FP8E4M3> { static constexpr int EPC = 16; };
 template <> struct WT<K2_MXFP4>   { static constexpr int EPC = 32; };
 
-// dot of one 16-byte weight chunk with EPC consecutive activations in LDS
-template <int WDT>
-__device__ __forceinline__ float chunk_dot(const k2_u4 w, const float *__restrict__ x)
+// Layout of activations staged in LDS.  A 16-byte weight chunk holds EPC
+// consecutive elements; lane c of a wave works on chunk c and needs EPC/4
+// float4s of x.  Stored linearly, lane c would read at a stride of 4*EPC
+// bytes (8-way LDS bank conflicts for MXFP4).  Instead float4 j of chunk c
+// is stored at float4 slot j*S + c ("planes" of S float4s): a wave's read of
+// plane j is 64 consecutive 16-byte words, and an odd S spreads the EPC/4
+// writes of one chunk over distinct banks.  One vector takes EPC*S floats.
+__host__ __device__ constexpr int xs_plane(int cpr) { return cpr | 1; }
+
+template <int EPC>
+__device__ __forceinline__ int xs_offset(int k, int S)
 {
-    float s0 = 0.f, s1 = 0.f;
+    return (((k % EPC) >> 2) * S + k / EPC) * 4 + (k & 3);
+}
+
+template <int I>
+__device__ __forceinline__ uint32_t word(const k2_u4 &w)
+{
+    if constexpr (I == 0) return w.x;
+    else if constexpr (I == 1) return w.y;
+    else if constexpr (I == 2) return w.z;
+    else return w.w;
+}
+
+// The 4 weights of plane J (elements 4J..4J+3) of a 16-byte chunk, decoded
+// (MXFP4 without its block scale).
+template <int WDT, int J>
+__device__ __forceinline__ float4 plane_w(const k2_u4 &w)
+{
     if constexpr (WDT == K2_F32) {
-        const float4 xv = *reinterpret_cast<const float4 *>(x);
-        s0 = __uint_as_float(w.x) * xv.x + __uint_as_float(w.y) * xv.y;
-        s1 = __uint_as_float(w.z) * xv.z + __uint_as_float(w.w) * xv.w;
+        return make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                           __uint_as_float(w.w));
     } else if constexpr (WDT == K2_BF16) {
-        const float4 a = *reinterpret_cast<const float4 *>(x);
-        const float4 b = *reinterpret_cast<const float4 *>(x + 4);
-        s0 = bf16_lo(w.x) * a.x + bf16_hi(w.x) * a.y;
-        s1 = bf16_lo(w.y) * a.z + bf16_hi(w.y) * a.w;
-        s0 += bf16_lo(w.z) * b.x + bf16_hi(w.z) * b.y;
-        s1 += bf16_lo(w.w) * b.z + bf16_hi(w.w) * b.w;
+        const uint32_t a = word<2 * J>(w), b = word<2 * J + 1>(w);
+        return make_float4(bf16_lo(a), bf16_hi(a), bf16_lo(b), bf16_hi(b));
     } else if constexpr (WDT == K2_FP8E4M3) {
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 xv = *reinterpret_cast<const float4 *>(x + 4 * i);
-            const k2_f2 lo = fp8x2_lo(ws[i]);
-            const k2_f2 hi = fp8x2_hi(ws[i]);
-            s0 += lo.x * xv.x + lo.y * xv.y;
-            s1 += hi.x * xv.z + hi.y * xv.w;
-        }
-    } else {  // MXFP4: 32 E2M1 values, low nibble first
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 xa = *reinterpret_cast<const float4 *>(x + 8 * i);
-            const float4 xb = *reinterpret_cast<const float4 *>(x + 8 * i + 4);
-            const k2_f2 v0 = fp4x2<0>(ws[i]);
-            const k2_f2 v1 = fp4x2<1>(ws[i]);
-            const k2_f2 v2 = fp4x2<2>(ws[i]);
-            const k2_f2 v3 = fp4x2<3>(ws[i]);
-            s0 += v0.x * xa.x + v0.y * xa.y;
-            s1 += v1.x * xa.z + v1.y * xa.w;
-            s0 += v2.x * xb.x + v2.y * xb.y;
-            s1 += v3.x * xb.z + v3.y * xb.w;
-        }
+        const uint32_t u = word<J>(w);
+        const k2_f2 lo = fp8x2_lo(u), hi = fp8x2_hi(u);
+        return make_float4(lo.x, lo.y, hi.x, hi.y);
+    } else {  // MXFP4: byte m of the chunk holds elements 2m (low nibble) and 2m+1
+        const uint32_t u = word<J / 2>(w);
+        const k2_f2 v0 = fp4x2<2 * (J % 2)>(u), v1 = fp4x2<2 * (J % 2) + 1>(u);
+        return make_float4(v0.x, v0.y, v1.x, v1.y);
     }
-    return s0 + s1;
+}
+
+// s[b][r] += dot(chunk of row r, chunk of token b) for R rows that share the
+// same activation chunk, nb <= B tokens.  Plane-major: one float4 of x per
+// token and 4 decoded weights per row are live at a time.  xc: float4 0 of
+// the chunk of token 0 in LDS; P: plane stride (floats); TS: token stride.
+template <int WDT, int R, int B, int J = 0>
+__device__ __forceinline__ void dot_planes(const k2_u4 (&w)[R], const float *__restrict__ xc, int P,
+                                           int TS, int nb, float (&s)[B][R])
+{
+    if constexpr (J < WT<WDT>::EPC / 4) {
+        float4 xv[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+            if (b < nb) xv[b] = *reinterpret_cast<const float4 *>(xc + b * TS + J * P);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float4 wv = plane_w<WDT, J>(w[r]);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                if (b < nb) {
+                    s[b][r] = fmaf(wv.x, xv[b].x, s[b][r]);
+                    s[b][r] = fmaf(wv.y, xv[b].y, s[b][r]);
+                    s[b][r] = fmaf(wv.z, xv[b].z, s[b][r]);
+                    s[b][r] = fmaf(wv.w, xv[b].w, s[b][r]);
+                }
+            }
+        }
+        dot_planes<WDT, R, B, J + 1>(w, xc, P, TS, nb, s);
+    }
+}
+
+// One 16-byte chunk per row into acc: MXFP4 applies each row's block scale
+// to its partial sum; the other formats accumulate directly (fp8 row scales
+// are applied once per row at the end).
+template <int WDT, int R, int B>
+__device__ __forceinline__ void chunk_rows(const k2_u4 (&w)[R], const float (&sc)[R],
+                                           const float *__restrict__ xc, int P, int TS, int nb,
+                                           float (&acc)[B][R])
+{
+    if constexpr (WDT == K2_MXFP4) {
+        float part[B][R];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int r = 0; r < R; ++r) part[b][r] = 0.f;
+        dot_planes<WDT, R, B>(w, xc, P, TS, nb, part);
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[b][r] = fmaf(part[b][r], sc[r], acc[b][r]);
+    } else {
+        dot_planes<WDT, R, B>(w, xc, P, TS, nb, acc);
+    }
 }
 
 // Activations are staged in LDS by the whole block.  Their global loads are
@@ -78,8 +133,9 @@ __device__ __forceinline__ void issue_x(const GemvArgs &a, float4 (&xr)[XV])
 // Write the staged activations to LDS.  With PRO_NORM the single vector is
 // the residual stream h and LDS receives GroupedRMSNorm(h) * gamma: G equal
 // contiguous groups, each divided by sqrt(mean of its squares + eps).
-template <int XV, int PRO>
-__device__ __forceinline__ void finish_x(float *xs, const GemvArgs &a, const float4 (&xr)[XV])
+template <int XV, int PRO, int EPC>
+__device__ __forceinline__ void finish_x(float *xs, const GemvArgs &a, const float4 (&xr)[XV],
+                                         int S)
 {
     const int n = a.B * a.K;
     if constexpr (PRO == PRO_NORM) {
@@ -123,14 +179,17 @@ __device__ __forceinline__ void finish_x(float *xs, const GemvArgs &a, const flo
                 float4 t = xr[v];
                 t.x = t.x * r * gm.x; t.y = t.y * r * gm.y;
                 t.z = t.z * r * gm.z; t.w = t.w * r * gm.w;
-                *reinterpret_cast<float4 *>(xs + i) = t;
+                *reinterpret_cast<float4 *>(xs + xs_offset<EPC>(i, S)) = t;   // B == 1
             }
         }
     } else {
 #pragma unroll
         for (int v = 0; v < XV; ++v) {
             const int i = (v * K2_BLOCK + threadIdx.x) * 4;
-            if (i < n) *reinterpret_cast<float4 *>(xs + i) = xr[v];
+            if (i < n) {
+                const int b = i / a.K, k = i - b * a.K;
+                *reinterpret_cast<float4 *>(xs + b * EPC * S + xs_offset<EPC>(k, S)) = xr[v];
+            }
         }
     }
     __syncthreads();
@@ -190,6 +249,7 @@ void gemv_kernel(const GemvArgs a)
     constexpr int EPC = WT<WDT>::EPC;
     const int K = a.K;
     const int CPR = K / EPC;                       // 16-byte chunks per row
+    const int S = xs_plane(CPR);
     const int passes = (CPR + U * K2_WAVE - 1) / (U * K2_WAVE);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -210,7 +270,7 @@ void gemv_kernel(const GemvArgs a)
     // ... then weights (unconditionally: a wave without a unit reads a clamped
     // row it never uses, which keeps the issue path free of branches)
     load_pass<WDT, R, U>(a, rows, ok, 0, CPR, lane, w, sc);
-    finish_x<XV, PRO>(xs, a, xr);                  // overlaps the weight loads
+    finish_x<XV, PRO, EPC>(xs, a, xr, S);                  // overlaps the weight loads
 
 #pragma unroll 1
     for (; unit < a.n_units; unit += stride) {
@@ -226,18 +286,7 @@ void gemv_kernel(const GemvArgs a)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = (p * U + u) * K2_WAVE + lane;
-                if (c < CPR) {
-#pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        const float *xc = xs + b * K + c * EPC;
-#pragma unroll
-                        for (int r = 0; r < R; ++r) {
-                            const float d = chunk_dot<WDT>(w[u][r], xc);
-                            if constexpr (WDT == K2_MXFP4) acc[b][r] += d * sc[u][r];
-                            else acc[b][r] += d;
-                        }
-                    }
-                }
+                if (c < CPR) chunk_rows<WDT, R, B>(w[u], sc[u], xs + c * 4, 4 * S, EPC * S, B, acc);
             }
         }
         // the next unit's first loads fly while this unit is reduced
@@ -316,7 +365,8 @@ static int launch(const GemvArgs &a0, hipStream_t st, int max_blocks)
     const int64_t blocks_needed = (a.n_units + K2_WAVES_PER_BLOCK - 1) / K2_WAVES_PER_BLOCK;
     int blocks = (int)(blocks_needed < max_blocks ? blocks_needed : max_blocks);
     if (blocks < 1) blocks = 1;
-    const size_t lds = (size_t)B * a.K * sizeof(float);
+    constexpr int EPC = WT<WDT>::EPC;
+    const size_t lds = (size_t)B * EPC * xs_plane(a.K / EPC) * sizeof(float);
     hipLaunchKernelGGL((gemv_kernel<WDT, R, U, B, PRO, EPI, XV>), dim3(blocks), dim3(K2_BLOCK), lds,
                        st, a);
     K2_CHECK_LAUNCH();

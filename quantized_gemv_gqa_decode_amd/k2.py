@@ -77,6 +77,13 @@ SIGNATURES = {
     "k2_model_check": (_i, [_vp]),
     "k2_decode_step": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "k2_decode_step_dev": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp]),
+    "k2_moe_route_workspace_bytes": (_sz, [_i, _i]),
+    "k2_moe_route": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+    "k2_moe_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "k2_moe_expert_gemv": (_i, [_vp, _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _sz, _vp]),
+    "k2_moe_layer_workspace_bytes": (_sz, [_vp, _i]),
+    "k2_moe_layer": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -249,3 +256,49 @@ def k2_decode_step_dev(model: k2_model, d_token, pos: int, logits, next_token, d
                        stream=None):
     return load().k2_decode_step_dev(C.addressof(model), ptr(d_token), int(pos), ptr(logits),
                                      ptr(next_token), ptr(d_err), stream_handle(stream))
+
+
+# --------------------------------------------------------------- latent MoE --
+
+def k2_moe_route_workspace_bytes(T, n_experts) -> int:
+    return load().k2_moe_route_workspace_bytes(T, n_experts)
+
+
+def k2_moe_route(Wr, bias, x, T, hidden, n_experts, top_k, routed_scale, topk_idx, topk_w, ws,
+                 ws_bytes, stream=None):
+    return load().k2_moe_route(ptr(Wr), ptr(bias), ptr(x), T, hidden, n_experts, top_k,
+                               float(routed_scale), ptr(topk_idx), ptr(topk_w), ptr(ws), ws_bytes,
+                               stream_handle(stream))
+
+
+def k2_moe_workspace_bytes(T, top_k, latent, inter) -> int:
+    return load().k2_moe_workspace_bytes(T, top_k, latent, inter)
+
+
+def k2_moe_expert_gemv(z, T, latent, inter, topk_idx, topk_w, top_k, n_experts, w13q, w13s, w2q,
+                       w2s, r, d_err, ws, ws_bytes, stream=None):
+    return load().k2_moe_expert_gemv(ptr(z), T, latent, inter, ptr(topk_idx), ptr(topk_w), top_k,
+                                     n_experts, ptr(w13q), ptr(w13s), ptr(w2q), ptr(w2s), ptr(r),
+                                     ptr(d_err), ptr(ws), ws_bytes, stream_handle(stream))
+
+
+class k2_moe_config(C.Structure):
+    _fields_ = [("hidden", _i), ("latent", _i), ("inter", _i), ("n_experts", _i), ("top_k", _i),
+                ("n_shared", _i), ("routed_scale", _f), ("eps", _f)]
+
+
+class k2_moe_layer_weights(C.Structure):
+    _fields_ = [("cfg", k2_moe_config), ("w_router", _vp), ("router_bias", _vp), ("w_down", _vp),
+                ("latent_gamma", _vp), ("w_up", _vp), ("w13q", _vp), ("w13s", _vp), ("w2q", _vp),
+                ("w2s", _vp), ("sh_w13", _vp), ("sh_w2", _vp)]
+
+
+def k2_moe_layer_workspace_bytes(cfg: k2_moe_config, T) -> int:
+    return load().k2_moe_layer_workspace_bytes(C.addressof(cfg), T)
+
+
+def k2_moe_layer(weights: k2_moe_layer_weights, x, T, y, topk_idx_out, topk_w_out, d_err, ws,
+                 ws_bytes, stream=None):
+    return load().k2_moe_layer(C.addressof(weights), ptr(x), T, ptr(y), ptr(topk_idx_out),
+                               ptr(topk_w_out), ptr(d_err), ptr(ws), ws_bytes,
+                               stream_handle(stream))

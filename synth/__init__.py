@@ -151,6 +151,10 @@ class MoeConfig:
     eps: float
     tokens: Tuple[int, ...]
     seed: int = 0
+    expert_pool: int = 1 << 25      # bf16 values shared by the routed experts' windows
+
+    def replace(self, **kw) -> "MoeConfig":
+        return dataclasses.replace(self, **kw)
 
 
 TINY = DecoderConfig(
@@ -259,12 +263,33 @@ def moe_router_bias(cfg: MoeConfig) -> np.ndarray:
     return normal_f32(cfg.seed, "moe.router_bias", (cfg.n_experts,), WEIGHT_STD).numpy()
 
 
-def moe_expert_draw(cfg: MoeConfig, e: int) -> Tuple[np.ndarray, np.ndarray]:
+def moe_expert_pool(cfg: MoeConfig) -> np.ndarray:
+    """Routed-expert weights are windows of one seeded pool of bf16 draws
+    (896 full-size experts are 29.6e9 values, too many to draw one by one;
+    each window has the same 0.02 * N(0, 1) bf16 distribution).  Returned
+    with its head repeated after its end, so that every window is one
+    contiguous slice: length expert_pool + 2 * inter * latent."""
+    base = normal_bf16_bits(cfg.seed, "moe.expert_pool", (cfg.expert_pool,))
+    return np.concatenate([base, np.resize(base, 2 * cfg.inter * cfg.latent)])
+
+
+def moe_expert_offsets(cfg: MoeConfig, e: int) -> Tuple[int, int]:
+    """Pool offsets (multiples of 64 values) of expert e's W13 and W2."""
+    slots = cfg.expert_pool // 64
+    o13 = (sub_seed(cfg.seed, f"moe.expert.{e}.w13") % slots) * 64
+    o2 = (sub_seed(cfg.seed, f"moe.expert.{e}.w2") % slots) * 64
+    return o13, o2
+
+
+def moe_expert_draw(cfg: MoeConfig, e: int, pool: Optional[np.ndarray] = None
+                    ) -> Tuple[np.ndarray, np.ndarray]:
     """bf16 draws of expert e: w13 [2*inter][latent] (gate rows, then up rows)
-    and w2 [latent][inter]."""
-    w13 = normal_bf16_bits(cfg.seed, f"moe.expert.{e}.w13", (2 * cfg.inter, cfg.latent))
-    w2 = normal_bf16_bits(cfg.seed, f"moe.expert.{e}.w2", (cfg.latent, cfg.inter))
-    return w13, w2
+    and w2 [latent][inter], as views of the pool."""
+    pool = moe_expert_pool(cfg) if pool is None else pool
+    o13, o2 = moe_expert_offsets(cfg, e)
+    n13, n2 = 2 * cfg.inter * cfg.latent, cfg.latent * cfg.inter
+    return (pool[o13:o13 + n13].reshape(2 * cfg.inter, cfg.latent),
+            pool[o2:o2 + n2].reshape(cfg.latent, cfg.inter))
 
 
 def moe_activations(cfg: MoeConfig, T: int, rep: int = 0) -> np.ndarray:

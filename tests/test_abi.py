@@ -142,3 +142,51 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(k2, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         k2.load(build_if_missing=False)
+
+
+def test_moe_validation():
+    L = k2.load()
+    st = None
+    assert k2.k2_moe_workspace_bytes(32, 16, 3584, 3072) > 32 * 16 * (3584 + 3072) * 4
+    assert k2.k2_moe_workspace_bytes(0, 16, 3584, 3072) == 0
+    assert k2.k2_moe_route_workspace_bytes(8, 896) >= 8 * 896 * 4
+    nb = k2.k2_moe_workspace_bytes(8, 16, 3584, 3072)
+
+    def ex(T=8, latent=3584, inter=3072, k=16, E=896, z=FAKE, ws=FAKE, wsb=nb):
+        return L.k2_moe_expert_gemv(z, T, latent, inter, FAKE, FAKE, k, E, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, None, ws, wsb, st)
+
+    assert ex(z=None) == k2.K2_EINVAL
+    assert ex(T=0) == k2.K2_EINVAL
+    assert ex(latent=3584 + 16) == k2.K2_EUNSUPPORTED
+    assert ex(inter=8192) == k2.K2_EUNSUPPORTED
+    assert ex(k=33) == k2.K2_EUNSUPPORTED
+    assert ex(E=1025) == k2.K2_EUNSUPPORTED
+    assert ex(E=8, k=16) == k2.K2_EUNSUPPORTED                  # top_k > n_experts
+    assert ex(T=65) == k2.K2_EUNSUPPORTED                       # 1040 pairs
+    assert ex(ws=FAKE + 16) == k2.K2_EINVAL                     # 256-byte alignment
+    assert ex(wsb=nb - 1) == k2.K2_EINVAL
+    rb = k2.k2_moe_route_workspace_bytes(8, 896)
+
+    def rt(T=8, H=7168, E=896, k=16, ws=FAKE, wsb=rb):
+        return L.k2_moe_route(FAKE, None, FAKE, T, H, E, k, 1.0, FAKE, FAKE, ws, wsb, st)
+
+    assert rt(H=12288 + 32) == k2.K2_EUNSUPPORTED
+    assert rt(H=7168 + 8) == k2.K2_EUNSUPPORTED
+    assert rt(E=2048) == k2.K2_EUNSUPPORTED
+    assert rt(E=8) == k2.K2_EUNSUPPORTED
+    assert rt(T=0) == k2.K2_EINVAL
+    assert rt(wsb=rb - 4) == k2.K2_EINVAL
+    cfg = k2.k2_moe_config(7168, 3584, 3072, 896, 16, 2, 1.0, 1e-5)
+    lb = k2.k2_moe_layer_workspace_bytes(cfg, 32)
+    assert lb > nb
+    w = k2.k2_moe_layer_weights(cfg, *([FAKE] * 11))
+    assert L.k2_moe_layer(C.addressof(w), FAKE, 32, FAKE, None, None, None, FAKE, lb - 1, st) \
+        == k2.K2_EINVAL
+    w.sh_w13 = None
+    assert L.k2_moe_layer(C.addressof(w), FAKE, 32, FAKE, None, None, None, FAKE, lb, st) \
+        == k2.K2_EINVAL                                          # 2 shared experts, no weights
+    w.sh_w13 = FAKE
+    w.cfg.hidden = 7168 + 16
+    assert L.k2_moe_layer(C.addressof(w), FAKE, 32, FAKE, None, None, None, FAKE, lb, st) \
+        == k2.K2_EUNSUPPORTED

@@ -1,0 +1,329 @@
+"""GPU parity of the latent-MoE path (k2_moe_route, k2_moe_expert_gemv,
+k2_moe_layer) against the CPU oracle.
+
+Routing: the GPU's top-k must be the oracle's, in order, except across a
+near-tie (two fp64 scores closer than 1e-5; fp32 and fp64 may order them
+either way).  Gates within 1e-5.  Expert and layer outputs: max-abs 5e-2 (the
+tolerance for quantized weights), with the routing the GPU chose fed to the
+oracle, after the routing itself has been checked as above.  The expert
+weights are MXFP4 quantized on the device from the same bf16 draws the oracle
+quantizes with its own quantizer (the two quantizers are bit-exact; that is
+pinned in the op tests).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import DEV, GPU, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+if GPU:
+    from quantized_gemv_gqa_decode_amd import k2
+    from quantized_gemv_gqa_decode_amd.moe import MoeLayer
+
+TOL = 5e-2
+TIE = 1e-5
+
+# ragged shapes: latent 160 = 5 MXFP4 chunks per row, inter 96 = 3 chunks,
+# 192 W13 rows and 160 W2 rows (partial row blocks), 40 experts
+SMALL = synth.K3_MOE.replace(name="moe-small", hidden=320, latent=160, inter=96, n_experts=40,
+                             top_k=6, n_shared=2, expert_pool=1 << 16, tokens=(1, 5, 8, 32))
+# rows spanning many blocks, latent 1056 = 33 chunks (most of a wave's lanes)
+MEDIUM = synth.K3_MOE.replace(name="moe-medium", hidden=1024, latent=1056, inter=544,
+                              n_experts=64, top_k=8, n_shared=1, expert_pool=1 << 20,
+                              tokens=(1, 8, 32))
+
+
+class OracleMoe:
+    """The oracle's view of a MoeConfig: dense weights as bf16 Mats, routed
+    experts quantized to MXFP4 on first use."""
+
+    def __init__(self, cfg):
+        self.cfg = cfg
+        self.wr = oracle.Mat.from_draw("bf16", synth.moe_dense_weight(cfg, "router"))
+        self.bias = synth.moe_router_bias(cfg)
+        self.wdn = oracle.Mat.from_draw("bf16", synth.moe_dense_weight(cfg, "down"))
+        self.wup = oracle.Mat.from_draw("bf16", synth.moe_dense_weight(cfg, "up"))
+        s13 = synth.moe_dense_weight(cfg, "shared_w13")
+        s2 = synth.moe_dense_weight(cfg, "shared_w2")
+        I, H = cfg.inter, cfg.hidden
+        self.sh13 = [oracle.Mat.from_draw("bf16", s13[s * 2 * I:(s + 1) * 2 * I])
+                     for s in range(cfg.n_shared)]
+        self.sh2 = [oracle.Mat.from_draw("bf16", s2[s * H:(s + 1) * H]) for s in range(cfg.n_shared)]
+        self.pool = synth.moe_expert_pool(cfg)
+        self.e13, self.e2 = {}, {}
+
+    def expert(self, e):
+        if e not in self.e13:
+            w13, w2 = synth.moe_expert_draw(self.cfg, e, self.pool)
+            self.e13[e] = oracle.Mat.from_draw("mxfp4", w13)
+            self.e2[e] = oracle.Mat.from_draw("mxfp4", w2)
+        return self.e13[e], self.e2[e]
+
+    def sigma(self, x):
+        return 1.0 / (1.0 + np.exp(-self.wr.matvec(x)))
+
+    def route(self, x):
+        return oracle.moe_route(self.wr, self.bias, x, self.cfg.top_k, self.cfg.routed_scale)
+
+    def gates_for(self, x, sel):
+        s = self.sigma(x)[sel]
+        return self.cfg.routed_scale * s / s.sum()
+
+    def layer(self, x, sel, gate):
+        for e in sel:
+            self.expert(int(e))
+        c = self.cfg
+        return oracle.moe_apply(self.wdn, self.wup, self.e13, self.e2, self.sh13, self.sh2, x,
+                                c.latent, c.inter, c.eps, sel, gate)
+
+    def routed(self, z, sel, gate):
+        r = np.zeros(self.cfg.latent)
+        for e, g in zip(sel, gate):
+            w13, w2 = self.expert(int(e))
+            r += g * oracle.swiglu_expert(w13, w2, z)
+        return r
+
+
+def check_routing(om: OracleMoe, x, gpu_sel, gpu_w):
+    """GPU selection == oracle ranking of sigma + bias, modulo near-ties."""
+    k = om.cfg.top_k
+    score = om.sigma(x) + om.bias.astype(np.float64)
+    order = np.argsort(-score, kind="stable")
+    ranked = score[order]
+    gpu_sel = np.asarray(gpu_sel)
+    assert len(set(gpu_sel.tolist())) == k
+    # every GPU pick is within TIE of the score at its rank
+    for j, e in enumerate(gpu_sel):
+        assert abs(score[e] - ranked[j]) < TIE, (j, int(e), score[e], ranked[j])
+    if ranked[k - 1] - ranked[k] >= TIE:
+        assert set(gpu_sel.tolist()) == set(order[:k].tolist())
+    ties = [j for j in range(k) if gpu_sel[j] != order[j]]
+    g_ref = om.gates_for(x, gpu_sel)
+    assert np.abs(np.asarray(gpu_w, np.float64) - g_ref).max() < 1e-5
+    return ties
+
+
+def layer_parity(cfg, T, lay=None, om=None):
+    om = om or OracleMoe(cfg)
+    lay = lay or MoeLayer(cfg, DEV)
+    x = synth.moe_activations(cfg, T)
+    say(f"{cfg.name}: T={T}")
+    y, idx, w = lay.forward(to_dev(x))
+    torch.cuda.synchronize()
+    assert int(lay.err.item()) == 0
+    y, idx, w = to_host(y), to_host(idx), to_host(w)
+    worst = 0.0
+    for t in range(T):
+        ties = check_routing(om, x[t], idx[t], w[t])
+        if ties:
+            say(f"  token {t}: routing near-tie at slots {ties}")
+        ref = om.layer(x[t], idx[t].astype(np.int32), om.gates_for(x[t], idx[t]))
+        err = float(np.abs(y[t].astype(np.float64) - ref).max())
+        worst = max(worst, err)
+        assert err <= TOL, (t, err)
+    say(f"  max|dy| = {worst:.3g} (tol {TOL}), max|y| = {np.abs(y).max():.3g}")
+    return worst
+
+
+@pytest.mark.parametrize("T", [1, 5, 8, 32])
+def test_moe_layer_small(T):
+    layer_parity(SMALL, T)
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_moe_layer_medium(T):
+    layer_parity(MEDIUM, T)
+
+
+def test_moe_layer_repeat_is_deterministic():
+    lay = MoeLayer(SMALL, DEV)
+    x = to_dev(synth.moe_activations(SMALL, 32))
+    y1 = lay.forward(x)[0].clone()
+    y2 = lay.forward(x)[0].clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_moe_route_standalone():
+    cfg = SMALL.replace(routed_scale=2.5)
+    om = OracleMoe(cfg)
+    lay = MoeLayer(SMALL, DEV)
+    T = 8
+    x = synth.moe_activations(cfg, T, rep=1)
+    nb = k2.k2_moe_route_workspace_bytes(T, cfg.n_experts)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+
+    def route(bias):
+        idx = torch.empty((T, cfg.top_k), dtype=torch.int32, device=DEV)
+        w = torch.empty((T, cfg.top_k), dtype=torch.float32, device=DEV)
+        k2.check(k2.k2_moe_route(lay.w_router, bias, to_dev(x), T, cfg.hidden, cfg.n_experts,
+                                 cfg.top_k, cfg.routed_scale, idx, w, ws, nb))
+        torch.cuda.synchronize()
+        return to_host(idx), to_host(w)
+
+    idx, w = route(lay.bias)
+    for t in range(T):
+        check_routing(om, x[t], idx[t], w[t])
+        sel, gate = om.route(x[t])
+        if (idx[t] == sel).all():
+            assert np.abs(w[t] - gate).max() < 1e-5
+    # without a bias the selection is the plain top-k of sigma
+    idx, w = route(None)
+    for t in range(T):
+        s = om.sigma(x[t])
+        order = np.argsort(-s, kind="stable")[:cfg.top_k]
+        assert all(abs(s[a] - s[b]) < TIE for a, b in zip(idx[t], order))
+        assert np.abs(w[t] - om.gates_for(x[t], idx[t])).max() < 1e-5
+
+
+def run_expert_gemv(lay, cfg, z, sel, gate, d_err=None):
+    T, k = sel.shape
+    r = torch.full((T, cfg.latent), 7.0, dtype=torch.float32, device=DEV)
+    nb = k2.k2_moe_workspace_bytes(T, k, cfg.latent, cfg.inter)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    k2.check(k2.k2_moe_expert_gemv(to_dev(z), T, cfg.latent, cfg.inter, to_dev(sel),
+                                   to_dev(gate), k, cfg.n_experts, lay.w13q, lay.w13s, lay.w2q,
+                                   lay.w2s, r, d_err, ws, nb))
+    torch.cuda.synchronize()
+    return to_host(r)
+
+
+@pytest.mark.parametrize("case", ["random", "shared_experts", "duplicate_slot", "many_per_expert"])
+def test_moe_expert_gemv_given_routing(case):
+    """k2_moe_expert_gemv with a routing passed in (so no near-tie can make the
+    two sides pick different experts), against the oracle's experts."""
+    cfg = SMALL
+    om = OracleMoe(cfg)
+    lay = MoeLayer(cfg, DEV)
+    rng = np.random.default_rng(7)
+    T, k, E = 11, cfg.top_k, cfg.n_experts
+    if case == "random":
+        sel = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+    elif case == "shared_experts":          # every token picks the same experts
+        sel = np.tile(rng.choice(E, k, replace=False), (T, 1))
+    elif case == "duplicate_slot":          # a token may list an expert twice
+        sel = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+        sel[:, 1] = sel[:, 0]
+    else:                                   # 3 experts shared by 11 tokens, odd counts
+        sel = rng.choice(3, (T, k)).astype(np.int64) + 5
+    sel = sel.astype(np.int32)
+    gate = rng.uniform(0.05, 1.0, (T, k)).astype(np.float32)
+    z = rng.standard_normal((T, cfg.latent)).astype(np.float32)
+    r = run_expert_gemv(lay, cfg, z, sel, gate)
+    worst = 0.0
+    for t in range(T):
+        ref = om.routed(z[t], sel[t], gate[t].astype(np.float64))
+        worst = max(worst, float(np.abs(r[t] - ref).max()))
+    say(f"{case}: max|dr| = {worst:.3g}")
+    assert worst <= TOL
+
+
+def test_moe_expert_gemv_bad_expert_id_is_flagged_and_dropped():
+    cfg = SMALL
+    om = OracleMoe(cfg)
+    lay = MoeLayer(cfg, DEV)
+    rng = np.random.default_rng(3)
+    T, k = 3, cfg.top_k
+    sel = np.stack([rng.choice(cfg.n_experts, k, replace=False) for _ in range(T)]).astype(np.int32)
+    sel[1, 2] = cfg.n_experts + 3
+    sel[2, 0] = -1
+    gate = np.full((T, k), 0.25, np.float32)
+    z = rng.standard_normal((T, cfg.latent)).astype(np.float32)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    r = run_expert_gemv(lay, cfg, z, sel, gate, err)
+    assert int(err.item()) == k2.K2_ERANGE
+    for t in range(T):
+        keep = (sel[t] >= 0) & (sel[t] < cfg.n_experts)
+        ref = om.routed(z[t], sel[t][keep], gate[t][keep].astype(np.float64))
+        assert np.abs(r[t] - ref).max() <= TOL
+
+
+def test_moe_layer_identity_closed_form():
+    """Identity-expert construction (avarok cpu_weights.rs synth_moe: w1 = w2
+    = w3 = identity, expert e > 0 with w3[0][0] = 1 + e, down/up identity, no
+    shared experts): with z = RMSNorm(x[:latent]) and a routing fixed by the
+    bias, y[i] = sum_j g_j silu(z_i) z_i for i > 0 and y[0] gains the factor
+    c_e = stored(1 + e) per expert.  Checked on the GPU layer against this
+    closed form, computed here in numpy."""
+    H = Lt = I = 64
+    E, k = 8, 2
+    one = 0x3F80
+    eye = np.zeros((64, 64), np.uint16)
+    np.fill_diagonal(eye, one)
+    dev = DEV
+    # router weights zero: sigma = 0.5 for all, the bias decides the selection
+    wr = torch.zeros((E, H), dtype=torch.int16, device=dev)
+    bias = torch.tensor([0.0, 0.3, 0.0, 0.2, 0.0, 0.0, 0.0, 0.0], dtype=torch.float32, device=dev)
+    from quantized_gemv_gqa_decode_amd.model import upload
+    w13q = torch.empty((E, 2 * I, Lt // 2), dtype=torch.uint8, device=dev)
+    w13s = torch.empty((E, 2 * I, Lt // 32), dtype=torch.uint8, device=dev)
+    w2q = torch.empty((E, Lt, I // 2), dtype=torch.uint8, device=dev)
+    w2s = torch.empty((E, Lt, I // 32), dtype=torch.uint8, device=dev)
+    for e in range(E):
+        w3 = eye.copy()
+        if e > 0:
+            w3[0, 0] = torch.tensor([1.0 + e]).to(torch.bfloat16).view(torch.int16).numpy().view(
+                np.uint16)[0]
+        k2.check(k2.k2_quantize_mxfp4(upload(np.concatenate([eye, w3]), dev), w13q[e], w13s[e],
+                                      2 * I, Lt))
+        k2.check(k2.k2_quantize_mxfp4(upload(eye, dev), w2q[e], w2s[e], Lt, I))
+    eye_d = upload(eye, dev)
+    gamma = torch.ones(Lt, dtype=torch.float32, device=dev)
+    cfgc = k2.k2_moe_config(H, Lt, I, E, k, 0, 1.0, 1e-5)
+    wts = k2.k2_moe_layer_weights(cfgc, k2.ptr(wr), k2.ptr(bias), k2.ptr(eye_d), k2.ptr(gamma),
+                                  k2.ptr(eye_d), k2.ptr(w13q), k2.ptr(w13s), k2.ptr(w2q),
+                                  k2.ptr(w2s), None, None)
+    T = 4
+    x = np.random.default_rng(5).standard_normal((T, H)).astype(np.float32)
+    nb = k2.k2_moe_layer_workspace_bytes(cfgc, T)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    k2.check(k2.k2_moe_layer(wts, to_dev(x), T, y, idx, gw, None, ws, nb))
+    torch.cuda.synchronize()
+    assert (to_host(idx) == np.array([[1, 3]] * T)).all()
+    assert np.abs(to_host(gw) - 0.5).max() < 1e-6
+    # row 0 of W3: 1 + e = 2 (e = 1) has block amax 2, E8M0 scale 2^(1 - 2) and
+    # element 2 / 0.5 = 4; 4 (e = 3) has scale 2^0 and element 4: both exact
+    c = {1: 2.0, 3: 4.0}
+    for t in range(T):
+        xd = x[t].astype(np.float64)
+        z = xd / np.sqrt(np.mean(xd * xd) + 1e-5)
+        # identity W1/W2 quantize exactly; z enters through exact bf16 identity GEMVs
+        base = z / (1 + np.exp(-z)) * z
+        want = base.copy()
+        want[0] = 0.5 * base[0] * (c[1] + c[3])
+        assert np.abs(to_host(y)[t] - want).max() < 1e-4, t
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_moe_layer_k3_full_size(T):
+    """The K3-shaped layer at full size (896 MXFP4 experts, 15.7 GB): every
+    output of a sample of tokens against the oracle (tokens are independent,
+    so a sample checks the same launch configuration the benchmark times)."""
+    cfg = synth.K3_MOE
+    say("gpu layer build (896 experts)")
+    lay = MoeLayer(cfg, DEV)
+    om = OracleMoe(cfg)
+    x = synth.moe_activations(cfg, T)
+    y, idx, w = lay.forward(to_dev(x))
+    torch.cuda.synchronize()
+    assert int(lay.err.item()) == 0
+    y, idx, w = to_host(y), to_host(idx), to_host(w)
+    sample = sorted(set([0, T - 1, T // 2]))
+    worst = 0.0
+    for t in sample:
+        check_routing(om, x[t], idx[t], w[t])
+        ref = om.layer(x[t], idx[t].astype(np.int32), om.gates_for(x[t], idx[t]))
+        err = float(np.abs(y[t].astype(np.float64) - ref).max())
+        worst = max(worst, err)
+        assert err <= TOL, (t, err)
+    # the routing of every token is checked (cheap: one router matvec each)
+    for t in range(T):
+        check_routing(om, x[t], idx[t], w[t])
+    say(f"K3 T={T}: sampled tokens {sample}, max|dy| = {worst:.3g}")
