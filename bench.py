@@ -12,7 +12,9 @@ norm, lm_head and argmax, with the argmax fed back on the device.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
-Prints one JSON line.
+With --config k3-latent-moe-layer it times the K3-shaped latent-MoE layer
+(896 MXFP4 routed experts, top-16, 2 shared bf16 experts) at 1, 8 and 32
+token rows instead.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -175,6 +177,162 @@ def cpu_baseline(cfg, budget_s: float, prefix: int = 0):
             "cpu": platform.processor() or platform.machine()}
 
 
+def graph_time(calls, stream) -> float:
+    """Average ms of one call of `calls` (a list of closures launched back to
+    back), captured once into a HIP graph and replayed twice (the first replay
+    warms), bracketed by HIP events on the replay stream."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.graph(g, stream=cap):
+        for c in calls:
+            c()
+    stream.wait_stream(cap)
+    with torch.cuda.stream(stream):
+        g.replay()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record(stream)
+        g.replay()
+        e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e) / len(calls)
+
+
+def moe_cpu_baseline(cfg, budget_s: float):
+    """The oracle's latent-MoE layer (router, latent norm, 16 MXFP4 experts
+    quantized from their bf16 windows, up-projection, 2 shared experts) on a
+    bounded sample of token rows."""
+    import numpy as np
+    import oracle
+    import synth
+    log("cpu baseline: oracle MoE weights")
+    wr = oracle.Mat.from_draw("bf16", synth.moe_dense_weight(cfg, "router"))
+    bias = synth.moe_router_bias(cfg)
+    wdn = oracle.Mat.from_draw("bf16", synth.moe_dense_weight(cfg, "down"))
+    wup = oracle.Mat.from_draw("bf16", synth.moe_dense_weight(cfg, "up"))
+    s13 = synth.moe_dense_weight(cfg, "shared_w13")
+    s2 = synth.moe_dense_weight(cfg, "shared_w2")
+    I, H = cfg.inter, cfg.hidden
+    sh13 = [oracle.Mat.from_draw("bf16", s13[s * 2 * I:(s + 1) * 2 * I]) for s in range(cfg.n_shared)]
+    sh2 = [oracle.Mat.from_draw("bf16", s2[s * H:(s + 1) * H]) for s in range(cfg.n_shared)]
+    pool = synth.moe_expert_pool(cfg)
+    x = synth.moe_activations(cfg, 32, rep=99)
+
+    def token(t):
+        sel, gate = oracle.moe_route(wr, bias, x[t], cfg.top_k, cfg.routed_scale)
+        e13, e2 = {}, {}
+        for e in sel:
+            a, b = synth.moe_expert_draw(cfg, int(e), pool)
+            e13[int(e)] = oracle.Mat.from_draw("mxfp4", a)
+            e2[int(e)] = oracle.Mat.from_draw("mxfp4", b)
+        return oracle.moe_apply(wdn, wup, e13, e2, sh13, sh2, x[t], cfg.latent, cfg.inter,
+                                cfg.eps, sel, gate)
+
+    t0 = time.perf_counter()
+    token(0)
+    t1 = time.perf_counter() - t0
+    n = int(max(1, min(31, budget_s / max(t1, 1e-6))))
+    t0 = time.perf_counter()
+    for t in range(1, n + 1):
+        token(t)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} token rows through the whole layer (routing, expert quantization "
+                      f"from the bf16 windows, 16 experts, 2 shared), fp64 oracle, after one "
+                      f"untimed row; {dt:.1f} s",
+            "cpu": platform.processor() or platform.machine()}
+
+
+def bench_moe(cfg, args, dev):
+    """The K3-shaped latent-MoE layer at T = 1, 8, 32 token rows.  Each timed
+    call uses the next of 8 seeded activation sets, so consecutive calls route
+    to different experts and no call finds its expert weights in a cache."""
+    import numpy as np
+    import torch
+    import synth
+    from quantized_gemv_gqa_decode_amd import k2
+    from quantized_gemv_gqa_decode_amd.moe import MoeLayer
+
+    tokens = [int(t) for t in args.tokens.split(",")] if args.tokens else list(cfg.tokens)
+    log(f"building {cfg.name}: {cfg.n_experts} MXFP4 experts")
+    t0 = time.perf_counter()
+    lay = MoeLayer(cfg, dev, max_tokens=max(tokens))
+    torch.cuda.synchronize()
+    eb, db = lay.expert_bytes(), lay.dense_bytes()
+    log(f"layer ready in {time.perf_counter() - t0:.1f} s: experts "
+        f"{eb * cfg.n_experts / 1e9:.2f} GB ({eb} B each), dense {db / 1e9:.3f} GB")
+    stream = torch.cuda.current_stream()
+    R = 8
+    per_T = {}
+    for T in tokens:
+        xs = [torch.from_numpy(synth.moe_activations(cfg, T, rep=r)).to(dev) for r in range(R)]
+        y = torch.empty((T, cfg.hidden), device=dev)
+        idx = [torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev) for _ in range(R)]
+        gw = [torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev) for _ in range(R)]
+        for r in range(R):
+            lay.forward(xs[r], y, idx[r], gw[r])
+        torch.cuda.synchronize()
+        if int(lay.err.item()) != 0:
+            sys.exit(f"device error flag {int(lay.err.item())}")
+        distinct = [len(np.unique(idx[r].cpu().numpy())) for r in range(R)]
+        n = max(R, (args.steps // R) * R)
+        ms = graph_time([lambda r=r: lay.forward(xs[r % R], y, idx[r % R], gw[r % R])
+                         for r in range(n)], stream)
+        u_mean = float(np.mean(distinct))
+        act_bytes = T * cfg.hidden * 4 * 2
+        call_bytes = db + u_mean * eb + act_bytes
+        # the routed-expert call alone (bucket, W13 + SwiGLU, W2, combine)
+        z = [torch.randn((T, cfg.latent), device=dev) for _ in range(R)]
+        r_out = torch.empty((T, cfg.latent), device=dev)
+        wsb = k2.k2_moe_workspace_bytes(T, cfg.top_k, cfg.latent, cfg.inter)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+
+        def routed(r):
+            return k2.k2_moe_expert_gemv(z[r], T, cfg.latent, cfg.inter, idx[r], gw[r],
+                                         cfg.top_k, cfg.n_experts, lay.w13q, lay.w13s, lay.w2q,
+                                         lay.w2s, r_out, lay.err, ws, wsb)
+
+        ms_r = graph_time([lambda r=r: routed(r % R) for r in range(n)], stream)
+        routed_bytes = u_mean * eb + T * cfg.latent * 4 * 2
+        per_T[T] = {"us_per_call": round(ms * 1000, 2), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                    "distinct_experts_mean": u_mean, "bytes_per_call": int(call_bytes),
+                    "GBps": round(call_bytes / (ms * 1e-3) / 1e9, 1),
+                    "routed_us": round(ms_r * 1000, 2), "routed_bytes": int(routed_bytes),
+                    "routed_GBps": round(routed_bytes / (ms_r * 1e-3) / 1e9, 1)}
+        log(f"T={T}: {per_T[T]}")
+    Th = max(tokens)
+    h = per_T[Th]
+    cpu = None if args.no_cpu_baseline else moe_cpu_baseline(cfg, args.cpu_budget)
+    out = {
+        "metric": "latent-MoE layer tokens/s (K3 shape, MXFP4 routed experts) + achieved HBM GB/s",
+        "value": h["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": R,
+        "ms_per_step": round(h["us_per_call"] / 1000, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": Th, "hidden": cfg.hidden, "latent": cfg.latent,
+                   "inter": cfg.inter, "n_experts": cfg.n_experts, "top_k": cfg.top_k,
+                   "n_shared": cfg.n_shared, "experts": "mxfp4", "dense": "bf16"},
+        "roofline": {"bound": "hbm", "kernel": "moe_expert_gemv (bucket, W13+SwiGLU, W2, combine)",
+                     "achieved": h["routed_GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(h["routed_GBps"] / PEAK_HBM_GBPS, 4),
+                     "bytes_per_launch": h["routed_bytes"], "us_per_launch": h["routed_us"],
+                     "traffic": None},
+        "per_tokens": per_T,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +346,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--tokens", default=None,
+                    help="latent-MoE workload only: comma-separated token counts")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -204,6 +364,11 @@ def main():
     from quantized_gemv_gqa_decode_amd.model import DecodeModel
 
     cfg = synth.CONFIGS[args.config]
+    if isinstance(cfg, synth.MoeConfig):
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        k2.load(build_if_missing=False)
+        return bench_moe(cfg, args, dev)
     P = cfg.prompt_len if args.prompt_len is None else args.prompt_len
     W, K = args.warmup, args.steps
     if args.prefix:
