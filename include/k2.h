@@ -185,7 +185,7 @@ int k2_kv_append_int8(const float *k, const float *v, int8_t *kc, int8_t *vc, fl
  * required).  q: [n_qh][hd] (already rotated); out: [n_qh][hd].
  * ws: workspace of k2_attn_workspace_bytes(n_qh, n_kv, head_dim, cap) bytes,
  * zero-filled by the caller before its first use (the kernels leave it zeroed
- * again on exit).  K2_ERANGE unless 1 <= len <= cap; K2_EUNSUPPORTED unless
+ * again on exit); calls that share a workspace must not overlap in time.  K2_ERANGE unless 1 <= len <= cap; K2_EUNSUPPORTED unless
  * hd is 16/32/64/128 and n_qh / n_kv is 1, 2, 4 or 8. */
 size_t k2_attn_workspace_bytes(int n_qh, int n_kv, int head_dim, int cap);
 int k2_gqa_decode_attn(k2_dtype kvdt, const float *q, const void *kc, const void *vc,
@@ -205,7 +205,8 @@ int k2_rope_append_attn(k2_dtype kvdt, const float *qkv, const float *cos_sin, v
 
 /* First-maximum argmax of x[0..n) ([k3_run.c] argmax_()): out_idx[0] is the
  * lowest index holding the largest value.  ws: k2_argmax_workspace_bytes(n)
- * bytes, zero-filled before first use (left zeroed on exit). */
+ * bytes, zero-filled before first use (left zeroed on exit); calls that share
+ * a workspace must not overlap in time. */
 size_t k2_argmax_workspace_bytes(int n);
 int k2_argmax(const float *x, int n, int32_t *out_idx, void *ws, size_t ws_bytes,
               void *stream);
@@ -261,7 +262,9 @@ int k2_model_check(const k2_model *m);
  * fp32 (nullable: prefill positions skip the head); next_token: device int32
  * (nullable), the first-maximum argmax.  K2_ERANGE if token is outside
  * [0, vocab) or pos outside [0, cap): refuse rather than clamp ([k3_run.c]
- * main()), nothing enqueued. */
+ * main()), nothing enqueued.  With the environment variable K2_PERSISTENT=1
+ * the position runs as one cooperative persistent kernel (head_dim 16 or
+ * 128, n_qh / n_kv 2 or 4; other shapes keep the multi-kernel form). */
 int k2_decode_step(const k2_model *m, int token, int pos, float *logits, int32_t *next_token,
                    void *stream);
 

@@ -118,7 +118,8 @@ __device__ __forceinline__ void chunk_rows(const k2_u4 (&w)[R], const float (&sc
 // operations in issue order, so loads issued later would make the prologue
 // wait for the weights), then written to LDS while the weights are in flight.
 // XV = float4s per thread: enough for B*K <= 1024*XV.
-template <int XV>
+// COH: x was written by other blocks of the same grid (device-scope loads).
+template <int XV, bool COH = false>
 __device__ __forceinline__ void issue_x(const GemvArgs &a, float4 (&xr)[XV])
 {
     const int n = a.B * a.K;
@@ -126,7 +127,7 @@ __device__ __forceinline__ void issue_x(const GemvArgs &a, float4 (&xr)[XV])
     for (int v = 0; v < XV; ++v) {
         const int i = (v * K2_BLOCK + threadIdx.x) * 4;
         // unconditional load (clamped address): no branch around it
-        xr[v] = *reinterpret_cast<const float4 *>(a.x + (i < n ? i : 0));
+        xr[v] = ld4<COH>(a.x + (i < n ? i : 0));
     }
 }
 
@@ -239,39 +240,29 @@ __device__ __forceinline__ void load_pass(const GemvArgs &a, const int64_t *rows
     }
 }
 
-template <int WDT, int R, int U, int B, int PRO, int EPI, int XV>
-__global__ __launch_bounds__(K2_BLOCK) __attribute__((amdgpu_waves_per_eu(3, 8)))
-void gemv_kernel(const GemvArgs a)
+// Rows of `unit` and its pass-0 loads (issued now, consumed by gemv_units).
+template <int WDT, int R, int U, int EPI>
+__device__ __forceinline__ void gemv_prefetch(const GemvArgs &a, int64_t unit, int64_t (&rows)[R],
+                                              bool (&ok)[R], k2_u4 (&w)[U][R], float (&sc)[U][R])
 {
-    extern __shared__ float4 lds4[];
-    float *xs = reinterpret_cast<float *>(lds4);
-
     constexpr int EPC = WT<WDT>::EPC;
-    const int K = a.K;
-    const int CPR = K / EPC;                       // 16-byte chunks per row
-    const int S = xs_plane(CPR);
-    const int passes = (CPR + U * K2_WAVE - 1) / (U * K2_WAVE);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int64_t stride = (int64_t)gridDim.x * K2_WAVES_PER_BLOCK;
-
-    // argmax candidate of this thread (EPI_ARGMAX)
-    float best_v = -INFINITY;
-    int best_i = 0x7FFFFFFF;
-
-    int64_t unit = (int64_t)blockIdx.x * K2_WAVES_PER_BLOCK + wave;
-    int64_t rows[R];
-    bool ok[R];
-    k2_u4 w[U][R];
-    float sc[U][R];
-    float4 xr[XV];
-    issue_x<XV>(a, xr);                            // activations first ...
     unit_rows<R, EPI>(a, unit, rows, ok);
-    // ... then weights (unconditionally: a wave without a unit reads a clamped
-    // row it never uses, which keeps the issue path free of branches)
-    load_pass<WDT, R, U>(a, rows, ok, 0, CPR, lane, w, sc);
-    finish_x<XV, PRO, EPC>(xs, a, xr, S);                  // overlaps the weight loads
+    load_pass<WDT, R, U>(a, rows, ok, 0, a.K / EPC, threadIdx.x & 63, w, sc);
+}
 
+// The unit loop of one wave, starting at `unit` whose pass-0 loads are in
+// rows/ok/w/sc; activations staged in xs (plane stride S).  COH: outputs are
+// stored at device scope (read by other blocks of the same grid).
+template <int WDT, int R, int U, int B, int EPI, bool COH>
+__device__ __forceinline__ void gemv_units(const GemvArgs &a, const float *xs, int S, int64_t unit,
+                                           int64_t stride, int64_t (&rows)[R], bool (&ok)[R],
+                                           k2_u4 (&w)[U][R], float (&sc)[U][R], float &best_v,
+                                           int &best_i)
+{
+    constexpr int EPC = WT<WDT>::EPC;
+    const int CPR = a.K / EPC;                     // 16-byte chunks per row
+    const int passes = (CPR + U * K2_WAVE - 1) / (U * K2_WAVE);
+    const int lane = threadIdx.x & 63;
 #pragma unroll 1
     for (; unit < a.n_units; unit += stride) {
         float acc[B][R];
@@ -296,7 +287,7 @@ void gemv_kernel(const GemvArgs a)
         for (int r = 0; r < R; ++r) { cur_rows[r] = rows[r]; cur_ok[r] = ok[r]; }
         const int64_t next = unit + stride;
         unit_rows<R, EPI>(a, next, rows, ok);
-        if (next < a.n_units) load_pass<WDT, R, U>(a, rows, ok, 0, CPR, lane, w, sc);  // wave-uniform
+        if (next < a.n_units) load_pass<WDT, R, U>(a, rows, ok, 0, CPR, lane, w, sc);  // uniform
 
 #pragma unroll
         for (int b = 0; b < B; ++b)
@@ -316,8 +307,8 @@ void gemv_kernel(const GemvArgs a)
 #pragma unroll
             for (int r = 0; r < R / 2; ++r) {
                 if (lane == r && cur_ok[r]) {
-                    const float g = acc[0][r], u = acc[0][r + R / 2];
-                    a.y[cur_rows[r]] = g / (1.0f + expf(-g)) * u;
+                    const float gt = acc[0][r], up = acc[0][r + R / 2];
+                    st1<COH>(a.y + cur_rows[r], gt / (1.0f + expf(-gt)) * up);
                 }
             }
         } else if constexpr (EPI == EPI_ARGMAX) {
@@ -340,11 +331,38 @@ void gemv_kernel(const GemvArgs a)
                     if (lane == (b * R + r) % K2_WAVE && cur_ok[r]) {
                         float v = acc[b][r];
                         if (a.residual) v += a.residual[(int64_t)b * a.N + cur_rows[r]];
-                        a.y[(int64_t)b * a.N + cur_rows[r]] = v;
+                        st1<COH>(a.y + (int64_t)b * a.N + cur_rows[r], v);
                     }
                 }
         }
     }
+}
+
+template <int WDT, int R, int U, int B, int PRO, int EPI, int XV>
+__global__ __launch_bounds__(K2_BLOCK) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void gemv_kernel(const GemvArgs a)
+{
+    extern __shared__ float4 lds4[];
+    float *xs = reinterpret_cast<float *>(lds4);
+    constexpr int EPC = WT<WDT>::EPC;
+    const int S = xs_plane(a.K / EPC);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t stride = (int64_t)gridDim.x * K2_WAVES_PER_BLOCK;
+    const int64_t unit = (int64_t)blockIdx.x * K2_WAVES_PER_BLOCK + wave;
+
+    float best_v = -INFINITY;                      // argmax candidate (EPI_ARGMAX)
+    int best_i = 0x7FFFFFFF;
+    int64_t rows[R];
+    bool ok[R];
+    k2_u4 w[U][R];
+    float sc[U][R];
+    float4 xr[XV];
+    issue_x<XV>(a, xr);                            // activations first ...
+    // ... then weights (unconditionally: a wave without a unit reads a clamped
+    // row it never uses, which keeps the issue path free of branches)
+    gemv_prefetch<WDT, R, U, EPI>(a, unit, rows, ok, w, sc);
+    finish_x<XV, PRO, EPC>(xs, a, xr, S);          // overlaps the weight loads
+    gemv_units<WDT, R, U, B, EPI, false>(a, xs, S, unit, stride, rows, ok, w, sc, best_v, best_i);
 
     if constexpr (EPI == EPI_ARGMAX) {
         // per-block candidate; argmax_final_kernel reduces them in block order

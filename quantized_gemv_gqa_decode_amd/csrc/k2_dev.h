@@ -153,6 +153,71 @@ __device__ __forceinline__ uint32_t f32_to_e2m1(float t)
     return code | sign;
 }
 
+// ------------------------------------------------- device-scope accesses --
+// Data handed between blocks of ONE grid (the persistent step kernel) may be
+// produced and consumed on different XCDs, whose L2 caches are not coherent
+// with each other.  Loads and stores with the sc1 (device scope) cache
+// policy are performed at device scope; a plain load could return a stale
+// line from the reader's L2.
+
+// raw buffer resource over [p, p + 2 GiB): base, no stride, 32-bit words
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t k2_rsrc(const void *p)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, 0x7FFFFFFF,
+                                             0x00020000);
+}
+
+constexpr int K2_SC1 = 16;                   // buffer cache-policy bit: sc1
+
+__device__ __forceinline__ float4 coh_load4(const float *p)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(k2_rsrc(p), 0, 0, K2_SC1);
+    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                       __uint_as_float(v[3]));
+}
+
+__device__ __forceinline__ float coh_load(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int coh_load_i(const int *p)
+{
+    return __hip_atomic_load(const_cast<int *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void coh_store(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void coh_store_i(int *p, int v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// load / store selected at compile time: COH = device scope, else plain
+template <bool COH>
+__device__ __forceinline__ float4 ld4(const float *p)
+{
+    if constexpr (COH) return coh_load4(p);
+    else return *reinterpret_cast<const float4 *>(p);
+}
+
+template <bool COH>
+__device__ __forceinline__ float ld1(const float *p)
+{
+    if constexpr (COH) return coh_load(p);
+    else return *p;
+}
+
+template <bool COH>
+__device__ __forceinline__ void st1(float *p, float v)
+{
+    if constexpr (COH) coh_store(p, v);
+    else *p = v;
+}
+
 }  // namespace k2
 
 // ------------------------------------------------------------ host helpers --

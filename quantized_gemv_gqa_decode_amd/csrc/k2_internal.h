@@ -21,7 +21,9 @@ enum { EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2 };
 // Cross-block argmax: every block of the producing kernel writes its
 // (value, index) candidate; argmax_final_kernel reduces them in block order
 // (a fixed order, so the result does not depend on timing).  The kernel
-// boundary orders the two: no cross-block synchronisation inside a kernel.
+// boundary orders the two.  (A last-arriving-block reduction would need one
+// device-scope atomic per block on one counter: thousands of them serialize
+// to tens of microseconds, far more than a second launch.)
 struct ArgmaxArgs {
     float *part_v;
     int *part_i;
@@ -58,12 +60,14 @@ struct AttnArgs {
     float *out;                // [n_qh][hd]
     float *part;               // [n_kv][S][rep][hd]
     float *part_ml;            // [n_kv][S][rep][2]
+    unsigned *head_cnt;        // [n_kv] split arrivals (zero between calls)
     int n_qh, n_kv, cap, len, pos, chunk, S;
     float scale;
 };
 
 size_t attn_ws_bytes(int n_qh, int n_kv, int hd, int cap);
 int attn_splits(int n_kv, int len, int *chunk);
+int attn_splits_fine(int n_kv, int cap, int len, int *chunk);
 int attn_launch(int kvdt, int hd, int rep, bool fused, const AttnArgs &a, hipStream_t st);
 void attn_ws_carve(void *ws, int n_qh, int n_kv, int hd, int cap, AttnArgs &a);
 

@@ -1,0 +1,11 @@
+// step_f32.hip -- persistent decode-step kernels for f32 weights (one
+// translation unit per weight format, so the instantiations build in parallel).
+#include "step_impl.h"
+
+namespace k2 {
+int step_dispatch_f32(int kvdt, int hd, int rep, const StepArgs &A, int H, int qd, int inter,
+                        int max_blocks, hipStream_t st)
+{
+    return step_dispatch_t<K2_F32>(kvdt, hd, rep, A, H, qd, inter, max_blocks, st);
+}
+}  // namespace k2

@@ -64,6 +64,23 @@ def test_tiny_decoder(wdt, kvdt):
     run_parity(cfg, synth.prompt(cfg), cfg.n_decode)
 
 
+@pytest.mark.parametrize("wdt,kvdt", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "i8"),
+                                      ("fp8", "i8"), ("mxfp4", "bf16")])
+def test_tiny_decoder_persistent_path(wdt, kvdt, monkeypatch):
+    """The same decode as one persistent cooperative kernel per position
+    (opt-in with K2_PERSISTENT=1): grid barriers, device-scope activation
+    hand-off, last-block attention combine and argmax."""
+    monkeypatch.setenv("K2_PERSISTENT", "1")
+    cfg = synth.TINY.replace(wdt=wdt, kvdt=kvdt)
+    run_parity(cfg, synth.prompt(cfg), cfg.n_decode)
+
+
+def test_tiny_decoder_persistent_n_kv1(monkeypatch):
+    monkeypatch.setenv("K2_PERSISTENT", "1")
+    cfg = synth.TINY.replace(n_kv=1)
+    run_parity(cfg, synth.prompt(cfg), 8)
+
+
 @pytest.mark.parametrize("change", [dict(groups=1), dict(n_kv=4), dict(n_kv=1),
                                     dict(head_dim=32, n_qh=2, n_kv=1), dict(cap=20)])
 def test_tiny_decoder_shapes(change):
