@@ -63,8 +63,10 @@ void attn_ws_carve(void *ws, int n_qh, int n_kv, int hd, int cap, AttnArgs &a)
 template <int KVDT, int HD, int REP, bool FUSED>
 static int attn_go(const AttnArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL((attn_kernel<KVDT, HD, REP, FUSED, K2_WAVES_PER_BLOCK>), dim3(a.S, a.n_kv),
-                       dim3(K2_BLOCK), 0, st, a);
+    constexpr size_t lds = sizeof(float) * attn_stream_lds_floats<KVDT, HD, REP>();
+    static_assert(lds <= 160 * 1024, "attention LDS per block");
+    hipLaunchKernelGGL((attn_kernel<KVDT, HD, REP, FUSED>), dim3(a.S, a.n_kv), dim3(ATT_NT), lds, st,
+                       a);
     K2_CHECK_LAUNCH();
     return K2_OK;
 }
@@ -245,3 +247,11 @@ extern "C" int k2_rope_append_attn(k2_dtype kvdt, const float *qkv, const float 
     a.S = attn_splits(n_kv, a.len, &a.chunk);
     return attn_launch(kvdt, head_dim, n_qh / n_kv, true, a, k2_stream(stream));
 }
+
+#ifdef K2_ATTN_TRACE
+extern "C" int k2_attn_trace_read(unsigned long long *out, int n)
+{
+    return hipMemcpyFromSymbol(out, HIP_SYMBOL(k2::k2_attn_trace), sizeof(unsigned long long) * n) ==
+                   hipSuccess ? 0 : -4;
+}
+#endif

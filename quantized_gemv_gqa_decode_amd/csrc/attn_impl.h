@@ -36,6 +36,31 @@ template <> struct KVT<K2_F32>  { static constexpr int EPC = 4;  using T = float
 template <> struct KVT<K2_BF16> { static constexpr int EPC = 8;  using T = uint16_t; };
 template <> struct KVT<K2_I8>   { static constexpr int EPC = 16; using T = int8_t;   };
 
+template <int KVDT> __device__ __forceinline__ void kv_decode(const k2_u4 w, float *v);
+
+constexpr float K2_LOG2E = 1.4426950408889634f;
+constexpr float K2_LN2 = 0.6931471805599453f;
+
+// 2^x with the hardware exponential (x <= 0 here; -inf gives 0)
+__device__ __forceinline__ float k2_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// decode one 16-byte cache chunk into EPC floats; int8 as unsigned bytes
+// u = code + 128 (one convert per element; callers subtract the offset)
+template <int KVDT>
+__device__ __forceinline__ void kv_decode_u(const k2_u4 w, float *v)
+{
+    if constexpr (KVDT == K2_I8) {
+        const uint32_t ws[4] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u, w.z ^ 0x80808080u,
+                                w.w ^ 0x80808080u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) v[4 * i + b] = (float)((ws[i] >> (8 * b)) & 0xFFu);
+    } else {
+        kv_decode<KVDT>(w, v);
+    }
+}
+
 // decode one 16-byte cache chunk into EPC floats (int8: the raw codes)
 template <int KVDT>
 __device__ __forceinline__ void kv_decode(const k2_u4 w, float *v)
@@ -56,9 +81,27 @@ __device__ __forceinline__ void kv_decode(const k2_u4 w, float *v)
     }
 }
 
+// Block barrier for data exchanged through LDS only: waits for this wave's
+// LDS operations, not for its global loads (LDS-DMA copies in flight stay
+// in flight, unlike __syncthreads, whose fence waits for them).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0); vmcnt, expcnt not waited
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <bool RAW>
+__device__ __forceinline__ void block_sync()
+{
+    if constexpr (RAW) lds_barrier();
+    else __syncthreads();
+}
+
 // Largest |x| over the head_dim values of k (threads [0, HD)) and of v
-// (threads [HD, 2 HD)); every thread must call it.
-template <int HD>
+// (threads [HD, 2 HD)); every thread must call it.  RAW: LDS-only barriers.
+template <int HD, bool RAW = false>
 __device__ __forceinline__ float kv_head_absmax(float ax, float *tmp4)
 {
     constexpr int W = HD < 64 ? HD : 64;
@@ -70,10 +113,10 @@ __device__ __forceinline__ float kv_head_absmax(float ax, float *tmp4)
     } else {
         const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
         if (lane == 0) tmp4[wave] = m;
-        __syncthreads();
+        block_sync<RAW>();
         const int t = (threadIdx.x / HD) & 1;
         const float r = fmaxf(tmp4[2 * t], tmp4[2 * t + 1]);
-        __syncthreads();
+        block_sync<RAW>();
         return r;
     }
 }
@@ -81,7 +124,7 @@ __device__ __forceinline__ float kv_head_absmax(float ax, float *tmp4)
 // Store one position of k (threads [0, HD)) and v (threads [HD, 2 HD)) for kv
 // head g into the cache; returns (through `stored`) the value read back from
 // the cache format.  Every thread of the block must call it.
-template <int KVDT, int HD>
+template <int KVDT, int HD, bool RAW = false>
 __device__ __forceinline__ float kv_store_head(float val, void *kc, void *vc, float *ks, float *vs,
                                                int g, int cap, int pos, float *tmp4)
 {
@@ -102,7 +145,7 @@ __device__ __forceinline__ float kv_store_head(float val, void *kc, void *vc, fl
             stored = bf16_to_f32(b);
         }
     } else {
-        const float amax = kv_head_absmax<HD>(active ? fabsf(val) : 0.f, tmp4);
+        const float amax = kv_head_absmax<HD, RAW>(active ? fabsf(val) : 0.f, tmp4);
         if (active) {
             const float s = amax / 127.0f;
             float q = 0.f;
@@ -365,21 +408,383 @@ __device__ __forceinline__ void attn_block(const AttnArgs &a, int g, int s, int 
     }
 }
 
-template <int REP>
-__host__ __device__ constexpr int combine_lds_floats()
+// ------------------------------------------------- streaming attention --
+// The same attention with K and V (and the int8 scales) streamed through
+// LDS by blocks of ATT_WPB waves: the block's positions are cut into tiles
+// of TP positions (16 KiB of K and 16 KiB of V for head_dim 128); tiles are
+// copied from HBM straight into LDS with LDS-DMA loads (global_load_lds, 16
+// bytes per lane, no registers), ATT_STAGES tiles in flight, and the waves
+// read them from LDS with the query heads held in registers.  A block keeps
+// up to 96 KiB in flight: long contexts become bandwidth-bound.
+
+#define K2_VMCNT(n) (((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
+
+// Optional per-block stage trace for performance work (never enabled in the
+// library build): thread 0 records the 100 MHz real-time counter.
+#ifdef K2_ATTN_TRACE
+static __device__ unsigned long long k2_attn_trace[4096][8];
+#define K2_ATRACE(i)                                                                         \
+    do {                                                                                     \
+        const int b_ = blockIdx.y * gridDim.x + blockIdx.x;                                  \
+        if (threadIdx.x == 0 && b_ < 4096) k2_attn_trace[b_][i] = __builtin_amdgcn_s_memrealtime(); \
+    } while (0)
+#else
+#define K2_ATRACE(i) \
+    do {         \
+    } while (0)
+#endif
+
+constexpr int ATT_WPB = 8;                 // waves per streaming block
+constexpr int ATT_NT = ATT_WPB * K2_WAVE;  // threads per streaming block
+constexpr int ATT_STAGES = 3;              // tiles in flight
+
+template <int KVDT, int HD>
+struct StreamGeom {
+    using T = typename KVT<KVDT>::T;
+    static constexpr int EPC = KVT<KVDT>::EPC;
+    static constexpr int LPP = HD / EPC;                       // lanes per position
+    static constexpr int PPI = K2_WAVE / LPP;                  // positions per slot
+    static constexpr int ROWB = HD * (int)sizeof(T);           // bytes per cache row
+    static constexpr int ROUND = ATT_WPB * PPI;                // positions of one slot of every wave
+    static constexpr int NSLOT = (16384 / (ROUND * ROWB)) > 1 ? 16384 / (ROUND * ROWB) : 1;
+    static constexpr int TP = ROUND * NSLOT;                   // positions per tile
+    static constexpr int TILEB = TP * ROWB;                    // bytes of one K (or V) tile
+    static constexpr int NI = TILEB / (16 * ATT_NT);           // 16-byte copies per thread per tile
+    static constexpr int SCF = KVDT == K2_I8 ? TP : 0;         // scale floats per tile (K or V)
+    static constexpr int NS = (2 * SCF + ATT_NT - 1) / ATT_NT; // 4-byte scale copies per thread
+    static constexpr int NPT = 2 * NI + NS;                    // LDS-DMA instructions per tile
+    static constexpr int STAGE_F = 2 * TILEB / 4 + NS * ATT_NT;   // floats per stage
+    static_assert(NI >= 1 && NI * 16 * ATT_NT == TILEB, "tile copy shape");
+};
+
+template <int KVDT, int HD, int REP>
+__host__ __device__ constexpr int attn_stream_lds_floats()
 {
-    return K2_ATTN_MAX_SPLITS * REP + 2 * REP;
+    // stages (reused for the wave merge afterwards), q, new k/v, merge (m, l)
+    return ATT_STAGES * StreamGeom<KVDT, HD>::STAGE_F + REP * HD + 2 * HD + ATT_WPB * REP * 2 +
+           ATT_WPB;
 }
 
-// Combine for kv head g (a block of K2_BLOCK threads; every thread calls it).
-template <int HD, int REP, bool COH>
+template <int KVDT, int HD, int REP, bool FUSED, bool COH>
+__device__ __forceinline__ void attn_stream_block(const AttnArgs &a, int g, int s, int S, float *smem)
+{
+    using G = StreamGeom<KVDT, HD>;
+    using T = typename G::T;
+    constexpr int EPC = G::EPC, LPP = G::LPP, PPI = G::PPI, TP = G::TP, NSLOT = G::NSLOT;
+    constexpr int WPB = ATT_WPB, NT = ATT_NT, NST = ATT_STAGES;
+    static_assert(WPB * REP * HD <= NST * G::STAGE_F, "wave merge fits the stages");
+
+    float *const stages = smem;
+    float *const rest = smem + NST * G::STAGE_F;
+    auto qs = reinterpret_cast<float (*)[HD]>(rest);                       // [REP][HD]
+    auto newkv = reinterpret_cast<float (*)[HD]>(rest + REP * HD);         // [2][HD]
+    auto red_ml = reinterpret_cast<float (*)[REP][2]>(rest + REP * HD + 2 * HD);
+    float *tmp4 = rest + REP * HD + 2 * HD + WPB * REP * 2;
+    auto red_o = reinterpret_cast<float (*)[REP][HD]>(stages);             // after the tiles
+
+    const int len = a.len;
+    const int j0 = s * a.chunk;
+    const int j1 = min(len, j0 + a.chunk);
+    const bool holds_new = FUSED && (j1 == len);
+    const int jc = holds_new ? j1 - 1 : j1;        // positions read from the cache
+    const int n_tiles = (jc - j0 + TP - 1) / TP;   // 0 when the block holds only the new position
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int sub = lane / LPP, cl = lane % LPP;
+    const char *kb = reinterpret_cast<const char *>(reinterpret_cast<const T *>(a.kc) + (int64_t)g * a.cap * HD);
+    const char *vb = reinterpret_cast<const char *>(reinterpret_cast<const T *>(a.vc) + (int64_t)g * a.cap * HD);
+    const float *ksb = KVDT == K2_I8 ? a.ks + (int64_t)g * a.cap : nullptr;
+    const float *vsb = KVDT == K2_I8 ? a.vs + (int64_t)g * a.cap : nullptr;
+    K2_ATRACE(0);
+
+    // q (and the new k, v) are loaded first, so that waiting for them never
+    // waits for the tile copies issued after them
+    constexpr int QV = (REP * HD + NT - 1) / NT;
+    constexpr int HALF = HD / 2;
+    float qx0[QV], qx1[QV], qc[QV], qsn[QV];
+#pragma unroll
+    for (int v = 0; v < QV; ++v) {
+        const int t = tid + v * NT;
+        const int tt = t < REP * HD ? t : 0;
+        const int hl = tt / HD, d = tt % HD, h = g * REP + hl;
+        if constexpr (FUSED) {
+            const float *u = a.qkv + (int64_t)h * HD;
+            qx0[v] = u[d % HALF];
+            qx1[v] = u[d % HALF + HALF];
+            qc[v] = a.cos_sin[((int64_t)a.pos * HALF + d % HALF) * 2];
+            qsn[v] = a.cos_sin[((int64_t)a.pos * HALF + d % HALF) * 2 + 1];
+        } else {
+            qx0[v] = a.q[(int64_t)h * HD + d];
+            qx1[v] = qc[v] = qsn[v] = 0.f;
+        }
+    }
+    float nk0 = 0.f, nk1 = 0.f, kc0 = 0.f, ks0 = 0.f;
+    if constexpr (FUSED) {
+        if (holds_new) {
+            if (tid < HD) {
+                const float *u = a.qkv + (int64_t)(a.n_qh + g) * HD;
+                nk0 = u[tid % HALF];
+                nk1 = u[tid % HALF + HALF];
+                kc0 = a.cos_sin[((int64_t)a.pos * HALF + tid % HALF) * 2];
+                ks0 = a.cos_sin[((int64_t)a.pos * HALF + tid % HALF) * 2 + 1];
+            } else if (tid < 2 * HD) {
+                nk0 = a.qkv[(int64_t)(a.n_qh + a.n_kv + g) * HD + (tid - HD)];
+            }
+        }
+    }
+
+    // tile t -> stage t % NST: K rows, V rows, then the int8 scales
+    auto issue_tile = [&](int t) {
+        float *st = stages + (t % NST) * G::STAGE_F;
+        const int64_t p0 = j0 + (int64_t)t * TP;
+        const int64_t lim = (int64_t)jc * G::ROWB - 16;         // last valid 16-byte chunk
+#pragma unroll
+        for (int i = 0; i < G::NI; ++i) {
+            const int c = i * NT + tid;                           // 16-byte chunk of the tile
+            int64_t off = p0 * G::ROWB + (int64_t)c * 16;
+            off = off < lim ? off : lim;
+            char *dst = reinterpret_cast<char *>(st) + (int64_t)(i * NT + wave * K2_WAVE) * 16;
+            __builtin_amdgcn_global_load_lds(kb + off, dst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vb + off, dst + G::TILEB, 16, 0, 0);
+        }
+        if constexpr (KVDT == K2_I8) {
+#pragma unroll
+            for (int i = 0; i < G::NS; ++i) {
+                const int e = i * NT + tid;                       // element of [K scales | V scales]
+                const bool isk = e < TP;
+                int64_t p = p0 + (isk ? e : e - TP);
+                p = p < jc ? p : jc - 1;
+                const float *src = (e < 2 * TP) ? (isk ? ksb : vsb) + p : ksb + j0;
+                float *dst = st + 2 * G::TILEB / 4 + i * NT + wave * K2_WAVE;
+                __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+            }
+        }
+    };
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+        if (t < n_tiles) issue_tile(t);
+
+    // 1. query heads of this kv head, rotated (fused) and pre-scaled
+#pragma unroll
+    for (int v = 0; v < QV; ++v) {
+        const int t = tid + v * NT;
+        if (t < REP * HD) {
+            const int hl = t / HD, d = t % HD;
+            float val;
+            if constexpr (FUSED)
+                val = d < HALF ? qx0[v] * qc[v] - qx1[v] * qsn[v] : qx0[v] * qsn[v] + qx1[v] * qc[v];
+            else
+                val = qx0[v];
+            qs[hl][d] = val * (a.scale * K2_LOG2E);   // scores in the base-2 domain
+        }
+    }
+    // 2. fused: rotate k, store k and v at slot pos (block-uniform branch)
+    if constexpr (FUSED) {
+        if (holds_new) {
+            float val = nk0;
+            if (tid < HD) val = tid < HALF ? nk0 * kc0 - nk1 * ks0 : nk0 * ks0 + nk1 * kc0;
+            const float st = kv_store_head<KVDT, HD, true>(val, a.kc, a.vc, a.ks, a.vs, g, a.cap, a.pos, tmp4);
+            if (tid < 2 * HD) newkv[tid / HD][tid % HD] = st;
+        }
+    }
+    lds_barrier();
+    K2_ATRACE(1);
+    // this lane's slice of every query head, in registers
+    float qv[REP][EPC], qsum[REP];
+#pragma unroll
+    for (int h = 0; h < REP; ++h) {
+        qsum[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+            qv[h][e] = qs[h][cl * EPC + e];
+            qsum[h] += qv[h][e];
+        }
+    }
+
+    // int8 codes are decoded as unsigned bytes u = code + 128 (one convert
+    // per element); q.k = q.u - 128 sum(q) per lane, and the V sum carries
+    // w = sum of the V weights to subtract 128 w at the end
+    float m[REP], l[REP], acc[REP][EPC], wsum[REP];
+#pragma unroll
+    for (int h = 0; h < REP; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+        wsum[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
+    }
+
+    // 3. tiles: wait for tile t (later tiles may stay in flight), compute it
+    //    from LDS, then reuse its stage for tile t + NST
+#pragma unroll 1
+    for (int t = 0; t < n_tiles; ++t) {
+        const int ahead = n_tiles - 1 - t < NST - 1 ? n_tiles - 1 - t : NST - 1;
+        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(K2_VMCNT(2 * G::NPT));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(K2_VMCNT(G::NPT));
+        else __builtin_amdgcn_s_waitcnt(K2_VMCNT(0));
+        lds_barrier();
+        if (t == 0) K2_ATRACE(2);
+        const float *st = stages + (t % NST) * G::STAGE_F;
+        const char *kt = reinterpret_cast<const char *>(st);
+        const char *vt = kt + G::TILEB;
+        const float *kst = st + 2 * G::TILEB / 4, *vst = kst + TP;
+        const int p0 = j0 + t * TP;
+        float sc[NSLOT][REP];
+        int pr[NSLOT];
+#pragma unroll
+        for (int n = 0; n < NSLOT; ++n) {
+            const int r = (n * WPB + wave) * PPI + sub;            // row within the tile
+            pr[n] = r;
+            float kv[EPC];
+            kv_decode_u<KVDT>(*reinterpret_cast<const k2_u4 *>(kt + r * G::ROWB + cl * 16), kv);
+            const bool valid = p0 + r < jc;
+            const float ksc = (KVDT == K2_I8) ? kst[r] : 1.0f;
+#pragma unroll
+            for (int h = 0; h < REP; ++h) {
+                float p = (KVDT == K2_I8) ? -128.0f * qsum[h] : 0.f;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) p += qv[h][e] * kv[e];
+                p = group_sum<LPP>(p) * ksc;
+                sc[n][h] = valid ? p : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < REP; ++h) {
+            float mx = sc[0][h];
+#pragma unroll
+            for (int n = 1; n < NSLOT; ++n) mx = fmaxf(mx, sc[n][h]);
+            mx = wave_max(mx);
+            const float mn = fmaxf(m[h], mx);
+            const float corr = (mn == -INFINITY) ? 1.0f : k2_exp2(m[h] - mn);
+            l[h] *= corr;
+            wsum[h] *= corr;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[h][e] *= corr;
+            m[h] = mn;
+        }
+#pragma unroll
+        for (int n = 0; n < NSLOT; ++n) {
+            if (p0 + pr[n] < jc) {
+                float vv[EPC];
+                kv_decode_u<KVDT>(*reinterpret_cast<const k2_u4 *>(vt + pr[n] * G::ROWB + cl * 16), vv);
+                const float vsc = (KVDT == K2_I8) ? vst[pr[n]] : 1.0f;
+#pragma unroll
+                for (int h = 0; h < REP; ++h) {
+                    const float p = k2_exp2(sc[n][h] - m[h]);
+                    l[h] += p;
+                    const float pv = p * vsc;
+                    if constexpr (KVDT == K2_I8) wsum[h] += pv;
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) acc[h][e] += pv * vv[e];
+                }
+            }
+        }
+        lds_barrier();                               // every wave is done with stage t % NST
+        if (t + NST < n_tiles) issue_tile(t + NST);
+    }
+    K2_ATRACE(3);
+    if constexpr (KVDT == K2_I8) {
+#pragma unroll
+        for (int h = 0; h < REP; ++h)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[h][e] -= 128.0f * wsum[h];
+    }
+    // the new position (fused): wave 0, values from LDS
+    if (holds_new && wave == 0) {
+#pragma unroll
+        for (int h = 0; h < REP; ++h) {
+            float p = 0.f;
+            for (int d = lane; d < HD; d += K2_WAVE) p += qs[h][d] * newkv[0][d];
+            const float snew = wave_sum(p);
+            const float mn = fmaxf(m[h], snew);
+            const float corr = k2_exp2(m[h] - mn);       // m = -inf gives 0
+            const float pn = k2_exp2(snew - mn);
+            l[h] = l[h] * corr + (sub == 0 ? pn : 0.f);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+                acc[h][e] = acc[h][e] * corr + (sub == 0 ? pn * newkv[1][cl * EPC + e] : 0.f);
+            m[h] = mn;
+        }
+    }
+    // 4. sum over the position sub-groups of the wave (same m across the wave)
+#pragma unroll
+    for (int h = 0; h < REP; ++h) {
+#pragma unroll
+        for (int o = LPP; o < K2_WAVE; o <<= 1) l[h] += __shfl_xor(l[h], o, K2_WAVE);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+            float v = acc[h][e];
+#pragma unroll
+            for (int o = LPP; o < K2_WAVE; o <<= 1) v += __shfl_xor(v, o, K2_WAVE);
+            acc[h][e] = v;
+        }
+    }
+    if (sub == 0) {
+#pragma unroll
+        for (int h = 0; h < REP; ++h)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) red_o[wave][h][cl * EPC + e] = acc[h][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < REP; ++h) { red_ml[wave][h][0] = m[h]; red_ml[wave][h][1] = l[h]; }
+    }
+    __syncthreads();
+
+    // 5. combine the waves; output directly (one split) or publish a partial
+    const int64_t pbase = ((int64_t)g * S + s) * REP;
+    for (int t = tid; t < REP * HD; t += NT) {
+        const int h = t / HD, d = t % HD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WPB; ++w) M = fmaxf(M, red_ml[w][h][0]);
+        float L = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < WPB; ++w) {
+            const float mw = red_ml[w][h][0];
+            const float f = (mw == -INFINITY) ? 0.f : k2_exp2(mw - M);
+            L += f * red_ml[w][h][1];
+            o += f * red_o[w][h][d];
+        }
+        if (S == 1) {
+            st1<COH>(a.out + (int64_t)(g * REP + h) * HD + d, o / L);
+        } else {
+            st1<COH>(a.part + (pbase + h) * HD + d, o);
+            if (d == 0) {
+                // the combine works with natural-log maxima
+                st1<COH>(a.part_ml + (pbase + h) * 2, M * K2_LN2);
+                st1<COH>(a.part_ml + (pbase + h) * 2 + 1, L);
+            }
+        }
+    }
+}
+
+template <int REP, int NTH = K2_BLOCK>
+__host__ __device__ constexpr int combine_lds_floats()
+{
+    return ((K2_ATTN_MAX_SPLITS * REP + 2 * REP + 3) & ~3) + NTH * 4;
+}
+
+// Combine for kv head g (a block of K2_BLOCK threads; every thread calls it):
+// M = max_s m_s, L = sum_s l_s e^(m_s - M), out = sum_s o_s e^(m_s - M) / L,
+// summed in split order per thread.  Float4 column c of the head's
+// REP*HD/4 columns belongs to threads c, c + C4, ...; each of them loads its
+// splits' float4s (16 at a time, all issued before any is used), so that a
+// batch costs one memory round trip.
+template <int HD, int REP, bool COH, int NTH = K2_BLOCK>
 __device__ __forceinline__ void attn_combine_block(const AttnArgs &a, int g, float *smem)
 {
-    auto f = reinterpret_cast<float (*)[REP]>(smem);                         // [MAX_SPLITS][REP]
+    constexpr int C4 = REP * HD / 4;                     // float4 columns of a split
+    constexpr int TPC = C4 >= NTH ? 1 : NTH / C4;        // threads per column
+    constexpr int CPT = C4 >= NTH ? C4 / NTH : 1;        // columns per thread
+    constexpr int NB = 16;                               // loads in flight per batch
+    static_assert(C4 % NTH == 0 || NTH % C4 == 0, "combine shape");
+    auto f = reinterpret_cast<float (*)[REP]>(smem);     // [MAX_SPLITS][REP]: m, then weights
     float *Mh = smem + K2_ATTN_MAX_SPLITS * REP, *Linv = Mh + REP;
+    float4 *part4 = reinterpret_cast<float4 *>(smem + ((K2_ATTN_MAX_SPLITS * REP + 2 * REP + 3) & ~3));
     const int S = a.S, tid = threadIdx.x;
     const float *ml = a.part_ml + (int64_t)g * S * REP * 2;
-    for (int t = tid; t < S * REP; t += K2_BLOCK) f[t / REP][t % REP] = ld1<COH>(ml + (int64_t)t * 2);
+    const float *po = a.part + (int64_t)g * S * REP * HD;
+    for (int t = tid; t < S * REP; t += NTH) f[t / REP][t % REP] = ld1<COH>(ml + (int64_t)t * 2);
     __syncthreads();
     if (tid < REP) {
         float M = -INFINITY;
@@ -387,42 +792,77 @@ __device__ __forceinline__ void attn_combine_block(const AttnArgs &a, int g, flo
         Mh[tid] = M;
     }
     __syncthreads();
-    for (int t = tid; t < S * REP; t += K2_BLOCK) f[t / REP][t % REP] = expf(f[t / REP][t % REP] - Mh[t % REP]);
+    for (int t = tid; t < S * REP; t += NTH) {
+        const float mq = f[t / REP][t % REP];
+        f[t / REP][t % REP] = mq == -INFINITY ? 0.f : expf(mq - Mh[t % REP]);
+    }
     __syncthreads();
     if (tid < REP) {
         float L = 0.f;
         for (int q = 0; q < S; ++q) L += f[q][tid] * ld1<COH>(ml + ((int64_t)q * REP + tid) * 2 + 1);
         Linv[tid] = 1.0f / L;
     }
-    __syncthreads();
-    for (int t = tid; t < REP * HD; t += K2_BLOCK) {
-        const int h = t / HD, d = t % HD;
-        const float *po = a.part + ((int64_t)g * S * REP + h) * HD + d;
-        float o = 0.f;
-        int q = 0;
-        for (; q + 8 <= S; q += 8) {
-            float v[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = ld1<COH>(po + (int64_t)(q + i) * REP * HD);
+    for (int cc = 0; cc < CPT; ++cc) {
+        const int c = (C4 >= NTH) ? tid + cc * NTH : tid % C4;   // float4 column
+        const int q0 = (C4 >= NTH) ? 0 : tid / C4;                     // first split
+        const int h = c * 4 / HD;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int qb = q0; qb < S; qb += TPC * NB) {
+            float4 v[NB];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o += f[q + i][h] * v[i];
+            for (int i = 0; i < NB; ++i) {
+                const int q = qb + i * TPC;
+                const int qq = q < S ? q : q0;
+                v[i] = ld4<COH>(po, (qq * C4 + c) * 4);
+            }
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int q = qb + i * TPC;
+                const float w = q < S ? f[q][h] : 0.f;
+                o.x += w * v[i].x; o.y += w * v[i].y; o.z += w * v[i].z; o.w += w * v[i].w;
+            }
         }
-        for (; q < S; ++q) o += f[q][h] * ld1<COH>(po + (int64_t)q * REP * HD);
-        st1<COH>(a.out + (int64_t)(g * REP + h) * HD + d, o * Linv[h]);
+        if constexpr (TPC > 1) {
+            part4[tid] = o;
+            __syncthreads();
+            if (tid < C4) {
+                o = part4[tid];
+#pragma unroll
+                for (int k = 1; k < TPC; ++k) {
+                    const float4 u = part4[tid + k * C4];
+                    o.x += u.x; o.y += u.y; o.z += u.z; o.w += u.w;
+                }
+            }
+        } else {
+            __syncthreads();                              // Linv
+        }
+        if (tid < C4 || C4 >= NTH) {
+            const float li = Linv[h];
+            float *out = a.out + (int64_t)g * REP * HD + c * 4;
+            st1<COH>(out, o.x * li);
+            st1<COH>(out + 1, o.y * li);
+            st1<COH>(out + 2, o.z * li);
+            st1<COH>(out + 3, o.w * li);
+        }
+        if constexpr (CPT > 1) __syncthreads();
     }
 }
 
 // One launch: every block attends over its split; with several splits the
 // last block of each kv head to finish (an arrival counter, reset by that
 // block) combines the partials of the head.  No block waits for another.
-template <int KVDT, int HD, int REP, bool FUSED, int WPB>
-__global__ __launch_bounds__(WPB * K2_WAVE) void attn_kernel(const AttnArgs a)
+template <int KVDT, int HD, int REP, bool FUSED>
+__global__ __launch_bounds__(ATT_NT) void attn_kernel(const AttnArgs a)
 {
-    constexpr int NA = attn_lds_floats<HD, REP, WPB>(), NC = combine_lds_floats<REP>();
-    __shared__ float smem[NA > NC ? NA : NC];
+    constexpr int NA = attn_stream_lds_floats<KVDT, HD, REP>(), NC = combine_lds_floats<REP, ATT_NT>();
+    extern __shared__ float4 lds4[];
+    float *smem = reinterpret_cast<float *>(lds4);
+    static_assert(NA >= NC, "combine fits the attention LDS");
     __shared__ int last;
     const int g = blockIdx.y, S = gridDim.x;
-    attn_block<KVDT, HD, REP, FUSED, WPB, true>(a, g, blockIdx.x, S, smem);
+    attn_stream_block<KVDT, HD, REP, FUSED, true>(a, g, blockIdx.x, S, smem);
+    K2_ATRACE(4);
     if (S == 1) return;
     __builtin_amdgcn_s_waitcnt(0);                 // this thread's partial stores completed
     __syncthreads();
@@ -433,7 +873,11 @@ __global__ __launch_bounds__(WPB * K2_WAVE) void attn_kernel(const AttnArgs a)
         if (last) __hip_atomic_store(a.head_cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    if (last) attn_combine_block<HD, REP, true>(a, g, smem);
+    K2_ATRACE(5);
+    if (last) {
+        attn_combine_block<HD, REP, true, ATT_NT>(a, g, smem);
+        K2_ATRACE(6);
+    }
 }
 
 // Standalone store of one position (k, v already rotated), grid = n_kv.

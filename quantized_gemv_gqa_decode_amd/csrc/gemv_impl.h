@@ -127,7 +127,7 @@ __device__ __forceinline__ void issue_x(const GemvArgs &a, float4 (&xr)[XV])
     for (int v = 0; v < XV; ++v) {
         const int i = (v * K2_BLOCK + threadIdx.x) * 4;
         // unconditional load (clamped address): no branch around it
-        xr[v] = ld4<COH>(a.x + (i < n ? i : 0));
+        xr[v] = ld4<COH>(a.x, i < n ? i : 0);
     }
 }
 

@@ -169,9 +169,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t k2_rsrc(const void *p)
 
 constexpr int K2_SC1 = 16;                   // buffer cache-policy bit: sc1
 
-__device__ __forceinline__ float4 coh_load4(const float *p)
+// base must be the same for every lane of the wave (a buffer resource is
+// scalar); off = per-lane offset in floats
+__device__ __forceinline__ float4 coh_load4(const float *base, int off)
 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(k2_rsrc(p), 0, 0, K2_SC1);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(k2_rsrc(base), off * 4, 0, K2_SC1);
     return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
                        __uint_as_float(v[3]));
 }
@@ -197,11 +199,12 @@ __device__ __forceinline__ void coh_store_i(int *p, int v)
 }
 
 // load / store selected at compile time: COH = device scope, else plain
+// base[off .. off + 4): base wave-uniform, off per lane
 template <bool COH>
-__device__ __forceinline__ float4 ld4(const float *p)
+__device__ __forceinline__ float4 ld4(const float *base, int off)
 {
-    if constexpr (COH) return coh_load4(p);
-    else return *reinterpret_cast<const float4 *>(p);
+    if constexpr (COH) return coh_load4(base, off);
+    else return *reinterpret_cast<const float4 *>(base + off);
 }
 
 template <bool COH>

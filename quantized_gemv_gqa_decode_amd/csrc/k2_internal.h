@@ -9,7 +9,9 @@
 #define K2_GEMV_MAX_BLOCKS 4096
 #define K2_ATTN_MAX_CHUNK 1024           // positions per attention block
 #define K2_ATTN_MIN_CHUNK 64
+#ifndef K2_ATTN_TARGET_BLOCKS
 #define K2_ATTN_TARGET_BLOCKS 256
+#endif
 #define K2_ATTN_MAX_SPLITS 512           // combine LDS bound: >= max splits
 #define K2_ARGMAX_MAX_BLOCKS K2_GEMV_MAX_BLOCKS
 

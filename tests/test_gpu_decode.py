@@ -136,6 +136,7 @@ def test_decode_step_dev_token_feedback_and_error_flag():
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_k2h_bf16_full_depth_teacher_forced():
     """The 3.7B-shaped bf16 model at full size (36 layers, vocab 250624), short
     prompt: every logit of every position against the oracle."""
@@ -145,6 +146,7 @@ def test_k2h_bf16_full_depth_teacher_forced():
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["k2h-3.7b-fp8-kvi8-ctx4096", "k2h-3.7b-mxfp4-kvi8-ctx4096"])
 def test_k2h_quantized_full_depth_teacher_forced(name):
     """fp8 E4M3 + row scale and MXFP4 weights quantized on the device from the
@@ -155,6 +157,7 @@ def test_k2h_quantized_full_depth_teacher_forced(name):
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("prefix", [1024, 8192, 32760])
 def test_k2h_int8_long_context(prefix):
     """int8 KV at long context: every layer starts from the same seeded int8

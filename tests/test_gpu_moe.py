@@ -301,6 +301,7 @@ def test_moe_layer_identity_closed_form():
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("T", [1, 8, 32])
 def test_moe_layer_k3_full_size(T):
     """The K3-shaped layer at full size (896 MXFP4 experts, 15.7 GB): every
