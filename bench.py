@@ -30,6 +30,44 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 
+# HBM bytes per launch from two profiler counter runs (FETCH_SIZE, then
+# WRITE_SIZE; KiB per dispatch, averaged over every dispatch of the kernel in
+# a short decode run), scaled by what the same counters read for the copy
+# probe (--copy-probe 1024: 1 GiB read reads as 524303.4 KiB fetched, 1 GiB
+# written as 1048576 KiB).  A reading holds only for the kernel sources it was
+# taken on: if their digest differs, the traffic is reported as null.
+FETCH_SCALE = 1073741824 / (524303.4 * 1024)
+WRITE_SCALE = 1073741824 / (1048576.0 * 1024)
+GEMV_BF16_SOURCES = ("k2_dev.h", "k2_internal.h", "gemv_impl.h", "gemv.hip", "gemv_bf16.hip")
+PMC_TRAFFIC = {
+    "k2h-3.7b-bf16-kvbf16-ctx4096": {
+        "sources": GEMV_BF16_SOURCES, "digest": "682f5a1f58858d6c",
+        "kib": {"qkv_norm_gemv": (15489.5, 24.0), "o_gemv_residual": (10386.5, 20.0),
+                "gate_up_norm_gemv_swiglu": (51351.0, 40.0),
+                "down_gemv_residual": (25857.1, 20.0),
+                "lm_head_norm_gemv_argmax": (626723.7, 1237.2)}},
+}
+
+
+def source_digest(files) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(f.encode())
+        with open(os.path.join(ROOT, "quantized_gemv_gqa_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(workload: str, kernel: str):
+    """Counter-measured HBM bytes per launch of `kernel`, or None when no
+    reading was taken for it or its sources changed since."""
+    e = PMC_TRAFFIC.get(workload)
+    if e is None or kernel not in e["kib"] or source_digest(e["sources"]) != e["digest"]:
+        return None
+    f, w = e["kib"][kernel]
+    return int(round(f * 1024 * FETCH_SCALE + w * 1024 * WRITE_SCALE))
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -333,6 +371,24 @@ def bench_moe(cfg, args, dev):
     print(json.dumps(out), flush=True)
 
 
+def copy_probe(mib: int):
+    """Five launches of an elementwise fp32 copy (y = x * 1) over mib MiB:
+    each reads and writes exactly mib MiB.  Profiler counters of these
+    launches calibrate the byte counters read for the decode kernels."""
+    import torch
+    n = mib * (1 << 20) // 4
+    dev = torch.device("cuda:0")
+    x = torch.rand(n, device=dev)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    assert torch.equal(x, y)
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "launches": 5}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,6 +404,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--tokens", default=None,
                     help="latent-MoE workload only: comma-separated token counts")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="instead of the decode bench: launch a plain fp32 copy kernel over "
+                         "MIB MiB five times (the known-size reference that scales the HBM "
+                         "byte counters of a profiler run)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -358,6 +418,9 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
 
     import synth
     from quantized_gemv_gqa_decode_amd import k2
@@ -446,7 +509,8 @@ def main():
     for name, (ms, nbytes) in kt.items():
         kernels[name] = {"us": round(ms * 1000, 2), "bytes": nbytes,
                          "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                         "us_per_step": round(ms * 1000 * per_step_share[name], 1)}
+                         "us_per_step": round(ms * 1000 * per_step_share[name], 1),
+                         "traffic": pmc_traffic(cfg.name, name)}
     dom = max(kernels, key=lambda k: kernels[k]["us_per_step"])
     d = kernels[dom]
     achieved = d["GBps"]
@@ -481,7 +545,8 @@ def main():
         "step_frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "bytes_per_launch": d["bytes"], "us_per_launch": d["us"], "traffic": None},
+                     "bytes_per_launch": d["bytes"], "us_per_launch": d["us"],
+                     "traffic": d["traffic"]},
         "kernels": kernels,
         "cpu_baseline": cpu,
         "tokens_head": toks[:8],
