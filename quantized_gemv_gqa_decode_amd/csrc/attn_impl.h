@@ -44,6 +44,75 @@ constexpr float K2_LN2 = 0.6931471805599453f;
 // 2^x with the hardware exponential (x <= 0 here; -inf gives 0)
 __device__ __forceinline__ float k2_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x plus its value in lane ^ 16 (permlane16_swap) or lane ^ 32
+// (permlane32_swap): VALU lane swaps, no LDS; every lane of a pair gets the
+// same bits.
+__device__ __forceinline__ float xor16_add(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_add(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Reduce-scatter over the position groups of a wave (lanes that share
+// lane % LPP, group = lane / LPP, LPP in {8, 16, 32}): each step pairs value
+// i with value i + n/2 and one lane swap leaves the sum of the first in the
+// lanes whose group bit is 0 and the sum of the second in the others, so
+// every step halves the values per lane.  On return v[j], j < NV * LPP / 64,
+// holds the total over the groups of value j + (NV * LPP / 64) * group.
+template <int NV, int LPP>
+__device__ __forceinline__ void group_reduce_scatter(float (&v)[NV], int lane)
+{
+    static_assert(LPP == 8 || LPP == 16 || LPP == 32, "group bits 3..5");
+    static_assert(NV % (64 / LPP) == 0, "values split evenly");
+    if constexpr (LPP <= 32) {                     // group bit 5: lane ^ 32
+#pragma unroll
+        for (int i = 0; i < NV / 2; ++i) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + NV / 2]),
+                                                            false, false);
+            v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+    }
+    if constexpr (LPP <= 16) {                     // group bit 4: lane ^ 16 (rows)
+        constexpr int n = NV / 2;                  // values left after bit 5
+#pragma unroll
+        for (int i = 0; i < n / 2; ++i) {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + n / 2]),
+                                                            false, false);
+            v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+    }
+    if constexpr (LPP <= 8) {                      // group bit 3: lane ^ 8 inside a row
+        constexpr int n = NV / 4;                  // values left after bits 5 and 4
+        const bool hi = (lane & 8) != 0;
+#pragma unroll
+        for (int i = 0; i < n / 2; ++i) {
+            const float keep = hi ? v[i + n / 2] : v[i];
+            const float send = hi ? v[i] : v[i + n / 2];
+            v[i] = keep + dpp<0x128>(send);        // row_ror:8 reads lane ^ 8
+        }
+    }
+}
+
+// Sum over the lanes that share lane % LPP (the 64 / LPP position groups of
+// a wave), result in every lane: rotations inside rows of 16 (row_ror by 8,
+// 4, ... down to LPP), then the lane swaps across rows and halves.
+template <int LPP>
+__device__ __forceinline__ float subgroup_sum(float x)
+{
+    if constexpr (LPP <= 8) x += dpp<0x128>(x);
+    if constexpr (LPP <= 4) x += dpp<0x124>(x);
+    if constexpr (LPP <= 2) x += dpp<0x122>(x);
+    if constexpr (LPP <= 1) x += dpp<0x121>(x);
+    if constexpr (LPP <= 16) x = xor16_add(x);
+    if constexpr (LPP <= 32) x = xor32_add(x);
+    return x;
+}
+
 // decode one 16-byte cache chunk into EPC floats; int8 as unsigned bytes
 // u = code + 128 (one convert per element; callers subtract the offset)
 template <int KVDT>
@@ -121,43 +190,69 @@ __device__ __forceinline__ float kv_head_absmax(float ax, float *tmp4)
     }
 }
 
-// Store one position of k (threads [0, HD)) and v (threads [HD, 2 HD)) for kv
-// head g into the cache; returns (through `stored`) the value read back from
-// the cache format.  Every thread of the block must call it.
+// One position of k (threads [0, HD)) and v (threads [HD, 2 HD)) of kv head
+// g in the cache format: `bits` is the element (fp32 bits, bf16 bits or the
+// int8 code), `scale` the int8 scale of the thread's row.  Returns the value
+// read back from the cache format.  Every thread of the block must call it.
+template <int KVDT, int HD, bool RAW = false>
+__device__ __forceinline__ float kv_encode_head(float val, float *tmp4, uint32_t &bits, float &scale)
+{
+    const bool active = threadIdx.x < 2 * HD;
+    float stored = 0.f;
+    bits = 0u;
+    scale = 0.f;
+    if constexpr (KVDT == K2_F32) {
+        bits = __float_as_uint(val);
+        stored = val;
+    } else if constexpr (KVDT == K2_BF16) {
+        const uint16_t b = f32_to_bf16_rne(val);
+        bits = b;
+        stored = bf16_to_f32(b);
+    } else {
+        const float amax = kv_head_absmax<HD, RAW>(active ? fabsf(val) : 0.f, tmp4);
+        const float s = amax / 127.0f;
+        float q = 0.f;
+        if (amax != 0.f) {
+            q = rintf(val / s);
+            q = fminf(fmaxf(q, -127.f), 127.f);
+        }
+        bits = (uint32_t)(uint8_t)(int8_t)(int)q;
+        scale = amax != 0.f ? s : 0.f;
+        stored = q * scale;
+    }
+    return active ? stored : 0.f;
+}
+
+// Write what kv_encode_head produced into slot pos of the cache (threads
+// [0, 2 HD); the first thread of each row also writes the int8 scale).
+template <int KVDT, int HD>
+__device__ __forceinline__ void kv_write_head(uint32_t bits, float scale, void *kc, void *vc,
+                                              float *ks, float *vs, int g, int cap, int pos)
+{
+    const int t = threadIdx.x;
+    if (t >= 2 * HD) return;
+    const bool is_k = t < HD;
+    const int d = is_k ? t : t - HD;
+    const int64_t idx = ((int64_t)g * cap + pos) * HD + d;
+    if constexpr (KVDT == K2_F32) {
+        (is_k ? (uint32_t *)kc : (uint32_t *)vc)[idx] = bits;
+    } else if constexpr (KVDT == K2_BF16) {
+        (is_k ? (uint16_t *)kc : (uint16_t *)vc)[idx] = (uint16_t)bits;
+    } else {
+        (is_k ? (uint8_t *)kc : (uint8_t *)vc)[idx] = (uint8_t)bits;
+        if (d == 0) (is_k ? ks : vs)[(int64_t)g * cap + pos] = scale;
+    }
+}
+
+// Encode and store one position (see kv_encode_head); returns the stored value.
 template <int KVDT, int HD, bool RAW = false>
 __device__ __forceinline__ float kv_store_head(float val, void *kc, void *vc, float *ks, float *vs,
                                                int g, int cap, int pos, float *tmp4)
 {
-    const int t = threadIdx.x;
-    const bool is_k = t < HD, active = t < 2 * HD;
-    const int d = is_k ? t : t - HD;
-    const int64_t idx = ((int64_t)g * cap + pos) * HD + d;
-    float stored = 0.f;
-    if constexpr (KVDT == K2_F32) {
-        if (active) {
-            (is_k ? (float *)kc : (float *)vc)[idx] = val;
-            stored = val;
-        }
-    } else if constexpr (KVDT == K2_BF16) {
-        if (active) {
-            const uint16_t b = f32_to_bf16_rne(val);
-            (is_k ? (uint16_t *)kc : (uint16_t *)vc)[idx] = b;
-            stored = bf16_to_f32(b);
-        }
-    } else {
-        const float amax = kv_head_absmax<HD, RAW>(active ? fabsf(val) : 0.f, tmp4);
-        if (active) {
-            const float s = amax / 127.0f;
-            float q = 0.f;
-            if (amax != 0.f) {
-                q = rintf(val / s);
-                q = fminf(fmaxf(q, -127.f), 127.f);
-            }
-            (is_k ? (int8_t *)kc : (int8_t *)vc)[idx] = (int8_t)(int)q;
-            if (d == 0) (is_k ? ks : vs)[(int64_t)g * cap + pos] = amax != 0.f ? s : 0.f;
-            stored = q * (amax != 0.f ? s : 0.f);
-        }
-    }
+    uint32_t bits;
+    float scale;
+    const float stored = kv_encode_head<KVDT, HD, RAW>(val, tmp4, bits, scale);
+    kv_write_head<KVDT, HD>(bits, scale, kc, vc, ks, vs, g, cap, pos);
     return stored;
 }
 
@@ -420,17 +515,36 @@ __device__ __forceinline__ void attn_block(const AttnArgs &a, int g, int s, int 
 #define K2_VMCNT(n) (((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
 
 // Optional per-block stage trace for performance work (never enabled in the
-// library build): thread 0 records the 100 MHz real-time counter.
+// library build): thread 0 keeps the 100 MHz real-time counter of each
+// stage in LDS and writes them out when the block ends (a global store in
+// between would be waited for by later waits and distort the stages).
 #ifdef K2_ATTN_TRACE
-static __device__ unsigned long long k2_attn_trace[4096][8];
+static __device__ unsigned long long k2_attn_trace[4096][12];
+static __shared__ unsigned long long k2_attn_trs[12];
 #define K2_ATRACE(i)                                                                         \
     do {                                                                                     \
+        if (threadIdx.x == 0) k2_attn_trs[i] = __builtin_amdgcn_s_memrealtime();             \
+    } while (0)
+#define K2_ATRACE_FLUSH()                                                                    \
+    do {                                                                                     \
         const int b_ = blockIdx.y * gridDim.x + blockIdx.x;                                  \
-        if (threadIdx.x == 0 && b_ < 4096) k2_attn_trace[b_][i] = __builtin_amdgcn_s_memrealtime(); \
+        if (threadIdx.x == 0 && b_ < 4096)                                                   \
+            for (int i_ = 0; i_ < 12; ++i_) k2_attn_trace[b_][i_] = k2_attn_trs[i_];         \
+    } while (0)
+#define K2_ATRACE_CLEAR()                                                                    \
+    do {                                                                                     \
+        if (threadIdx.x == 0)                                                                \
+            for (int i_ = 0; i_ < 12; ++i_) k2_attn_trs[i_] = 0ull;                          \
     } while (0)
 #else
 #define K2_ATRACE(i) \
     do {         \
+    } while (0)
+#define K2_ATRACE_FLUSH() \
+    do {              \
+    } while (0)
+#define K2_ATRACE_CLEAR() \
+    do {              \
     } while (0)
 #endif
 
@@ -465,8 +579,14 @@ __host__ __device__ constexpr int attn_stream_lds_floats()
            ATT_WPB;
 }
 
+// The new position's cache element is returned in kv_bits / kv_scale (see
+// kv_encode_head) instead of being stored: the caller writes it at the end,
+// so that no wait inside the block (a barrier, or the wait the compiler
+// places before LDS writes that could race an LDS-DMA) waits for its
+// store.  Returns whether this block holds the new position.
 template <int KVDT, int HD, int REP, bool FUSED, bool COH>
-__device__ __forceinline__ void attn_stream_block(const AttnArgs &a, int g, int s, int S, float *smem)
+__device__ __forceinline__ bool attn_stream_block(const AttnArgs &a, int g, int s, int S, float *smem,
+                                                  uint32_t &kv_bits, float &kv_scale)
 {
     using G = StreamGeom<KVDT, HD>;
     using T = typename G::T;
@@ -582,7 +702,7 @@ __device__ __forceinline__ void attn_stream_block(const AttnArgs &a, int g, int 
         if (holds_new) {
             float val = nk0;
             if (tid < HD) val = tid < HALF ? nk0 * kc0 - nk1 * ks0 : nk0 * ks0 + nk1 * kc0;
-            const float st = kv_store_head<KVDT, HD, true>(val, a.kc, a.vc, a.ks, a.vs, g, a.cap, a.pos, tmp4);
+            const float st = kv_encode_head<KVDT, HD, true>(val, tmp4, kv_bits, kv_scale);
             if (tid < 2 * HD) newkv[tid / HD][tid % HD] = st;
         }
     }
@@ -688,8 +808,12 @@ __device__ __forceinline__ void attn_stream_block(const AttnArgs &a, int g, int 
 #pragma unroll
             for (int e = 0; e < EPC; ++e) acc[h][e] -= 128.0f * wsum[h];
     }
-    // the new position (fused): wave 0, values from LDS
+    // the new position (fused): wave 0, values from LDS (read by every lane;
+    // only sub-group 0 adds them)
     if (holds_new && wave == 0) {
+        float nv[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) nv[e] = newkv[1][cl * EPC + e];
 #pragma unroll
         for (int h = 0; h < REP; ++h) {
             float p = 0.f;
@@ -697,38 +821,50 @@ __device__ __forceinline__ void attn_stream_block(const AttnArgs &a, int g, int 
             const float snew = wave_sum(p);
             const float mn = fmaxf(m[h], snew);
             const float corr = k2_exp2(m[h] - mn);       // m = -inf gives 0
-            const float pn = k2_exp2(snew - mn);
-            l[h] = l[h] * corr + (sub == 0 ? pn : 0.f);
+            const float pw = sub == 0 ? k2_exp2(snew - mn) : 0.f;
+            l[h] = l[h] * corr + pw;
 #pragma unroll
-            for (int e = 0; e < EPC; ++e)
-                acc[h][e] = acc[h][e] * corr + (sub == 0 ? pn * newkv[1][cl * EPC + e] : 0.f);
+            for (int e = 0; e < EPC; ++e) acc[h][e] = acc[h][e] * corr + pw * nv[e];
             m[h] = mn;
         }
     }
-    // 4. sum over the position sub-groups of the wave (same m across the wave)
+    K2_ATRACE(7);
+    // 4. sum over the position sub-groups of the wave (m is the same across
+    // the wave): lane swaps and rotations, no LDS
 #pragma unroll
-    for (int h = 0; h < REP; ++h) {
-#pragma unroll
-        for (int o = LPP; o < K2_WAVE; o <<= 1) l[h] += __shfl_xor(l[h], o, K2_WAVE);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-            float v = acc[h][e];
-#pragma unroll
-            for (int o = LPP; o < K2_WAVE; o <<= 1) v += __shfl_xor(v, o, K2_WAVE);
-            acc[h][e] = v;
-        }
-    }
-    if (sub == 0) {
+    for (int h = 0; h < REP; ++h) l[h] = subgroup_sum<LPP>(l[h]);
+    if constexpr (LPP >= 8 && LPP <= 32 && (REP * EPC) % PPI == 0) {
+        // reduce-scatter: every lane ends with REP*EPC/PPI of the sums
+        constexpr int NV = REP * EPC, NJ = NV / PPI;
+        float v[NV];
 #pragma unroll
         for (int h = 0; h < REP; ++h)
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) red_o[wave][h][cl * EPC + e] = acc[h][e];
+            for (int e = 0; e < EPC; ++e) v[h * EPC + e] = acc[h][e];
+        group_reduce_scatter<NV, LPP>(v, lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int k = j + NJ * sub;            // flat (head, element) index
+            red_o[wave][k / EPC][cl * EPC + k % EPC] = v[j];
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < REP; ++h)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[h][e] = subgroup_sum<LPP>(acc[h][e]);
+        if (sub == 0) {
+#pragma unroll
+            for (int h = 0; h < REP; ++h)
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) red_o[wave][h][cl * EPC + e] = acc[h][e];
+        }
     }
     if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < REP; ++h) { red_ml[wave][h][0] = m[h]; red_ml[wave][h][1] = l[h]; }
     }
     __syncthreads();
+    K2_ATRACE(8);
 
     // 5. combine the waves; output directly (one split) or publish a partial
     const int64_t pbase = ((int64_t)g * S + s) * REP;
@@ -756,20 +892,23 @@ __device__ __forceinline__ void attn_stream_block(const AttnArgs &a, int g, int 
             }
         }
     }
+    return holds_new;
 }
 
 template <int REP, int NTH = K2_BLOCK>
 __host__ __device__ constexpr int combine_lds_floats()
 {
-    return ((K2_ATTN_MAX_SPLITS * REP + 2 * REP + 3) & ~3) + NTH * 4;
+    return ((2 * K2_ATTN_MAX_SPLITS * REP + 2 * REP + 3) & ~3) + NTH * 4;
 }
 
-// Combine for kv head g (a block of K2_BLOCK threads; every thread calls it):
-// M = max_s m_s, L = sum_s l_s e^(m_s - M), out = sum_s o_s e^(m_s - M) / L,
-// summed in split order per thread.  Float4 column c of the head's
-// REP*HD/4 columns belongs to threads c, c + C4, ...; each of them loads its
-// splits' float4s (16 at a time, all issued before any is used), so that a
-// batch costs one memory round trip.
+// Combine for kv head g (a block of NTH threads; every thread calls it):
+// M = max_s m_s, L = sum_s l_s e^(m_s - M), out = sum_s o_s e^(m_s - M) / L
+// (a fixed summation order, so the result does not depend on which block
+// combines).  Float4 column c of the head's
+// REP*HD/4 columns belongs to threads c, c + C4, ...; every thread issues
+// its first NB partial float4s and its (m, l) pairs before it uses any of
+// them, so that (for S <= NB * threads per column) the whole combine costs
+// one memory round trip.
 template <int HD, int REP, bool COH, int NTH = K2_BLOCK>
 __device__ __forceinline__ void attn_combine_block(const AttnArgs &a, int g, float *smem)
 {
@@ -778,49 +917,74 @@ __device__ __forceinline__ void attn_combine_block(const AttnArgs &a, int g, flo
     constexpr int CPT = C4 >= NTH ? C4 / NTH : 1;        // columns per thread
     constexpr int NB = 16;                               // loads in flight per batch
     static_assert(C4 % NTH == 0 || NTH % C4 == 0, "combine shape");
-    auto f = reinterpret_cast<float (*)[REP]>(smem);     // [MAX_SPLITS][REP]: m, then weights
-    float *Mh = smem + K2_ATTN_MAX_SPLITS * REP, *Linv = Mh + REP;
-    float4 *part4 = reinterpret_cast<float4 *>(smem + ((K2_ATTN_MAX_SPLITS * REP + 2 * REP + 3) & ~3));
+    auto fm = reinterpret_cast<float (*)[REP]>(smem);    // [MAX_SPLITS][REP] maxima
+    auto fl = reinterpret_cast<float (*)[REP]>(smem + K2_ATTN_MAX_SPLITS * REP);   // sums
+    float *Linv = smem + 2 * K2_ATTN_MAX_SPLITS * REP;                            // [REP]
+    float4 *part4 = reinterpret_cast<float4 *>(smem + ((2 * K2_ATTN_MAX_SPLITS * REP + 2 * REP + 3) & ~3));
     const int S = a.S, tid = threadIdx.x;
     const float *ml = a.part_ml + (int64_t)g * S * REP * 2;
     const float *po = a.part + (int64_t)g * S * REP * HD;
-    for (int t = tid; t < S * REP; t += NTH) f[t / REP][t % REP] = ld1<COH>(ml + (int64_t)t * 2);
-    __syncthreads();
-    if (tid < REP) {
-        float M = -INFINITY;
-        for (int q = 0; q < S; ++q) M = fmaxf(M, f[q][tid]);
-        Mh[tid] = M;
-    }
-    __syncthreads();
+    const int c0 = (C4 >= NTH) ? tid : tid % C4;          // first float4 column
+    const int q0 = (C4 >= NTH) ? 0 : tid / C4;            // first split
+    // 1. every load of the first batch, then the (m, l) pairs (q0 is
+    // uniform over a wave, so the guards do not diverge; no load is issued
+    // past the last split: repeated reads of one line from every thread
+    // would all queue on one memory channel)
+    float4 v[CPT][NB];
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc)
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int q = q0 + i * TPC;
+            v[cc][i] = q < S ? ld4<COH>(po, (q * C4 + c0 + cc * NTH) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     for (int t = tid; t < S * REP; t += NTH) {
-        const float mq = f[t / REP][t % REP];
-        f[t / REP][t % REP] = mq == -INFINITY ? 0.f : expf(mq - Mh[t % REP]);
+        const float m = ld1<COH>(ml + (int64_t)t * 2), l = ld1<COH>(ml + (int64_t)t * 2 + 1);
+        fm[t / REP][t % REP] = m;
+        fl[t / REP][t % REP] = l;
     }
     __syncthreads();
-    if (tid < REP) {
-        float L = 0.f;
-        for (int q = 0; q < S; ++q) L += f[q][tid] * ld1<COH>(ml + ((int64_t)q * REP + tid) * 2 + 1);
-        Linv[tid] = 1.0f / L;
+    K2_ATRACE(9);
+    // 2. per head (one wave each): M, the split weights e^(m_s - M) in place
+    // of the maxima, and 1 / L
+    {
+        const int wave = tid >> 6, lane = tid & 63;
+        for (int h = wave; h < REP; h += NTH / K2_WAVE) {
+            float M = -INFINITY;
+            for (int q = lane; q < S; q += K2_WAVE) M = fmaxf(M, fm[q][h]);
+            M = wave_max(M);
+            float L = 0.f;
+            for (int q = lane; q < S; q += K2_WAVE) {
+                const float mq = fm[q][h];
+                const float w = mq == -INFINITY ? 0.f : expf(mq - M);
+                fm[q][h] = w;
+                L += w * fl[q][h];
+            }
+            L = wave_sum(L);
+            if (lane == 0) Linv[h] = 1.0f / L;
+        }
     }
+    __syncthreads();
+    K2_ATRACE(10);
+    // 3. weighted sums of the partials
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
-        const int c = (C4 >= NTH) ? tid + cc * NTH : tid % C4;   // float4 column
-        const int q0 = (C4 >= NTH) ? 0 : tid / C4;                     // first split
+        const int c = c0 + cc * NTH;
         const int h = c * 4 / HD;
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int qb = q0; qb < S; qb += TPC * NB) {
-            float4 v[NB];
+            if (qb != q0) {                                // later batches (S > NB * TPC)
 #pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const int q = qb + i * TPC;
-                const int qq = q < S ? q : q0;
-                v[i] = ld4<COH>(po, (qq * C4 + c) * 4);
+                for (int i = 0; i < NB; ++i) {
+                    const int q = qb + i * TPC;
+                    v[cc][i] = q < S ? ld4<COH>(po, (q * C4 + c) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
             }
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 const int q = qb + i * TPC;
-                const float w = q < S ? f[q][h] : 0.f;
-                o.x += w * v[i].x; o.y += w * v[i].y; o.z += w * v[i].z; o.w += w * v[i].w;
+                const float w = q < S ? fm[q][h] : 0.f;
+                o.x += w * v[cc][i].x; o.y += w * v[cc][i].y; o.z += w * v[cc][i].z; o.w += w * v[cc][i].w;
             }
         }
         if constexpr (TPC > 1) {
@@ -834,8 +998,6 @@ __device__ __forceinline__ void attn_combine_block(const AttnArgs &a, int g, flo
                     o.x += u.x; o.y += u.y; o.z += u.z; o.w += u.w;
                 }
             }
-        } else {
-            __syncthreads();                              // Linv
         }
         if (tid < C4 || C4 >= NTH) {
             const float li = Linv[h];
@@ -845,7 +1007,6 @@ __device__ __forceinline__ void attn_combine_block(const AttnArgs &a, int g, flo
             st1<COH>(out + 2, o.z * li);
             st1<COH>(out + 3, o.w * li);
         }
-        if constexpr (CPT > 1) __syncthreads();
     }
 }
 
@@ -861,23 +1022,32 @@ __global__ __launch_bounds__(ATT_NT) void attn_kernel(const AttnArgs a)
     static_assert(NA >= NC, "combine fits the attention LDS");
     __shared__ int last;
     const int g = blockIdx.y, S = gridDim.x;
-    attn_stream_block<KVDT, HD, REP, FUSED, true>(a, g, blockIdx.x, S, smem);
+    K2_ATRACE_CLEAR();
+    uint32_t kv_bits = 0u;
+    float kv_scale = 0.f;
+    const bool holder = attn_stream_block<KVDT, HD, REP, FUSED, true>(a, g, blockIdx.x, S, smem, kv_bits,
+                                                                      kv_scale);
     K2_ATRACE(4);
-    if (S == 1) return;
-    __builtin_amdgcn_s_waitcnt(0);                 // this thread's partial stores completed
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned old = __hip_atomic_fetch_add(a.head_cnt + g, 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        last = old == (unsigned)S - 1;
-        if (last) __hip_atomic_store(a.head_cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (S > 1) {
+        __builtin_amdgcn_s_waitcnt(0);             // this thread's partial stores completed
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned old = __hip_atomic_fetch_add(a.head_cnt + g, 1u, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+            last = old == (unsigned)S - 1;
+            if (last) __hip_atomic_store(a.head_cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        K2_ATRACE(5);
+        if (last) {
+            attn_combine_block<HD, REP, true, ATT_NT>(a, g, smem);
+            K2_ATRACE(6);
+        }
     }
-    __syncthreads();
-    K2_ATRACE(5);
-    if (last) {
-        attn_combine_block<HD, REP, true, ATT_NT>(a, g, smem);
-        K2_ATRACE(6);
-    }
+    // the new position's K/V: no other block of this launch reads slot pos
+    // (the block holding it used the values from LDS)
+    if (FUSED && holder) kv_write_head<KVDT, HD>(kv_bits, kv_scale, a.kc, a.vc, a.ks, a.vs, g, a.cap, a.pos);
+    K2_ATRACE_FLUSH();
 }
 
 // Standalone store of one position (k, v already rotated), grid = n_kv.
