@@ -748,12 +748,23 @@ __device__ __forceinline__ bool attn_stream_block(const AttnArgs &a, int g, int 
         const char *vt = kt + G::TILEB;
         const float *kst = st + 2 * G::TILEB / 4, *vst = kst + TP;
         const int p0 = j0 + t * TP;
+        // slots of this wave with at least one cached position (a prefix of
+        // the slots; wave-uniform): short chunks leave later slots empty
+        int ns = 0;
+#pragma unroll
+        for (int n = 0; n < NSLOT; ++n)
+            if (p0 + (n * WPB + wave) * PPI < jc) ns = n + 1;
         float sc[NSLOT][REP];
         int pr[NSLOT];
 #pragma unroll
         for (int n = 0; n < NSLOT; ++n) {
             const int r = (n * WPB + wave) * PPI + sub;            // row within the tile
             pr[n] = r;
+            if (n >= ns) {
+#pragma unroll
+                for (int h = 0; h < REP; ++h) sc[n][h] = -INFINITY;
+                continue;
+            }
             float kv[EPC];
             kv_decode_u<KVDT>(*reinterpret_cast<const k2_u4 *>(kt + r * G::ROWB + cl * 16), kv);
             const bool valid = p0 + r < jc;

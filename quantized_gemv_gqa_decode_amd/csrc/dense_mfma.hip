@@ -1,0 +1,231 @@
+// dense_mfma.hip -- a bf16 weight matrix times a few fp32 activation rows
+// (2 to 32 tokens at a time) on the matrix cores.
+//
+// The latent-MoE layer ([k3_run.c] forward(): router, W_dn, W_up and the
+// shared experts) multiplies every dense matrix by T token rows.  With T rows
+// a weight byte feeds 2T flops; past a few tokens that outgrows fp32 vector
+// arithmetic, so here the product runs on v_mfma_f32_16x16x32_bf16:
+//   * each activation is split into bf16 hi + bf16 lo (x - hi rounded again),
+//     two MFMAs per weight tile, fp32 accumulation: the weights are exact in
+//     bf16 and the split keeps ~16 bits of every activation;
+//   * a block of 4 waves owns 256 rows and one k-range (split-K); it stages
+//     its slice of the activations once in LDS as the two bf16 planes, each
+//     wave streams 4 row tiles of 16 rows from HBM, one 128-column chunk
+//     ahead of the MFMAs;
+//   * the k order inside a chunk is permuted so that every lane reads 64
+//     contiguous bytes of its row (the sum over k does not depend on the
+//     order as long as both operands use the same one);
+//   * per-split partials [split][token][row] are summed in split order by a
+//     second kernel, which also applies the epilogue (plain, add into y, or
+//     SwiGLU of row pairs i, i + N/2).
+// MFMA operand layout (16x16x32 bf16): lane l holds A row l % 16 and B column
+// l % 16, elements k = 8 (l / 16) + [0, 8); D holds column l % 16, rows
+// 4 (l / 16) + [0, 4).
+#include "k2_dev.h"
+#include "k2_internal.h"
+
+namespace k2 {
+
+typedef short dm_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float dm_f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int DM_RT = 4;                          // 16-row tiles per wave
+constexpr int DM_WAVES = 4;                       // waves per block
+constexpr int DM_ROWS = DM_RT * 16 * DM_WAVES;    // rows per block
+constexpr int DM_KC = 128;                        // columns per chunk (4 MFMA k-steps)
+constexpr int DM_MAX_KS = 512;                    // columns per split
+constexpr int DM_MAX_T = 32;                      // tokens per launch
+
+struct DenseArgs {
+    const uint16_t *W;       // [N][K] bf16
+    const float *x;          // [T][K] fp32
+    float *part;             // [splits][TP][N]
+    int N, K, T, KS;
+};
+
+__host__ __device__ constexpr int dm_lds_bytes(int tp, int ks) { return 2 * tp * (ks + 8) * 2; }
+
+template <int NTT, int KS>
+__global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
+{
+    constexpr int TP = 16 * NTT;
+    constexpr int RS = KS + 8;                    // LDS row stride (bf16): 16 B of pad per row
+    constexpr int NCH = KS / DM_KC;               // chunks per split
+    constexpr int NG = TP * KS / 4 / 256;         // activation float4s per thread
+    extern __shared__ float4 lds4[];
+    uint16_t *xh = reinterpret_cast<uint16_t *>(lds4);
+    uint16_t *xl = xh + TP * RS;
+    const int split = blockIdx.y, k0 = split * KS;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int q = lane >> 4, c16 = lane & 15;
+
+    // rows of this wave's tiles (tiles past N read the last tile again and
+    // are never stored)
+    int64_t rowoff[DM_RT];
+    bool rok[DM_RT];
+#pragma unroll
+    for (int rt = 0; rt < DM_RT; ++rt) {
+        const int r0 = blockIdx.x * DM_ROWS + (wave * DM_RT + rt) * 16;
+        rok[rt] = r0 < a.N;
+        const int row = (rok[rt] ? r0 : a.N - 16) + c16;
+        rowoff[rt] = (int64_t)row * a.K + k0 + q * 32;
+    }
+    const dm_bf16x8 *Wv = reinterpret_cast<const dm_bf16x8 *>(a.W);
+    // chunk c of tile rt, k-step j: the 16 B at element rowoff + c*128 + 8j
+    auto load_chunk = [&](int c, dm_bf16x8 (&w)[DM_RT][4]) {
+#pragma unroll
+        for (int rt = 0; rt < DM_RT; ++rt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                w[rt][j] = __builtin_nontemporal_load(Wv + (rowoff[rt] + c * DM_KC + 8 * j) / 8);
+    };
+    dm_bf16x8 wc[DM_RT][4];
+    load_chunk(0, wc);                            // weights first: their latency covers the staging
+
+    // stage the activation slice as bf16 hi / lo planes (tokens >= T are 0):
+    // every load is issued before any is converted
+    float4 xv[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int i = g * 256 + tid, t = i / (KS / 4), k = (i % (KS / 4)) * 4;
+        xv[g] = t < a.T ? *reinterpret_cast<const float4 *>(a.x + (int64_t)t * a.K + k0 + k)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int i = g * 256 + tid, t = i / (KS / 4), k = (i % (KS / 4)) * 4;
+        const float f[4] = {xv[g].x, xv[g].y, xv[g].z, xv[g].w};
+        uint16_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = f32_to_bf16_rne(f[e]);
+            l[e] = f32_to_bf16_rne(f[e] - bf16_to_f32(h[e]));
+        }
+        uint2 hv, lv;
+        hv.x = h[0] | ((uint32_t)h[1] << 16); hv.y = h[2] | ((uint32_t)h[3] << 16);
+        lv.x = l[0] | ((uint32_t)l[1] << 16); lv.y = l[2] | ((uint32_t)l[3] << 16);
+        *reinterpret_cast<uint2 *>(xh + t * RS + k) = hv;
+        *reinterpret_cast<uint2 *>(xl + t * RS + k) = lv;
+    }
+    __syncthreads();
+
+    dm_f32x4 acc[DM_RT][NTT];
+#pragma unroll
+    for (int rt = 0; rt < DM_RT; ++rt)
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) acc[rt][tt] = dm_f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int c, const dm_bf16x8 (&w)[DM_RT][4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int kk = c * DM_KC + q * 32 + 8 * j;
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+                const int t = tt * 16 + c16;
+                const dm_bf16x8 bh = *reinterpret_cast<const dm_bf16x8 *>(xh + t * RS + kk);
+                const dm_bf16x8 bl = *reinterpret_cast<const dm_bf16x8 *>(xl + t * RS + kk);
+#pragma unroll
+                for (int rt = 0; rt < DM_RT; ++rt) {
+                    acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[rt][j], bh, acc[rt][tt], 0, 0, 0);
+                    acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[rt][j], bl, acc[rt][tt], 0, 0, 0);
+                }
+            }
+        }
+    };
+    // one chunk ahead of the MFMAs; the last chunk without a next one
+#pragma unroll 1
+    for (int c = 0; c + 1 < NCH; ++c) {
+        dm_bf16x8 wn[DM_RT][4];
+        load_chunk(c + 1, wn);
+        compute(c, wc);
+#pragma unroll
+        for (int rt = 0; rt < DM_RT; ++rt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wc[rt][j] = wn[rt][j];
+    }
+    compute(NCH - 1, wc);
+
+    // partials: the lane holds rows 4q..4q+3 of each tile for token c16 + 16 tt
+#pragma unroll
+    for (int rt = 0; rt < DM_RT; ++rt) {
+        if (!rok[rt]) continue;
+        const int r0 = blockIdx.x * DM_ROWS + (wave * DM_RT + rt) * 16 + 4 * q;
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) {
+            const int t = tt * 16 + c16;
+            if (t < a.T)
+                *reinterpret_cast<float4 *>(a.part + ((int64_t)split * TP + t) * a.N + r0) =
+                    make_float4(acc[rt][tt][0], acc[rt][tt][1], acc[rt][tt][2], acc[rt][tt][3]);
+        }
+    }
+}
+
+// y[t][n] (+)= sum over splits in split order; SwiGLU: n < N/2 pairs rows n
+// (gate) and n + N/2 (up) and y has N/2 columns.
+__global__ __launch_bounds__(256) void dense_reduce_kernel(const float *part, int splits, int TP, int N,
+                                                           int epi, float *y)
+{
+    const int t = blockIdx.y;
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    const int n_out = epi == DM_EPI_SWIGLU ? N / 2 : N;
+    if (n >= n_out) return;
+    float s = 0.f, u = 0.f;
+    for (int sp = 0; sp < splits; ++sp) {
+        const float *p = part + ((int64_t)sp * TP + t) * N;
+        s += p[n];
+        if (epi == DM_EPI_SWIGLU) u += p[n + n_out];
+    }
+    float *dst = y + (int64_t)t * n_out + n;
+    if (epi == DM_EPI_SWIGLU) *dst = s / (1.0f + expf(-s)) * u;
+    else if (epi == DM_EPI_ADD) *dst += s;
+    else *dst = s;
+}
+
+// Columns per split: the largest of 512, 256, 128 dividing K that still
+// gives at least 256 blocks (else 128).
+static int dm_ks(int N, int K)
+{
+    const int rb = (N + DM_ROWS - 1) / DM_ROWS;
+    for (int ks = DM_MAX_KS; ks >= DM_KC; ks >>= 1)
+        if (K % ks == 0 && (int64_t)rb * (K / ks) >= 256) return ks;
+    return DM_KC;
+}
+
+bool dense_mfma_ok(int N, int K) { return N >= 16 && N % 16 == 0 && K % DM_KC == 0; }
+
+size_t dense_mfma_ws_bytes(int N, int K, int T)
+{
+    if (!dense_mfma_ok(N, K) || T < 2) return 0;
+    const int tp = (T < DM_MAX_T ? T : DM_MAX_T) <= 16 ? 16 : 32;
+    return (size_t)(K / dm_ks(N, K)) * tp * N * 4;
+}
+
+// y = W x for T token rows (T >= 2), through per-split partials in `part`
+// (dense_mfma_ws_bytes); groups of up to 32 tokens run one after another.
+int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi, float *part,
+               hipStream_t st)
+{
+    if (!dense_mfma_ok(N, K) || T < 2) return K2_EUNSUPPORTED;
+    const int KS = dm_ks(N, K), splits = K / KS;
+    const int n_out = epi == DM_EPI_SWIGLU ? N / 2 : N;
+    for (int t0 = 0; t0 < T; t0 += DM_MAX_T) {
+        const int tg = T - t0 < DM_MAX_T ? T - t0 : DM_MAX_T;
+        DenseArgs a{W, x + (int64_t)t0 * K, part, N, K, tg, KS};
+        const dim3 grid((N + DM_ROWS - 1) / DM_ROWS, splits);
+        const int tp = tg <= 16 ? 16 : 32;
+        const size_t lds = dm_lds_bytes(tp, KS);
+#define DM_GO(NTT, KSV) hipLaunchKernelGGL((dense_mfma_kernel<NTT, KSV>), grid, dim3(256), lds, st, a)
+        if (tp == 16) {
+            if (KS == 512) DM_GO(1, 512); else if (KS == 256) DM_GO(1, 256); else DM_GO(1, 128);
+        } else {
+            if (KS == 512) DM_GO(2, 512); else if (KS == 256) DM_GO(2, 256); else DM_GO(2, 128);
+        }
+#undef DM_GO
+        K2_CHECK_LAUNCH();
+        hipLaunchKernelGGL(dense_reduce_kernel, dim3((n_out + 255) / 256, tg), dim3(256), 0, st, part,
+                           splits, tp, N, epi, y + (int64_t)t0 * n_out);
+        K2_CHECK_LAUNCH();
+    }
+    return K2_OK;
+}
+
+}  // namespace k2

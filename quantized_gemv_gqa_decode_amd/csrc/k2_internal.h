@@ -8,7 +8,9 @@
 #define K2_MAX_LDS_FLOATS 12288          // 48 KiB of staged activations
 #define K2_GEMV_MAX_BLOCKS 4096
 #define K2_ATTN_MAX_CHUNK 1024           // positions per attention block
+#ifndef K2_ATTN_MIN_CHUNK
 #define K2_ATTN_MIN_CHUNK 64
+#endif
 #ifndef K2_ATTN_TARGET_BLOCKS
 #define K2_ATTN_TARGET_BLOCKS 256
 #endif
@@ -115,5 +117,13 @@ __device__ __forceinline__ void argmax_block(float &v, int &i)
     }
     __syncthreads();
 }
+
+// bf16-weight product with 2..32+ token rows on the matrix cores
+// (dense_mfma.hip): y = W x for T >= 2 rows through per-split partials.
+enum { DM_EPI_PLAIN = 0, DM_EPI_ADD = 1, DM_EPI_SWIGLU = 2 };
+bool dense_mfma_ok(int N, int K);
+size_t dense_mfma_ws_bytes(int N, int K, int T);
+int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi, float *part,
+               hipStream_t st);
 
 }  // namespace k2

@@ -422,6 +422,38 @@ static int gemv_rows_bf16(const uint16_t *W, const float *x, float *y, int N, in
     return K2_OK;
 }
 
+// Partials of the matrix-core path for the layer's dense products at T rows.
+static size_t moe_dense_part_bytes(const k2_moe_config *c, int T)
+{
+    size_t m = dense_mfma_ws_bytes(c->n_experts, c->hidden, T);
+    const size_t o[4] = {dense_mfma_ws_bytes(c->latent, c->hidden, T),
+                         dense_mfma_ws_bytes(c->hidden, c->latent, T),
+                         dense_mfma_ws_bytes(2 * c->inter, c->hidden, T),
+                         dense_mfma_ws_bytes(c->hidden, c->inter, T)};
+    for (size_t v : o) m = v > m ? v : m;
+    return m;
+}
+
+// y (+)= W x for T rows of bf16 weights: the matrix cores for T >= 2 when
+// the shape allows, else the GEMV (rows staged 1, 2, 4 or 8 at a time)
+// followed by the epilogue kernel.
+static int dense_rows_bf16(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi,
+                           float *part, float *tmp, hipStream_t st)
+{
+    if (T >= 2 && dense_mfma_ok(N, K)) return dense_mfma(W, x, y, N, K, T, epi, part, st);
+    if (epi == DM_EPI_PLAIN) return gemv_rows_bf16(W, x, y, N, K, T, st);
+    int rc = gemv_rows_bf16(W, x, tmp, N, K, T, st);
+    if (rc) return rc;
+    if (epi == DM_EPI_SWIGLU) {
+        hipLaunchKernelGGL(swiglu_rows_kernel, dim3((N / 2 + 255) / 256, T), dim3(256), 0, st, tmp, N / 2, y);
+    } else {
+        const int64_t n = (int64_t)T * N;
+        hipLaunchKernelGGL(add_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, y, tmp, n);
+    }
+    K2_CHECK_LAUNCH();
+    return K2_OK;
+}
+
 static int moe_dims_check(int T, int latent, int inter, int top_k, int n_experts)
 {
     if (T <= 0 || latent <= 0 || inter <= 0 || top_k <= 0 || n_experts <= 0) return K2_EINVAL;
@@ -503,6 +535,7 @@ extern "C" size_t k2_moe_layer_workspace_bytes(const k2_moe_config *c, int T)
     n += k2_align256((size_t)T * 2 * c->inter * 4);                 // shared gate/up
     n += k2_align256((size_t)T * c->inter * 4);                     // shared act
     n += k2_align256((size_t)T * c->hidden * 4);                    // shared out
+    n += k2_align256(moe_dense_part_bytes(c, T));                   // matrix-core partials
     n += moe_ws_layout(T, c->top_k, c->inter, c->latent, nullptr, nullptr);
     return n;
 }
@@ -534,35 +567,35 @@ extern "C" int k2_moe_layer(const k2_moe_layer_weights *w, const float *x, int T
     float *sgu = (float *)take((size_t)T * 2 * c->inter * 4);
     float *sact = (float *)take((size_t)T * c->inter * 4);
     float *sout = (float *)take((size_t)T * c->hidden * 4);
+    float *part = (float *)take(moe_dense_part_bytes(c, T));
     void *ews = p;
 
     // router on the hidden input
-    if ((rc = gemv_rows_bf16(w->w_router, x, logits, c->n_experts, c->hidden, T, st))) return rc;
+    if ((rc = dense_rows_bf16(w->w_router, x, logits, c->n_experts, c->hidden, T, DM_EPI_PLAIN, part,
+                              nullptr, st)))
+        return rc;
     hipLaunchKernelGGL(moe_route_kernel, dim3(T), dim3(K2_BLOCK), 0, st, logits, w->router_bias,
                        c->n_experts, c->top_k, c->routed_scale, tidx, tw);
     K2_CHECK_LAUNCH();
     // latent: z = RMSNorm(W_dn x)
-    if ((rc = gemv_rows_bf16(w->w_down, x, z, c->latent, c->hidden, T, st))) return rc;
+    if ((rc = dense_rows_bf16(w->w_down, x, z, c->latent, c->hidden, T, DM_EPI_PLAIN, part, nullptr, st)))
+        return rc;
     if ((rc = k2_rmsnorm_grouped(z, w->latent_gamma, z, T, c->latent, 1, c->eps, stream))) return rc;
     // routed experts
     if ((rc = moe_expert_launch(z, T, c->latent, c->inter, tidx, tw, c->top_k, c->n_experts, w->w13q,
                                 w->w13s, w->w2q, w->w2s, r, d_err, ews, st)))
         return rc;
     // y = W_up r
-    if ((rc = gemv_rows_bf16(w->w_up, r, y, c->hidden, c->latent, T, st))) return rc;
-    // shared experts on the hidden input
+    if ((rc = dense_rows_bf16(w->w_up, r, y, c->hidden, c->latent, T, DM_EPI_PLAIN, part, nullptr, st)))
+        return rc;
+    // shared experts on the hidden input, added into y
     for (int s = 0; s < c->n_shared; ++s) {
         const uint16_t *w13 = w->sh_w13 + (int64_t)s * 2 * c->inter * c->hidden;
         const uint16_t *w2 = w->sh_w2 + (int64_t)s * c->hidden * c->inter;
-        if ((rc = gemv_rows_bf16(w13, x, sgu, 2 * c->inter, c->hidden, T, st))) return rc;
-        hipLaunchKernelGGL(swiglu_rows_kernel, dim3((c->inter + 255) / 256, T), dim3(256), 0, st,
-                           sgu, c->inter, sact);
-        K2_CHECK_LAUNCH();
-        if ((rc = gemv_rows_bf16(w2, sact, sout, c->hidden, c->inter, T, st))) return rc;
-        const int64_t n = (int64_t)T * c->hidden;
-        hipLaunchKernelGGL(add_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, y,
-                           sout, n);
-        K2_CHECK_LAUNCH();
+        if ((rc = dense_rows_bf16(w13, x, sact, 2 * c->inter, c->hidden, T, DM_EPI_SWIGLU, part, sgu, st)))
+            return rc;
+        if ((rc = dense_rows_bf16(w2, sact, y, c->hidden, c->inter, T, DM_EPI_ADD, part, sout, st)))
+            return rc;
     }
     if (topk_idx_out) {
         if (hipMemcpyAsync(topk_idx_out, tidx, (size_t)T * c->top_k * 4, hipMemcpyDeviceToDevice, st))
