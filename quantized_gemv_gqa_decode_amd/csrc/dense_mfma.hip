@@ -12,9 +12,6 @@
 //     its slice of the activations once in LDS as the two bf16 planes, each
 //     wave streams 4 row tiles of 16 rows from HBM, one 128-column chunk
 //     ahead of the MFMAs;
-//   * the k order inside a chunk is permuted so that every lane reads 64
-//     contiguous bytes of its row (the sum over k does not depend on the
-//     order as long as both operands use the same one);
 //   * per-split partials [split][token][row] are summed in split order by a
 //     second kernel, which also applies the epilogue (plain, add into y, or
 //     SwiGLU of row pairs i, i + N/2).
@@ -68,16 +65,17 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
         const int r0 = blockIdx.x * DM_ROWS + (wave * DM_RT + rt) * 16;
         rok[rt] = r0 < a.N;
         const int row = (rok[rt] ? r0 : a.N - 16) + c16;
-        rowoff[rt] = (int64_t)row * a.K + k0 + q * 32;
+        rowoff[rt] = (int64_t)row * a.K + k0 + q * 8;
     }
     const dm_bf16x8 *Wv = reinterpret_cast<const dm_bf16x8 *>(a.W);
-    // chunk c of tile rt, k-step j: the 16 B at element rowoff + c*128 + 8j
+    // chunk c of tile rt, k-step j: the 16 B at element rowoff + c*128 + 32j
+    // (the 4 lanes of a row read 64 contiguous bytes per instruction)
     auto load_chunk = [&](int c, dm_bf16x8 (&w)[DM_RT][4]) {
 #pragma unroll
         for (int rt = 0; rt < DM_RT; ++rt)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                w[rt][j] = __builtin_nontemporal_load(Wv + (rowoff[rt] + c * DM_KC + 8 * j) / 8);
+                w[rt][j] = __builtin_nontemporal_load(Wv + (rowoff[rt] + c * DM_KC + 32 * j) / 8);
     };
     dm_bf16x8 wc[DM_RT][4];
     load_chunk(0, wc);                            // weights first: their latency covers the staging
@@ -117,7 +115,7 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
     auto compute = [&](int c, const dm_bf16x8 (&w)[DM_RT][4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int kk = c * DM_KC + q * 32 + 8 * j;
+            const int kk = c * DM_KC + 32 * j + q * 8;
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
                 const int t = tt * 16 + c16;

@@ -63,39 +63,73 @@ static size_t moe_ws_layout(int T, int top_k, int inter, int latent, MoeWs *w, v
 // sigma + bias in descending order, the lower index first on equal scores
 // (top_k rounds of a block argmax); gates renormalised over the selected
 // sigma and scaled by routed_scale.
-__global__ __launch_bounds__(K2_BLOCK) void moe_route_kernel(const float *logits, const float *bias,
-                                                             int n_experts, int top_k,
-                                                             float routed_scale, int32_t *topk_idx,
-                                                             float *topk_w)
+// (value, index) first maximum across the wave, in every lane: DPP inside
+// rows, then lane swaps across rows and halves (VALU only; the order in
+// which pairs meet does not matter for a maximum with an index tie-break).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true); }
+__device__ __forceinline__ void argmax_wave_valu(float &v, int &i)
 {
-    __shared__ float sig[MOE_MAX_EXPERTS], score[MOE_MAX_EXPERTS];
-    __shared__ int sel[32];
-    const int t = blockIdx.x;
-    for (int e = threadIdx.x; e < n_experts; e += K2_BLOCK) {
-        const float l = logits[(int64_t)t * n_experts + e];
-        const float s = 1.0f / (1.0f + expf(-l));
-        sig[e] = s;
-        score[e] = s + (bias ? bias[e] : 0.f);
+    argmax_pair_max(v, i, dpp<0xB1>(v), dpp_i<0xB1>(i));     // quad_perm [1,0,3,2]
+    argmax_pair_max(v, i, dpp<0x4E>(v), dpp_i<0x4E>(i));     // quad_perm [2,3,0,1]
+    argmax_pair_max(v, i, dpp<0x141>(v), dpp_i<0x141>(i));   // row_half_mirror
+    argmax_pair_max(v, i, dpp<0x140>(v), dpp_i<0x140>(i));   // row_mirror
+    auto r16v = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    auto r16i = __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false);
+    v = __uint_as_float(r16v[0]); i = (int)r16i[0];
+    argmax_pair_max(v, i, __uint_as_float(r16v[1]), (int)r16i[1]);
+    auto r32v = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    auto r32i = __builtin_amdgcn_permlane32_swap((unsigned)i, (unsigned)i, false, false);
+    v = __uint_as_float(r32v[0]); i = (int)r32i[0];
+    argmax_pair_max(v, i, __uint_as_float(r32v[1]), (int)r32i[1]);
+}
+
+__global__ __launch_bounds__(K2_WAVE) void moe_route_kernel(const float *logits, const float *bias,
+                                                            int n_experts, int top_k,
+                                                            float routed_scale, int32_t *topk_idx,
+                                                            float *topk_w)
+{
+    // one wave per token: lane l keeps experts l, l + 64, ... in registers;
+    // every round is a lane-local first maximum plus a wave (value, index)
+    // reduction, with no barriers
+    constexpr int RPL = MOE_MAX_EXPERTS / K2_WAVE;
+    __shared__ float sel_sig[32];
+    const int t = blockIdx.x, lane = threadIdx.x;
+    float sc[RPL], sg[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        const int e = lane + K2_WAVE * i;
+        sc[i] = -INFINITY;
+        sg[i] = 0.f;
+        if (e < n_experts) {
+            const float l = logits[(int64_t)t * n_experts + e];
+            sg[i] = 1.0f / (1.0f + expf(-l));
+            sc[i] = sg[i] + (bias ? bias[e] : 0.f);
+        }
     }
-    __syncthreads();
     for (int j = 0; j < top_k; ++j) {
         float bv = -INFINITY;
         int bi = 0x7FFFFFFF;
-        for (int e = threadIdx.x; e < n_experts; e += K2_BLOCK) argmax_pair_max(bv, bi, score[e], e);
-        argmax_block(bv, bi);                      // ends with a block barrier
-        if (threadIdx.x == 0) {
-            sel[j] = bi;
-            score[bi] = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)               // increasing expert id: ties keep the lower
+            if (sc[i] > bv) { bv = sc[i]; bi = lane + K2_WAVE * i; }
+        argmax_wave_valu(bv, bi);                   // the same (value, index) in every lane
+        bi = __builtin_amdgcn_readfirstlane(bi);
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+            if (lane + K2_WAVE * i == bi) { s = sg[i]; sc[i] = -INFINITY; }
+        s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), bi % K2_WAVE));
+        if (lane == 0) {
+            topk_idx[(int64_t)t * top_k + j] = bi;
+            sel_sig[j] = s;
         }
-        __syncthreads();
     }
-    if (threadIdx.x == 0) {
+    __syncthreads();
+    if (lane == 0) {
         float tot = 0.f;
-        for (int j = 0; j < top_k; ++j) tot += sig[sel[j]];
-        for (int j = 0; j < top_k; ++j) {
-            topk_idx[(int64_t)t * top_k + j] = sel[j];
-            topk_w[(int64_t)t * top_k + j] = routed_scale * sig[sel[j]] / tot;
-        }
+        for (int j = 0; j < top_k; ++j) tot += sel_sig[j];
+        for (int j = 0; j < top_k; ++j) topk_w[(int64_t)t * top_k + j] = routed_scale * sel_sig[j] / tot;
     }
 }
 
@@ -110,10 +144,13 @@ __global__ __launch_bounds__(1024) void moe_bucket_kernel(const int32_t *topk_id
                                                           int32_t *d_err)
 {
     constexpr int BAD = 0x7FFFFFFF;
-    __shared__ int ex[MOE_MAX_PAIRS];
-    __shared__ int groups[MOE_MAX_PAIRS];     // items of the expert at its first pair, else 0
+    __shared__ int4 ex4[MOE_MAX_PAIRS / 4];
+    __shared__ int4 groups4[MOE_MAX_PAIRS / 4];   // items of the expert at its first pair, else 0
     __shared__ int n_items;
+    int *ex = reinterpret_cast<int *>(ex4);
+    int *groups = reinterpret_cast<int *>(groups4);
     const int p = threadIdx.x;
+    const int P4 = (P + 3) / 4;                   // scans read 4 pairs at a time; the pad is BAD
     if (p == 0) n_items = 0;
     int e = BAD;
     if (p < P) {
@@ -122,17 +159,23 @@ __global__ __launch_bounds__(1024) void moe_bucket_kernel(const int32_t *topk_id
             if (d_err) *d_err = K2_ERANGE;
             e = BAD;
         }
+    }
+    if (p < 4 * P4) {
         ex[p] = e;
+        groups[p] = 0;
     }
     __syncthreads();
     int idx = 0, same = 0, g = 0;
     if (p < P) {
         int less = 0, before = 0;
-        for (int q = 0; q < P; ++q) {
-            const int f = ex[q];
-            less += f < e;
-            same += f == e;
-            before += (q < p) & (f == e);
+#pragma unroll 8
+        for (int q4 = 0; q4 < P4; ++q4) {
+            const int4 f = ex4[q4];
+            const int q = 4 * q4;
+            less += (f.x < e) + (f.y < e) + (f.z < e) + (f.w < e);
+            same += (f.x == e) + (f.y == e) + (f.z == e) + (f.w == e);
+            before += ((q < p) & (f.x == e)) + ((q + 1 < p) & (f.y == e)) + ((q + 2 < p) & (f.z == e)) +
+                      ((q + 3 < p) & (f.w == e));
         }
         idx = less + before;
         g = (before == 0 && e != BAD) ? (same + TB - 1) / TB : 0;
@@ -143,7 +186,11 @@ __global__ __launch_bounds__(1024) void moe_bucket_kernel(const int32_t *topk_id
     __syncthreads();
     if (g > 0) {
         int base = 0;
-        for (int q = 0; q < P; ++q) base += (ex[q] < e) ? groups[q] : 0;
+#pragma unroll 8
+        for (int q4 = 0; q4 < P4; ++q4) {
+            const int4 f = ex4[q4], gr = groups4[q4];
+            base += (f.x < e ? gr.x : 0) + (f.y < e ? gr.y : 0) + (f.z < e ? gr.z : 0) + (f.w < e ? gr.w : 0);
+        }
         for (int i = 0; i < g; ++i) {
             const int left = same - i * TB;
             w.item_e[base + i] = e;
@@ -493,7 +540,7 @@ extern "C" int k2_moe_route(const uint16_t *Wr, const float *bias, const float *
     float *logits = (float *)ws;
     const int rc = gemv_rows_bf16(Wr, x, logits, n_experts, hidden, T, st);
     if (rc) return rc;
-    hipLaunchKernelGGL(moe_route_kernel, dim3(T), dim3(K2_BLOCK), 0, st, logits, bias, n_experts,
+    hipLaunchKernelGGL(moe_route_kernel, dim3(T), dim3(K2_WAVE), 0, st, logits, bias, n_experts,
                        top_k, routed_scale, topk_idx, topk_w);
     K2_CHECK_LAUNCH();
     return K2_OK;
@@ -574,7 +621,7 @@ extern "C" int k2_moe_layer(const k2_moe_layer_weights *w, const float *x, int T
     if ((rc = dense_rows_bf16(w->w_router, x, logits, c->n_experts, c->hidden, T, DM_EPI_PLAIN, part,
                               nullptr, st)))
         return rc;
-    hipLaunchKernelGGL(moe_route_kernel, dim3(T), dim3(K2_BLOCK), 0, st, logits, w->router_bias,
+    hipLaunchKernelGGL(moe_route_kernel, dim3(T), dim3(K2_WAVE), 0, st, logits, w->router_bias,
                        c->n_experts, c->top_k, c->routed_scale, tidx, tw);
     K2_CHECK_LAUNCH();
     // latent: z = RMSNorm(W_dn x)
