@@ -46,5 +46,13 @@ def near_tie_ok(gpu_tok: int, ref_logits: np.ndarray, gap: float = 1e-3) -> bool
     return best - float(ref_logits[gpu_tok]) < gap
 
 
+def tie_gap(err: float) -> float:
+    """Near-tie width for a position whose logits differ from the oracle's by
+    at most `err` (max-abs): the GPU can pick token t over the oracle's best b
+    only if logit_b - logit_t <= e_t + e_b <= 2 err, so an oracle gap within
+    2 err is beyond what the fp32 arithmetic resolves (floor 1e-3)."""
+    return max(1e-3, 2.0 * err)
+
+
 def say(msg: str):
     print(msg, flush=True)

@@ -1,10 +1,11 @@
 """End-to-end GPU parity of k2_decode_step against the CPU oracle.
 
-Greedy tokens must match the oracle at every position (a position where the
-oracle's two best logits are closer than 1e-3 is a reported near-tie and
-either token is accepted); logits must be within max-abs 2e-2 for bf16/fp32
-weights with fp32/bf16 KV and 5e-2 with fp8/MXFP4 weights or int8 KV, after
-fp32 accumulation.  Runs are teacher-forced on the oracle's token stream (so
+Greedy tokens must match the oracle at every position, except at a reported
+near-tie: the oracle's gap between its best token and the GPU's is within
+twice the measured max-abs logit error of that position (floor 1e-3), where
+fp32 arithmetic cannot resolve the order.  Logits must be within max-abs
+2e-2 for bf16/fp32 weights with fp32/bf16 KV and 5e-2 with fp8/MXFP4 weights
+or int8 KV, after fp32 accumulation.  Runs are teacher-forced on the oracle's token stream (so
 a single near-tie cannot cascade) and free-running.
 """
 import numpy as np
@@ -13,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from helpers import DEV, GPU, near_tie_ok, say, to_host
+from helpers import DEV, GPU, near_tie_ok, say, tie_gap, to_host
 
 pytestmark = pytest.mark.gpu
 if GPU:
@@ -38,11 +39,13 @@ def run_parity(cfg, prompt, n_decode, free_running=True, n_layers=None):
     tol = tol_for(cfg)
     worst = 0.0
     ties = []
+    errs = []
     for i, (t, g, r) in enumerate(zip(toks, lgs, ref_lg)):
         err = float(np.abs(g.astype(np.float64) - r).max())
+        errs.append(err)
         worst = max(worst, err)
         assert err <= tol, (i, err)
-        assert near_tie_ok(t, r), (i, t, int(np.argmax(r)))
+        assert near_tie_ok(t, r, tie_gap(err)), (i, t, int(np.argmax(r)), err)
         if t != int(np.argmax(r)):
             ties.append(i)
     say(f"teacher-forced max|dlogit| = {worst:.3g} (tol {tol}); near-ties at {ties}")
@@ -51,7 +54,7 @@ def run_parity(cfg, prompt, n_decode, free_running=True, n_layers=None):
         toks2, _ = gm2.generate(prompt, n_decode, collect_logits=False)
         for i, (a, b) in enumerate(zip(toks2, ref_toks)):
             if a != b:
-                assert near_tie_ok(a, ref_lg[i]), (i, a, b)
+                assert near_tie_ok(a, ref_lg[i], tie_gap(errs[i])), (i, a, b)
                 say(f"free-running diverged at {i} on a reported near-tie")
                 break
     return worst
@@ -181,6 +184,6 @@ def test_k2h_int8_long_context(prefix):
         err = float(np.abs(g - rl).max())
         worst = max(worst, err)
         assert err <= 5e-2, (i, err)
-        assert near_tie_ok(int(nx.item()), rl)
+        assert near_tie_ok(int(nx.item()), rl, tie_gap(err)), (i, int(nx.item()), int(np.argmax(rl)), err)
         feed = rt                                    # teacher-forced on the oracle's token
     say(f"int8 history {prefix}: max|dlogit| = {worst:.3g}")
