@@ -33,15 +33,15 @@ PEAK_HBM_GBPS = 8000.0
 # HBM bytes per launch from two profiler counter runs (FETCH_SIZE, then
 # WRITE_SIZE; KiB per dispatch, averaged over every dispatch of the kernel in
 # a short decode run), scaled by what the same counters read for the copy
-# probe (--copy-probe 1024: 1 GiB read reads as 524303.4 KiB fetched, 1 GiB
+# probe (--copy-probe 1024: 1 GiB read reads as 524301.8 KiB fetched, 1 GiB
 # written as 1048576 KiB).  A reading holds only for the kernel sources it was
 # taken on: if their digest differs, the traffic is reported as null.
-FETCH_SCALE = 1073741824 / (524303.4 * 1024)
+FETCH_SCALE = 1073741824 / (524301.8 * 1024)
 WRITE_SCALE = 1073741824 / (1048576.0 * 1024)
 GEMV_BF16_SOURCES = ("k2_dev.h", "k2_internal.h", "gemv_impl.h", "gemv.hip", "gemv_bf16.hip")
 PMC_TRAFFIC = {
     "k2h-3.7b-bf16-kvbf16-ctx4096": {
-        "sources": GEMV_BF16_SOURCES, "digest": "682f5a1f58858d6c",
+        "sources": GEMV_BF16_SOURCES, "digest": "84e75d42212c7252",
         "kib": {"qkv_norm_gemv": (15489.5, 24.0), "o_gemv_residual": (10386.5, 20.0),
                 "gate_up_norm_gemv_swiglu": (51351.0, 40.0),
                 "down_gemv_residual": (25857.1, 20.0),
