@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libk2.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["gemv.hip", "gemv_f32.hip", "gemv_bf16.hip", "gemv_fp8.hip", "gemv_mxfp4.hip",
-           "attn.hip", "misc.hip", "decode.hip", "moe.hip", "dense_mfma.hip",
+           "attn.hip", "misc.hip", "decode.hip", "moe.hip", "dense_mfma.hip", "fused.hip",
            "step_f32.hip", "step_bf16.hip", "step_fp8.hip", "step_mxfp4.hip"]
 ARCH = "gfx950"
 

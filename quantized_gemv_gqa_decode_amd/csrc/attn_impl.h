@@ -505,10 +505,10 @@ __device__ __forceinline__ void attn_block(const AttnArgs &a, int g, int s, int 
 
 // ------------------------------------------------- streaming attention --
 // The same attention with K and V (and the int8 scales) streamed through
-// LDS by blocks of ATT_WPB waves: the block's positions are cut into tiles
+// LDS by blocks of C::WPB waves: the block's positions are cut into tiles
 // of TP positions (16 KiB of K and 16 KiB of V for head_dim 128); tiles are
 // copied from HBM straight into LDS with LDS-DMA loads (global_load_lds, 16
-// bytes per lane, no registers), ATT_STAGES tiles in flight, and the waves
+// bytes per lane, no registers), C::NST tiles in flight, and the waves
 // read them from LDS with the query heads held in registers.  A block keeps
 // up to 96 KiB in flight: long contexts become bandwidth-bound.
 
@@ -548,35 +548,70 @@ static __shared__ unsigned long long k2_attn_trs[12];
     } while (0)
 #endif
 
-constexpr int ATT_WPB = 8;                 // waves per streaming block
-constexpr int ATT_NT = ATT_WPB * K2_WAVE;  // threads per streaming block
-constexpr int ATT_STAGES = 3;              // tiles in flight
+// Block shape of the streaming attention: waves per block, tiles in flight,
+// bytes per K (or V) tile.  The stand-alone kernel uses 8 waves, 3 stages of
+// 16 KiB; the fused layer kernel (fused_impl.h) a leaner 4 waves, 2 stages
+// of 8 KiB, to share one LDS budget with its GEMV blocks.
+template <int WPB_, int NST_, int TILE_>
+struct StreamCfg {
+    static constexpr int WPB = WPB_, NT = WPB_ * K2_WAVE, NST = NST_, TILE = TILE_;
+};
+using StreamWide = StreamCfg<8, 3, 16384>;
+constexpr int ATT_NT = StreamWide::NT;     // threads per stand-alone attention block
 
-template <int KVDT, int HD>
+template <int KVDT, int HD, class C = StreamWide>
 struct StreamGeom {
     using T = typename KVT<KVDT>::T;
     static constexpr int EPC = KVT<KVDT>::EPC;
     static constexpr int LPP = HD / EPC;                       // lanes per position
     static constexpr int PPI = K2_WAVE / LPP;                  // positions per slot
     static constexpr int ROWB = HD * (int)sizeof(T);           // bytes per cache row
-    static constexpr int ROUND = ATT_WPB * PPI;                // positions of one slot of every wave
-    static constexpr int NSLOT = (16384 / (ROUND * ROWB)) > 1 ? 16384 / (ROUND * ROWB) : 1;
+    static constexpr int ROUND = C::WPB * PPI;                 // positions of one slot of every wave
+    static constexpr int NSLOT = (C::TILE / (ROUND * ROWB)) > 1 ? C::TILE / (ROUND * ROWB) : 1;
     static constexpr int TP = ROUND * NSLOT;                   // positions per tile
     static constexpr int TILEB = TP * ROWB;                    // bytes of one K (or V) tile
-    static constexpr int NI = TILEB / (16 * ATT_NT);           // 16-byte copies per thread per tile
+    static constexpr int NI = TILEB / (16 * C::NT);            // 16-byte copies per thread per tile
     static constexpr int SCF = KVDT == K2_I8 ? TP : 0;         // scale floats per tile (K or V)
-    static constexpr int NS = (2 * SCF + ATT_NT - 1) / ATT_NT; // 4-byte scale copies per thread
+    static constexpr int NS = (2 * SCF + C::NT - 1) / C::NT;   // 4-byte scale copies per thread
     static constexpr int NPT = 2 * NI + NS;                    // LDS-DMA instructions per tile
-    static constexpr int STAGE_F = 2 * TILEB / 4 + NS * ATT_NT;   // floats per stage
-    static_assert(NI >= 1 && NI * 16 * ATT_NT == TILEB, "tile copy shape");
+    static constexpr int STAGE_F = 2 * TILEB / 4 + NS * C::NT; // floats per stage
+    static_assert(NI >= 1 && NI * 16 * C::NT == TILEB, "tile copy shape");
 };
 
-template <int KVDT, int HD, int REP>
+template <int KVDT, int HD, int REP, class C = StreamWide>
 __host__ __device__ constexpr int attn_stream_lds_floats()
 {
     // stages (reused for the wave merge afterwards), q, new k/v, merge (m, l)
-    return ATT_STAGES * StreamGeom<KVDT, HD>::STAGE_F + REP * HD + 2 * HD + ATT_WPB * REP * 2 +
-           ATT_WPB;
+    return C::NST * StreamGeom<KVDT, HD, C>::STAGE_F + REP * HD + 2 * HD + C::WPB * REP * 2 + C::WPB;
+}
+
+// Bounded wait until *p >= need (device scope; thread 0 polls, the block
+// then meets at a barrier).  Returns false, after reporting K2_EHIP in
+// d_err, if the count never arrives: every caller then still runs to its end,
+// so the grid always drains.
+constexpr int K2_WAIT_SPIN_LIMIT = 1 << 20;
+#ifndef K2_WAIT_SLEEP
+#define K2_WAIT_SLEEP 1
+#endif
+__device__ __forceinline__ unsigned coh_load_u(const unsigned *p)
+{
+    return __hip_atomic_load(const_cast<unsigned *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool block_wait_count(const unsigned *p, unsigned need, int32_t *d_err)
+{
+    __shared__ int ok_s;
+    if (threadIdx.x == 0) {
+        int spins = 0;
+        unsigned v = coh_load_u(p);
+        while (v < need && ++spins < K2_WAIT_SPIN_LIMIT) {
+            __builtin_amdgcn_s_sleep(K2_WAIT_SLEEP);
+            v = coh_load_u(p);
+        }
+        ok_s = v >= need;
+        if (v < need && d_err) coh_store_i(d_err, K2_EHIP);
+    }
+    __syncthreads();
+    return ok_s != 0;
 }
 
 // The new position's cache element is returned in kv_bits / kv_scale (see
@@ -584,14 +619,23 @@ __host__ __device__ constexpr int attn_stream_lds_floats()
 // so that no wait inside the block (a barrier, or the wait the compiler
 // places before LDS writes that could race an LDS-DMA) waits for its
 // store.  Returns whether this block holds the new position.
-template <int KVDT, int HD, int REP, bool FUSED, bool COH>
+struct NoWait {
+    __device__ void operator()() const {}
+};
+
+// QSYNC (fused layer kernel): q, k and v are written by other blocks of the
+// same launch; the block first issues its tile copies, then calls
+// wait_qkv() (every thread; it returns once they are stored), then reads
+// q/k/v at device scope.
+template <int KVDT, int HD, int REP, bool FUSED, bool COH, class C = StreamWide, bool QSYNC = false,
+          class W = NoWait>
 __device__ __forceinline__ bool attn_stream_block(const AttnArgs &a, int g, int s, int S, float *smem,
-                                                  uint32_t &kv_bits, float &kv_scale)
+                                                  uint32_t &kv_bits, float &kv_scale, W wait_qkv = W())
 {
-    using G = StreamGeom<KVDT, HD>;
+    using G = StreamGeom<KVDT, HD, C>;
     using T = typename G::T;
     constexpr int EPC = G::EPC, LPP = G::LPP, PPI = G::PPI, TP = G::TP, NSLOT = G::NSLOT;
-    constexpr int WPB = ATT_WPB, NT = ATT_NT, NST = ATT_STAGES;
+    constexpr int WPB = C::WPB, NT = C::NT, NST = C::NST;
     static_assert(WPB * REP * HD <= NST * G::STAGE_F, "wave merge fits the stages");
 
     float *const stages = smem;
@@ -616,41 +660,45 @@ __device__ __forceinline__ bool attn_stream_block(const AttnArgs &a, int g, int 
     const float *vsb = KVDT == K2_I8 ? a.vs + (int64_t)g * a.cap : nullptr;
     K2_ATRACE(0);
 
-    // q (and the new k, v) are loaded first, so that waiting for them never
-    // waits for the tile copies issued after them
+    // q (and the new k, v): loaded first, so that waiting for them never
+    // waits for the tile copies issued after them -- except under QSYNC,
+    // where they exist only once the QKV blocks of this launch have counted
     constexpr int QV = (REP * HD + NT - 1) / NT;
     constexpr int HALF = HD / 2;
     float qx0[QV], qx1[QV], qc[QV], qsn[QV];
-#pragma unroll
-    for (int v = 0; v < QV; ++v) {
-        const int t = tid + v * NT;
-        const int tt = t < REP * HD ? t : 0;
-        const int hl = tt / HD, d = tt % HD, h = g * REP + hl;
-        if constexpr (FUSED) {
-            const float *u = a.qkv + (int64_t)h * HD;
-            qx0[v] = u[d % HALF];
-            qx1[v] = u[d % HALF + HALF];
-            qc[v] = a.cos_sin[((int64_t)a.pos * HALF + d % HALF) * 2];
-            qsn[v] = a.cos_sin[((int64_t)a.pos * HALF + d % HALF) * 2 + 1];
-        } else {
-            qx0[v] = a.q[(int64_t)h * HD + d];
-            qx1[v] = qc[v] = qsn[v] = 0.f;
-        }
-    }
     float nk0 = 0.f, nk1 = 0.f, kc0 = 0.f, ks0 = 0.f;
-    if constexpr (FUSED) {
-        if (holds_new) {
-            if (tid < HD) {
-                const float *u = a.qkv + (int64_t)(a.n_qh + g) * HD;
-                nk0 = u[tid % HALF];
-                nk1 = u[tid % HALF + HALF];
-                kc0 = a.cos_sin[((int64_t)a.pos * HALF + tid % HALF) * 2];
-                ks0 = a.cos_sin[((int64_t)a.pos * HALF + tid % HALF) * 2 + 1];
-            } else if (tid < 2 * HD) {
-                nk0 = a.qkv[(int64_t)(a.n_qh + a.n_kv + g) * HD + (tid - HD)];
+    auto load_qkv = [&]() {
+#pragma unroll
+        for (int v = 0; v < QV; ++v) {
+            const int t = tid + v * NT;
+            const int tt = t < REP * HD ? t : 0;
+            const int hl = tt / HD, d = tt % HD, h = g * REP + hl;
+            if constexpr (FUSED) {
+                const float *u = a.qkv + (int64_t)h * HD;
+                qx0[v] = ld1<QSYNC>(u + d % HALF);
+                qx1[v] = ld1<QSYNC>(u + d % HALF + HALF);
+                qc[v] = a.cos_sin[((int64_t)a.pos * HALF + d % HALF) * 2];
+                qsn[v] = a.cos_sin[((int64_t)a.pos * HALF + d % HALF) * 2 + 1];
+            } else {
+                qx0[v] = a.q[(int64_t)h * HD + d];
+                qx1[v] = qc[v] = qsn[v] = 0.f;
             }
         }
-    }
+        if constexpr (FUSED) {
+            if (holds_new) {
+                if (tid < HD) {
+                    const float *u = a.qkv + (int64_t)(a.n_qh + g) * HD;
+                    nk0 = ld1<QSYNC>(u + tid % HALF);
+                    nk1 = ld1<QSYNC>(u + tid % HALF + HALF);
+                    kc0 = a.cos_sin[((int64_t)a.pos * HALF + tid % HALF) * 2];
+                    ks0 = a.cos_sin[((int64_t)a.pos * HALF + tid % HALF) * 2 + 1];
+                } else if (tid < 2 * HD) {
+                    nk0 = ld1<QSYNC>(a.qkv + (int64_t)(a.n_qh + a.n_kv + g) * HD + (tid - HD));
+                }
+            }
+        }
+    };
+    if constexpr (!QSYNC) load_qkv();
 
     // tile t -> stage t % NST: K rows, V rows, then the int8 scales
     auto issue_tile = [&](int t) {
@@ -682,6 +730,10 @@ __device__ __forceinline__ bool attn_stream_block(const AttnArgs &a, int g, int 
 #pragma unroll
     for (int t = 0; t < NST; ++t)
         if (t < n_tiles) issue_tile(t);
+    if constexpr (QSYNC) {
+        wait_qkv();
+        load_qkv();
+    }
 
     // 1. query heads of this kv head, rotated (fused) and pre-scaled
 #pragma unroll
@@ -1027,7 +1079,7 @@ __device__ __forceinline__ void attn_combine_block(const AttnArgs &a, int g, flo
 template <int KVDT, int HD, int REP, bool FUSED>
 __global__ __launch_bounds__(ATT_NT) void attn_kernel(const AttnArgs a)
 {
-    constexpr int NA = attn_stream_lds_floats<KVDT, HD, REP>(), NC = combine_lds_floats<REP, ATT_NT>();
+    constexpr int NA = attn_stream_lds_floats<KVDT, HD, REP, StreamWide>(), NC = combine_lds_floats<REP, ATT_NT>();
     extern __shared__ float4 lds4[];
     float *smem = reinterpret_cast<float *>(lds4);
     static_assert(NA >= NC, "combine fits the attention LDS");

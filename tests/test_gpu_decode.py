@@ -84,6 +84,25 @@ def test_tiny_decoder_persistent_n_kv1(monkeypatch):
     run_parity(cfg, synth.prompt(cfg), 8)
 
 
+# head_dim 128 with 4 query heads per kv head: the shape of the fused
+# QKV + attention + O layer kernel, small enough for a quick oracle
+HEAD128 = synth.TINY.replace(name="head128-small", hidden=512, n_qh=8, n_kv=2, head_dim=128,
+                             inter=1024, vocab=1024, cap=512, n_decode=4)
+
+
+@pytest.mark.parametrize("fused", ["1", "0"])
+@pytest.mark.parametrize("wdt,kvdt", [("bf16", "bf16"), ("bf16", "i8"), ("fp8", "i8"),
+                                      ("mxfp4", "i8"), ("f32", "f32")])
+@pytest.mark.parametrize("P", [20, 200])
+def test_head128_fused_layer_front(wdt, kvdt, P, fused, monkeypatch):
+    """QKV, attention and O as one dataflow launch (opt-in, K2_FUSED=1) and
+    as three launches (the default); 200 prompt positions give several
+    attention splits per kv head, 20 give one."""
+    monkeypatch.setenv("K2_FUSED", fused)
+    cfg = HEAD128.replace(wdt=wdt, kvdt=kvdt)
+    run_parity(cfg, synth.prompt(cfg, P), cfg.n_decode)
+
+
 @pytest.mark.parametrize("change", [dict(groups=1), dict(n_kv=4), dict(n_kv=1),
                                     dict(head_dim=32, n_qh=2, n_kv=1), dict(cap=20)])
 def test_tiny_decoder_shapes(change):
