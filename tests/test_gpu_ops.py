@@ -127,7 +127,9 @@ def _gemv_call(wdt, m, X, Y, R, N, K, B):
 @pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "mxfp4"])
 @pytest.mark.parametrize("N,K,B", [(1, 32, 1), (37, 96, 1), (131, 640, 1), (517, 2560, 1),
                                    (70, 4096, 1), (33, 10240, 1), (45, 320, 2), (19, 1024, 4),
-                                   (23, 1536, 8)])
+                                   (23, 1536, 8),
+                                   # rows split over 2 or 4 waves (long rows), ragged row counts
+                                   (2561, 10240, 1), (1001, 5632, 1), (3, 3072, 1)])
 def test_gemv_matches_oracle(wdt, N, K, B):
     say(f"gemv {wdt} N={N} K={K} B={B}")
     m, dense = _mat_and_dense(wdt, N, K, seed=N * 31 + K)
