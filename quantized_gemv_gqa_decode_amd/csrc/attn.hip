@@ -65,8 +65,7 @@ static int attn_go(const AttnArgs &a, hipStream_t st)
 {
     constexpr size_t lds = sizeof(float) * attn_stream_lds_floats<KVDT, HD, REP>();
     static_assert(lds <= 160 * 1024, "attention LDS per block");
-    hipLaunchKernelGGL((attn_kernel<KVDT, HD, REP, FUSED>), dim3(a.S, a.n_kv), dim3(ATT_NT), lds, st,
-                       a);
+    hipLaunchKernelGGL((attn_kernel<KVDT, HD, REP, FUSED>), dim3(a.S, a.n_kv), dim3(ATT_NT), lds, st, a);
     K2_CHECK_LAUNCH();
     return K2_OK;
 }

@@ -836,13 +836,14 @@ __device__ __forceinline__ bool attn_stream_block(const AttnArgs &a, int g, int 
 #pragma unroll
             for (int n = 1; n < NSLOT; ++n) mx = fmaxf(mx, sc[n][h]);
             mx = wave_max(mx);
-            const float mn = fmaxf(m[h], mx);
-            const float corr = (mn == -INFINITY) ? 1.0f : k2_exp2(m[h] - mn);
-            l[h] *= corr;
-            wsum[h] *= corr;
+            if (mx > m[h]) {                         // uniform: rescale only when the maximum moves
+                const float corr = k2_exp2(m[h] - mx);   // m = -inf gives 0
+                l[h] *= corr;
+                wsum[h] *= corr;
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[h][e] *= corr;
-            m[h] = mn;
+                for (int e = 0; e < EPC; ++e) acc[h][e] *= corr;
+                m[h] = mx;
+            }
         }
 #pragma unroll
         for (int n = 0; n < NSLOT; ++n) {

@@ -270,7 +270,8 @@ def _dev_cache(oc):
 
 @pytest.mark.parametrize("kvdt", ["f32", "bf16", "i8"])
 @pytest.mark.parametrize("hd,n_qh,n_kv", [(128, 32, 8), (16, 4, 2), (128, 8, 8), (64, 16, 2)])
-@pytest.mark.parametrize("L", [1, 5, 33, 100, 777, 5000])
+@pytest.mark.parametrize("L", [1, 5, 33, 100, 777, 5000,
+                               16500, 20000])   # >= 512 positions per block: int8 matrix-core scores
 def test_gqa_decode_attn_matches_oracle(kvdt, hd, n_qh, n_kv, L):
     say(f"attn {kvdt} hd={hd} {n_qh}/{n_kv} L={L}")
     cap = max(L, 8) + 3
@@ -293,7 +294,7 @@ def test_gqa_decode_attn_matches_oracle(kvdt, hd, n_qh, n_kv, L):
 
 @pytest.mark.parametrize("kvdt", ["f32", "bf16", "i8"])
 @pytest.mark.parametrize("hd,n_qh,n_kv", [(128, 32, 8), (16, 4, 2)])
-@pytest.mark.parametrize("pos", [0, 31, 32, 700, 1024, 2000])
+@pytest.mark.parametrize("pos", [0, 31, 32, 700, 1024, 2000, 17000])
 def test_rope_append_attn_matches_oracle(kvdt, hd, n_qh, n_kv, pos):
     say(f"fused attn {kvdt} hd={hd} pos={pos}")
     cap = pos + 5
