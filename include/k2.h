@@ -203,6 +203,27 @@ int k2_rope_append_attn(k2_dtype kvdt, const float *qkv, const float *cos_sin, v
                         int head_dim, int cap, int pos, void *ws, size_t ws_bytes,
                         void *stream);
 
+/* k2_rope_append_attn followed by the O projection with its residual
+ * ([k2-burn] "Project layout": layer.rs, attention residual):
+ *   h[n] += sum_k Wo[n][k] * out[k],  n < hidden, k < n_qh * head_dim.
+ * wdt, Wo and Wo_s as for k2_gemv_q* / k2_gemv_f32 (Wo [hidden][n_qh*hd];
+ * Wo_s: fp32 row scales for K2_FP8E4M3, E8M0 bytes for K2_MXFP4, NULL
+ * otherwise).  out receives the attention output as in k2_rope_append_attn;
+ * h is read and written in place.  Where the shape has one (head_dim 128,
+ * 4 query heads per kv head, n_qh*hd <= 4096, and the attention and O grids
+ * fit the device at once) this is ONE launch whose O blocks stream their
+ * weights while the attention runs; otherwise the attention kernel and the
+ * GEMV.  Either way h is bit-identical to k2_rope_append_attn followed by
+ * the GEMV.  d_err (device int32, nullable): set to K2_EHIP if a wait inside
+ * the launch times out (outputs then undefined).  Same workspace as
+ * k2_gqa_decode_attn; K2_EUNSUPPORTED unless n_qh*hd % 32 == 0 and
+ * n_qh*hd <= 12288. */
+int k2_rope_append_attn_o(k2_dtype kvdt, const float *qkv, const float *cos_sin, void *kc,
+                          void *vc, float *ks, float *vs, float *out, int n_qh, int n_kv,
+                          int head_dim, int cap, int pos, k2_dtype wdt, const void *Wo,
+                          const void *Wo_s, float *h, int hidden, void *ws, size_t ws_bytes,
+                          int32_t *d_err, void *stream);
+
 /* First-maximum argmax of x[0..n) ([k3_run.c] argmax_()): out_idx[0] is the
  * lowest index holding the largest value.  ws: k2_argmax_workspace_bytes(n)
  * bytes, zero-filled before first use (left zeroed on exit); calls that share

@@ -1,6 +1,9 @@
 // attn.hip -- split-K GQA decode attention for gfx950, with the RoPE and
 // KV-cache append of the new position fused in: launchers and C ABI (the
 // device code is in attn_impl.h).
+#include <stdlib.h>
+#include <string.h>
+
 #include "attn_impl.h"
 
 namespace k2 {
@@ -45,7 +48,7 @@ size_t attn_ws_bytes(int n_qh, int n_kv, int hd, int cap)
     const size_t S = (size_t)attn_max_splits(n_kv, cap);
     const size_t rep = (size_t)(n_qh / n_kv);
     return k2_align256((size_t)n_kv * S * rep * hd * 4) + k2_align256((size_t)n_kv * S * rep * 2 * 4) +
-           k2_align256((size_t)n_kv * 4);
+           k2_align256((size_t)n_kv * 4) + k2_align256((size_t)AO_SYNC_WORDS * 4);
 }
 
 void attn_ws_carve(void *ws, int n_qh, int n_kv, int hd, int cap, AttnArgs &a)
@@ -58,6 +61,22 @@ void attn_ws_carve(void *ws, int n_qh, int n_kv, int hd, int cap, AttnArgs &a)
     a.part_ml = (float *)p;
     p += k2_align256((size_t)n_kv * S * rep * 2 * 4);
     a.head_cnt = (unsigned *)p;
+    p += k2_align256((size_t)n_kv * 4);
+    a.ao_sync = (unsigned *)p;
+}
+
+// Compute units of the current device (cached per device id).
+int device_cus()
+{
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
 }
 
 template <int KVDT, int HD, int REP, bool FUSED>
@@ -65,7 +84,15 @@ static int attn_go(const AttnArgs &a, hipStream_t st)
 {
     constexpr size_t lds = sizeof(float) * attn_stream_lds_floats<KVDT, HD, REP>();
     static_assert(lds <= 160 * 1024, "attention LDS per block");
-    hipLaunchKernelGGL((attn_kernel<KVDT, HD, REP, FUSED>), dim3(a.S, a.n_kv), dim3(ATT_NT), lds, st, a);
+    // Prefetch rows only fill compute units the attention blocks leave idle
+    // (one block per compute unit at this LDS size).
+    int rows = 0;
+    if (a.pf && a.pf_bytes >= 16) {
+        const int free_blocks = device_cus() - a.S * a.n_kv;
+        rows = free_blocks > 0 ? free_blocks / a.S : 0;
+    }
+    hipLaunchKernelGGL((attn_kernel<KVDT, HD, REP, FUSED>), dim3(a.S, a.n_kv + rows), dim3(ATT_NT), lds, st,
+                       a);
     K2_CHECK_LAUNCH();
     return K2_OK;
 }
@@ -245,6 +272,82 @@ extern "C" int k2_rope_append_attn(k2_dtype kvdt, const float *qkv, const float 
     a.scale = 1.0f / sqrtf((float)head_dim);
     a.S = attn_splits(n_kv, a.len, &a.chunk);
     return attn_launch(kvdt, head_dim, n_qh / n_kv, true, a, k2_stream(stream));
+}
+
+static bool env_off(const char *name)
+{
+    const char *e = getenv(name);
+    return e && strcmp(e, "0") == 0;
+}
+
+static int64_t weight_code_bytes(int wdt, int64_t N, int64_t K)
+{
+    switch (wdt) {
+    case K2_F32: return N * K * 4;
+    case K2_BF16: return N * K * 2;
+    case K2_FP8E4M3: return N * K;
+    default: return N * K / 2;
+    }
+}
+
+int k2::attn_then_o(int wdt, int kvdt, int hd, int rep, AttnArgs at, const GemvArgs &o, int32_t *d_err,
+                hipStream_t st)
+{
+    int rc;
+    if (!env_off("K2_ATTN_O")) {
+        rc = attn_o_launch(wdt, kvdt, hd, rep, at, o, d_err, st);
+        if (rc != K2_EUNSUPPORTED) return rc;
+    }
+    if (!env_off("K2_PREFETCH")) {
+        at.pf = o.W;
+        at.pf_bytes = weight_code_bytes(wdt, o.N, o.K);
+    }
+    if ((rc = attn_launch(kvdt, hd, rep, true, at, st))) return rc;
+    return gemv_dispatch(wdt, o, PRO_NONE, EPI_PLAIN, st);
+}
+
+extern "C" int k2_rope_append_attn_o(k2_dtype kvdt, const float *qkv, const float *cos_sin, void *kc,
+                                     void *vc, float *ks, float *vs, float *out, int n_qh, int n_kv,
+                                     int head_dim, int cap, int pos, k2_dtype wdt, const void *Wo,
+                                     const void *Wo_s, float *h, int hidden, void *ws, size_t ws_bytes,
+                                     int32_t *d_err, void *stream)
+{
+    int rc = attn_common_check(kvdt, kc, vc, ks, vs, out, n_qh, n_kv, head_dim, cap, ws, ws_bytes);
+    if (rc) return rc;
+    if (!k2_ptr_ok(qkv) || !k2_ptr_ok(cos_sin) || !k2_ptr_ok(Wo) || !k2_ptr_ok(h)) return K2_EINVAL;
+    if ((wdt == K2_FP8E4M3 || wdt == K2_MXFP4) && !k2_ptr_ok(Wo_s)) return K2_EINVAL;
+    if (hidden <= 0) return K2_EINVAL;
+    if (wdt != K2_F32 && wdt != K2_BF16 && wdt != K2_FP8E4M3 && wdt != K2_MXFP4) return K2_EUNSUPPORTED;
+    const int K = n_qh * head_dim;
+    if (K % 32 || K > K2_MAX_LDS_FLOATS) return K2_EUNSUPPORTED;
+    if (pos < 0 || pos >= cap) return K2_ERANGE;
+    AttnArgs a{};
+    attn_ws_carve(ws, n_qh, n_kv, head_dim, cap, a);
+    a.qkv = qkv;
+    a.cos_sin = cos_sin;
+    a.kc = kc;
+    a.vc = vc;
+    a.ks = ks;
+    a.vs = vs;
+    a.out = out;
+    a.n_qh = n_qh;
+    a.n_kv = n_kv;
+    a.cap = cap;
+    a.pos = pos;
+    a.len = pos + 1;
+    a.scale = 1.0f / sqrtf((float)head_dim);
+    a.S = attn_splits(n_kv, a.len, &a.chunk);
+    GemvArgs o{};
+    o.W = Wo;
+    o.Sf = (const float *)Wo_s;
+    o.S8 = (const uint8_t *)Wo_s;
+    o.x = out;
+    o.y = h;
+    o.residual = h;
+    o.N = hidden;
+    o.K = K;
+    o.B = 1;
+    return attn_then_o(wdt, kvdt, head_dim, n_qh / n_kv, a, o, d_err, k2_stream(stream));
 }
 
 #ifdef K2_ATTN_TRACE

@@ -1074,6 +1074,33 @@ __device__ __forceinline__ void attn_combine_block(const AttnArgs &a, int g, flo
     }
 }
 
+// Blocks with blockIdx.y >= n_kv read the weight range pf, split evenly over
+// them in 16-byte units, with plain loads (which allocate in the memory-side
+// cache), and exit.  They share no state with the attention blocks; the
+// kernel's duration bounds theirs.
+__device__ __forceinline__ void attn_prefetch_block(const AttnArgs &a)
+{
+    const int64_t nblk = (int64_t)gridDim.x * (gridDim.y - a.n_kv);
+    const int64_t b = (int64_t)(blockIdx.y - a.n_kv) * gridDim.x + blockIdx.x;
+    const int64_t units = a.pf_bytes >> 4;
+    const int64_t per = (units + nblk - 1) / nblk;
+    const int64_t lo = b * per, hi = lo + per < units ? lo + per : units;
+    const k2_u4 *p = reinterpret_cast<const k2_u4 *>(a.pf);
+    constexpr int D = 8;
+    uint32_t acc = 0u;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += (int64_t)D * blockDim.x) {
+        k2_u4 v[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int64_t j = i + (int64_t)d * blockDim.x;
+            v[d] = p[j < hi ? j : lo];                 // clamp: in-range, branch-free
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
+    }
+    asm volatile("" ::"v"(acc));                      // keep the loads
+}
+
 // One launch: every block attends over its split; with several splits the
 // last block of each kv head to finish (an arrival counter, reset by that
 // block) combines the partials of the head.  No block waits for another.
@@ -1085,6 +1112,10 @@ __global__ __launch_bounds__(ATT_NT) void attn_kernel(const AttnArgs a)
     float *smem = reinterpret_cast<float *>(lds4);
     static_assert(NA >= NC, "combine fits the attention LDS");
     __shared__ int last;
+    if ((int)blockIdx.y >= a.n_kv) {
+        attn_prefetch_block(a);
+        return;
+    }
     const int g = blockIdx.y, S = gridDim.x;
     K2_ATRACE_CLEAR();
     uint32_t kv_bits = 0u;

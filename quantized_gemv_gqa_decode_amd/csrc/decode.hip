@@ -381,7 +381,6 @@ static int decode_impl(const k2_model *m, int token, const int32_t *d_token, int
         at.vc = L->vc;
         at.ks = L->ks;
         at.vs = L->vs;
-        if ((rc = attn_launch(c->kvdt, hd, c->n_qh / c->n_kv, true, at, st))) return rc;
 
         GemvArgs o{};
         o.W = L->o;
@@ -393,7 +392,7 @@ static int decode_impl(const k2_model *m, int token, const int32_t *d_token, int
         o.N = H;
         o.K = c->n_qh * hd;
         o.B = 1;
-        if ((rc = gemv_dispatch(wdt, o, PRO_NONE, EPI_PLAIN, st))) return rc;
+        if ((rc = attn_then_o(wdt, c->kvdt, hd, c->n_qh / c->n_kv, at, o, d_err, st))) return rc;
         }
 
         GemvArgs gu{};

@@ -65,14 +65,43 @@ struct AttnArgs {
     float *part;               // [n_kv][S][rep][hd]
     float *part_ml;            // [n_kv][S][rep][2]
     unsigned *head_cnt;        // [n_kv] split arrivals (zero between calls)
+    unsigned *ao_sync;         // attention + O launch: AO_SYNC_WORDS (zero between calls)
     int n_qh, n_kv, cap, len, pos, chunk, S;
     float scale;
+    // Weight bytes of the phase that follows (optional): blocks of the
+    // launch beyond the attention grid read this range once so that it sits
+    // in the memory-side cache when the next GEMV streams it.  Read only;
+    // nothing is computed from it here.
+    const void *pf;
+    int64_t pf_bytes;
 };
 
 size_t attn_ws_bytes(int n_qh, int n_kv, int hd, int cap);
 int attn_splits(int n_kv, int len, int *chunk);
 int attn_splits_fine(int n_kv, int cap, int len, int *chunk);
 int attn_launch(int kvdt, int hd, int rep, bool fused, const AttnArgs &a, hipStream_t st);
+int device_cus();
+
+// Sync words of the attention + O launch (one 256-byte line each; the ready
+// flag is replicated so that the O blocks' polling spreads over channels).
+constexpr int AO_SYNC_HEADS = 0;           // kv heads whose output is stored
+constexpr int AO_SYNC_ODONE = 64;          // O blocks finished
+constexpr int AO_READY_COPIES = 16;
+constexpr int AO_SYNC_READY = 128;         // [copy * 64]: every head stored
+constexpr int AO_SYNC_WORDS = AO_SYNC_READY + AO_READY_COPIES * 64;
+
+// Attention followed by the O projection (+ residual) in one launch when
+// the shape has an instantiation and both grids fit on the chip at once;
+// K2_EUNSUPPORTED otherwise (nothing enqueued).
+int attn_o_launch(int wdt, int kvdt, int hd, int rep, const AttnArgs &at, const GemvArgs &o,
+                  int32_t *d_err, hipStream_t st);
+
+// Fused-form attention (at) and then the O GEMV + residual (o, B = 1): one
+// launch where attn_o_launch has one (unless K2_ATTN_O=0), else the two
+// kernels, the attention launch's idle compute units prefetching the O
+// weights (unless K2_PREFETCH=0).
+int attn_then_o(int wdt, int kvdt, int hd, int rep, AttnArgs at, const GemvArgs &o, int32_t *d_err,
+                hipStream_t st);
 void attn_ws_carve(void *ws, int n_qh, int n_kv, int hd, int cap, AttnArgs &a);
 
 // --------------------------------------------------------------- argmax --

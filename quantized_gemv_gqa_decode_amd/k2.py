@@ -71,6 +71,8 @@ SIGNATURES = {
                                 _sz, _vp]),
     "k2_rope_append_attn": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
                                  _sz, _vp]),
+    "k2_rope_append_attn_o": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                   _vp, _vp, _vp, _i, _vp, _sz, _vp, _vp]),
     "k2_argmax_workspace_bytes": (_sz, [_i]),
     "k2_argmax": (_i, [_vp, _i, _vp, _vp, _sz, _vp]),
     "k2_decode_workspace_bytes": (_sz, [_vp]),
@@ -209,6 +211,14 @@ def k2_rope_append_attn(kvdt, qkv, cos_sin, kc, vc, ks, vs, out, n_qh, n_kv, hea
     return load().k2_rope_append_attn(kvdt, ptr(qkv), ptr(cos_sin), ptr(kc), ptr(vc), ptr(ks),
                                       ptr(vs), ptr(out), n_qh, n_kv, head_dim, cap, pos, ptr(ws),
                                       ws_bytes, stream_handle(stream))
+
+
+def k2_rope_append_attn_o(kvdt, qkv, cos_sin, kc, vc, ks, vs, out, n_qh, n_kv, head_dim, cap, pos,
+                          wdt, Wo, Wo_s, h, hidden, ws, ws_bytes, d_err=None, stream=None):
+    return load().k2_rope_append_attn_o(kvdt, ptr(qkv), ptr(cos_sin), ptr(kc), ptr(vc), ptr(ks),
+                                        ptr(vs), ptr(out), n_qh, n_kv, head_dim, cap, pos, wdt,
+                                        ptr(Wo), ptr(Wo_s), ptr(h), hidden, ptr(ws), ws_bytes,
+                                        ptr(d_err), stream_handle(stream))
 
 
 def k2_argmax_workspace_bytes(n) -> int:

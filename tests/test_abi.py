@@ -95,6 +95,18 @@ def test_rope_append_attention_validation():
     assert L.k2_rope_append_attn(k2.K2_BF16, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 32, 8, 128,
                                  4096, 4096, ws, wsb, st) == k2.K2_ERANGE
     assert L.k2_argmax(FAKE, 100, FAKE, ws, 16, st) == k2.K2_EINVAL
+    # attention + O projection: refusals before any launch
+    ao = (FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 32, 8, 128, 4096)
+    assert L.k2_rope_append_attn_o(k2.K2_BF16, *ao, 4096, k2.K2_BF16, FAKE, None, FAKE, 2560,
+                                   ws, wsb, None, st) == k2.K2_ERANGE
+    assert L.k2_rope_append_attn_o(k2.K2_BF16, *ao, 0, k2.K2_FP8E4M3, FAKE, None, FAKE, 2560,
+                                   ws, wsb, None, st) == k2.K2_EINVAL       # fp8 needs row scales
+    assert L.k2_rope_append_attn_o(k2.K2_BF16, *ao, 0, k2.K2_I8, FAKE, None, FAKE, 2560,
+                                   ws, wsb, None, st) == k2.K2_EUNSUPPORTED  # not a weight format
+    assert L.k2_rope_append_attn_o(k2.K2_BF16, *ao, 0, k2.K2_BF16, FAKE, None, None, 2560,
+                                   ws, wsb, None, st) == k2.K2_EINVAL       # h missing
+    assert L.k2_rope_append_attn_o(k2.K2_BF16, *ao, 0, k2.K2_BF16, FAKE, None, FAKE, 0,
+                                   ws, wsb, None, st) == k2.K2_EINVAL
 
 
 def _fake_model(cfg_kw=None):

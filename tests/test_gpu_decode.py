@@ -103,6 +103,28 @@ def test_head128_fused_layer_front(wdt, kvdt, P, fused, monkeypatch):
     run_parity(cfg, synth.prompt(cfg, P), cfg.n_decode)
 
 
+@pytest.mark.parametrize("wdt,kvdt", [("bf16", "bf16"), ("bf16", "i8"), ("fp8", "i8"),
+                                      ("mxfp4", "i8"), ("f32", "f32"), ("f32", "bf16")])
+@pytest.mark.parametrize("P", [3, 200])
+def test_head128_attention_o_one_launch_bit_identical(wdt, kvdt, P, monkeypatch):
+    """Attention and the O projection as one launch (the default where both
+    grids fit on the chip) against the two-kernel form (K2_ATTN_O=0): the O
+    rows are summed in the same order, so every logit and token is the same
+    bit for bit.  3 prompt positions give one attention split per kv head,
+    200 give several (the combine runs before the heads are counted)."""
+    cfg = HEAD128.replace(wdt=wdt, kvdt=kvdt)
+    prompt = synth.prompt(cfg, P)
+    out = {}
+    for ao in ("1", "0"):
+        monkeypatch.setenv("K2_ATTN_O", ao)
+        gm = DecodeModel(cfg, DEV)
+        out[ao] = gm.generate(prompt, cfg.n_decode)
+    (t1, l1), (t0, l0) = out["1"], out["0"]
+    assert t1 == t0
+    for i, (a, b) in enumerate(zip(l1, l0)):
+        assert np.array_equal(a, b), (i, float(np.abs(a - b).max()))
+
+
 @pytest.mark.parametrize("change", [dict(groups=1), dict(n_kv=4), dict(n_kv=1),
                                     dict(head_dim=32, n_qh=2, n_kv=1), dict(cap=20)])
 def test_tiny_decoder_shapes(change):

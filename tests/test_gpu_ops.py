@@ -340,6 +340,73 @@ def test_rope_append_attn_matches_oracle(kvdt, hd, n_qh, n_kv, pos):
         assert np.array_equal(gv[:, pos], oc.v[:, pos])
 
 
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("kvdt", ["bf16", "i8"])
+@pytest.mark.parametrize("pos", [0, 200, 700, 3000])
+def test_rope_append_attn_o(wdt, kvdt, pos):
+    """Attention then the O projection + residual at the 3.7B head shape (32 q /
+    8 kv heads, hd 128, hidden 2560).  Up to ~770 positions it is one launch
+    (O blocks beside the attention blocks), beyond it the attention kernel and
+    the GEMV; either way out, h and the cache are bit-identical to
+    k2_rope_append_attn followed by the GEMV, and h matches the oracle
+    (fp64 attention, then the dequantized O matvec) within the attention's
+    error carried through |W_o| plus the fp32 summation bound."""
+    n_qh, n_kv, hd, H = 32, 8, 128, 2560
+    K = n_qh * hd
+    say(f"attn+O {wdt} {kvdt} pos={pos}")
+    cap = pos + 5
+    oc = _filled_cache(kvdt, n_kv, cap, hd, pos, seed=pos + 11)
+    rng = np.random.default_rng(pos + 1)
+    qkv = (rng.standard_normal((n_qh + 2 * n_kv) * hd) * 1.5).astype(np.float32)
+    h0 = rng.standard_normal(H).astype(np.float32)
+    m, dense = _mat_and_dense(wdt, H, K, seed=pos + 3)
+    cs = torch.empty((cap, hd // 2, 2), dtype=torch.float32, device=DEV)
+    check(k2.k2_rope_table(cs, cap, hd, 1e4))
+    ws_b = k2.k2_attn_workspace_bytes(n_qh, n_kv, hd, cap)
+    view = np.uint16 if kvdt == "bf16" else None
+    res = []
+    for one in (True, False):
+        kc, vc, ks, vs = _dev_cache(oc)
+        ws = torch.zeros(ws_b, dtype=torch.uint8, device=DEV)
+        out = torch.empty(K, dtype=torch.float32, device=DEV)
+        h = to_dev(h0)
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        for rep in range(2):                     # the second call reuses the workspace
+            if rep:
+                h.copy_(to_dev(h0))
+            if one:
+                check(k2.k2_rope_append_attn_o(k2.DTYPES[kvdt], to_dev(qkv), cs, kc, vc, ks, vs, out,
+                                               n_qh, n_kv, hd, cap, pos, k2.DTYPES[wdt], to_dev(m.w),
+                                               None if m.s is None else to_dev(m.s), h, H, ws, ws_b,
+                                               err))
+            else:
+                check(k2.k2_rope_append_attn(k2.DTYPES[kvdt], to_dev(qkv), cs, kc, vc, ks, vs, out,
+                                             n_qh, n_kv, hd, cap, pos, ws, ws_b))
+                check(_gemv_call(wdt, m, out, h, h, H, K, 1))
+        sync()
+        assert int(err.item()) == 0
+        # the workspace ends with the split counters ([n_kv] words, one
+        # 256-byte line) and the one-launch sync words (1152 words): both are
+        # left zeroed for the next call
+        assert not torch.any(ws[-(256 + 4608):] != 0), "counters left zeroed"
+        res.append((to_host(out), to_host(h), to_host(kc, view), to_host(vc, view), to_host(ks),
+                    to_host(vs)))
+    for a, b in zip(res[0], res[1]):
+        assert np.array_equal(a, b)
+    q = oracle.rope(qkv[:K].astype(np.float64), n_qh, hd, pos, 1e4)
+    k = oracle.rope(qkv[K:K + n_kv * hd].astype(np.float64), n_kv, hd, pos, 1e4)
+    v = qkv[K + n_kv * hd:].astype(np.float64)
+    oc.store(k, v, pos)
+    att = oracle.attention(q, oc, n_qh, pos + 1)
+    href = h0.astype(np.float64) + m.matvec(att)
+    vmax = np.abs(oc.dequant("v", pos + 1)).max()
+    step = (np.abs(v).max() / 127) if kvdt == "i8" else 0.0
+    att_tol = 5e-5 * vmax + 2 * step + 1e-5
+    bound = np.abs(dense) @ np.full(K, att_tol) + sumabs_bound(dense, att) + 1e-5
+    got = res[0][1].astype(np.float64)
+    assert np.all(np.abs(got - href) <= bound), float(np.abs(got - href).max())
+
+
 # ------------------------------------------------------------------ argmax ---
 
 @pytest.mark.parametrize("n", [1, 7, 255, 256, 257, 250624])
