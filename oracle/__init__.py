@@ -24,8 +24,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "liboracle.so")
 _lib = None
 
-F32, BF16, FP8, MXFP4, I8 = 0, 1, 2, 3, 4
-DT = {"f32": F32, "bf16": BF16, "fp8": FP8, "mxfp4": MXFP4, "i8": I8}
+F32, BF16, FP8, MXFP4, I8, Q4S = 0, 1, 2, 3, 4, 5
+DT = {"f32": F32, "bf16": BF16, "fp8": FP8, "mxfp4": MXFP4, "i8": I8, "q4s": Q4S}
 
 _dp = C.POINTER(C.c_double)
 _vp = C.c_void_p
@@ -50,6 +50,9 @@ def lib():
             getattr(L, n).argtypes = [C.c_float]
         L.orc_quant_fp8_rows.argtypes = [_vp, C.c_int64, C.c_int64, _vp, _vp]
         L.orc_quant_mxfp4.argtypes = [_vp, C.c_int64, C.c_int64, _vp, _vp]
+        L.orc_quant_q4s.argtypes = [_vp, C.c_int64, C.c_int64, _vp, _vp]
+        L.orc_q4s_value.argtypes = [C.c_uint8]
+        L.orc_q4s_value.restype = C.c_double
         L.orc_kv_quant_int8.argtypes = [_vp, C.c_int, _vp, _vp]
         L.orc_int8_dequant.restype = C.c_double
         L.orc_int8_dequant.argtypes = [C.c_int8, C.c_float]
@@ -149,6 +152,25 @@ def quant_mxfp4(w_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return q, e
 
 
+def q4s_value(codes) -> np.ndarray:
+    """Signed value of Q4S nibbles (two's complement, [-8, 7])."""
+    L = lib()
+    a = np.asarray(codes, dtype=np.uint8)
+    return np.array([L.orc_q4s_value(int(c)) for c in a.ravel()], np.float64).reshape(a.shape)
+
+
+def quant_q4s(w_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Q4S: int4 codes on [-7, 7] packed two per byte (low nibble = even k)
+    and one fp32 scale per 64 consecutive k of a row."""
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    N, K = w.shape
+    assert K % 64 == 0
+    q = np.empty((N, K // 2), np.uint8)
+    s = np.empty((N, K // 64), np.float32)
+    lib().orc_quant_q4s(_p(w), N, K, _p(q), _p(s))
+    return q, s
+
+
 def kv_quant_int8(x) -> Tuple[np.ndarray, float]:
     a = np.ascontiguousarray(x, dtype=np.float32)
     codes = np.empty(a.shape, np.int8)
@@ -177,7 +199,7 @@ class Mat:
         self.s = None if s is None else np.ascontiguousarray(s)
         if shape is None:
             N = self.w.shape[0]
-            K = self.w.shape[1] * (2 if dtype == "mxfp4" else 1)
+            K = self.w.shape[1] * (2 if dtype in ("mxfp4", "q4s") else 1)
             shape = (N, K)
         self.shape = shape
         self.c = _Mat(DT[dtype], _p(self.w), _p(self.s))
@@ -196,6 +218,9 @@ class Mat:
         if wdt == "mxfp4":
             q, e = quant_mxfp4(draw)
             return Mat("mxfp4", q, e, draw.shape)
+        if wdt == "q4s":
+            q, sc = quant_q4s(draw)
+            return Mat("q4s", q, sc, draw.shape)
         raise ValueError(wdt)
 
     def matvec(self, x: np.ndarray) -> np.ndarray:

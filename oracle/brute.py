@@ -48,6 +48,12 @@ def dequant(dtype: str, w: np.ndarray, s: Optional[np.ndarray] = None) -> torch.
         vals = table[nib]
         sc = torch.from_numpy(np.asarray(s, np.uint8)).view(torch.float8_e8m0fnu).double()
         return vals * sc.repeat_interleave(32, dim=1)
+    if dtype == "q4s":
+        q = torch.from_numpy(np.asarray(w, np.uint8)).long()
+        nib = torch.stack([q & 15, q >> 4], dim=-1).reshape(q.shape[0], -1)   # even k = low nibble
+        vals = torch.where(nib >= 8, nib - 16, nib).double()                 # two's complement
+        sc = torch.from_numpy(np.asarray(s, np.float32)).double()
+        return vals * sc.repeat_interleave(64, dim=1)
     raise ValueError(dtype)
 
 

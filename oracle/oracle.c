@@ -35,7 +35,7 @@
 #define ORC_EXPORT __attribute__((visibility("default")))
 
 /* dtype tags used by the oracle's own structs */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2, ORC_MXFP4 = 3, ORC_I8 = 4 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2, ORC_MXFP4 = 3, ORC_I8 = 4, ORC_Q4S = 5 };
 
 /* ------------------------------------------------------------------------ */
 /* Storage codecs                                                            */
@@ -206,6 +206,52 @@ ORC_EXPORT void orc_quant_mxfp4(const uint16_t *w, int64_t N, int64_t K,
 }
 
 /*
+ * Q4S weights ([k2-burn] "Working end to end" and "Quantization": the
+ * quantizer writes int4 "Q4S" checkpoints, block size 64).  The pages name
+ * nothing more; reading taken: symmetric signed int4 on [-7, 7] (the S of
+ * Q4S; two's complement nibbles, -8 never produced) with one fp32 scale per
+ * 64 consecutive k of a row, built like the int8 KV codec:
+ *   a = max|w| over the block, s = fp32(a / 7),
+ *   code = clamp(rint(fp32(w / s)), -7, 7)   (ties to even),
+ *   a = 0 gives s = 0 and codes 0;  value = code * s.
+ * Packing: q[n][k/2], low nibble = even k, high nibble = odd k; s[n][k/64].
+ */
+ORC_EXPORT double orc_q4s_value(uint8_t nib)
+{
+    nib &= 15;
+    return (double)((nib & 8) ? (int)nib - 16 : (int)nib);
+}
+
+ORC_EXPORT void orc_quant_q4s(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s)
+{
+    const int64_t nb = K / 64;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t *blk = w + n * K + b * 64;
+            float amax = 0.0f;
+            for (int i = 0; i < 64; ++i) {
+                float a = fabsf(f32_from_bits((uint32_t)blk[i] << 16));
+                if (a > amax) amax = a;
+            }
+            volatile float sc = amax / 7.0f;
+            s[n * nb + b] = amax == 0.0f ? 0.0f : sc;
+            for (int i = 0; i < 64; i += 2) {
+                int c[2] = {0, 0};
+                for (int j = 0; j < 2 && amax != 0.0f; ++j) {
+                    volatile float t = f32_from_bits((uint32_t)blk[i + j] << 16) / sc;
+                    double r = nearbyint((double)t);
+                    if (r > 7) r = 7;
+                    if (r < -7) r = -7;
+                    c[j] = (int)r;
+                }
+                q[n * (K / 2) + b * 32 + i / 2] = (uint8_t)((c[0] & 15) | ((c[1] & 15) << 4));
+            }
+        }
+    }
+}
+
+/*
  * int8 KV-cache codec ([k2-burn] "KV cache storage": symmetric int8 with a
  * scale per head_dim block).  Reading taken: a = max|x| over the block,
  * s = fp32(a / 127), code = clamp(rint(fp32(x / s)), -127, 127) (ties to
@@ -245,7 +291,8 @@ ORC_EXPORT double orc_int8_dequant(int8_t code, float scale)
  *   F32:   w = float[N][K]
  *   BF16:  w = uint16[N][K]
  *   FP8:   w = uint8 codes [N][K], s = float row scale [N]
- *   MXFP4: w = uint8 [N][K/2] (low nibble even k), s = uint8 E8M0 [N][K/32] */
+ *   MXFP4: w = uint8 [N][K/2] (low nibble even k), s = uint8 E8M0 [N][K/32]
+ *   Q4S:   w = uint8 [N][K/2] (low nibble even k), s = float [N][K/64] */
 typedef struct {
     int dtype;
     const void *w;
@@ -278,6 +325,16 @@ static double row_dot(const orc_mat *m, int64_t n, int64_t K, const double *x)
             uint8_t byte = r[k / 2];
             uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 15);
             acc += orc_e2m1_value(nib) * orc_e8m0_value(sc[k / 32]) * x[k];
+        }
+        return acc;
+    }
+    case ORC_Q4S: {
+        const uint8_t *r = (const uint8_t *)m->w + n * (K / 2);
+        const float *sc = (const float *)m->s + n * (K / 64);
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t byte = r[k / 2];
+            uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 15);
+            acc += orc_q4s_value(nib) * (double)sc[k / 64] * x[k];
         }
         return acc;
     }

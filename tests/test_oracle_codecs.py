@@ -1,4 +1,4 @@
-"""Pins for the oracle's storage codecs (bf16, fp8 E4M3FN, E2M1, E8M0, int8 KV).
+"""Pins for the oracle's storage codecs (bf16, fp8 E4M3FN, E2M1, E8M0, Q4S int4, int8 KV).
 
 Each codec is checked against something other than its own formula: torch's
 independent dtype decoders, the published OCP E2M1 table, brute-force nearest
@@ -211,6 +211,65 @@ def test_mxfp4_expert_bytes_match_k3_page():
     assert round(92 * 896 * per_expert / 1e12, 2) == 1.45
     # embed + lm_head, 2 x 163840 x 7168 bf16 = the page's 4.70 GB
     assert round(2 * 163840 * 7168 * 2 / 1e9, 2) == 4.70
+
+
+# -------------------------------------------------------------------- Q4S ---
+
+def test_q4s_values_are_twos_complement_nibbles():
+    assert list(oracle.q4s_value(np.arange(16, dtype=np.uint8))) == \
+        [0, 1, 2, 3, 4, 5, 6, 7, -8, -7, -6, -5, -4, -3, -2, -1]
+
+
+def _q4s_nibbles(q):
+    n, half = q.shape
+    return np.stack([q & 15, q >> 4], -1).reshape(n, 2 * half)      # even k = low nibble
+
+
+def test_quant_q4s_hand_values():
+    # block max 7/16 makes s = a/7 = 1/16 exactly; codes are then w * 16 with
+    # ties to even (0.5 -> 0, 1.5 -> 2, 2.5 -> 2, 3.5 -> 4)
+    w = torch.zeros(2, 128, dtype=torch.bfloat16)
+    vals = [0.03125, 0.09375, 0.15625, -0.15625, 0.21875, 0.4375, -0.4375, 0.0625, -0.03125]
+    w[0, :len(vals)] = torch.tensor(vals)
+    w[0, 64] = 1.75                       # second block: a = 1.75, s = 0.25
+    w[0, 65] = -0.375                     # -1.5 steps -> -2
+    q, sc = oracle.quant_q4s(w.view(torch.int16).numpy().view(np.uint16))
+    assert q.shape == (2, 64) and sc.shape == (2, 2)
+    assert sc[0, 0] == 0.0625 and sc[0, 1] == 0.25
+    assert sc[1, 0] == 0.0 and sc[1, 1] == 0.0 and not q[1].any()     # all-zero blocks
+    codes = oracle.q4s_value(_q4s_nibbles(q))
+    assert list(codes[0, :len(vals)]) == [0, 2, 2, -2, 4, 7, -7, 1, 0]
+    assert list(codes[0, 64:66]) == [7, -2]
+    assert not codes[0, len(vals):64].any() and not codes[0, 66:].any()
+    assert q[0, 0] == (0 | (2 << 4)) and q[0, 1] == (2 | (0xE << 4))  # -2 is nibble 0xE, high
+
+
+def test_quant_q4s_properties():
+    bits, w = _bf16_draw(16, 256)
+    bits[5, 64:128] = 0
+    w[5, 64:128] = 0.0
+    q, sc = oracle.quant_q4s(bits)
+    nib = _q4s_nibbles(q)
+    assert not (nib == 8).any()                                      # -8 is never produced
+    codes = oracle.q4s_value(nib)
+    assert sc[5, 1] == 0.0 and not codes[5, 64:128].any()
+    levels = np.arange(-7, 8, dtype=np.float64)
+    for n in range(16):
+        for b in range(4):
+            blk = w[n, b * 64:(b + 1) * 64]
+            amax = np.abs(blk).max()
+            if amax == 0:
+                continue
+            s = float(sc[n, b])
+            assert s == float(np.float32(np.float32(amax) / np.float32(7)))
+            t = (blk.astype(np.float32) / np.float32(s)).astype(np.float64)
+            for i, tv in enumerate(t):                               # brute-force nearest level
+                d = np.abs(levels - tv)
+                best = levels[d == d.min()]
+                want = best[0] if len(best) == 1 else best[np.argmin(np.abs(best) % 2)]
+                assert codes[n, b * 64 + i] == want, (n, b, i, tv)
+            assert np.abs(codes[n, b * 64:(b + 1) * 64]).max() == 7
+            assert np.all(np.abs(codes[n, b * 64:(b + 1) * 64] * s - blk) <= s * 0.5 * (1 + 1e-6))
 
 
 # ----------------------------------------------------------------- int8 KV ---

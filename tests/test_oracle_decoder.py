@@ -33,7 +33,8 @@ def _incremental_vs_full(cfg, n_decode=None):
 
 
 @pytest.mark.parametrize("wdt,kvdt", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "i8"),
-                                      ("fp8", "i8"), ("mxfp4", "i8"), ("mxfp4", "bf16")])
+                                      ("fp8", "i8"), ("mxfp4", "i8"), ("mxfp4", "bf16"),
+                                      ("q4s", "i8")])
 def test_incremental_equals_full_recompute(wdt, kvdt):
     cfg = synth.TINY.replace(wdt=wdt, kvdt=kvdt)
     toks, lg, ref = _incremental_vs_full(cfg)

@@ -86,6 +86,19 @@ def test_matvec_equals_numpy_matmul_on_library_decoded_weights(wdt):
     assert got.shape == (N,)
 
 
+def test_matvec_q4s_equals_numpy_matmul_on_decoded_weights():
+    N, K = 37, 192
+    w32 = torch.randn(N, K, generator=torch.Generator().manual_seed(4)) * 0.02
+    bits = _bits(w32.to(torch.bfloat16))
+    m = oracle.Mat.from_draw("q4s", bits)
+    assert m.w.shape == (N, K // 2) and m.s.shape == (N, K // 64)
+    nib = np.stack([m.w & 15, m.w >> 4], -1).reshape(N, K).astype(np.int64)
+    dense = np.where(nib >= 8, nib - 16, nib) * np.repeat(m.s.astype(np.float64), 64, axis=1)
+    x = RNG.standard_normal(K)
+    got = m.matvec(x)
+    assert np.allclose(got, dense @ x, rtol=1e-12, atol=1e-15)
+
+
 def test_matvec_dequant_is_close_to_bf16_weights():
     # quantization error stays inside the formats' half-step bounds
     N, K = 64, 256
@@ -104,6 +117,9 @@ def test_matvec_dequant_is_close_to_bf16_weights():
         blk = np.abs(wd[:, (k // 32) * 32:(k // 32 + 1) * 32]).max(axis=1)
         # step 2 * 2^e at the top, 2^e <= amax / 4, saturation from [7, 8) to 6
         assert np.all(np.abs(y4 - wd[:, k]) <= blk * 0.5 + 1e-12)
+        yq = oracle.Mat.from_draw("q4s", bits).matvec(x)
+        b64 = np.abs(wd[:, (k // 64) * 64:(k // 64 + 1) * 64]).max(axis=1)
+        assert np.all(np.abs(yq - wd[:, k]) <= b64 / 7 * 0.5 * (1 + 1e-6) + 1e-12)
 
 
 # ------------------------------------------------------------------- RoPE ---
