@@ -146,6 +146,8 @@ def kernel_table(gm, stream, reps: int):
             return k2.k2_gemv_f32(w, x, y, y, N, K, 1)
         if cfg.wdt == "fp8":
             return k2.k2_gemv_qfp8(w, s, x, y, y, N, K, 1)
+        if cfg.wdt == "q4s":
+            return k2.k2_gemv_qq4s(w, s, x, y, y, N, K, 1)
         return k2.k2_gemv_qmxfp4(w, s, x, y, y, N, K, 1)
 
     n = reps * nl

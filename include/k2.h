@@ -70,7 +70,8 @@ typedef enum {
     K2_BF16 = 1,
     K2_FP8E4M3 = 2,
     K2_MXFP4 = 3,
-    K2_I8 = 4
+    K2_I8 = 4,
+    K2_Q4S = 5             /* int4 weights, one fp32 scale per 64 columns */
 } k2_dtype;
 
 int k2_abi_version(void);
@@ -98,6 +99,16 @@ int k2_quantize_fp8_rows(const uint16_t *W, uint8_t *codes, float *row_scale,
  *   code = E2M1 round-to-nearest-even, saturating at +-6, of W * 2^-e_b.
  * W: uint16 bf16 [N][K]; q: uint8 [N][K/2]; e8m0: uint8 [N][K/32].
  * K2_EUNSUPPORTED if K % 32 != 0. */
+/* Q4S ([k2-burn] "Working end to end" / "Quantization": int4 "Q4S" with
+ * block size 64; the pages give no more, the reading taken is symmetric
+ * int4 with one fp32 scale per block):
+ *   a = max |W| over 64 consecutive columns of a row, s[n][b] = fp32(a / 7),
+ *   code = clamp(rint(fp32(W / s)), -7, 7) (ties to even; two's complement
+ *   nibble, -8 never written), a = 0 gives s = 0 and codes 0.
+ * W: uint16 bf16 [N][K]; q: uint8 [N][K/2] (low nibble = even column);
+ * s: float [N][K/64].  K2_EUNSUPPORTED if K % 64 != 0. */
+int k2_quantize_q4s(const uint16_t *W, uint8_t *q, float *s, int N, int K, void *stream);
+
 int k2_quantize_mxfp4(const uint16_t *W, uint8_t *q, uint8_t *e8m0, int N, int K,
                       void *stream);
 
@@ -119,9 +130,13 @@ int k2_rmsnorm_grouped(const float *x, const float *gamma, float *y, int rows, i
  *   qfp8:   W uint8 E4M3FN [N][K], row_scale float [N] (applied after the sum)
  *   qmxfp4: Wq uint8 [N][K/2], We8m0 uint8 [N][K/32] (per-block scale
  *           applied to each 32-column partial sum)
+ *   qq4s:   Wq uint8 [N][K/2], Ws float [N][K/64] (per-block scale applied
+ *           to each block's partial sum; K % 64 == 0)
  *   f32:    W float [N][K]
  * x: [B][K]; y: [B][N]; residual (nullable): [B][N], may alias y.
- * K2_EUNSUPPORTED if K % 32 != 0 or B * K > 12288. */
+ * K2_EUNSUPPORTED if K % 32 != 0 (K % 64 for Q4S) or B * K > 12288. */
+int k2_gemv_qq4s(const uint8_t *Wq, const float *Ws, const float *x, float *y,
+                 const float *residual, int N, int K, int B, void *stream);
 int k2_gemv_qbf16(const uint16_t *W, const float *x, float *y, const float *residual,
                   int N, int K, int B, void *stream);
 int k2_gemv_qfp8(const uint8_t *W, const float *row_scale, const float *x, float *y,
@@ -207,7 +222,8 @@ int k2_rope_append_attn(k2_dtype kvdt, const float *qkv, const float *cos_sin, v
  * ([k2-burn] "Project layout": layer.rs, attention residual):
  *   h[n] += sum_k Wo[n][k] * out[k],  n < hidden, k < n_qh * head_dim.
  * wdt, Wo and Wo_s as for k2_gemv_q* / k2_gemv_f32 (Wo [hidden][n_qh*hd];
- * Wo_s: fp32 row scales for K2_FP8E4M3, E8M0 bytes for K2_MXFP4, NULL
+ * Wo_s: fp32 row scales for K2_FP8E4M3, E8M0 bytes for K2_MXFP4, fp32
+ * block scales for K2_Q4S, NULL
  * otherwise).  out receives the attention output as in k2_rope_append_attn;
  * h is read and written in place.  Where the shape has one (head_dim 128,
  * 4 query heads per kv head, n_qh*hd <= 4096, and the attention and O grids
@@ -242,7 +258,7 @@ typedef struct {
     int hidden, n_layers, n_qh, n_kv, head_dim, inter, vocab, groups, cap;
     float eps;
     double rope_theta;
-    k2_dtype wdt;    /* projections + lm_head: K2_F32, K2_BF16, K2_FP8E4M3, K2_MXFP4 */
+    k2_dtype wdt;    /* projections + lm_head: K2_F32, K2_BF16, K2_FP8E4M3, K2_MXFP4, K2_Q4S */
     k2_dtype kvdt;   /* K2_F32, K2_BF16, K2_I8 */
     k2_dtype embdt;  /* K2_F32 or K2_BF16 */
 } k2_config;

@@ -315,11 +315,12 @@ extern "C" int k2_rope_append_attn_o(k2_dtype kvdt, const float *qkv, const floa
     int rc = attn_common_check(kvdt, kc, vc, ks, vs, out, n_qh, n_kv, head_dim, cap, ws, ws_bytes);
     if (rc) return rc;
     if (!k2_ptr_ok(qkv) || !k2_ptr_ok(cos_sin) || !k2_ptr_ok(Wo) || !k2_ptr_ok(h)) return K2_EINVAL;
-    if ((wdt == K2_FP8E4M3 || wdt == K2_MXFP4) && !k2_ptr_ok(Wo_s)) return K2_EINVAL;
+    if ((wdt == K2_FP8E4M3 || wdt == K2_MXFP4 || wdt == K2_Q4S) && !k2_ptr_ok(Wo_s)) return K2_EINVAL;
     if (hidden <= 0) return K2_EINVAL;
-    if (wdt != K2_F32 && wdt != K2_BF16 && wdt != K2_FP8E4M3 && wdt != K2_MXFP4) return K2_EUNSUPPORTED;
+    if (wdt != K2_F32 && wdt != K2_BF16 && wdt != K2_FP8E4M3 && wdt != K2_MXFP4 && wdt != K2_Q4S)
+        return K2_EUNSUPPORTED;
     const int K = n_qh * head_dim;
-    if (K % 32 || K > K2_MAX_LDS_FLOATS) return K2_EUNSUPPORTED;
+    if (K % 32 || K > K2_MAX_LDS_FLOATS || (wdt == K2_Q4S && K % 64)) return K2_EUNSUPPORTED;
     if (pos < 0 || pos >= cap) return K2_ERANGE;
     AttnArgs a{};
     attn_ws_carve(ws, n_qh, n_kv, head_dim, cap, a);

@@ -113,7 +113,7 @@ static size_t ws_layout(const k2_config *c, DecodeWs *w, void *base)
 static bool mat_ok(int wdt, const void *w, const void *s)
 {
     if (!k2_ptr_ok(w)) return false;
-    if ((wdt == K2_FP8E4M3 || wdt == K2_MXFP4) && !s) return false;
+    if ((wdt == K2_FP8E4M3 || wdt == K2_MXFP4 || wdt == K2_Q4S) && !s) return false;
     return true;
 }
 
@@ -134,8 +134,10 @@ static int config_check(const k2_config *c)
     if (c->hidden % 32 || qd % 32 || c->inter % 32) return K2_EUNSUPPORTED;
     if (c->hidden > K2_MAX_LDS_FLOATS || qd > K2_MAX_LDS_FLOATS || c->inter > K2_MAX_LDS_FLOATS)
         return K2_EUNSUPPORTED;
-    if (c->wdt != K2_F32 && c->wdt != K2_BF16 && c->wdt != K2_FP8E4M3 && c->wdt != K2_MXFP4)
+    if (c->wdt != K2_F32 && c->wdt != K2_BF16 && c->wdt != K2_FP8E4M3 && c->wdt != K2_MXFP4 &&
+        c->wdt != K2_Q4S)
         return K2_EUNSUPPORTED;
+    if (c->wdt == K2_Q4S && (c->hidden % 64 || qd % 64 || c->inter % 64)) return K2_EUNSUPPORTED;
     if (c->kvdt != K2_F32 && c->kvdt != K2_BF16 && c->kvdt != K2_I8) return K2_EUNSUPPORTED;
     if (c->embdt != K2_F32 && c->embdt != K2_BF16) return K2_EUNSUPPORTED;
     if (c->cap > K2_ATTN_MAX_SPLITS * K2_ATTN_MAX_CHUNK) return K2_EUNSUPPORTED;
@@ -327,7 +329,7 @@ static int decode_impl(const k2_model *m, int token, const int32_t *d_token, int
     at.len = pos + 1;
     at.scale = 1.0f / sqrtf((float)hd);
     at.S = attn_splits(c->n_kv, at.len, &at.chunk);
-    const bool fused = fused_enabled() && fused_ok(hd, c->n_qh / c->n_kv, c->n_kv, H, c->n_qh * hd);
+    const bool fused = fused_enabled() && wdt != K2_Q4S && fused_ok(hd, c->n_qh / c->n_kv, c->n_kv, H, c->n_qh * hd);
     if (fused && (rc = fused_zero_sync(w.fsync, c->n_layers * FUSE_SYNC_WORDS, st))) return rc;
 
     for (int l = 0; l < c->n_layers; ++l) {

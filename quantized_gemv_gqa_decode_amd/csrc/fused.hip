@@ -76,7 +76,7 @@ int fused_qao_launch(int wdt, int kvdt, const FusedArgs &f, hipStream_t st)
 // ------------------------------------------------ attention + O, one launch --
 
 // O rows per wave; chunks per lane cover one 4096-wide row of each format in
-// one pass (f32 16, bf16 8, fp8 4, MXFP4 2)
+// one pass (f32 16, bf16 8, fp8 4, MXFP4 and Q4S 2)
 constexpr int AO_R = 2;
 template <int WDT> struct AoTile { static constexpr int U = 4096 / (K2_WAVE * WT<WDT>::EPC); };
 
@@ -127,6 +127,7 @@ int attn_o_launch(int wdt, int kvdt, int hd, int rep, const AttnArgs &at, const 
     case K2_BF16: return attn_o_kv<K2_BF16>(kvdt, f, st);
     case K2_FP8E4M3: return attn_o_kv<K2_FP8E4M3>(kvdt, f, st);
     case K2_MXFP4: return attn_o_kv<K2_MXFP4>(kvdt, f, st);
+    case K2_Q4S: return attn_o_kv<K2_Q4S>(kvdt, f, st);
     default: return K2_EUNSUPPORTED;
     }
 }

@@ -32,6 +32,7 @@ int gemv_dispatch_f32(const GemvArgs &a, int pro, int epi, hipStream_t st);
 int gemv_dispatch_bf16(const GemvArgs &a, int pro, int epi, hipStream_t st);
 int gemv_dispatch_fp8(const GemvArgs &a, int pro, int epi, hipStream_t st);
 int gemv_dispatch_mxfp4(const GemvArgs &a, int pro, int epi, hipStream_t st);
+int gemv_dispatch_q4s(const GemvArgs &a, int pro, int epi, hipStream_t st);
 
 int gemv_dispatch(int wdt, const GemvArgs &a, int pro, int epi, hipStream_t st)
 {
@@ -40,6 +41,7 @@ int gemv_dispatch(int wdt, const GemvArgs &a, int pro, int epi, hipStream_t st)
     case K2_BF16: return gemv_dispatch_bf16(a, pro, epi, st);
     case K2_FP8E4M3: return gemv_dispatch_fp8(a, pro, epi, st);
     case K2_MXFP4: return gemv_dispatch_mxfp4(a, pro, epi, st);
+    case K2_Q4S: return gemv_dispatch_q4s(a, pro, epi, st);
     default: return K2_EUNSUPPORTED;
     }
 }
@@ -57,8 +59,9 @@ static int gemv_entry(int wdt, const void *W, const void *S, const float *x, flo
     if (!k2_ptr_ok(W) || !k2_ptr_ok(x) || !k2_ptr_ok(y)) return K2_EINVAL;
     if (residual && !k2_aligned16(residual)) return K2_EINVAL;
     if (N <= 0 || K <= 0 || B <= 0) return K2_EINVAL;
-    if ((wdt == K2_FP8E4M3 || wdt == K2_MXFP4) && !S) return K2_EINVAL;
+    if ((wdt == K2_FP8E4M3 || wdt == K2_MXFP4 || wdt == K2_Q4S) && !S) return K2_EINVAL;
     if (K % 32 != 0 || (int64_t)B * K > K2_MAX_LDS_FLOATS) return K2_EUNSUPPORTED;
+    if (wdt == K2_Q4S && K % 64) return K2_EUNSUPPORTED;
     if (B != 1 && B != 2 && B != 4 && B != 8) return K2_EUNSUPPORTED;
     GemvArgs a{};
     a.W = W;
@@ -91,6 +94,12 @@ extern "C" int k2_gemv_qmxfp4(const uint8_t *Wq, const uint8_t *We8m0, const flo
     return gemv_entry(K2_MXFP4, Wq, We8m0, x, y, residual, N, K, B, stream);
 }
 
+extern "C" int k2_gemv_qq4s(const uint8_t *Wq, const float *Ws, const float *x, float *y,
+                            const float *residual, int N, int K, int B, void *stream)
+{
+    return gemv_entry(K2_Q4S, Wq, Ws, x, y, residual, N, K, B, stream);
+}
+
 extern "C" int k2_gemv_f32(const float *W, const float *x, float *y, const float *residual,
                            int N, int K, int B, void *stream)
 {
@@ -102,11 +111,13 @@ static int norm_gemv_check(int wdt, const void *W, const void *S, const float *h
                            int groups, const float *y, int N, int K)
 {
     if (!k2_ptr_ok(W) || !k2_ptr_ok(h) || !k2_ptr_ok(gamma) || !k2_ptr_ok(y)) return K2_EINVAL;
-    if ((wdt == K2_FP8E4M3 || wdt == K2_MXFP4) && !S) return K2_EINVAL;
+    if ((wdt == K2_FP8E4M3 || wdt == K2_MXFP4 || wdt == K2_Q4S) && !S) return K2_EINVAL;
     if (N <= 0 || K <= 0 || groups <= 0) return K2_EINVAL;
-    if (wdt != K2_F32 && wdt != K2_BF16 && wdt != K2_FP8E4M3 && wdt != K2_MXFP4) return K2_EUNSUPPORTED;
+    if (wdt != K2_F32 && wdt != K2_BF16 && wdt != K2_FP8E4M3 && wdt != K2_MXFP4 && wdt != K2_Q4S)
+        return K2_EUNSUPPORTED;
     if (K % 32 || K > K2_MAX_LDS_FLOATS || groups > K2_MAX_GROUPS || K % (4 * groups))
         return K2_EUNSUPPORTED;
+    if (wdt == K2_Q4S && K % 64) return K2_EUNSUPPORTED;
     return K2_OK;
 }
 

@@ -12,6 +12,7 @@ template <> struct WT<K2_F32>     { static constexpr int EPC = 4;  };
 template <> struct WT<K2_BF16>    { static constexpr int EPC = 8;  };
 template <> struct WT<K2_FP8E4M3> { static constexpr int EPC = 16; };
 template <> struct WT<K2_MXFP4>   { static constexpr int EPC = 32; };
+template <> struct WT<K2_Q4S>     { static constexpr int EPC = 32; };
 
 // Layout of activations staged in LDS.  A 16-byte weight chunk holds EPC
 // consecutive elements; lane c of a wave works on chunk c and needs EPC/4
@@ -52,10 +53,14 @@ __device__ __forceinline__ float4 plane_w(const k2_u4 &w)
         const uint32_t u = word<J>(w);
         const k2_f2 lo = fp8x2_lo(u), hi = fp8x2_hi(u);
         return make_float4(lo.x, lo.y, hi.x, hi.y);
-    } else {  // MXFP4: byte m of the chunk holds elements 2m (low nibble) and 2m+1
+    } else if constexpr (WDT == K2_MXFP4) {
+        // byte m of the chunk holds elements 2m (low nibble) and 2m+1
         const uint32_t u = word<J / 2>(w);
         const k2_f2 v0 = fp4x2<2 * (J % 2)>(u), v1 = fp4x2<2 * (J % 2) + 1>(u);
         return make_float4(v0.x, v0.y, v1.x, v1.y);
+    } else {  // Q4S: same nibble order; two's complement int4 -> code / 16
+        const uint32_t u = word<J / 2>(w) >> (16 * (J % 2));
+        return make_float4(q4s_off(u), q4s_off(u >> 4), q4s_off(u >> 8), q4s_off(u >> 12));
     }
 }
 
@@ -97,7 +102,7 @@ __device__ __forceinline__ void chunk_rows(const k2_u4 (&w)[R], const float (&sc
                                            const float *__restrict__ xc, int P, int TS, int nb,
                                            float (&acc)[B][R])
 {
-    if constexpr (WDT == K2_MXFP4) {
+    if constexpr (WDT == K2_MXFP4 || WDT == K2_Q4S) {
         float part[B][R];
 #pragma unroll
         for (int b = 0; b < B; ++b)
@@ -236,6 +241,8 @@ __device__ __forceinline__ void load_pass(const GemvArgs &a, const int64_t *rows
             const int64_t rr = rows[r] < last_row ? rows[r] : last_row;
             w[u][r] = __builtin_nontemporal_load(reinterpret_cast<const k2_u4 *>(Wb + rr * row_bytes) + cc);
             if constexpr (WDT == K2_MXFP4) sc[u][r] = e8m0_to_f32(a.S8[rr * CPR + cc]);
+            // Q4S: one scale per two chunks; x16 undoes the code / 16 of the decode
+            if constexpr (WDT == K2_Q4S) sc[u][r] = 16.0f * a.Sf[rr * (CPR / 2) + cc / 2];
         }
     }
 }
@@ -402,12 +409,12 @@ struct TileChoice { int R, U; };
 // (the wider the decode, the fewer: 32 E2M1 values per MXFP4 chunk).
 static constexpr int load_budget(int wdt)
 {
-    return wdt == K2_MXFP4 ? 8 : wdt == K2_FP8E4M3 ? 12 : 20;
+    return (wdt == K2_MXFP4 || wdt == K2_Q4S) ? 8 : wdt == K2_FP8E4M3 ? 12 : 20;
 }
 
 static TileChoice choose_tile(int wdt, int N, int K, int B, int epi)
 {
-    const int epc = wdt == K2_F32 ? 4 : wdt == K2_BF16 ? 8 : wdt == K2_FP8E4M3 ? 16 : 32;
+    const int epc = wdt == K2_F32 ? 4 : wdt == K2_BF16 ? 8 : wdt == K2_FP8E4M3 ? 16 : 32;  // MXFP4, Q4S 32
     const int cpl = (K / epc + K2_WAVE - 1) / K2_WAVE;
     int passes = (cpl + 9) / 10;
     int U = (cpl + passes - 1) / passes;

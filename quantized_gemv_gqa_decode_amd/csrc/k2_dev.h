@@ -105,6 +105,10 @@ __device__ __forceinline__ k2_f2 fp4x2(uint32_t u)
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, SEL);
 }
 
+// Low nibble of u as a two's complement int4, divided by 16 (exact:
+// v_cvt_off_f32_i4); the Q4S block scale carries the factor 16 back.
+__device__ __forceinline__ float q4s_off(uint32_t u) { return __builtin_amdgcn_cvt_off_f32_i4((int)u); }
+
 // E8M0 scale byte -> 2^(b - 127) as fp32 (b = 0 is the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b)
 {

@@ -144,6 +144,33 @@ __global__ void quant_mxfp4_kernel(const uint16_t *W, uint8_t *q, uint8_t *e8m0,
     }
 }
 
+// Q4S (int4 codes on [-7, 7], fp32 scale per 64 columns): one thread per
+// block.  s = fp32(amax / 7) and fp32(w / s) use the correctly rounded fp32
+// division (this build keeps HIP's default), rint = round to nearest even.
+__global__ void quant_q4s_kernel(const uint16_t *W, uint8_t *q, float *s, int64_t n_blocks, int K)
+{
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= n_blocks) return;
+    const int64_t nb_row = K / 64;
+    const int64_t n = b / nb_row, bb = b % nb_row;
+    const uint16_t *src = W + n * K + bb * 64;
+    float amax = 0.f;
+    for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(bf16_to_f32(src[i])));
+    const float sc = amax / 7.0f;
+    s[b] = amax == 0.f ? 0.f : sc;
+    uint8_t *dst = q + n * (K / 2) + bb * 32;
+    for (int i = 0; i < 64; i += 2) {
+        int c[2] = {0, 0};
+        if (amax != 0.f) {
+            for (int j = 0; j < 2; ++j) {
+                const float r = rintf(bf16_to_f32(src[i + j]) / sc);
+                c[j] = (int)fminf(fmaxf(r, -7.f), 7.f);
+            }
+        }
+        dst[i / 2] = (uint8_t)((c[0] & 15) | ((c[1] & 15) << 4));
+    }
+}
+
 // ----------------------------------------------------------------- argmax --
 // Candidates of a grid-stride pass over x, one per block.
 __global__ __launch_bounds__(K2_BLOCK) void argmax_kernel(const float *x, int n, ArgmaxArgs am)
@@ -266,6 +293,18 @@ extern "C" int k2_quantize_mxfp4(const uint16_t *W, uint8_t *q, uint8_t *e8m0, i
     const int64_t nb = (int64_t)N * (K / 32);
     hipLaunchKernelGGL(quant_mxfp4_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0,
                        k2_stream(stream), W, q, e8m0, nb, K);
+    K2_CHECK_LAUNCH();
+    return K2_OK;
+}
+
+extern "C" int k2_quantize_q4s(const uint16_t *W, uint8_t *q, float *s, int N, int K, void *stream)
+{
+    if (!k2_ptr_ok(W) || !k2_ptr_ok(q) || !k2_ptr_ok(s)) return K2_EINVAL;
+    if (N <= 0 || K <= 0) return K2_EINVAL;
+    if (K % 64) return K2_EUNSUPPORTED;
+    const int64_t nb = (int64_t)N * (K / 64);
+    hipLaunchKernelGGL(quant_q4s_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0,
+                       k2_stream(stream), W, q, s, nb, K);
     K2_CHECK_LAUNCH();
     return K2_OK;
 }

@@ -19,8 +19,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libk2.so")
 
 K2_OK, K2_EINVAL, K2_ERANGE, K2_EUNSUPPORTED, K2_EHIP = 0, -1, -2, -3, -4
-K2_F32, K2_BF16, K2_FP8E4M3, K2_MXFP4, K2_I8 = 0, 1, 2, 3, 4
-DTYPES = {"f32": K2_F32, "bf16": K2_BF16, "fp8": K2_FP8E4M3, "mxfp4": K2_MXFP4, "i8": K2_I8}
+K2_F32, K2_BF16, K2_FP8E4M3, K2_MXFP4, K2_I8, K2_Q4S = 0, 1, 2, 3, 4, 5
+DTYPES = {"f32": K2_F32, "bf16": K2_BF16, "fp8": K2_FP8E4M3, "mxfp4": K2_MXFP4, "i8": K2_I8,
+          "q4s": K2_Q4S}
 
 _lib = None
 
@@ -54,10 +55,12 @@ SIGNATURES = {
     "k2_status_str": (C.c_char_p, [_i]),
     "k2_quantize_fp8_rows": (_i, [_vp, _vp, _vp, _i, _i, _vp]),
     "k2_quantize_mxfp4": (_i, [_vp, _vp, _vp, _i, _i, _vp]),
+    "k2_quantize_q4s": (_i, [_vp, _vp, _vp, _i, _i, _vp]),
     "k2_rmsnorm_grouped": (_i, [_vp, _vp, _vp, _i, _i, _i, _f, _vp]),
     "k2_gemv_qbf16": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "k2_gemv_qfp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "k2_gemv_qmxfp4": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
+    "k2_gemv_qq4s": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "k2_gemv_f32": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "k2_norm_gemv": (_i, [_i, _vp, _vp, _vp, _vp, _i, _f, _vp, _i, _i, _vp]),
     "k2_norm_gemv_swiglu": (_i, [_i, _vp, _vp, _vp, _vp, _i, _f, _vp, _i, _i, _vp]),
@@ -147,6 +150,15 @@ def k2_gemv_qbf16(W, x, y, residual, N, K, B, stream=None):
 
 def k2_gemv_qfp8(W, row_scale, x, y, residual, N, K, B, stream=None):
     return load().k2_gemv_qfp8(ptr(W), ptr(row_scale), ptr(x), ptr(y), ptr(residual), N, K, B,
+                               stream_handle(stream))
+
+
+def k2_quantize_q4s(W, q, s, N, K, stream=None):
+    return load().k2_quantize_q4s(ptr(W), ptr(q), ptr(s), N, K, stream_handle(stream))
+
+
+def k2_gemv_qq4s(Wq, Ws, x, y, residual, N, K, B, stream=None):
+    return load().k2_gemv_qq4s(ptr(Wq), ptr(Ws), ptr(x), ptr(y), ptr(residual), N, K, B,
                                stream_handle(stream))
 
 

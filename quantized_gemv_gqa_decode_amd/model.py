@@ -44,6 +44,10 @@ class DeviceMat:
                 self.w = torch.empty((N, K // 2), dtype=torch.uint8, device=device)
                 self.s = torch.empty((N, K // 32), dtype=torch.uint8, device=device)
                 k2.check(k2.k2_quantize_mxfp4(src, self.w, self.s, N, K, stream))
+            elif wdt == "q4s":
+                self.w = torch.empty((N, K // 2), dtype=torch.uint8, device=device)
+                self.s = torch.empty((N, K // 64), dtype=torch.float32, device=device)
+                k2.check(k2.k2_quantize_q4s(src, self.w, self.s, N, K, stream))
             else:
                 raise ValueError(wdt)
             torch.cuda.current_stream().synchronize()

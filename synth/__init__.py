@@ -115,7 +115,7 @@ class DecoderConfig:
     eps: float
     theta: float
     cap: int
-    wdt: str            # "f32" | "bf16" | "fp8" | "mxfp4"  (projection + lm_head storage)
+    wdt: str            # "f32" | "bf16" | "fp8" | "mxfp4" | "q4s"  (projection + lm_head storage)
     kvdt: str           # "f32" | "bf16" | "i8"
     prompt_len: int
     n_decode: int
@@ -173,13 +173,15 @@ K2H_BF16_I8_LONG = K2H_BF16.replace(
 
 K2H_FP8 = K2H_BF16.replace(name="k2h-3.7b-fp8-kvi8-ctx4096", wdt="fp8", kvdt="i8")
 K2H_MXFP4 = K2H_BF16.replace(name="k2h-3.7b-mxfp4-kvi8-ctx4096", wdt="mxfp4", kvdt="i8")
+K2H_Q4S = K2H_BF16.replace(name="k2h-3.7b-q4s-kvi8-ctx4096", wdt="q4s", kvdt="i8")
 
 K3_MOE = MoeConfig(
     name="k3-latent-moe-layer", hidden=7168, latent=3584, inter=3072, n_experts=896,
     top_k=16, n_shared=2, routed_scale=1.0, eps=1e-5, tokens=(1, 8, 32))
 
 CONFIGS: Dict[str, object] = {c.name: c for c in
-                              (TINY, K2H_BF16, K2H_BF16_I8_LONG, K2H_FP8, K2H_MXFP4, K3_MOE)}
+                              (TINY, K2H_BF16, K2H_BF16_I8_LONG, K2H_FP8, K2H_MXFP4, K2H_Q4S,
+                               K3_MOE)}
 
 
 # --------------------------------------------------------------------------

@@ -70,6 +70,10 @@ def test_gemv_validation():
     assert L.k2_gemv_qbf16(FAKE, FAKE, FAKE, None, 8, 12288 + 32, 1, st) == k2.K2_EUNSUPPORTED
     assert L.k2_gemv_qfp8(FAKE, None, FAKE, FAKE, None, 8, 64, 1, st) == k2.K2_EINVAL
     assert L.k2_gemv_qmxfp4(FAKE, None, FAKE, FAKE, None, 8, 64, 1, st) == k2.K2_EINVAL
+    assert L.k2_gemv_qq4s(FAKE, None, FAKE, FAKE, None, 8, 64, 1, st) == k2.K2_EINVAL
+    assert L.k2_gemv_qq4s(FAKE, FAKE, FAKE, FAKE, None, 8, 96, 1, st) == k2.K2_EUNSUPPORTED
+    assert L.k2_quantize_q4s(FAKE, FAKE, FAKE, 8, 96, st) == k2.K2_EUNSUPPORTED
+    assert L.k2_quantize_q4s(FAKE, FAKE, None, 8, 64, st) == k2.K2_EINVAL
     assert L.k2_quantize_mxfp4(FAKE, FAKE, FAKE, 8, 48, st) == k2.K2_EUNSUPPORTED
     assert L.k2_quantize_fp8_rows(FAKE, FAKE, FAKE, 8, 40, st) == k2.K2_EINVAL
 

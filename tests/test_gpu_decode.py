@@ -23,7 +23,7 @@ if GPU:
 
 
 def tol_for(cfg) -> float:
-    return 5e-2 if (cfg.wdt in ("fp8", "mxfp4") or cfg.kvdt == "i8") else 2e-2
+    return 5e-2 if (cfg.wdt in ("fp8", "mxfp4", "q4s") or cfg.kvdt == "i8") else 2e-2
 
 
 def run_parity(cfg, prompt, n_decode, free_running=True, n_layers=None):
@@ -61,7 +61,8 @@ def run_parity(cfg, prompt, n_decode, free_running=True, n_layers=None):
 
 
 @pytest.mark.parametrize("wdt,kvdt", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "i8"),
-                                      ("fp8", "i8"), ("mxfp4", "i8"), ("f32", "bf16")])
+                                      ("fp8", "i8"), ("mxfp4", "i8"), ("f32", "bf16"),
+                                      ("q4s", "i8"), ("q4s", "bf16")])
 def test_tiny_decoder(wdt, kvdt):
     cfg = synth.TINY.replace(wdt=wdt, kvdt=kvdt)
     run_parity(cfg, synth.prompt(cfg), cfg.n_decode)
@@ -92,7 +93,7 @@ HEAD128 = synth.TINY.replace(name="head128-small", hidden=512, n_qh=8, n_kv=2, h
 
 @pytest.mark.parametrize("fused", ["1", "0"])
 @pytest.mark.parametrize("wdt,kvdt", [("bf16", "bf16"), ("bf16", "i8"), ("fp8", "i8"),
-                                      ("mxfp4", "i8"), ("f32", "f32")])
+                                      ("mxfp4", "i8"), ("f32", "f32"), ("q4s", "i8")])
 @pytest.mark.parametrize("P", [20, 200])
 def test_head128_fused_layer_front(wdt, kvdt, P, fused, monkeypatch):
     """QKV, attention and O as one dataflow launch (opt-in, K2_FUSED=1) and
@@ -104,7 +105,8 @@ def test_head128_fused_layer_front(wdt, kvdt, P, fused, monkeypatch):
 
 
 @pytest.mark.parametrize("wdt,kvdt", [("bf16", "bf16"), ("bf16", "i8"), ("fp8", "i8"),
-                                      ("mxfp4", "i8"), ("f32", "f32"), ("f32", "bf16")])
+                                      ("mxfp4", "i8"), ("f32", "f32"), ("f32", "bf16"),
+                                      ("q4s", "i8")])
 @pytest.mark.parametrize("P", [3, 200])
 def test_head128_attention_o_one_launch_bit_identical(wdt, kvdt, P, monkeypatch):
     """Attention and the O projection as one launch (the default where both
@@ -191,7 +193,8 @@ def test_k2h_bf16_full_depth_teacher_forced():
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["k2h-3.7b-fp8-kvi8-ctx4096", "k2h-3.7b-mxfp4-kvi8-ctx4096"])
+@pytest.mark.parametrize("name", ["k2h-3.7b-fp8-kvi8-ctx4096", "k2h-3.7b-mxfp4-kvi8-ctx4096",
+                                  "k2h-3.7b-q4s-kvi8-ctx4096"])
 def test_k2h_quantized_full_depth_teacher_forced(name):
     """fp8 E4M3 + row scale and MXFP4 weights quantized on the device from the
     bf16 draw (bit-exact with the oracle's quantizers, pinned elsewhere), int8

@@ -59,6 +59,24 @@ def test_quantize_mxfp4_bit_exact(N, K):
     assert np.array_equal(to_host(q), q_o)
 
 
+@pytest.mark.parametrize("N,K", [(1, 64), (37, 192), (130, 2560), (512, 4096)])
+def test_quantize_q4s_bit_exact(N, K):
+    say(f"q4s quantizer N={N} K={K}")
+    w = bf16_draw((N, K), seed=5 * N + K)
+    if N > 3:
+        w[2, 64:128] = 0                         # zero block
+        w[3, 7] = 0x8000                         # -0.0
+        w[1, 0:64] = bf16_draw((1, 64), std=40.0, seed=11)[0]   # large block
+    q_o, s_o = oracle.quant_q4s(w)
+    W = to_dev(w)
+    q = torch.empty((N, K // 2), dtype=torch.uint8, device=DEV)
+    s = torch.empty((N, K // 64), dtype=torch.float32, device=DEV)
+    check(k2.k2_quantize_q4s(W, q, s, N, K))
+    sync()
+    assert np.array_equal(to_host(s).view(np.uint32), s_o.view(np.uint32))
+    assert np.array_equal(to_host(q), q_o)
+
+
 # --------------------------------------------------- decoders (lane layout) ---
 
 def test_fp8_decode_every_code_via_gemv():
@@ -115,6 +133,8 @@ def _mat_and_dense(wdt, N, K, seed):
 
 
 def _gemv_call(wdt, m, X, Y, R, N, K, B):
+    if wdt == "q4s":
+        return k2.k2_gemv_qq4s(to_dev(m.w), to_dev(m.s), X, Y, R, N, K, B)
     if wdt == "f32":
         return k2.k2_gemv_f32(to_dev(m.w), X, Y, R, N, K, B)
     if wdt == "bf16":
@@ -124,13 +144,39 @@ def _gemv_call(wdt, m, X, Y, R, N, K, B):
     return k2.k2_gemv_qmxfp4(to_dev(m.w), to_dev(m.s), X, Y, R, N, K, B)
 
 
-@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "mxfp4"])
+def test_q4s_decode_every_nibble_via_gemv():
+    """A one-hot x reads one column of the dequantized matrix exactly: every
+    (low, high) nibble pair in every byte position of a 16-byte chunk, under
+    block scales that are not powers of two."""
+    K = 512
+    byts = np.arange(256, dtype=np.uint8)
+    q = np.stack([byts, np.roll(byts, 7)])                   # 2 rows x 256 bytes = 512 columns
+    s = np.array([[1.0, 0.3, 7.5e-3, 2.0 ** -20, 123.0, 0.0, 1.0 / 3.0, 5.0],
+                  [0.25] * 8], np.float32)
+    N = 2
+    Qd, Sd = to_dev(q), to_dev(s)
+    y = torch.empty(N, dtype=torch.float32, device=DEV)
+    for k in range(0, K, 3):
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        check(k2.k2_gemv_qq4s(Qd, Sd, to_dev(x), y, None, N, K, 1))
+        got = to_host(y)
+        for n in range(N):
+            b = q[n, k // 2]
+            nib = (b >> 4) if (k & 1) else (b & 15)
+            want = oracle.q4s_value(nib)[()] * float(s[n, k // 64])
+            assert got[n] == np.float32(want), (n, k, got[n], want)
+
+
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "mxfp4", "q4s"])
 @pytest.mark.parametrize("N,K,B", [(1, 32, 1), (37, 96, 1), (131, 640, 1), (517, 2560, 1),
                                    (70, 4096, 1), (33, 10240, 1), (45, 320, 2), (19, 1024, 4),
                                    (23, 1536, 8),
                                    # rows split over 2 or 4 waves (long rows), ragged row counts
                                    (2561, 10240, 1), (1001, 5632, 1), (3, 3072, 1)])
 def test_gemv_matches_oracle(wdt, N, K, B):
+    if wdt == "q4s" and K % 64:
+        pytest.skip("Q4S blocks are 64 columns")
     say(f"gemv {wdt} N={N} K={K} B={B}")
     m, dense = _mat_and_dense(wdt, N, K, seed=N * 31 + K)
     rng = np.random.default_rng(K + B)
@@ -340,7 +386,7 @@ def test_rope_append_attn_matches_oracle(kvdt, hd, n_qh, n_kv, pos):
         assert np.array_equal(gv[:, pos], oc.v[:, pos])
 
 
-@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "mxfp4", "q4s"])
 @pytest.mark.parametrize("kvdt", ["bf16", "i8"])
 @pytest.mark.parametrize("pos", [0, 200, 700, 3000])
 def test_rope_append_attn_o(wdt, kvdt, pos):
