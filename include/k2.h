@@ -225,11 +225,11 @@ int k2_rope_append_attn(k2_dtype kvdt, const float *qkv, const float *cos_sin, v
  * Wo_s: fp32 row scales for K2_FP8E4M3, E8M0 bytes for K2_MXFP4, fp32
  * block scales for K2_Q4S, NULL
  * otherwise).  out receives the attention output as in k2_rope_append_attn;
- * h is read and written in place.  Where the shape has one (head_dim 128,
- * 4 query heads per kv head, n_qh*hd <= 4096, and the attention and O grids
- * fit the device at once) this is ONE launch whose O blocks stream their
- * weights while the attention runs; otherwise the attention kernel and the
- * GEMV.  Either way h is bit-identical to k2_rope_append_attn followed by
+ * h is read and written in place.  Where the shape has one (fp32 or bf16
+ * cache, head_dim 128, 4 query heads per kv head, n_qh*hd <= 4096, and the
+ * attention and O grids fit the device at once) this is ONE launch whose O
+ * blocks stream their weights while the attention runs; otherwise the
+ * attention kernel and the GEMV.  Either way h is bit-identical to k2_rope_append_attn followed by
  * the GEMV.  d_err (device int32, nullable): set to K2_EHIP if a wait inside
  * the launch times out (outputs then undefined).  Same workspace as
  * k2_gqa_decode_attn; K2_EUNSUPPORTED unless n_qh*hd % 32 == 0 and

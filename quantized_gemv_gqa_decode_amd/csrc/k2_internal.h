@@ -97,9 +97,9 @@ int attn_o_launch(int wdt, int kvdt, int hd, int rep, const AttnArgs &at, const 
                   int32_t *d_err, hipStream_t st);
 
 // Fused-form attention (at) and then the O GEMV + residual (o, B = 1): one
-// launch where attn_o_launch has one (unless K2_ATTN_O=0), else the two
-// kernels, the attention launch's idle compute units prefetching the O
-// weights (unless K2_PREFETCH=0).
+// launch where attn_o_launch has one and the cache is fp32 or bf16 (unless
+// K2_ATTN_O=0), else the two kernels, the attention launch's idle compute
+// units prefetching the O weights (unless K2_PREFETCH=0).
 int attn_then_o(int wdt, int kvdt, int hd, int rep, AttnArgs at, const GemvArgs &o, int32_t *d_err,
                 hipStream_t st);
 void attn_ws_carve(void *ws, int n_qh, int n_kv, int hd, int cap, AttnArgs &a);

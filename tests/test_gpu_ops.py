@@ -391,9 +391,9 @@ def test_rope_append_attn_matches_oracle(kvdt, hd, n_qh, n_kv, pos):
 @pytest.mark.parametrize("pos", [0, 200, 700, 3000])
 def test_rope_append_attn_o(wdt, kvdt, pos):
     """Attention then the O projection + residual at the 3.7B head shape (32 q /
-    8 kv heads, hd 128, hidden 2560).  Up to ~770 positions it is one launch
-    (O blocks beside the attention blocks), beyond it the attention kernel and
-    the GEMV; either way out, h and the cache are bit-identical to
+    8 kv heads, hd 128, hidden 2560).  With a bf16 cache up to ~770 positions
+    it is one launch (O blocks beside the attention blocks), otherwise the
+    attention kernel and the GEMV; either way out, h and the cache are bit-identical to
     k2_rope_append_attn followed by the GEMV, and h matches the oracle
     (fp64 attention, then the dequantized O matvec) within the attention's
     error carried through |W_o| plus the fp32 summation bound."""
