@@ -3,14 +3,16 @@
 // layers -> norm -> lm_head; layer.rs norm + attention residual, norm + MLP
 // residual; mlp.rs SwiGLU).
 //
-// Per layer, five kernels, each reading its weights exactly once:
+// Per layer, five phases, each reading its weights exactly once:
 //   1. GroupedRMSNorm (in the GEMV prologue) + QKV GEMV          -> qkv
 //   2. RoPE + KV append at pos + split-K GQA attention + combine  -> o
 //   3. O GEMV + residual                                          -> h
 //   4. GroupedRMSNorm (prologue) + gate/up GEMV + SwiGLU          -> act
 //   5. down GEMV + residual                                       -> h
-// then GroupedRMSNorm + lm_head GEMV + first-maximum argmax (one kernel).
-// The embedding gather opens the step.  All activations are fp32.
+// Phases 2 and 3 are one launch where the shape allows it (attn_then_o),
+// so a layer is four or five kernels.  Then GroupedRMSNorm + lm_head GEMV +
+// first-maximum argmax.  The embedding gather opens the step.  All
+// activations are fp32.
 //
 // The environment variable K2_PERSISTENT=1 runs the position as one
 // cooperative launch of the persistent step kernel instead (step_impl.h),
@@ -329,7 +331,8 @@ static int decode_impl(const k2_model *m, int token, const int32_t *d_token, int
     at.len = pos + 1;
     at.scale = 1.0f / sqrtf((float)hd);
     at.S = attn_splits(c->n_kv, at.len, &at.chunk);
-    const bool fused = fused_enabled() && wdt != K2_Q4S && fused_ok(hd, c->n_qh / c->n_kv, c->n_kv, H, c->n_qh * hd);
+    const bool fused = fused_enabled() && wdt != K2_Q4S &&
+                       fused_ok(hd, c->n_qh / c->n_kv, c->n_kv, H, c->n_qh * hd);
     if (fused && (rc = fused_zero_sync(w.fsync, c->n_layers * FUSE_SYNC_WORDS, st))) return rc;
 
     for (int l = 0; l < c->n_layers; ++l) {
@@ -365,36 +368,36 @@ static int decode_impl(const k2_model *m, int token, const int32_t *d_token, int
             f.d_err = d_err;
             if ((rc = fused_qao_launch(wdt, c->kvdt, f, st))) return rc;
         } else {
-        GemvArgs g{};
-        g.W = L->qkv;
-        g.Sf = (const float *)L->qkv_s;
-        g.S8 = (const uint8_t *)L->qkv_s;
-        g.x = w.h;
-        g.gamma = L->g_in;
-        g.eps = c->eps;
-        g.groups = c->groups;
-        g.y = w.qkv;
-        g.N = qkv_rows;
-        g.K = H;
-        g.B = 1;
-        if ((rc = gemv_dispatch(wdt, g, PRO_NORM, EPI_PLAIN, st))) return rc;
+            GemvArgs g{};
+            g.W = L->qkv;
+            g.Sf = (const float *)L->qkv_s;
+            g.S8 = (const uint8_t *)L->qkv_s;
+            g.x = w.h;
+            g.gamma = L->g_in;
+            g.eps = c->eps;
+            g.groups = c->groups;
+            g.y = w.qkv;
+            g.N = qkv_rows;
+            g.K = H;
+            g.B = 1;
+            if ((rc = gemv_dispatch(wdt, g, PRO_NORM, EPI_PLAIN, st))) return rc;
 
-        at.kc = L->kc;
-        at.vc = L->vc;
-        at.ks = L->ks;
-        at.vs = L->vs;
+            at.kc = L->kc;
+            at.vc = L->vc;
+            at.ks = L->ks;
+            at.vs = L->vs;
 
-        GemvArgs o{};
-        o.W = L->o;
-        o.Sf = (const float *)L->o_s;
-        o.S8 = (const uint8_t *)L->o_s;
-        o.x = w.o;
-        o.y = w.h;
-        o.residual = w.h;
-        o.N = H;
-        o.K = c->n_qh * hd;
-        o.B = 1;
-        if ((rc = attn_then_o(wdt, c->kvdt, hd, c->n_qh / c->n_kv, at, o, d_err, st))) return rc;
+            GemvArgs o{};
+            o.W = L->o;
+            o.Sf = (const float *)L->o_s;
+            o.S8 = (const uint8_t *)L->o_s;
+            o.x = w.o;
+            o.y = w.h;
+            o.residual = w.h;
+            o.N = H;
+            o.K = c->n_qh * hd;
+            o.B = 1;
+            if ((rc = attn_then_o(wdt, c->kvdt, hd, c->n_qh / c->n_kv, at, o, d_err, st))) return rc;
         }
 
         GemvArgs gu{};
