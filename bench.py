@@ -381,6 +381,46 @@ def bench_moe(cfg, args, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_prefill(cfg, gm, P, args, stream):
+    """Prompt prefill throughput: the P-position prompt through k2_prefill in
+    chunks (weights streamed once per chunk, projections on the matrix cores,
+    attention per position), timed with HIP events after one untimed pass;
+    the next token is checked against position-by-position decode."""
+    import torch
+    import synth
+    prompt = synth.prompt(cfg, P)
+    T = args.prefill_chunk
+    gm.prefill(prompt, 0, chunk=T)                   # warm (also the caches' first write)
+    torch.cuda.synchronize()
+    first = int(gm.next.item())
+    reps = 3
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(reps):
+        gm.prefill(prompt, 0, chunk=T)
+    e.record(stream)
+    e.synchronize()
+    ms = s.elapsed_time(e) / reps
+    for p, t in enumerate(prompt):                   # position by position, same caches
+        gm.step(int(t), p, want_logits=(p == P - 1))
+    torch.cuda.synchronize()
+    serial = int(gm.next.item())
+    chunks = (P + T - 1) // T
+    out = {
+        "metric": "prompt prefill tokens/s (chunked, matrix-core projections)",
+        "value": round(P / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": reps,
+        "warmup": 1, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 activations (bf16 hi+lo on the matrix cores)",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "prompt_len": P, "chunk": T, "chunks": chunks,
+                   "weights": cfg.wdt, "kv_cache": cfg.kvdt},
+        "weight_GBps": round(chunks * gm.weight_bytes() / (ms * 1e-3) / 1e9, 1),
+        "next_token": first, "next_token_serial_decode": serial,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def copy_probe(mib: int):
     """Five launches of an elementwise fp32 copy (y = x * 1) over mib MiB:
     each reads and writes exactly mib MiB.  Profiler counters of these
@@ -414,6 +454,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--tokens", default=None,
                     help="latent-MoE workload only: comma-separated token counts")
+    ap.add_argument("--prefill-chunk", type=int, default=0, metavar="T",
+                    help="instead of the decode bench: time the prompt's prefill through "
+                         "k2_prefill in chunks of T positions (2..32; bf16 weights)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the decode bench: launch a plain fp32 copy kernel over "
                          "MIB MiB five times (the known-size reference that scales the HBM "
@@ -458,6 +501,9 @@ def main():
     torch.cuda.synchronize()
     log(f"model ready in {time.perf_counter() - t0:.1f} s, weights {gm.weight_bytes() / 1e9:.3f} GB")
     stream = torch.cuda.current_stream()
+
+    if args.prefill_chunk:
+        return bench_prefill(cfg, gm, P, args, stream)
 
     if args.prefix:
         if cfg.kvdt != "i8":

@@ -293,6 +293,23 @@ size_t k2_decode_workspace_bytes(const k2_config *cfg);
 /* Validate a model description (sizes, dtypes, pointers, alignment). */
 int k2_model_check(const k2_model *m);
 
+/* Prefill of T prompt positions pos0 .. pos0+T-1 in one sweep ([k2-burn]
+ * "Working end to end": prefill + single-token decode).  Same result as T
+ * calls of k2_decode_step at those positions, up to rounding: the
+ * projections of the T rows run on the matrix cores with each fp32
+ * activation split into bf16 hi + lo (about 16 significant bits, fp32
+ * accumulation); the caches receive every position; logits (nullable) and
+ * next_token (nullable) are those of the LAST position.  tokens: HOST array
+ * [T].  Needs bf16 projection weights and 2 <= T <= 32 (K2_EUNSUPPORTED
+ * otherwise; a single position is k2_decode_step).  ws: device workspace of
+ * k2_prefill_workspace_bytes(&m->cfg, T) bytes, 256-byte aligned,
+ * zero-filled before its first use (left zeroed where it must be); calls that
+ * share it must not overlap in time.  K2_ERANGE if a token is outside the
+ * vocabulary or pos0 + T > cap (nothing enqueued). */
+size_t k2_prefill_workspace_bytes(const k2_config *cfg, int T);
+int k2_prefill(const k2_model *m, const int32_t *tokens, int T, int pos0, float *logits,
+               int32_t *next_token, void *ws, size_t ws_bytes, void *stream);
+
 /* One decode position: embed `token` (host int), run every layer at `pos`
  * (its K and V are stored at slot pos before attending), then, when `logits`
  * is non-NULL, the final norm, the lm_head and the argmax.  logits: [vocab]

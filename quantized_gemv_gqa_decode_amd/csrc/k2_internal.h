@@ -113,6 +113,9 @@ void argmax_ws_carve(void *ws, ArgmaxArgs &am);
 
 int embed_launch(int embdt, const void *E, int H, int vocab, int token, const int32_t *d_token,
                  int32_t *d_err, float *h, hipStream_t st);
+// GroupedRMSNorm of `rows` rows (one block per row and group)
+int rmsnorm_rows_launch(const float *x, const float *gamma, float *y, int rows, int hidden, int groups,
+                        float eps, hipStream_t st);
 int argmax_final_launch(const ArgmaxArgs &am, int n_blocks, hipStream_t st);
 
 // ------------------------------------------------------ device functions --

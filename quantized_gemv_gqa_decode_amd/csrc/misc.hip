@@ -236,6 +236,15 @@ extern "C" const char *k2_status_str(int status)
     return "unknown status";
 }
 
+int k2::rmsnorm_rows_launch(const float *x, const float *gamma, float *y, int rows, int hidden,
+                            int groups, float eps, hipStream_t st)
+{
+    hipLaunchKernelGGL(rmsnorm_grouped_kernel, dim3(rows * groups), dim3(K2_BLOCK), 0, st, x, gamma, y,
+                       hidden, groups, eps);
+    K2_CHECK_LAUNCH();
+    return K2_OK;
+}
+
 extern "C" int k2_rmsnorm_grouped(const float *x, const float *gamma, float *y, int rows, int hidden,
                                   int groups, float eps, void *stream)
 {

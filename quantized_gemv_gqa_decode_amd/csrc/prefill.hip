@@ -1,0 +1,206 @@
+// prefill.hip -- a chunk of prompt positions through the whole model in one
+// sweep, the projections on the matrix cores.
+//
+// [k2-burn] "Working end to end" names prefill beside single-token decode:
+// the prompt is consumed before the first decode step, and consuming it
+// position by position gives exactly the incremental (cached) result.  With
+// T positions at once every projection is a [N][K] x [K][T] product, so a
+// weight byte feeds 2T flops: past a few positions that is a dense
+// contraction, run here on v_mfma_f32_16x16x32_bf16 by the bf16 product of
+// dense_mfma.hip (activations split into bf16 hi + lo, fp32 accumulation).
+//
+// Per layer, for the T rows of the chunk:
+//   1. GroupedRMSNorm of every row                       (one launch)
+//   2. QKV = W_qkv X                                     (matrix cores)
+//   3. per position p = pos0 + t, in order: RoPE, KV append at p, attention
+//      over [0, p] -- position t sees the K/V rows of the earlier positions
+//      of the chunk because their launches come first on the stream
+//   4. H += W_o O                                        (matrix cores, add)
+//   5. GroupedRMSNorm, then ACT = silu(W_g X) * (W_u X)  (matrix cores, SwiGLU)
+//   6. H += W_d ACT                                      (matrix cores, add)
+// then the final norm, lm_head and first-maximum argmax of the LAST row only
+// (the GEMV of the decode step).
+#include "k2_dev.h"
+#include "k2_internal.h"
+
+namespace k2 {
+
+constexpr int PF_MAX_T = 32;               // positions per call (one matrix-core token group)
+
+struct PfTokens {
+    int tok[PF_MAX_T];
+};
+
+// h[t] = E[tok[t]] (bf16 widened exactly, or fp32), t < T
+__global__ void embed_rows_kernel(const PfTokens tk, int embdt, const void *E, int H, float *h)
+{
+    const int t = blockIdx.y;
+    const int64_t base = (int64_t)tk.tok[t] * H;
+    float *dst = h + (int64_t)t * H;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < H; i += gridDim.x * blockDim.x)
+        dst[i] = embdt == K2_BF16 ? bf16_to_f32(((const uint16_t *)E)[base + i]) : ((const float *)E)[base + i];
+}
+
+struct PrefillWs {
+    float *h, *x, *qkv, *o, *act, *part;
+    void *attn, *am;
+    int32_t *next;
+};
+
+static size_t pf_part_bytes(const k2_config *c, int T)
+{
+    const int qkv_rows = (c->n_qh + 2 * c->n_kv) * c->head_dim, qd = c->n_qh * c->head_dim;
+    const size_t b[4] = {dense_mfma_ws_bytes(qkv_rows, c->hidden, T), dense_mfma_ws_bytes(c->hidden, qd, T),
+                         dense_mfma_ws_bytes(2 * c->inter, c->hidden, T),
+                         dense_mfma_ws_bytes(c->hidden, c->inter, T)};
+    size_t m = 0;
+    for (size_t v : b) m = v > m ? v : m;
+    return m;
+}
+
+static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base)
+{
+    const size_t qkv_rows = (size_t)(c->n_qh + 2 * c->n_kv) * c->head_dim, qd = (size_t)c->n_qh * c->head_dim;
+    size_t off = 0;
+    char *b = (char *)base;
+    auto take = [&](size_t bytes) {
+        char *p = b ? b + off : nullptr;
+        off += k2_align256(bytes);
+        return p;
+    };
+    // the parts that must stay zero between calls (the attention's split
+    // counters, the argmax's) come first, at offsets that do not depend on T:
+    // a workspace sized for one T serves every smaller T
+    char *attn = take(attn_ws_bytes(c->n_qh, c->n_kv, c->head_dim, c->cap));
+    char *am = take(argmax_ws_bytes());
+    char *nx = take(4);
+    char *h = take((size_t)T * c->hidden * 4);
+    char *x = take((size_t)T * c->hidden * 4);
+    char *qkv = take((size_t)T * qkv_rows * 4);
+    char *o = take((size_t)T * qd * 4);
+    char *act = take((size_t)T * c->inter * 4);
+    char *part = take(pf_part_bytes(c, T));
+    if (w) {
+        w->h = (float *)h;
+        w->x = (float *)x;
+        w->qkv = (float *)qkv;
+        w->o = (float *)o;
+        w->act = (float *)act;
+        w->part = (float *)part;
+        w->attn = attn;
+        w->am = am;
+        w->next = (int32_t *)nx;
+    }
+    return off;
+}
+
+// Shapes this path handles (K2_EUNSUPPORTED otherwise): bf16 projection
+// weights whose products the matrix-core kernel takes.
+static int pf_shape_ok(const k2_config *c)
+{
+    if (c->wdt != K2_BF16) return K2_EUNSUPPORTED;
+    const int qkv_rows = (c->n_qh + 2 * c->n_kv) * c->head_dim, qd = c->n_qh * c->head_dim;
+    if (!dense_mfma_ok(qkv_rows, c->hidden) || !dense_mfma_ok(c->hidden, qd) ||
+        !dense_mfma_ok(2 * c->inter, c->hidden) || !dense_mfma_ok(c->hidden, c->inter))
+        return K2_EUNSUPPORTED;
+    return K2_OK;
+}
+
+static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos0, float *logits,
+                        int32_t *next, void *ws, size_t ws_bytes, hipStream_t st)
+{
+    int rc = k2_model_check(m);
+    if (rc) return rc;
+    const k2_config *c = &m->cfg;
+    if (T < 2 || T > PF_MAX_T) return K2_EUNSUPPORTED;
+    if (!tokens) return K2_EINVAL;
+    if ((rc = pf_shape_ok(c))) return rc;
+    if (logits && !k2_aligned16(logits)) return K2_EINVAL;
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pf_layout(c, T, nullptr, nullptr)) return K2_EINVAL;
+    if (pos0 < 0 || (int64_t)pos0 + T > c->cap) return K2_ERANGE;
+    PfTokens tk{};
+    for (int t = 0; t < T; ++t) {
+        if (tokens[t] < 0 || tokens[t] >= c->vocab) return K2_ERANGE;
+        tk.tok[t] = tokens[t];
+    }
+
+    PrefillWs w;
+    pf_layout(c, T, &w, ws);
+    const int H = c->hidden, hd = c->head_dim, I = c->inter, rep = c->n_qh / c->n_kv;
+    const int qkv_rows = (c->n_qh + 2 * c->n_kv) * hd, qd = c->n_qh * hd;
+
+    int blocks = (H + K2_BLOCK - 1) / K2_BLOCK;
+    if (blocks > 16) blocks = 16;
+    hipLaunchKernelGGL(embed_rows_kernel, dim3(blocks, T), dim3(K2_BLOCK), 0, st, tk, c->embdt, m->embed,
+                       H, w.h);
+    K2_CHECK_LAUNCH();
+
+    AttnArgs at{};
+    attn_ws_carve(w.attn, c->n_qh, c->n_kv, hd, c->cap, at);
+    at.cos_sin = m->rope;
+    at.n_qh = c->n_qh;
+    at.n_kv = c->n_kv;
+    at.cap = c->cap;
+    at.scale = 1.0f / sqrtf((float)hd);
+
+    for (int l = 0; l < c->n_layers; ++l) {
+        const k2_layer *L = &m->layers[l];
+        if ((rc = rmsnorm_rows_launch(w.h, L->g_in, w.x, T, H, c->groups, c->eps, st))) return rc;
+        if ((rc = dense_mfma((const uint16_t *)L->qkv, w.x, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, st)))
+            return rc;
+        at.kc = L->kc;
+        at.vc = L->vc;
+        at.ks = L->ks;
+        at.vs = L->vs;
+        for (int t = 0; t < T; ++t) {
+            at.qkv = w.qkv + (int64_t)t * qkv_rows;
+            at.out = w.o + (int64_t)t * qd;
+            at.pos = pos0 + t;
+            at.len = at.pos + 1;
+            at.S = attn_splits(c->n_kv, at.len, &at.chunk);
+            if ((rc = attn_launch(c->kvdt, hd, rep, true, at, st))) return rc;
+        }
+        if ((rc = dense_mfma((const uint16_t *)L->o, w.o, w.h, H, qd, T, DM_EPI_ADD, w.part, st))) return rc;
+        if ((rc = rmsnorm_rows_launch(w.h, L->g_post, w.x, T, H, c->groups, c->eps, st))) return rc;
+        if ((rc = dense_mfma((const uint16_t *)L->gu, w.x, w.act, 2 * I, H, T, DM_EPI_SWIGLU, w.part, st)))
+            return rc;
+        if ((rc = dense_mfma((const uint16_t *)L->down, w.act, w.h, H, I, T, DM_EPI_ADD, w.part, st)))
+            return rc;
+    }
+
+    if (logits) {
+        ArgmaxArgs am{};
+        argmax_ws_carve(w.am, am);
+        GemvArgs lm{};
+        lm.W = m->lm;
+        lm.x = w.h + (int64_t)(T - 1) * H;
+        lm.gamma = m->g_final;
+        lm.eps = c->eps;
+        lm.groups = c->groups;
+        lm.y = logits;
+        lm.N = c->vocab;
+        lm.K = H;
+        lm.B = 1;
+        lm.am = am;
+        lm.am.out_idx = next ? next : w.next;
+        if ((rc = gemv_dispatch(c->wdt, lm, PRO_NORM, EPI_ARGMAX, st))) return rc;
+    }
+    return K2_OK;
+}
+
+}  // namespace k2
+
+using namespace k2;
+
+extern "C" size_t k2_prefill_workspace_bytes(const k2_config *cfg, int T)
+{
+    if (!cfg || T < 2 || T > PF_MAX_T || pf_shape_ok(cfg)) return 0;
+    if (k2_decode_workspace_bytes(cfg) == 0) return 0;
+    return pf_layout(cfg, T, nullptr, nullptr);
+}
+
+extern "C" int k2_prefill(const k2_model *m, const int32_t *tokens, int T, int pos0, float *logits,
+                          int32_t *next_token, void *ws, size_t ws_bytes, void *stream)
+{
+    return prefill_impl(m, tokens, T, pos0, logits, next_token, ws, ws_bytes, k2_stream(stream));
+}

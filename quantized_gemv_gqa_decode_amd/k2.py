@@ -81,6 +81,8 @@ SIGNATURES = {
     "k2_decode_workspace_bytes": (_sz, [_vp]),
     "k2_model_check": (_i, [_vp]),
     "k2_decode_step": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+    "k2_prefill_workspace_bytes": (_sz, [_vp, _i]),
+    "k2_prefill": (_i, [_vp, _vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "k2_decode_step_dev": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp]),
     "k2_moe_route_workspace_bytes": (_sz, [_i, _i]),
     "k2_moe_route": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
@@ -324,3 +326,14 @@ def k2_moe_layer(weights: k2_moe_layer_weights, x, T, y, topk_idx_out, topk_w_ou
     return load().k2_moe_layer(C.addressof(weights), ptr(x), T, ptr(y), ptr(topk_idx_out),
                                ptr(topk_w_out), ptr(d_err), ptr(ws), ws_bytes,
                                stream_handle(stream))
+
+
+def k2_prefill_workspace_bytes(cfg, T) -> int:
+    return load().k2_prefill_workspace_bytes(C.addressof(cfg), T)
+
+
+def k2_prefill(model, tokens, T, pos0, logits, next_token, ws, ws_bytes, stream=None):
+    """tokens: a host sequence of T ints (copied into a C array here)."""
+    arr = (C.c_int32 * T)(*[int(t) for t in tokens])
+    return load().k2_prefill(C.addressof(model), arr, T, pos0, ptr(logits), ptr(next_token), ptr(ws),
+                             ws_bytes, stream_handle(stream))

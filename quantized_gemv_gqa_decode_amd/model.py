@@ -153,6 +153,33 @@ class DecodeModel:
         k2.check(k2.k2_decode_step(self.model, token, pos, lg, nx, stream))
         return lg, nx
 
+    def prefill(self, tokens, pos0: int = 0, chunk: int = 32, want_logits: bool = True,
+                stream=None):
+        """Consume prompt positions pos0 .. pos0+len(tokens)-1 with k2_prefill,
+        ``chunk`` (2..32) positions per call; a lone last position goes through
+        k2_decode_step.  The logits/next of the last position land in
+        self.logits / self.next when want_logits."""
+        toks = [int(t) for t in tokens]
+        n = len(toks)
+        if not hasattr(self, "_pf_ws") or self._pf_chunk != chunk:
+            b = k2.k2_prefill_workspace_bytes(self.model.cfg, chunk)
+            if b == 0:
+                raise k2.K2Error(k2.K2_EUNSUPPORTED)
+            self._pf_ws = torch.zeros(b, dtype=torch.uint8, device=self.device)
+            self._pf_chunk = chunk
+        i = 0
+        while i < n:
+            T = min(chunk, n - i)
+            last = i + T == n
+            lg = self.logits if (want_logits and last) else None
+            nx = self.next if (want_logits and last) else None
+            if T == 1:
+                k2.check(k2.k2_decode_step(self.model, toks[i], pos0 + i, lg, nx, stream))
+            else:
+                k2.check(k2.k2_prefill(self.model, toks[i:i + T], T, pos0 + i, lg, nx, self._pf_ws,
+                                       self._pf_ws.numel(), stream))
+            i += T
+
     def step_dev(self, d_token: torch.Tensor, pos: int, d_next: torch.Tensor,
                  d_err: Optional[torch.Tensor] = None, want_logits: bool = True, stream=None):
         lg = self.logits if want_logits else None

@@ -144,6 +144,29 @@ def test_decode_step_refuses_before_launch():
     assert L.k2_decode_step(None, 0, 0, FAKE, FAKE, None) == k2.K2_EINVAL
 
 
+def test_prefill_refuses_unsupported_shapes():
+    # fp32 weights, and a bf16 model whose hidden size the matrix-core product
+    # does not take (64 is not a multiple of 128): no workspace, no launch
+    assert k2.k2_prefill_workspace_bytes(_fake_model().cfg, 8) == 0
+    m = _fake_model(dict(wdt=k2.K2_BF16))
+    assert k2.k2_prefill_workspace_bytes(m.cfg, 8) == 0
+    assert k2.load().k2_prefill(C.addressof(m), (C.c_int32 * 8)(*[1] * 8), 8, 0, None, None,
+                                0x100000, 1 << 20, None) == k2.K2_EUNSUPPORTED
+    ok = dict(hidden=512, n_qh=8, n_kv=2, head_dim=128, inter=1024, vocab=1024, wdt=k2.K2_BF16)
+    m = _fake_model(ok)
+    assert k2.k2_prefill_workspace_bytes(m.cfg, 8) > 0
+    assert k2.k2_prefill_workspace_bytes(m.cfg, 1) == 0
+    assert k2.k2_prefill_workspace_bytes(m.cfg, 33) == 0
+    wsb = k2.k2_prefill_workspace_bytes(m.cfg, 8)
+    L = k2.load()
+    toks = (C.c_int32 * 8)(*[1] * 8)
+    assert L.k2_prefill(C.addressof(m), toks, 8, 30, None, None, 0x100000, wsb, None) == k2.K2_ERANGE
+    bad = (C.c_int32 * 8)(*([1] * 7 + [1024]))
+    assert L.k2_prefill(C.addressof(m), bad, 8, 0, None, None, 0x100000, wsb, None) == k2.K2_ERANGE
+    assert L.k2_prefill(C.addressof(m), toks, 8, 0, None, None, 0x100000, wsb - 1, None) == k2.K2_EINVAL
+    assert L.k2_prefill(C.addressof(m), None, 8, 0, None, None, 0x100000, wsb, None) == k2.K2_EINVAL
+
+
 @pytest.mark.parametrize("change,rc", [(dict(head_dim=96), -3), (dict(n_kv=3), -3),
                                        (dict(groups=3), -3), (dict(hidden=48), -3),
                                        (dict(wdt=k2.K2_I8), -3), (dict(kvdt=k2.K2_MXFP4), -3),

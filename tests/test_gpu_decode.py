@@ -231,3 +231,92 @@ def test_k2h_int8_long_context(prefix):
         assert near_tie_ok(int(nx.item()), rl, tie_gap(err)), (i, int(nx.item()), int(np.argmax(rl)), err)
         feed = rt                                    # teacher-forced on the oracle's token
     say(f"int8 history {prefix}: max|dlogit| = {worst:.3g}")
+
+
+# ------------------------------------------------------------------ prefill ---
+
+def _prefill_parity(cfg, P, n_after, chunk=32):
+    """Prompt of P positions through k2_prefill (chunks of up to 32 rows on
+    the matrix cores), then n_after decode steps teacher-forced on the
+    oracle's tokens: the last prompt position's logits and every later
+    position's logits against the oracle (the later ones read the caches the
+    prefill wrote)."""
+    prompt = synth.prompt(cfg, P)
+    dec = oracle.Decoder.from_synth(cfg)
+    ref_toks, ref_lg = dec.generate(prompt, n_after + 1)
+    gm = DecodeModel(cfg, DEV)
+    gm.prefill(prompt, 0, chunk=chunk)
+    torch.cuda.synchronize()
+    tol = tol_for(cfg)
+    worst = 0.0
+    got = [(to_host(gm.logits).astype(np.float64), int(gm.next.item()))]
+    for i in range(n_after):
+        lg, nx = gm.step(ref_toks[i], P + i)
+        torch.cuda.synchronize()
+        got.append((to_host(lg).astype(np.float64), int(nx.item())))
+    for i, ((g, t), r) in enumerate(zip(got, ref_lg)):
+        err = float(np.abs(g - r).max())
+        worst = max(worst, err)
+        assert err <= tol, (i, err)
+        assert near_tie_ok(t, r, tie_gap(err)), (i, t, int(np.argmax(r)), err)
+    say(f"prefill P={P}: max|dlogit| = {worst:.3g} (tol {tol})")
+    return worst
+
+
+@pytest.mark.parametrize("kvdt", ["bf16", "i8", "f32"])
+@pytest.mark.parametrize("P", [2, 3, 33, 70, 100])
+def test_head128_prefill_matches_oracle(kvdt, P):
+    """bf16 weights at the head-128 shape: 2 and 3 positions are one chunk,
+    33 is a chunk of 32 and a lone position through the decode step, 70 is
+    32 + 32 + 6 and 100 is 32 + 32 + 32 + 4 (from 65 positions on the
+    attention splits, so a smaller last chunk must find the split counters
+    of the workspace zeroed)."""
+    cfg = HEAD128.replace(wdt="bf16", kvdt=kvdt, cap=128)
+    _prefill_parity(cfg, P, 3)
+
+
+def test_prefill_equals_decode_steps_on_cache():
+    """The caches a prefill writes decode the same next positions as the
+    caches of position-by-position decode, within the bf16 cache's rounding:
+    the logits of three later steps agree to the logit tolerance."""
+    cfg = HEAD128.replace(wdt="bf16", kvdt="bf16", cap=128)
+    prompt = synth.prompt(cfg, 40)
+    a = DecodeModel(cfg, DEV)
+    a.prefill(prompt, 0)
+    b = DecodeModel(cfg, DEV)
+    for p, t in enumerate(prompt):
+        b.step(int(t), p, want_logits=(p == len(prompt) - 1))
+    torch.cuda.synchronize()
+    assert np.abs(to_host(a.logits) - to_host(b.logits)).max() <= 2e-2
+    feed = int(b.next.item())
+    for i in range(3):
+        la, _ = a.step(feed, 40 + i)
+        lb, nb = b.step(feed, 40 + i)
+        torch.cuda.synchronize()
+        assert np.abs(to_host(la) - to_host(lb)).max() <= 2e-2
+        feed = int(nb.item())
+
+
+def test_prefill_refuses_before_launch():
+    cfg = HEAD128.replace(wdt="bf16", kvdt="bf16", cap=64)
+    gm = DecodeModel(cfg, DEV)
+    b = k2.k2_prefill_workspace_bytes(gm.model.cfg, 8)
+    assert b > 0
+    ws = torch.zeros(b, dtype=torch.uint8, device=DEV)
+    gm.logits.fill_(7.0)
+    assert k2.k2_prefill(gm.model, [1] * 8, 8, 60, gm.logits, gm.next, ws, b) == k2.K2_ERANGE
+    assert k2.k2_prefill(gm.model, [1] * 7 + [cfg.vocab], 8, 0, gm.logits, gm.next, ws, b) == k2.K2_ERANGE
+    assert k2.k2_prefill(gm.model, [1] * 8, 8, 0, gm.logits, gm.next, ws, b - 256) == k2.K2_EINVAL
+    assert k2.k2_prefill(gm.model, [1], 1, 0, gm.logits, gm.next, ws, b) == k2.K2_EUNSUPPORTED
+    assert k2.k2_prefill(gm.model, [1] * 33, 33, 0, gm.logits, gm.next, ws, b) == k2.K2_EUNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(gm.logits == 7.0)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_k2h_bf16_prefill_full_depth():
+    """The 3.7B-shaped bf16 model at full size: a 40-position prompt through
+    k2_prefill (32 + 8), then two decode steps, against the oracle."""
+    cfg = synth.K2H_BF16
+    _prefill_parity(cfg, 40, 2)
