@@ -21,7 +21,7 @@ int attn_splits(int n_kv, int len, int *chunk)
     return (len + c - 1) / c;
 }
 
-static int attn_max_splits(int n_kv, int cap)
+int attn_max_splits(int n_kv, int cap)
 {
     int target = K2_ATTN_TARGET_BLOCKS / n_kv;
     if (target < 1) target = 1;

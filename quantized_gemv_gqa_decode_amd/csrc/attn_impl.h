@@ -1145,6 +1145,85 @@ __global__ __launch_bounds__(ATT_NT) void attn_kernel(const AttnArgs a)
     K2_ATRACE_FLUSH();
 }
 
+// Attention of T consecutive query positions (a prefill chunk) in one
+// launch, grid (S, n_kv, T): slice t (blockIdx.z) is the query of position
+// a.len - T + t over [0, that position] -- the chunk's K/V rows are already
+// in the cache and q is already rotated (rope_append_rows_kernel).  Every
+// slice has its own split count S_t <= gridDim.x (blocks past it exit at
+// once), its own partials and its own arrival counters; within a slice the
+// blocks run exactly as in attn_kernel.
+template <int KVDT, int HD, int REP>
+__global__ __launch_bounds__(ATT_NT) void attn_rows_kernel(const AttnArgs a0, int n_rows, int64_t part_stride,
+                                                           int64_t ml_stride)
+{
+    extern __shared__ float4 lds4[];
+    float *smem = reinterpret_cast<float *>(lds4);
+    __shared__ int last;
+    const int t = blockIdx.z, g = blockIdx.y, s = blockIdx.x;
+    AttnArgs a = a0;
+    a.len = a0.len - (n_rows - 1 - t);
+    a.pos = a.len - 1;
+    const int S = (a.len + a.chunk - 1) / a.chunk;
+    if (s >= S) return;
+    a.S = S;
+    a.q = a0.q + (int64_t)t * a0.n_qh * HD;
+    a.out = a0.out + (int64_t)t * a0.n_qh * HD;
+    a.part = a0.part + t * part_stride;
+    a.part_ml = a0.part_ml + t * ml_stride;
+    a.head_cnt = a0.head_cnt + (int64_t)t * a0.n_kv;
+    uint32_t kv_bits = 0u;
+    float kv_scale = 0.f;
+    attn_stream_block<KVDT, HD, REP, false, true>(a, g, s, S, smem, kv_bits, kv_scale);
+    if (S > 1) {
+        __builtin_amdgcn_s_waitcnt(0);             // this thread's partial stores completed
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned old = __hip_atomic_fetch_add(a.head_cnt + g, 1u, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+            last = old == (unsigned)S - 1;
+            if (last) __hip_atomic_store(a.head_cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (last) attn_combine_block<HD, REP, true, ATT_NT>(a, g, smem);
+    }
+}
+
+// RoPE and cache append for the T rows of a prefill chunk, grid (n_kv, T),
+// K2_BLOCK threads: block (g, t) takes row t of qkv [T][(n_qh + 2 n_kv) HD]
+// at position pos0 + t, rotates the REP query heads of kv head g into
+// qrot [T][n_qh][HD] and k of head g, and stores k and v of head g at that
+// slot in the cache format (kv_store_head: the same encoding as every other
+// append).
+template <int KVDT, int HD>
+__global__ __launch_bounds__(K2_BLOCK) void rope_append_rows_kernel(const float *qkv, const float *cs,
+                                                                    float *qrot, void *kc, void *vc,
+                                                                    float *ks, float *vs, int n_qh,
+                                                                    int n_kv, int cap, int pos0)
+{
+    __shared__ float tmp4[K2_WAVES_PER_BLOCK];
+    constexpr int HALF = HD / 2;
+    const int g = blockIdx.x, t = blockIdx.y, tid = threadIdx.x, rep = n_qh / n_kv;
+    const int pos = pos0 + t;
+    const float *row = qkv + (int64_t)t * (n_qh + 2 * n_kv) * HD;
+    const float *csp = cs + (int64_t)pos * HALF * 2;
+    for (int e = tid; e < rep * HD; e += K2_BLOCK) {
+        const int h = g * rep + e / HD, d = e % HD, i = d % HALF;
+        const float *u = row + (int64_t)h * HD;
+        const float c = csp[i * 2], sn = csp[i * 2 + 1], x0 = u[i], x1 = u[i + HALF];
+        qrot[((int64_t)t * n_qh + h) * HD + d] = d < HALF ? x0 * c - x1 * sn : x0 * sn + x1 * c;
+    }
+    float val = 0.f;
+    if (tid < HD) {
+        const float *u = row + (int64_t)(n_qh + g) * HD;
+        const int i = tid % HALF;
+        const float c = csp[i * 2], sn = csp[i * 2 + 1], x0 = u[i], x1 = u[i + HALF];
+        val = tid < HALF ? x0 * c - x1 * sn : x0 * sn + x1 * c;
+    } else if (tid < 2 * HD) {
+        val = row[(int64_t)(n_qh + n_kv + g) * HD + tid - HD];
+    }
+    kv_store_head<KVDT, HD>(val, kc, vc, ks, vs, g, cap, pos, tmp4);
+}
+
 // Standalone store of one position (k, v already rotated), grid = n_kv.
 template <int KVDT, int HD>
 __global__ __launch_bounds__(K2_BLOCK) void kv_append_kernel(const float *k, const float *v,

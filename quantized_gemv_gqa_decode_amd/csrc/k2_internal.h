@@ -79,8 +79,20 @@ struct AttnArgs {
 size_t attn_ws_bytes(int n_qh, int n_kv, int hd, int cap);
 int attn_splits(int n_kv, int len, int *chunk);
 int attn_splits_fine(int n_kv, int cap, int len, int *chunk);
+int attn_max_splits(int n_kv, int cap);
 int attn_launch(int kvdt, int hd, int rep, bool fused, const AttnArgs &a, hipStream_t st);
 int device_cus();
+
+// A prefill chunk's attention: RoPE and cache append of the T rows of qkv
+// ([T][(n_qh + 2 n_kv) hd], positions pos0 ..), then every row's query over
+// the cache up to its own position, in one launch (out [T][n_qh][hd];
+// qrot [T][n_qh][hd] scratch).  ws: attn_rows_ws_bytes, zero-filled before
+// its first use.  K2_EUNSUPPORTED (nothing enqueued) unless hd = 128 and
+// n_qh / n_kv is 1, 2, 4 or 8.
+size_t attn_rows_ws_bytes(int n_qh, int n_kv, int hd, int cap, int T);
+int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qrot, float *out, void *kc,
+                     void *vc, float *ks, float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T,
+                     void *ws, hipStream_t st);
 
 // Sync words of the attention + O launch (one 256-byte line each; the ready
 // flag is replicated so that the O blocks' polling spreads over channels).

@@ -20,6 +20,9 @@
 //   6. H += W_d ACT                                      (matrix cores, add)
 // then the final norm, lm_head and first-maximum argmax of the LAST row only
 // (the GEMV of the decode step).
+#include <stdlib.h>
+#include <string.h>
+
 #include "k2_dev.h"
 #include "k2_internal.h"
 
@@ -42,8 +45,8 @@ __global__ void embed_rows_kernel(const PfTokens tk, int embdt, const void *E, i
 }
 
 struct PrefillWs {
-    float *h, *x, *qkv, *o, *act, *part;
-    void *attn, *am;
+    float *h, *x, *qkv, *o, *act, *part, *qrot;
+    void *attn, *rows, *am;
     int32_t *next;
 };
 
@@ -72,6 +75,7 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base)
     // counters, the argmax's) come first, at offsets that do not depend on T:
     // a workspace sized for one T serves every smaller T
     char *attn = take(attn_ws_bytes(c->n_qh, c->n_kv, c->head_dim, c->cap));
+    char *rows = take(attn_rows_ws_bytes(c->n_qh, c->n_kv, c->head_dim, c->cap, PF_MAX_T));
     char *am = take(argmax_ws_bytes());
     char *nx = take(4);
     char *h = take((size_t)T * c->hidden * 4);
@@ -80,7 +84,10 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base)
     char *o = take((size_t)T * qd * 4);
     char *act = take((size_t)T * c->inter * 4);
     char *part = take(pf_part_bytes(c, T));
+    char *qrot = take((size_t)T * qd * 4);
     if (w) {
+        w->rows = rows;
+        w->qrot = (float *)qrot;
         w->h = (float *)h;
         w->x = (float *)x;
         w->qkv = (float *)qkv;
@@ -104,6 +111,13 @@ static int pf_shape_ok(const k2_config *c)
         !dense_mfma_ok(2 * c->inter, c->hidden) || !dense_mfma_ok(c->hidden, c->inter))
         return K2_EUNSUPPORTED;
     return K2_OK;
+}
+
+// K2_PREFILL_ROWS=0 runs the chunk's attention one position per launch
+static bool chunk_attn_off()
+{
+    const char *e = getenv("K2_PREFILL_ROWS");
+    return e && strcmp(e, "0") == 0;
 }
 
 static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos0, float *logits,
@@ -135,6 +149,8 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
                        H, w.h);
     K2_CHECK_LAUNCH();
 
+    // the chunk's attention as one launch (hd 128), else per position
+    const bool rows_ok = !chunk_attn_off();
     AttnArgs at{};
     attn_ws_carve(w.attn, c->n_qh, c->n_kv, hd, c->cap, at);
     at.cos_sin = m->rope;
@@ -152,7 +168,11 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
         at.vc = L->vc;
         at.ks = L->ks;
         at.vs = L->vs;
-        for (int t = 0; t < T; ++t) {
+        rc = rows_ok ? attn_rows_launch(c->kvdt, w.qkv, m->rope, w.qrot, w.o, L->kc, L->vc, L->ks, L->vs,
+                                        c->n_qh, c->n_kv, hd, c->cap, pos0, T, w.rows, st)
+                     : K2_EUNSUPPORTED;
+        if (rc && rc != K2_EUNSUPPORTED) return rc;
+        for (int t = 0; rc == K2_EUNSUPPORTED && t < T; ++t) {
             at.qkv = w.qkv + (int64_t)t * qkv_rows;
             at.out = w.o + (int64_t)t * qd;
             at.pos = pos0 + t;

@@ -275,6 +275,15 @@ def test_head128_prefill_matches_oracle(kvdt, P):
     _prefill_parity(cfg, P, 3)
 
 
+@pytest.mark.parametrize("kvdt", ["bf16", "i8"])
+def test_head128_prefill_per_position_attention(kvdt, monkeypatch):
+    """The chunk's attention one position per launch (K2_PREFILL_ROWS=0),
+    the form used before the one-launch chunk attention: same parity bar."""
+    monkeypatch.setenv("K2_PREFILL_ROWS", "0")
+    cfg = HEAD128.replace(wdt="bf16", kvdt=kvdt, cap=128)
+    _prefill_parity(cfg, 70, 2)
+
+
 def test_prefill_equals_decode_steps_on_cache():
     """The caches a prefill writes decode the same next positions as the
     caches of position-by-position decode, within the bf16 cache's rounding:
