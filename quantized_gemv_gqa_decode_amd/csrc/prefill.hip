@@ -172,7 +172,8 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
                                         c->n_qh, c->n_kv, hd, c->cap, pos0, T, w.rows, st)
                      : K2_EUNSUPPORTED;
         if (rc && rc != K2_EUNSUPPORTED) return rc;
-        for (int t = 0; rc == K2_EUNSUPPORTED && t < T; ++t) {
+        const bool per_position = rc == K2_EUNSUPPORTED;
+        for (int t = 0; per_position && t < T; ++t) {
             at.qkv = w.qkv + (int64_t)t * qkv_rows;
             at.out = w.o + (int64_t)t * qd;
             at.pos = pos0 + t;
