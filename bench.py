@@ -421,6 +421,44 @@ def bench_prefill(cfg, gm, P, args, stream):
     print(json.dumps(out), flush=True)
 
 
+def bench_verify(cfg, gm, P, args, stream):
+    """One draft-and-verify round: k2_verify of T positions right after the
+    prompt (the weights and lm_head read once for all T), timed with HIP
+    events over repeated rounds at the same positions.  T positions per round
+    is what the round yields when every draft is accepted (an upper bound;
+    with synthetic random weights there is no drafter to measure)."""
+    import torch
+    import synth
+    prompt = synth.prompt(cfg, P)
+    T = args.verify_chunk
+    gm.prefill(prompt, 0)
+    torch.cuda.synchronize()
+    feed = [int(gm.next.item())] + [int(t) for t in synth.prompt(cfg, T - 1)]
+    gm.verify(feed, P)                               # warm
+    torch.cuda.synchronize()
+    reps = 16
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(reps):
+        gm.verify(feed, P)
+    e.record(stream)
+    e.synchronize()
+    ms = s.elapsed_time(e) / reps
+    wb = gm.weight_bytes()
+    out = {
+        "metric": "batched greedy verification: positions verified per second (all drafts accepted)",
+        "value": round(T / (ms * 1e-3), 1), "unit": "positions/s", "n_gpus": 1, "steps": reps,
+        "warmup": 1, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 activations (bf16 hi+lo on the matrix cores)",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "prompt_len": P, "positions_per_round": T,
+                   "weights": cfg.wdt, "kv_cache": cfg.kvdt},
+        "weight_GBps": round(wb / (ms * 1e-3) / 1e9, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def copy_probe(mib: int):
     """Five launches of an elementwise fp32 copy (y = x * 1) over mib MiB:
     each reads and writes exactly mib MiB.  Profiler counters of these
@@ -457,6 +495,9 @@ def main():
     ap.add_argument("--prefill-chunk", type=int, default=0, metavar="T",
                     help="instead of the decode bench: time the prompt's prefill through "
                          "k2_prefill in chunks of T positions (2..32; bf16 weights)")
+    ap.add_argument("--verify-chunk", type=int, default=0, metavar="T",
+                    help="instead of the decode bench: time k2_verify of T positions (2..32; "
+                         "bf16 weights) after the prompt, i.e. one draft-and-verify round")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the decode bench: launch a plain fp32 copy kernel over "
                          "MIB MiB five times (the known-size reference that scales the HBM "
@@ -504,6 +545,8 @@ def main():
 
     if args.prefill_chunk:
         return bench_prefill(cfg, gm, P, args, stream)
+    if args.verify_chunk:
+        return bench_verify(cfg, gm, P, args, stream)
 
     if args.prefix:
         if cfg.kvdt != "i8":

@@ -310,6 +310,23 @@ size_t k2_prefill_workspace_bytes(const k2_config *cfg, int T);
 int k2_prefill(const k2_model *m, const int32_t *tokens, int T, int pos0, float *logits,
                int32_t *next_token, void *ws, size_t ws_bytes, void *stream);
 
+/* Batched greedy verification of T positions in one sweep (speculative
+ * decoding: the pages' drafter proposes tokens and one pass over the
+ * weights checks them all): the k2_prefill computation, plus the final norm,
+ * the lm_head (matrix cores) and the first-maximum argmax of EVERY row.
+ * next_tokens[t] (device int32 [T], required) is the greedy token after
+ * position pos0 + t, the same as a k2_decode_step at that position would
+ * give up to rounding; logits (nullable, device [T][vocab]) receives every
+ * row's logits.  A caller feeding [last accepted, d_1 .. d_{T-1}] accepts
+ * d_i while d_i == next_tokens[i - 1]; cache slots past the accepted ones
+ * are simply written again by later calls.  ws: k2_verify_workspace_bytes
+ * (it includes the lm_head partials and a logits buffer), zero-filled
+ * before its first use.  Same refusals as k2_prefill; K2_EINVAL without
+ * next_tokens. */
+size_t k2_verify_workspace_bytes(const k2_config *cfg, int T);
+int k2_verify(const k2_model *m, const int32_t *tokens, int T, int pos0, float *logits,
+              int32_t *next_tokens, void *ws, size_t ws_bytes, void *stream);
+
 /* One decode position: embed `token` (host int), run every layer at `pos`
  * (its K and V are stored at slot pos before attending), then, when `logits`
  * is non-NULL, the final norm, the lm_head and the argmax.  logits: [vocab]

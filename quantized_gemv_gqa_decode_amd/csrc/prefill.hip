@@ -45,10 +45,21 @@ __global__ void embed_rows_kernel(const PfTokens tk, int embdt, const void *E, i
 }
 
 struct PrefillWs {
-    float *h, *x, *qkv, *o, *act, *part, *qrot;
+    float *h, *x, *qkv, *o, *act, *part, *qrot, *lm_part, *logits;
     void *attn, *rows, *am;
     int32_t *next;
 };
+
+// First maximum of every row of x [rows][n] (one block per row).
+__global__ __launch_bounds__(K2_BLOCK) void argmax_rows_kernel(const float *x, int n, int32_t *out)
+{
+    const float *r = x + (int64_t)blockIdx.x * n;
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int i = threadIdx.x; i < n; i += K2_BLOCK) argmax_pair_max(bv, bi, r[i], i);
+    argmax_block(bv, bi);
+    if (threadIdx.x == 0) out[blockIdx.x] = bi;
+}
 
 static size_t pf_part_bytes(const k2_config *c, int T)
 {
@@ -61,7 +72,9 @@ static size_t pf_part_bytes(const k2_config *c, int T)
     return m;
 }
 
-static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base)
+// verify: also the lm_head of every row (matrix-core partials and, for a
+// caller that passes no logits buffer, the [T][vocab] logits)
+static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base, bool verify = false)
 {
     const size_t qkv_rows = (size_t)(c->n_qh + 2 * c->n_kv) * c->head_dim, qd = (size_t)c->n_qh * c->head_dim;
     size_t off = 0;
@@ -85,7 +98,11 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base)
     char *act = take((size_t)T * c->inter * 4);
     char *part = take(pf_part_bytes(c, T));
     char *qrot = take((size_t)T * qd * 4);
+    char *lm_part = verify ? take(dense_mfma_ws_bytes(c->vocab, c->hidden, T)) : nullptr;
+    char *lgt = verify ? take((size_t)T * c->vocab * 4) : nullptr;
     if (w) {
+        w->lm_part = (float *)lm_part;
+        w->logits = (float *)lgt;
         w->rows = rows;
         w->qrot = (float *)qrot;
         w->h = (float *)h;
@@ -103,9 +120,10 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base)
 
 // Shapes this path handles (K2_EUNSUPPORTED otherwise): bf16 projection
 // weights whose products the matrix-core kernel takes.
-static int pf_shape_ok(const k2_config *c)
+static int pf_shape_ok(const k2_config *c, bool verify = false)
 {
     if (c->wdt != K2_BF16) return K2_EUNSUPPORTED;
+    if (verify && !dense_mfma_ok(c->vocab, c->hidden)) return K2_EUNSUPPORTED;
     const int qkv_rows = (c->n_qh + 2 * c->n_kv) * c->head_dim, qd = c->n_qh * c->head_dim;
     if (!dense_mfma_ok(qkv_rows, c->hidden) || !dense_mfma_ok(c->hidden, qd) ||
         !dense_mfma_ok(2 * c->inter, c->hidden) || !dense_mfma_ok(c->hidden, c->inter))
@@ -120,17 +138,19 @@ static bool chunk_attn_off()
     return e && strcmp(e, "0") == 0;
 }
 
+// verify: logits [T][vocab] (nullable: kept in the workspace) and next [T]
+// (required) for every row; else logits [vocab] and next of the last row.
 static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos0, float *logits,
-                        int32_t *next, void *ws, size_t ws_bytes, hipStream_t st)
+                        int32_t *next, void *ws, size_t ws_bytes, bool verify, hipStream_t st)
 {
     int rc = k2_model_check(m);
     if (rc) return rc;
     const k2_config *c = &m->cfg;
     if (T < 2 || T > PF_MAX_T) return K2_EUNSUPPORTED;
-    if (!tokens) return K2_EINVAL;
-    if ((rc = pf_shape_ok(c))) return rc;
+    if (!tokens || (verify && !k2_ptr_ok(next))) return K2_EINVAL;
+    if ((rc = pf_shape_ok(c, verify))) return rc;
     if (logits && !k2_aligned16(logits)) return K2_EINVAL;
-    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pf_layout(c, T, nullptr, nullptr)) return K2_EINVAL;
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pf_layout(c, T, nullptr, nullptr, verify)) return K2_EINVAL;
     if (pos0 < 0 || (int64_t)pos0 + T > c->cap) return K2_ERANGE;
     PfTokens tk{};
     for (int t = 0; t < T; ++t) {
@@ -139,7 +159,7 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
     }
 
     PrefillWs w;
-    pf_layout(c, T, &w, ws);
+    pf_layout(c, T, &w, ws, verify);
     const int H = c->hidden, hd = c->head_dim, I = c->inter, rep = c->n_qh / c->n_kv;
     const int qkv_rows = (c->n_qh + 2 * c->n_kv) * hd, qd = c->n_qh * hd;
 
@@ -189,7 +209,15 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
             return rc;
     }
 
-    if (logits) {
+    if (verify) {
+        // every row: final norm, lm_head on the matrix cores, first-maximum argmax
+        float *lg = logits ? logits : w.logits;
+        if ((rc = rmsnorm_rows_launch(w.h, m->g_final, w.x, T, H, c->groups, c->eps, st))) return rc;
+        if ((rc = dense_mfma((const uint16_t *)m->lm, w.x, lg, c->vocab, H, T, DM_EPI_PLAIN, w.lm_part, st)))
+            return rc;
+        hipLaunchKernelGGL(argmax_rows_kernel, dim3(T), dim3(K2_BLOCK), 0, st, lg, c->vocab, next);
+        K2_CHECK_LAUNCH();
+    } else if (logits) {
         ArgmaxArgs am{};
         argmax_ws_carve(w.am, am);
         GemvArgs lm{};
@@ -223,5 +251,18 @@ extern "C" size_t k2_prefill_workspace_bytes(const k2_config *cfg, int T)
 extern "C" int k2_prefill(const k2_model *m, const int32_t *tokens, int T, int pos0, float *logits,
                           int32_t *next_token, void *ws, size_t ws_bytes, void *stream)
 {
-    return prefill_impl(m, tokens, T, pos0, logits, next_token, ws, ws_bytes, k2_stream(stream));
+    return prefill_impl(m, tokens, T, pos0, logits, next_token, ws, ws_bytes, false, k2_stream(stream));
+}
+
+extern "C" size_t k2_verify_workspace_bytes(const k2_config *cfg, int T)
+{
+    if (!cfg || T < 2 || T > PF_MAX_T || pf_shape_ok(cfg, true)) return 0;
+    if (k2_decode_workspace_bytes(cfg) == 0) return 0;
+    return pf_layout(cfg, T, nullptr, nullptr, true);
+}
+
+extern "C" int k2_verify(const k2_model *m, const int32_t *tokens, int T, int pos0, float *logits,
+                         int32_t *next_tokens, void *ws, size_t ws_bytes, void *stream)
+{
+    return prefill_impl(m, tokens, T, pos0, logits, next_tokens, ws, ws_bytes, true, k2_stream(stream));
 }

@@ -83,6 +83,8 @@ SIGNATURES = {
     "k2_decode_step": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "k2_prefill_workspace_bytes": (_sz, [_vp, _i]),
     "k2_prefill": (_i, [_vp, _vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "k2_verify_workspace_bytes": (_sz, [_vp, _i]),
+    "k2_verify": (_i, [_vp, _vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "k2_decode_step_dev": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp]),
     "k2_moe_route_workspace_bytes": (_sz, [_i, _i]),
     "k2_moe_route": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
@@ -337,3 +339,14 @@ def k2_prefill(model, tokens, T, pos0, logits, next_token, ws, ws_bytes, stream=
     arr = (C.c_int32 * T)(*[int(t) for t in tokens])
     return load().k2_prefill(C.addressof(model), arr, T, pos0, ptr(logits), ptr(next_token), ptr(ws),
                              ws_bytes, stream_handle(stream))
+
+
+def k2_verify_workspace_bytes(cfg, T) -> int:
+    return load().k2_verify_workspace_bytes(C.addressof(cfg), T)
+
+
+def k2_verify(model, tokens, T, pos0, logits, next_tokens, ws, ws_bytes, stream=None):
+    """tokens: a host sequence of T ints; next_tokens: device int32 [T]."""
+    arr = (C.c_int32 * T)(*[int(t) for t in tokens])
+    return load().k2_verify(C.addressof(model), arr, T, pos0, ptr(logits), ptr(next_tokens), ptr(ws),
+                            ws_bytes, stream_handle(stream))

@@ -180,6 +180,52 @@ class DecodeModel:
                                        self._pf_ws.numel(), stream))
             i += T
 
+    def verify(self, tokens, pos0: int, logits: Optional[torch.Tensor] = None, stream=None):
+        """k2_verify of len(tokens) (2..32) positions from pos0: returns the
+        device int32 tensor of the greedy token after every position."""
+        T = len(tokens)
+        if not hasattr(self, "_vf_ws"):
+            b = k2.k2_verify_workspace_bytes(self.model.cfg, 32)
+            if b == 0:
+                raise k2.K2Error(k2.K2_EUNSUPPORTED)
+            self._vf_ws = torch.zeros(b, dtype=torch.uint8, device=self.device)
+            self._vf_next = torch.zeros(32, dtype=torch.int32, device=self.device)
+        k2.check(k2.k2_verify(self.model, tokens, T, pos0, logits, self._vf_next, self._vf_ws,
+                              self._vf_ws.numel(), stream))
+        return self._vf_next[:T]
+
+    def generate_speculative(self, prompt, n_decode: int, draft, k: int):
+        """Greedy decode with draft-and-verify: after the prompt (prefill),
+        each round feeds [last token, k drafted tokens] to k2_verify and keeps
+        the greedy tokens up to the first draft that disagrees.  draft(history,
+        k) returns k proposed tokens.  Returns (tokens, rounds); the tokens are
+        those of plain greedy decode."""
+        P = len(prompt)
+        n_decode = min(n_decode, self.cfg.cap - P)
+        self.prefill(prompt, 0)
+        torch.cuda.synchronize()
+        toks = [int(self.next.item())]
+        rounds = 0
+        while len(toks) < n_decode:
+            pos = P + len(toks) - 1                   # where the last token goes
+            kk = min(k, self.cfg.cap - 1 - pos, 31)
+            if kk < 1:
+                lg, nx = self.step(toks[-1], pos)
+                torch.cuda.synchronize()
+                toks.append(int(nx.item()))
+                rounds += 1
+                continue
+            d = [int(t) for t in draft(list(prompt) + toks, kk)]
+            g = self.verify([toks[-1]] + d, pos).cpu().numpy().tolist()
+            rounds += 1
+            new = [g[0]]
+            for i in range(1, kk + 1):
+                if d[i - 1] != new[-1]:
+                    break
+                new.append(g[i])
+            toks.extend(new[:n_decode - len(toks)])
+        return toks, rounds
+
     def step_dev(self, d_token: torch.Tensor, pos: int, d_next: torch.Tensor,
                  d_err: Optional[torch.Tensor] = None, want_logits: bool = True, stream=None):
         lg = self.logits if want_logits else None

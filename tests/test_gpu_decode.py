@@ -329,3 +329,76 @@ def test_k2h_bf16_prefill_full_depth():
     k2_prefill (32 + 8), then two decode steps, against the oracle."""
     cfg = synth.K2H_BF16
     _prefill_parity(cfg, 40, 2)
+
+
+# ------------------------------------------------------- batched verification ---
+
+def test_head128_verify_every_row_matches_oracle():
+    """k2_verify of 12 positions fed the oracle's own tokens: every row's
+    logits and greedy token against the oracle at that position."""
+    cfg = HEAD128.replace(wdt="bf16", kvdt="bf16", cap=128)
+    P = 20
+    prompt = synth.prompt(cfg, P)
+    dec = oracle.Decoder.from_synth(cfg)
+    ref_toks, ref_lg = dec.generate(prompt, 12)
+    gm = DecodeModel(cfg, DEV)
+    gm.prefill(prompt[:-1], 0)
+    feed = [int(prompt[-1])] + ref_toks[:11]
+    lg = torch.empty((12, cfg.vocab), dtype=torch.float32, device=DEV)
+    nxt = gm.verify(feed, P - 1, lg)
+    torch.cuda.synchronize()
+    got = to_host(lg).astype(np.float64)
+    nx = to_host(nxt).tolist()
+    for i in range(12):
+        err = float(np.abs(got[i] - ref_lg[i]).max())
+        assert err <= tol_for(cfg), (i, err)
+        assert near_tie_ok(nx[i], ref_lg[i], tie_gap(err)), (i, nx[i], int(np.argmax(ref_lg[i])))
+
+
+@pytest.mark.parametrize("kvdt", ["bf16", "i8"])
+@pytest.mark.parametrize("mode", ["exact", "wrong", "half"])
+def test_head128_speculative_decode_equals_greedy(kvdt, mode):
+    """Draft-and-verify greedy decode gives the oracle's greedy tokens
+    whatever the drafts: all right (every draft accepted), all wrong (one
+    token per round), or right every other round."""
+    cfg = HEAD128.replace(wdt="bf16", kvdt=kvdt, cap=128)
+    P, n = 16, 40
+    prompt = synth.prompt(cfg, P)
+    dec = oracle.Decoder.from_synth(cfg)
+    ref_toks, ref_lg = dec.generate(prompt, n + 8)
+    calls = [0]
+
+    def draft(history, k):
+        calls[0] += 1
+        done = len(history) - P
+        true = (ref_toks[done:done + k] + [0] * k)[:k]
+        if mode == "exact" or (mode == "half" and calls[0] % 2 == 0):
+            return true
+        return [(t + 1) % cfg.vocab for t in true]
+
+    gm = DecodeModel(cfg, DEV)
+    toks, rounds = gm.generate_speculative(prompt, n, draft, 7)
+    for i, (a, b) in enumerate(zip(toks, ref_toks)):
+        if a != b:
+            assert near_tie_ok(a, ref_lg[i], 1e-3), (i, a, b)
+            say(f"speculative run diverged at {i} on a near-tie")
+            return
+    assert len(toks) == n
+    if mode == "exact":
+        assert rounds <= (n + 7) // 8 + 1
+    if mode == "wrong":
+        assert rounds == n - 1
+    say(f"{mode}: {n} tokens in {rounds} rounds")
+
+
+def test_verify_refusals():
+    cfg = HEAD128.replace(wdt="bf16", kvdt="bf16", cap=64)
+    gm = DecodeModel(cfg, DEV)
+    b = k2.k2_verify_workspace_bytes(gm.model.cfg, 8)
+    assert b > k2.k2_prefill_workspace_bytes(gm.model.cfg, 8)
+    ws = torch.zeros(b, dtype=torch.uint8, device=DEV)
+    nx = torch.zeros(8, dtype=torch.int32, device=DEV)
+    assert k2.k2_verify(gm.model, [1] * 8, 8, 0, None, None, ws, b) == k2.K2_EINVAL
+    assert k2.k2_verify(gm.model, [1] * 8, 8, 60, None, nx, ws, b) == k2.K2_ERANGE
+    assert k2.k2_verify(gm.model, [1] * 8, 8, 0, None, nx, ws, b - 256) == k2.K2_EINVAL
+    assert k2.k2_verify(gm.model, [1], 1, 0, None, nx, ws, b) == k2.K2_EUNSUPPORTED
