@@ -561,10 +561,15 @@ def main():
     else:
         prompt = synth.prompt(cfg, P)
         t0 = time.perf_counter()
-        for p, t in enumerate(prompt):
-            gm.step(int(t), p, want_logits=(p == P - 1))
+        if cfg.wdt == "bf16" and P >= 2:
+            gm.prefill(prompt, 0, chunk=32)          # k2_prefill, 32 positions per call
+            how = "k2_prefill, chunks of 32"
+        else:
+            for p, t in enumerate(prompt):
+                gm.step(int(t), p, want_logits=(p == P - 1))
+            how = "as decode steps"
         torch.cuda.synchronize()
-        log(f"prefill of {P} positions (as decode steps) in {time.perf_counter() - t0:.2f} s")
+        log(f"prefill of {P} positions ({how}) in {time.perf_counter() - t0:.2f} s")
 
     hist = torch.zeros(W + K + 1, dtype=torch.int32, device=dev)
     hist[0:1].copy_(gm.next)
