@@ -41,11 +41,11 @@ WRITE_SCALE = 1073741824 / (1048576.0 * 1024)
 GEMV_BF16_SOURCES = ("k2_dev.h", "k2_internal.h", "gemv_impl.h", "gemv.hip", "gemv_bf16.hip")
 PMC_TRAFFIC = {
     "k2h-3.7b-bf16-kvbf16-ctx4096": {
-        "sources": GEMV_BF16_SOURCES, "digest": "d49fef0dad99b732",
+        "sources": GEMV_BF16_SOURCES, "digest": "8fd6a2d01ae1ccef",
         "kib": {"qkv_norm_gemv": (15489.5, 24.0), "o_gemv_residual": (10377.6, 20.0),
                 "gate_up_norm_gemv_swiglu": (51351.0, 40.0),
                 "down_gemv_residual": (25847.3, 20.0),
-                "lm_head_norm_gemv_argmax": (626726.0, 1237.4)}},
+                "lm_head_norm_gemv_argmax": (626725.4, 1237.5)}},
 }
 
 
@@ -498,6 +498,8 @@ def main():
     ap.add_argument("--verify-chunk", type=int, default=0, metavar="T",
                     help="instead of the decode bench: time k2_verify of T positions (2..32; "
                          "bf16 weights) after the prompt, i.e. one draft-and-verify round")
+    ap.add_argument("--prefill-steps", action="store_true",
+                    help="consume the prompt one decode step per position instead of k2_prefill")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the decode bench: launch a plain fp32 copy kernel over "
                          "MIB MiB five times (the known-size reference that scales the HBM "
@@ -561,7 +563,7 @@ def main():
     else:
         prompt = synth.prompt(cfg, P)
         t0 = time.perf_counter()
-        if cfg.wdt == "bf16" and P >= 2:
+        if cfg.wdt == "bf16" and P >= 2 and not args.prefill_steps:
             gm.prefill(prompt, 0, chunk=32)          # k2_prefill, 32 positions per call
             how = "k2_prefill, chunks of 32"
         else:
