@@ -240,6 +240,34 @@ int k2_rope_append_attn_o(k2_dtype kvdt, const float *qkv, const float *cos_sin,
                           const void *Wo_s, float *h, int hidden, void *ws, size_t ws_bytes,
                           int32_t *d_err, void *stream);
 
+/* Seeded sampling of one token from logits [vocab] ([k2-burn] "Project
+ * layout": sampling.rs -- temperature / top-k / top-p / min-p / repetition
+ * penalty; the order is the conventional one, the pages give none):
+ * repetition penalty r on the distinct ids of prev (l > 0 -> l / r, else
+ * l * r), temperature, top-k (ties: lower id first), softmax, top-p (the
+ * shortest prefix whose probability reaches top_p), min-p (keep p >=
+ * min_p * max p), then the first kept token whose cumulative probability
+ * exceeds u * the kept total, u = (word 0 of Philox4x32-10(counter = (counter
+ * lo, counter hi, 0, 0), key = (seed lo, seed hi))) >> 8) * 2^-24.
+ * logits: device float [vocab], vocab <= 262144, read only; prev: device
+ * int32 [n_prev] (nullable when n_prev = 0); out_token: device int32.
+ * sp (host): 0 < temperature, 1 <= top_k <= 64, 0 < top_p <= 1,
+ * 0 <= min_p < 1, repetition_penalty >= 1 (K2_EINVAL / K2_EUNSUPPORTED
+ * otherwise); n_prev <= 64.  Greedy decoding is k2_argmax.  ws: device,
+ * k2_sample_workspace_bytes(vocab) bytes, 256-byte aligned (no state kept
+ * between calls). */
+typedef struct {
+    float temperature;
+    int top_k;
+    float top_p;
+    float min_p;
+    float repetition_penalty;
+} k2_sampling;
+size_t k2_sample_workspace_bytes(int vocab);
+int k2_sample(const float *logits, int vocab, const k2_sampling *sp, const int32_t *prev, int n_prev,
+              uint64_t seed, uint64_t counter, int32_t *out_token, void *ws, size_t ws_bytes,
+              void *stream);
+
 /* First-maximum argmax of x[0..n) ([k3_run.c] argmax_()): out_idx[0] is the
  * lowest index holding the largest value.  ws: k2_argmax_workspace_bytes(n)
  * bytes, zero-filled before first use (left zeroed on exit); calls that share

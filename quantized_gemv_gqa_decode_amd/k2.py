@@ -77,6 +77,8 @@ SIGNATURES = {
     "k2_rope_append_attn_o": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                                    _vp, _vp, _vp, _i, _vp, _sz, _vp, _vp]),
     "k2_argmax_workspace_bytes": (_sz, [_i]),
+    "k2_sample_workspace_bytes": (_sz, [_i]),
+    "k2_sample": (_i, [_vp, _i, _vp, _vp, _i, C.c_uint64, C.c_uint64, _vp, _vp, _sz, _vp]),
     "k2_argmax": (_i, [_vp, _i, _vp, _vp, _sz, _vp]),
     "k2_decode_workspace_bytes": (_sz, [_vp]),
     "k2_model_check": (_i, [_vp]),
@@ -350,3 +352,18 @@ def k2_verify(model, tokens, T, pos0, logits, next_tokens, ws, ws_bytes, stream=
     arr = (C.c_int32 * T)(*[int(t) for t in tokens])
     return load().k2_verify(C.addressof(model), arr, T, pos0, ptr(logits), ptr(next_tokens), ptr(ws),
                             ws_bytes, stream_handle(stream))
+
+
+class k2_sampling(C.Structure):
+    _fields_ = [("temperature", C.c_float), ("top_k", C.c_int), ("top_p", C.c_float),
+                ("min_p", C.c_float), ("repetition_penalty", C.c_float)]
+
+
+def k2_sample_workspace_bytes(vocab) -> int:
+    return load().k2_sample_workspace_bytes(vocab)
+
+
+def k2_sample(logits, vocab, sp: "k2_sampling", prev, n_prev, seed, counter, out_token, ws, ws_bytes,
+              stream=None):
+    return load().k2_sample(ptr(logits), vocab, C.addressof(sp), ptr(prev), n_prev, int(seed),
+                            int(counter), ptr(out_token), ptr(ws), ws_bytes, stream_handle(stream))

@@ -468,3 +468,46 @@ def test_argmax_first_max(n):
         check(k2.k2_argmax(to_dev(x), n, out, ws, ws_b))
         sync()
         assert int(out.item()) == oracle.argmax(x.astype(np.float64))
+
+
+# ---------------------------------------------------------------- sampling ---
+
+@pytest.mark.parametrize("vocab", [1000, 250624])
+@pytest.mark.parametrize("params", [
+    dict(temperature=1.0, top_k=64, top_p=1.0, min_p=0.0, repetition_penalty=1.0),
+    dict(temperature=0.7, top_k=40, top_p=0.9, min_p=0.05, repetition_penalty=1.3),
+    dict(temperature=1.5, top_k=8, top_p=0.5, min_p=0.0, repetition_penalty=1.1),
+    dict(temperature=0.3, top_k=1, top_p=1.0, min_p=0.0, repetition_penalty=2.0),
+])
+def test_sample_matches_oracle(vocab, params):
+    """k2_sample against the sampling oracle on the same logits, previous
+    ids, seed and counters: the same token, except where the oracle's
+    decision margin (a filter threshold or the draw within 1e-5 of a
+    cumulative boundary) is below what fp32 arithmetic can resolve."""
+    from oracle import sampling as S
+    rng = np.random.default_rng(vocab + params["top_k"])
+    lg = (rng.standard_normal(vocab) * 1.5).astype(np.float32)
+    lg[rng.integers(0, vocab, 5)] += 4.0                     # a few clear leaders
+    prev = rng.integers(0, vocab, 24).astype(np.int32)
+    prev[:4] = np.argsort(-lg)[:4]                           # penalise some of the leaders
+    sp = k2.k2_sampling(**params)
+    wsb = k2.k2_sample_workspace_bytes(vocab)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    X, P = to_dev(lg), to_dev(prev)
+    out = torch.zeros(64, dtype=torch.int32, device=DEV)
+    n = 64
+    for c in range(n):
+        check(k2.k2_sample(X, vocab, sp, P, prev.size, 1234, c, out[c:c + 1], ws, wsb))
+    sync()
+    got = to_host(out).tolist()
+    near = 0
+    for c in range(n):
+        want, margin = S.sample(lg.astype(np.float64), params["temperature"], params["top_k"],
+                                params["top_p"], params["min_p"], params["repetition_penalty"],
+                                prev.tolist(), 1234, c)
+        if got[c] != want:
+            assert margin < 1e-5, (c, got[c], want, margin)
+            near += 1
+    assert near <= 2, near
+    if params["top_k"] == 1:
+        assert len(set(got)) == 1
