@@ -459,6 +459,55 @@ def bench_verify(cfg, gm, P, args, stream):
     print(json.dumps(out), flush=True)
 
 
+def synth_config(name):
+    import synth
+    return synth.CONFIGS[name]
+
+
+def bench_sample(cfg):
+    """k2_sample on seeded N(0, 1.5) logits of the config's vocabulary: one
+    call per decode position, 200 calls with consecutive counters timed with
+    HIP events; every token is checked against the sampling oracle."""
+    import numpy as np
+    import torch
+    from quantized_gemv_gqa_decode_amd import k2
+    dev = torch.device("cuda:0")
+    k2.load(build_if_missing=False)
+    V = cfg.vocab
+    rng = np.random.default_rng(3)
+    lg = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    prev = rng.integers(0, V, 32).astype(np.int32)
+    X = torch.from_numpy(lg).to(dev)
+    P = torch.from_numpy(prev).to(dev)
+    sp = k2.k2_sampling(temperature=0.8, top_k=40, top_p=0.9, min_p=0.05, repetition_penalty=1.2)
+    wsb = k2.k2_sample_workspace_bytes(V)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    n = 200
+    out = torch.zeros(n, dtype=torch.int32, device=dev)
+    for c in range(8):
+        k2.check(k2.k2_sample(X, V, sp, P, 32, 5, c, out[c:c + 1], ws, wsb))
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for c in range(n):
+        k2.check(k2.k2_sample(X, V, sp, P, 32, 5, c, out[c:c + 1], ws, wsb))
+    e.record()
+    e.synchronize()
+    us = s.elapsed_time(e) / n * 1000
+    from oracle import sampling as S
+    got = out.cpu().numpy().tolist()
+    agree = sum(int(got[c] == S.sample(lg.astype(np.float64), 0.8, 40, 0.9, 0.05, 1.2, prev.tolist(),
+                                       5, c)[0]) for c in range(n))
+    print(json.dumps({"metric": "k2_sample calls per second", "value": round(1e6 / us, 1),
+                      "unit": "calls/s", "n_gpus": 1, "steps": n, "warmup": 8,
+                      "ms_per_step": round(us / 1000, 4), "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+                      "data": "synthetic", "config": {"workload": cfg.name, "vocab": V,
+                                                      "top_k": 40, "n_prev": 32},
+                      "us_per_call": round(us, 1), "oracle_agreement": f"{agree}/{n}"}))
+
+
 def copy_probe(mib: int):
     """Five launches of an elementwise fp32 copy (y = x * 1) over mib MiB:
     each reads and writes exactly mib MiB.  Profiler counters of these
@@ -498,6 +547,9 @@ def main():
     ap.add_argument("--verify-chunk", type=int, default=0, metavar="T",
                     help="instead of the decode bench: time k2_verify of T positions (2..32; "
                          "bf16 weights) after the prompt, i.e. one draft-and-verify round")
+    ap.add_argument("--sample", action="store_true",
+                    help="instead of the decode bench: time k2_sample over the config's vocabulary "
+                         "(temperature 0.8, top-k 40, top-p 0.9, min-p 0.05, penalty 1.2 on 32 ids)")
     ap.add_argument("--prefill-steps", action="store_true",
                     help="consume the prompt one decode step per position instead of k2_prefill")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -517,6 +569,8 @@ def main():
 
     if args.copy_probe:
         return copy_probe(args.copy_probe)
+    if args.sample:
+        return bench_sample(synth_config(args.config))
 
     import synth
     from quantized_gemv_gqa_decode_amd import k2

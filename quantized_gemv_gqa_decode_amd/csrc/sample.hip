@@ -11,20 +11,23 @@
 // al., SC 2011), the same 24-bit value everywhere.
 //
 // The penalty never raises a logit, so the top-k after it lies among the
-// top k + n_prev raw logits: a selection round keeps the best 128 of every
-// 2048-wide slice (bitonic sort in LDS); two rounds leave at most 2048
-// survivors, which one block sorts before doing the rest on at most 128
-// candidates.
+// top kk = k + n_prev raw logits (kk <= 128).  Selection is a radix select,
+// not a sort: logits map to order-preserving 32-bit keys, four passes pick the
+// key of the kk-th largest one 8-bit digit at a time (a 256-bin LDS histogram
+// and one wave's scan per pass), and a second select on the inverted ids
+// breaks ties at that key in favour of lower ids.  Every 2048-wide slice keeps
+// its kk best (one block each), one block selects the kk best of those, and
+// one wave sorts them in registers and does the rest with wave scans.
 #include "k2_dev.h"
 
 namespace k2 {
 
-constexpr int SP_SLICE = 2048;             // values per selection block
-constexpr int SP_KEEP = 128;               // survivors per slice (>= top_k + n_prev)
-constexpr int SP_NT = 1024;
-constexpr int SP_FINAL_NT = 1024;
-constexpr int SP_MAX_SLICES = 128;         // vocab <= 262144: two selection rounds leave <= 2048
-constexpr int SP_MAX_K = 64, SP_MAX_PREV = 64;
+constexpr int SP_SLICE = 2048;             // logits per selection block
+constexpr int SP_NT = 256, SP_PER = SP_SLICE / SP_NT;
+constexpr int SP_FINAL_NT = 1024, SP_FINAL_PER = 16;
+constexpr int SP_MAX_SLICES = 128;         // vocab <= 262144: <= 128 * 128 candidates
+constexpr int SP_MAX_K = 64, SP_MAX_PREV = 64, SP_MAX_KK = 128;
+static_assert(SP_MAX_SLICES * SP_MAX_KK <= SP_FINAL_NT * SP_FINAL_PER, "final block holds every candidate");
 
 // a sorts before b: larger value, then lower id
 __device__ __forceinline__ bool sp_before(float av, int ai, float bv, int bi)
@@ -32,48 +35,143 @@ __device__ __forceinline__ bool sp_before(float av, int ai, float bv, int bi)
     return av > bv || (av == bv && ai < bi);
 }
 
-// Bitonic sort of n (a power of two) (value, id) pairs in LDS, best first.
-__device__ void sp_bitonic(float *v, int *id, int n)
+// float -> unsigned key with the same order (-0 taken as +0); and back
+__device__ __forceinline__ uint32_t sp_key(float x)
 {
-    for (int k = 2; k <= n; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < n; i += blockDim.x) {
-                const int l = i ^ j;
-                if (l > i) {
-                    const bool first = (i & k) == 0;
-                    const bool sw = first ? sp_before(v[l], id[l], v[i], id[i])
-                                          : sp_before(v[i], id[i], v[l], id[l]);
-                    if (sw) {
-                        const float tv = v[i]; v[i] = v[l]; v[l] = tv;
-                        const int ti = id[i]; id[i] = id[l]; id[l] = ti;
+    uint32_t u = __float_as_uint(x);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float sp_val(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+struct SpLds {
+    int hist[2][256];
+    int digit[4], need[4], eq[4];
+    int slot, dup;
+};
+
+// The need-th largest key among the live elements of the block (1 <= need <=
+// their number), 8 bits per pass from the top.  On return n_above = how many
+// live keys exceed it and n_eq how many equal it.  Expects s.hist[0] zeroed
+// and visible; leaves it so.
+template <int NT, int PER>
+__device__ uint32_t sp_select(const uint32_t (&key)[PER], const bool (&live)[PER], int need, SpLds &s,
+                              int &n_above, int &n_eq)
+{
+    const int want = need;
+    uint32_t prefix = 0u, mask = 0u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int shift = 24 - 8 * p;
+        int *h = s.hist[p & 1];
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            if (live[j] && (key[j] & mask) == prefix) atomicAdd(&h[(key[j] >> shift) & 255u], 1);
+        for (int b = threadIdx.x; b < 256; b += NT) s.hist[(p + 1) & 1][b] = 0;
+        __syncthreads();
+        if (threadIdx.x < 64) {
+            // lane l holds bins 255 - 4l .. 252 - 4l; an inclusive scan from the top bin
+            const int lane = threadIdx.x, g0 = 255 - 4 * lane;
+            const int c0 = h[g0], c1 = h[g0 - 1], c2 = h[g0 - 2], c3 = h[g0 - 3];
+            const int tot = c0 + c1 + c2 + c3;
+            int inc = tot;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(inc, o, 64);
+                if (lane >= o) inc += y;
+            }
+            const int exc = inc - tot;
+            if (exc < need && need <= inc) {
+                int above = exc, q, cq;
+                if (above + c0 >= need) { q = 0; cq = c0; }
+                else {
+                    above += c0;
+                    if (above + c1 >= need) { q = 1; cq = c1; }
+                    else {
+                        above += c1;
+                        if (above + c2 >= need) { q = 2; cq = c2; }
+                        else { above += c2; q = 3; cq = c3; }
                     }
                 }
+                s.digit[p] = g0 - q;
+                s.need[p] = need - above;
+                s.eq[p] = cq;
             }
-            __syncthreads();
         }
+        __syncthreads();
+        prefix |= (uint32_t)s.digit[p] << shift;
+        mask |= 0xFFu << shift;
+        need = s.need[p];
+    }
+    n_above = want - need;
+    n_eq = s.eq[3];
+    return prefix;
+}
+
+// take[j]: element j is one of the m best live elements (key desc, id asc);
+// exactly m are taken over the block.  Expects s.dup == 0.
+template <int NT, int PER>
+__device__ void sp_top(const uint32_t (&key)[PER], const int (&id)[PER], const bool (&live)[PER], int m,
+                       SpLds &s, bool (&take)[PER])
+{
+    int n_above, n_eq;
+    const uint32_t t = sp_select<NT, PER>(key, live, m, s, n_above, n_eq);
+    if (n_above + n_eq == m) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) take[j] = live[j] && key[j] >= t;
+        return;
+    }
+    // more elements share key t than fit: the lowest ids among them
+    uint32_t inv[PER];
+    bool tied[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        inv[j] = ~(uint32_t)id[j];
+        tied[j] = live[j] && key[j] == t;
+    }
+    int n2_above, n2_eq;
+    const uint32_t t2 = sp_select<NT, PER>(inv, tied, m - n_above, s, n2_above, n2_eq);
+    const int rest = m - n_above - n2_above;      // of the (duplicate) ids equal to ~t2
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        take[j] = live[j] && (key[j] > t || (tied[j] && inv[j] > t2));
+        if (tied[j] && inv[j] == t2) take[j] = rest == n2_eq || atomicAdd(&s.dup, 1) < rest;
     }
 }
 
-// One selection round: block b keeps the best SP_KEEP of values
-// [b * SP_SLICE, (b + 1) * SP_SLICE) of vin (ids: iin, or the position when
-// iin is null).
-__global__ __launch_bounds__(SP_NT) void sample_cand_kernel(const float *vin, const int *iin, int n, float *cv,
-                                                            int *ci)
+// Selection: block b writes the kk best logits of [b * SP_SLICE, (b + 1) *
+// SP_SLICE) to cv/ci[b * kk, (b + 1) * kk), unordered (past vocab: -inf, id
+// INT_MAX, after every real logit).
+__global__ __launch_bounds__(SP_NT) void sample_sel_kernel(const float *logits, int vocab, int kk, float *cv,
+                                                           int *ci)
 {
-    __shared__ float v[SP_SLICE];
-    __shared__ int id[SP_SLICE];
+    __shared__ SpLds s;
     const int base = blockIdx.x * SP_SLICE;
-    for (int j = threadIdx.x; j < SP_SLICE; j += SP_NT) {
-        const int g = base + j;
-        const bool ok = g < n;
-        v[j] = ok ? vin[g] : -INFINITY;
-        id[j] = ok ? (iin ? iin[g] : g) : 0x7FFFFFFF;
+    uint32_t key[SP_PER];
+    int id[SP_PER];
+    bool live[SP_PER], take[SP_PER];
+#pragma unroll
+    for (int j = 0; j < SP_PER; ++j) {
+        const int g = base + j * SP_NT + threadIdx.x;
+        const bool ok = g < vocab;
+        key[j] = ok ? sp_key(logits[g]) : 0u;
+        id[j] = ok ? g : 0x7FFFFFFF;
+        live[j] = true;
     }
+    for (int b = threadIdx.x; b < 256; b += SP_NT) s.hist[0][b] = 0;
+    if (threadIdx.x == 0) { s.slot = 0; s.dup = 0; }
     __syncthreads();
-    sp_bitonic(v, id, SP_SLICE);
-    for (int j = threadIdx.x; j < SP_KEEP; j += SP_NT) {
-        cv[blockIdx.x * SP_KEEP + j] = v[j];
-        ci[blockIdx.x * SP_KEEP + j] = id[j];
+    sp_top<SP_NT, SP_PER>(key, id, live, kk, s, take);
+#pragma unroll
+    for (int j = 0; j < SP_PER; ++j) {
+        if (!take[j]) continue;
+        const int o = atomicAdd(&s.slot, 1);
+        if (o >= kk) continue;                     // exactly kk are taken; the bound keeps writes in the slice
+        cv[blockIdx.x * kk + o] = key[j] ? sp_val(key[j]) : -INFINITY;
+        ci[blockIdx.x * kk + o] = id[j];
     }
 }
 
@@ -93,75 +191,126 @@ __device__ __forceinline__ uint32_t philox_word0(uint64_t counter, uint64_t seed
     return c0;
 }
 
+// a (value, id) pair's place in a 128-wide bitonic sort held by one wave as
+// two slots per lane (element i = slot * 64 + lane): after the exchange with
+// element i ^ j, the lower index of the pair holds the better of the two when
+// its block of width w runs best-first, else the worse
+__device__ __forceinline__ void sp_exchange(float &v, int &id, int i, int j, int w)
+{
+    const float pv = __shfl_xor(v, j, 64);
+    const int pi = __shfl_xor(id, j, 64);
+    const bool lower = (i & j) == 0, best_first = (i & w) == 0;
+    // both lanes of the pair evaluate "the upper element beats the lower one"
+    const bool upper_wins = lower ? sp_before(pv, pi, v, id) : sp_before(v, id, pv, pi);
+    if (best_first ? upper_wins : !upper_wins) { v = pv; id = pi; }
+}
+
+__device__ void sp_sort128(float &v0, int &i0, float &v1, int &i1)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int w = 2; w <= 128; w <<= 1) {
+#pragma unroll
+        for (int j = w >> 1; j > 0; j >>= 1) {
+            if (j == 64) {                         // lane's two slots pair up; w == 128 runs best-first
+                if (sp_before(v1, i1, v0, i0)) {
+                    const float tv = v0; v0 = v1; v1 = tv;
+                    const int ti = i0; i0 = i1; i1 = ti;
+                }
+            } else {
+                sp_exchange(v0, i0, lane, j, w);
+                sp_exchange(v1, i1, lane + 64, j, w);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float sp_scan(float x, int lane)      // inclusive prefix sum over the wave
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// One block: the kk best of the n_cand candidates, penalised, sorted, then
+// temperature, top-k (k <= 64: lanes 0..k-1 of wave 0), softmax, top-p,
+// min-p and the draw.
 __global__ __launch_bounds__(SP_FINAL_NT) void sample_final_kernel(const float *cv, const int *ci, int n_cand,
-                                                                   int n_pow2, const k2_sampling sp,
+                                                                   int kk, int k, const k2_sampling sp,
                                                                    const int32_t *prev, int n_prev,
                                                                    uint64_t seed, uint64_t counter,
                                                                    int32_t *out)
 {
-    extern __shared__ float lds_f[];
-    float *v = lds_f;
-    int *id = reinterpret_cast<int *>(lds_f + n_pow2);
+    __shared__ SpLds s;
+    __shared__ float tv[SP_MAX_KK];
+    __shared__ int ti[SP_MAX_KK];
     __shared__ int pv[SP_MAX_PREV];
-    for (int j = threadIdx.x; j < n_pow2; j += SP_FINAL_NT) {
-        const bool ok = j < n_cand;
-        v[j] = ok ? cv[j] : -INFINITY;
-        id[j] = ok ? ci[j] : 0x7FFFFFFF;
+    constexpr int PER = SP_FINAL_PER;
+    uint32_t key[PER];
+    int id[PER];
+    bool live[PER], take[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int g = j * SP_FINAL_NT + threadIdx.x;
+        live[j] = g < n_cand;
+        key[j] = live[j] ? sp_key(cv[g]) : 0u;
+        id[j] = live[j] ? ci[g] : 0x7FFFFFFF;
     }
-    for (int j = threadIdx.x; j < n_prev; j += SP_FINAL_NT) pv[j] = prev[j];
+    for (int b = threadIdx.x; b < 256; b += SP_FINAL_NT) s.hist[0][b] = 0;
+    if (threadIdx.x < SP_MAX_KK) { tv[threadIdx.x] = -INFINITY; ti[threadIdx.x] = 0x7FFFFFFF; }
+    if (threadIdx.x < n_prev) pv[threadIdx.x] = prev[threadIdx.x];
+    if (threadIdx.x == 0) { s.slot = 0; s.dup = 0; }
     __syncthreads();
-    sp_bitonic(v, id, n_pow2);
-    if (threadIdx.x != 0) return;
+    sp_top<SP_FINAL_NT, PER>(key, id, live, kk, s, take);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        if (!take[j]) continue;
+        const int o = atomicAdd(&s.slot, 1);
+        if (o >= SP_MAX_KK) continue;
+        tv[o] = sp_val(key[j]);
+        ti[o] = id[j];
+    }
+    __syncthreads();
+    if (threadIdx.x >= 64) return;
 
-    // the top k + n_prev raw logits, penalised, re-sorted (insertion sort)
-    const int kk = sp.top_k + n_prev < n_cand ? sp.top_k + n_prev : n_cand;
-    for (int c = 0; c < kk; ++c) {
-        bool seen = false;
-        for (int p = 0; p < n_prev; ++p) seen |= pv[p] == id[c];
-        if (seen) v[c] = v[c] > 0.f ? v[c] / sp.repetition_penalty : v[c] * sp.repetition_penalty;
+    const int lane = threadIdx.x;
+    float v0 = tv[lane], v1 = tv[lane + 64];
+    int i0 = ti[lane], i1 = ti[lane + 64];
+    bool s0 = false, s1 = false;                   // repetition penalty, once per distinct id
+    for (int p = 0; p < n_prev; ++p) {
+        const int q = pv[p];
+        s0 |= q == i0;
+        s1 |= q == i1;
     }
-    for (int c = 1; c < kk; ++c) {
-        const float tv = v[c];
-        const int ti = id[c];
-        int d = c - 1;
-        while (d >= 0 && sp_before(tv, ti, v[d], id[d])) {
-            v[d + 1] = v[d];
-            id[d + 1] = id[d];
-            --d;
-        }
-        v[d + 1] = tv;
-        id[d + 1] = ti;
-    }
-    const int k = sp.top_k < kk ? sp.top_k : kk;
-    // softmax over the top k (unnormalised weights in v), top-p, min-p
-    const float m = v[0] / sp.temperature;
-    float sum = 0.f;
-    for (int c = 0; c < k; ++c) {
-        v[c] = expf(v[c] / sp.temperature - m);
-        sum += v[c];
-    }
+    const float r = sp.repetition_penalty;
+    if (s0) v0 = v0 > 0.f ? v0 / r : v0 * r;
+    if (s1) v1 = v1 > 0.f ? v1 / r : v1 * r;
+    sp_sort128(v0, i0, v1, i1);
+
+    // lanes 0..k-1 now hold the top k, best first
+    const bool in_k = lane < k;
+    const float m = __shfl(v0, 0, 64) / sp.temperature;
+    const float w = in_k ? expf(v0 / sp.temperature - m) : 0.f;
+    const float sum = __shfl(sp_scan(w, lane), 63, 64);
     int n = k;
     if (sp.top_p < 1.f) {
-        float cum = 0.f;
-        for (int c = 0; c < k; ++c) {
-            cum += v[c] / sum;
-            if (cum >= sp.top_p) { n = c + 1; break; }
-        }
+        const float cum = sp_scan(w / sum, lane);
+        const unsigned long long hit = __ballot(in_k && cum >= sp.top_p);
+        if (hit) n = __ffsll((long long)hit);      // the shortest prefix reaching top_p
     }
-    const float thr = sp.min_p * v[0];
-    float total = 0.f;
-    for (int c = 0; c < n; ++c) total += v[c] >= thr ? v[c] : 0.f;
+    const float thr = sp.min_p * __shfl(w, 0, 64);
+    const bool kept = lane < n && w >= thr;
+    const float acc = sp_scan(kept ? w : 0.f, lane);
+    const float total = __shfl(acc, 63, 64);
     const float u = (float)(philox_word0(counter, seed) >> 8) * 5.9604644775390625e-8f;   // 2^-24
-    const float target = u * total;
-    float acc = 0.f;
-    int pick = id[0];
-    for (int c = 0; c < n; ++c) {
-        if (v[c] < thr) continue;
-        pick = id[c];
-        acc += v[c];
-        if (acc > target) break;
-    }
-    *out = pick;
+    const unsigned long long over = __ballot(kept && acc > u * total);
+    const unsigned long long all = __ballot(kept);
+    const int at = over ? __ffsll((long long)over) - 1 : (all ? 63 - __clzll((long long)all) : 0);
+    const int pick = __shfl(i0, at, 64);
+    if (lane == 0) *out = pick;
 }
 
 }  // namespace k2
@@ -170,14 +319,13 @@ using namespace k2;
 
 static int sp_slices(int n) { return (n + SP_SLICE - 1) / SP_SLICE; }
 
-// two rounds of (values, ids) buffers: round 1 holds sp_slices(vocab) *
-// SP_KEEP survivors, round 2 those of round 1's
-static size_t sp_round_bytes(int n) { return k2_align256((size_t)sp_slices(n) * SP_KEEP * 4); }
+// per slice up to SP_MAX_KK (value, id) survivors
+static size_t sp_half_bytes(int vocab) { return k2_align256((size_t)sp_slices(vocab) * SP_MAX_KK * 4); }
 
 extern "C" size_t k2_sample_workspace_bytes(int vocab)
 {
     if (vocab <= 0 || sp_slices(vocab) > SP_MAX_SLICES) return 0;
-    return 2 * sp_round_bytes(vocab) + 2 * sp_round_bytes(sp_slices(vocab) * SP_KEEP);
+    return 2 * sp_half_bytes(vocab);
 }
 
 extern "C" int k2_sample(const float *logits, int vocab, const k2_sampling *sp, const int32_t *prev,
@@ -193,27 +341,15 @@ extern "C" int k2_sample(const float *logits, int vocab, const k2_sampling *sp, 
         return K2_EINVAL;
     if (ws_bytes < k2_sample_workspace_bytes(vocab)) return K2_EINVAL;
     hipStream_t st = k2_stream(stream);
-    char *w = (char *)ws;
-    float *cv = (float *)w;
-    int *ci = (int *)(w + sp_round_bytes(vocab));
-    hipLaunchKernelGGL(sample_cand_kernel, dim3(sp_slices(vocab)), dim3(SP_NT), 0, st, logits, nullptr, vocab, cv,
-                       ci);
+    const int k = sp->top_k < vocab ? sp->top_k : vocab;
+    const int kk = sp->top_k + n_prev < vocab ? sp->top_k + n_prev : vocab;
+    float *cv = (float *)ws;
+    int *ci = (int *)((char *)ws + sp_half_bytes(vocab));
+    const int slices = sp_slices(vocab);
+    hipLaunchKernelGGL(sample_sel_kernel, dim3(slices), dim3(SP_NT), 0, st, logits, vocab, kk, cv, ci);
     K2_CHECK_LAUNCH();
-    int n_cand = sp_slices(vocab) * SP_KEEP;
-    if (n_cand > SP_SLICE) {                       // a second round over the survivors
-        float *cv2 = (float *)(w + 2 * sp_round_bytes(vocab));
-        int *ci2 = (int *)(w + 2 * sp_round_bytes(vocab) + sp_round_bytes(n_cand));
-        hipLaunchKernelGGL(sample_cand_kernel, dim3(sp_slices(n_cand)), dim3(SP_NT), 0, st, cv, ci, n_cand, cv2,
-                           ci2);
-        K2_CHECK_LAUNCH();
-        n_cand = sp_slices(n_cand) * SP_KEEP;
-        cv = cv2;
-        ci = ci2;
-    }
-    int n_pow2 = SP_KEEP;
-    while (n_pow2 < n_cand) n_pow2 <<= 1;
-    hipLaunchKernelGGL(sample_final_kernel, dim3(1), dim3(SP_FINAL_NT), (size_t)n_pow2 * 8, st, cv, ci, n_cand,
-                       n_pow2, *sp, prev, n_prev, seed, counter, out_token);
+    hipLaunchKernelGGL(sample_final_kernel, dim3(1), dim3(SP_FINAL_NT), 0, st, cv, ci, slices * kk, kk, k, *sp,
+                       prev, n_prev, seed, counter, out_token);
     K2_CHECK_LAUNCH();
     return K2_OK;
 }

@@ -511,3 +511,58 @@ def test_sample_matches_oracle(vocab, params):
     assert near <= 2, near
     if params["top_k"] == 1:
         assert len(set(got)) == 1
+
+
+@pytest.mark.parametrize("vocab", [1000, 4100, 250624])
+@pytest.mark.parametrize("top_k", [1, 64])
+def test_sample_ties_take_lower_ids(vocab, top_k):
+    """300 logits tie for the lead inside one 2048-wide slice (and 50 more in
+    the next): top-k keeps the lowest ids among them.  All kept weights are
+    exactly 1 in fp32 and fp64, so every draw must match the oracle."""
+    from oracle import sampling as S
+    rng = np.random.default_rng(vocab + top_k)
+    lg = rng.standard_normal(vocab).astype(np.float32)
+    lead = np.concatenate([np.arange(100, 400), np.arange(min(2100, vocab - 50), min(2150, vocab))])
+    lg[lead] = 6.0
+    prev = np.array([lead[0], lead[7], 5], dtype=np.int32)   # penalised leaders drop out of the tie
+    sp = k2.k2_sampling(temperature=1.0, top_k=top_k, top_p=1.0, min_p=0.0, repetition_penalty=1.5)
+    wsb = k2.k2_sample_workspace_bytes(vocab)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    X, P = to_dev(lg), to_dev(prev)
+    n = 48
+    out = torch.zeros(n, dtype=torch.int32, device=DEV)
+    for c in range(n):
+        check(k2.k2_sample(X, vocab, sp, P, prev.size, 99, c, out[c:c + 1], ws, wsb))
+    sync()
+    got = to_host(out).tolist()
+    for c in range(n):
+        want, _ = S.sample(lg.astype(np.float64), 1.0, top_k, 1.0, 0.0, 1.5, prev.tolist(), 99, c)
+        assert got[c] == want, (c, got[c], want)
+
+
+@pytest.mark.parametrize("vocab", [1, 10, 130, 2049, 2050])
+def test_sample_small_and_ragged_vocab(vocab):
+    """Vocabularies below top_k + n_prev and one past a slice boundary: the
+    token always matches the oracle's (no padding entry is ever drawn)."""
+    from oracle import sampling as S
+    rng = np.random.default_rng(vocab)
+    lg = (rng.standard_normal(vocab) * 2.0).astype(np.float32)
+    prev = rng.integers(0, vocab, 6).astype(np.int32)
+    sp = k2.k2_sampling(temperature=0.9, top_k=64, top_p=0.95, min_p=0.0, repetition_penalty=1.2)
+    wsb = k2.k2_sample_workspace_bytes(vocab)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    X, P = to_dev(lg), to_dev(prev)
+    n = 32
+    out = torch.zeros(n, dtype=torch.int32, device=DEV)
+    for c in range(n):
+        check(k2.k2_sample(X, vocab, sp, P, prev.size, 7, c, out[c:c + 1], ws, wsb))
+    sync()
+    got = to_host(out).tolist()
+    near = 0
+    for c in range(n):
+        want, margin = S.sample(lg.astype(np.float64), 0.9, 64, 0.95, 0.0, 1.2, prev.tolist(), 7, c)
+        assert 0 <= got[c] < vocab
+        if got[c] != want:
+            assert margin < 1e-5, (c, got[c], want, margin)
+            near += 1
+    assert near <= 1, near
