@@ -16,18 +16,21 @@
 // key of the kk-th largest one 8-bit digit at a time (a 256-bin LDS histogram
 // and one wave's scan per pass), and a second select on the inverted ids
 // breaks ties at that key in favour of lower ids.  Every 2048-wide slice keeps
-// its kk best (one block each), one block selects the kk best of those, and
-// one wave sorts them in registers and does the rest with wave scans.
+// its kk best (one block each), a second round of the same kernel does the
+// same over the survivors (at most 8 blocks), one block applies the penalty to
+// what is left and selects the k best, and one wave sorts them in registers
+// and does the rest with wave scans.
 #include "k2_dev.h"
 
 namespace k2 {
 
 constexpr int SP_SLICE = 2048;             // logits per selection block
 constexpr int SP_NT = 256, SP_PER = SP_SLICE / SP_NT;
-constexpr int SP_FINAL_NT = 1024, SP_FINAL_PER = 16;
-constexpr int SP_MAX_SLICES = 128;         // vocab <= 262144: <= 128 * 128 candidates
+constexpr int SP_FINAL_NT = 1024, SP_FINAL_PER = 1;
+constexpr int SP_MAX_SLICES = 128;         // vocab <= 262144: <= 128 * 128 survivors of the first round
 constexpr int SP_MAX_K = 64, SP_MAX_PREV = 64, SP_MAX_KK = 128;
-static_assert(SP_MAX_SLICES * SP_MAX_KK <= SP_FINAL_NT * SP_FINAL_PER, "final block holds every candidate");
+constexpr int SP_MAX_SLICES2 = SP_MAX_SLICES * SP_MAX_KK / SP_SLICE;   // second round: <= 8 blocks
+static_assert(SP_MAX_SLICES2 * SP_MAX_KK <= SP_FINAL_NT * SP_FINAL_PER, "final block holds every candidate");
 
 // a sorts before b: larger value, then lower id
 __device__ __forceinline__ bool sp_before(float av, int ai, float bv, int bi)
@@ -142,11 +145,12 @@ __device__ void sp_top(const uint32_t (&key)[PER], const int (&id)[PER], const b
     }
 }
 
-// Selection: block b writes the kk best logits of [b * SP_SLICE, (b + 1) *
-// SP_SLICE) to cv/ci[b * kk, (b + 1) * kk), unordered (past vocab: -inf, id
-// INT_MAX, after every real logit).
-__global__ __launch_bounds__(SP_NT) void sample_sel_kernel(const float *logits, int vocab, int kk, float *cv,
-                                                           int *ci)
+// Selection: block b writes the kk best of entries [b * SP_SLICE, (b + 1) *
+// SP_SLICE) of vin (ids: iin, or the position when iin is null) to cv/ci[b *
+// kk, (b + 1) * kk), unordered (past n: -inf, id INT_MAX, after every real
+// entry).
+__global__ __launch_bounds__(SP_NT) void sample_sel_kernel(const float *vin, const int *iin, int n, int kk,
+                                                           float *cv, int *ci)
 {
     __shared__ SpLds s;
     const int base = blockIdx.x * SP_SLICE;
@@ -156,9 +160,9 @@ __global__ __launch_bounds__(SP_NT) void sample_sel_kernel(const float *logits, 
 #pragma unroll
     for (int j = 0; j < SP_PER; ++j) {
         const int g = base + j * SP_NT + threadIdx.x;
-        const bool ok = g < vocab;
-        key[j] = ok ? sp_key(logits[g]) : 0u;
-        id[j] = ok ? g : 0x7FFFFFFF;
+        const bool ok = g < n;
+        key[j] = ok ? sp_key(vin[g]) : 0u;
+        id[j] = ok ? (iin ? iin[g] : g) : 0x7FFFFFFF;
         live[j] = true;
     }
     for (int b = threadIdx.x; b < 256; b += SP_NT) s.hist[0][b] = 0;
@@ -191,10 +195,10 @@ __device__ __forceinline__ uint32_t philox_word0(uint64_t counter, uint64_t seed
     return c0;
 }
 
-// a (value, id) pair's place in a 128-wide bitonic sort held by one wave as
-// two slots per lane (element i = slot * 64 + lane): after the exchange with
-// element i ^ j, the lower index of the pair holds the better of the two when
-// its block of width w runs best-first, else the worse
+// a (value, id) pair's place in a 64-wide bitonic sort held by one wave, one
+// element per lane: after the exchange with element i ^ j, the lower index of
+// the pair holds the better of the two when its block of width w runs
+// best-first, else the worse
 __device__ __forceinline__ void sp_exchange(float &v, int &id, int i, int j, int w)
 {
     const float pv = __shfl_xor(v, j, 64);
@@ -205,23 +209,14 @@ __device__ __forceinline__ void sp_exchange(float &v, int &id, int i, int j, int
     if (best_first ? upper_wins : !upper_wins) { v = pv; id = pi; }
 }
 
-__device__ void sp_sort128(float &v0, int &i0, float &v1, int &i1)
+// 64 (value, id) pairs, one per lane, best first
+__device__ void sp_sort64(float &v, int &id)
 {
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int w = 2; w <= 128; w <<= 1) {
+    for (int w = 2; w <= 64; w <<= 1) {
 #pragma unroll
-        for (int j = w >> 1; j > 0; j >>= 1) {
-            if (j == 64) {                         // lane's two slots pair up; w == 128 runs best-first
-                if (sp_before(v1, i1, v0, i0)) {
-                    const float tv = v0; v0 = v1; v1 = tv;
-                    const int ti = i0; i0 = i1; i1 = ti;
-                }
-            } else {
-                sp_exchange(v0, i0, lane, j, w);
-                sp_exchange(v1, i1, lane + 64, j, w);
-            }
-        }
+        for (int j = w >> 1; j > 0; j >>= 1) sp_exchange(v, id, lane, j, w);
     }
 }
 
@@ -235,41 +230,52 @@ __device__ __forceinline__ float sp_scan(float x, int lane)      // inclusive pr
     return x;
 }
 
-// One block: the kk best of the n_cand candidates, penalised, sorted, then
-// temperature, top-k (k <= 64: lanes 0..k-1 of wave 0), softmax, top-p,
-// min-p and the draw.
+// One block: the n_cand candidates (which hold the k best after the
+// penalty) penalised, the k best selected and sorted by one wave (k <= 64:
+// lanes 0..k-1), then temperature, softmax, top-p, min-p and the draw.
 __global__ __launch_bounds__(SP_FINAL_NT) void sample_final_kernel(const float *cv, const int *ci, int n_cand,
-                                                                   int kk, int k, const k2_sampling sp,
+                                                                   int k, const k2_sampling sp,
                                                                    const int32_t *prev, int n_prev,
                                                                    uint64_t seed, uint64_t counter,
                                                                    int32_t *out)
 {
     __shared__ SpLds s;
-    __shared__ float tv[SP_MAX_KK];
-    __shared__ int ti[SP_MAX_KK];
+    __shared__ float tv[SP_MAX_K];
+    __shared__ int ti[SP_MAX_K];
     __shared__ int pv[SP_MAX_PREV];
     constexpr int PER = SP_FINAL_PER;
     uint32_t key[PER];
     int id[PER];
     bool live[PER], take[PER];
+    float val[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int g = j * SP_FINAL_NT + threadIdx.x;
         live[j] = g < n_cand;
-        key[j] = live[j] ? sp_key(cv[g]) : 0u;
+        val[j] = live[j] ? cv[g] : -INFINITY;
         id[j] = live[j] ? ci[g] : 0x7FFFFFFF;
     }
     for (int b = threadIdx.x; b < 256; b += SP_FINAL_NT) s.hist[0][b] = 0;
-    if (threadIdx.x < SP_MAX_KK) { tv[threadIdx.x] = -INFINITY; ti[threadIdx.x] = 0x7FFFFFFF; }
+    if (threadIdx.x < SP_MAX_K) { tv[threadIdx.x] = -INFINITY; ti[threadIdx.x] = 0x7FFFFFFF; }
     if (threadIdx.x < n_prev) pv[threadIdx.x] = prev[threadIdx.x];
     if (threadIdx.x == 0) { s.slot = 0; s.dup = 0; }
     __syncthreads();
-    sp_top<SP_FINAL_NT, PER>(key, id, live, kk, s, take);
+    // repetition penalty, once per distinct id, then the k best
+    const float rp = sp.repetition_penalty;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        bool seen = false;
+#pragma unroll 8
+        for (int p = 0; p < n_prev; ++p) seen |= pv[p] == id[j];
+        if (seen && live[j]) val[j] = val[j] > 0.f ? val[j] / rp : val[j] * rp;
+        key[j] = live[j] ? sp_key(val[j]) : 0u;
+    }
+    sp_top<SP_FINAL_NT, PER>(key, id, live, k, s, take);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         if (!take[j]) continue;
         const int o = atomicAdd(&s.slot, 1);
-        if (o >= SP_MAX_KK) continue;
+        if (o >= SP_MAX_K) continue;
         tv[o] = sp_val(key[j]);
         ti[o] = id[j];
     }
@@ -277,18 +283,9 @@ __global__ __launch_bounds__(SP_FINAL_NT) void sample_final_kernel(const float *
     if (threadIdx.x >= 64) return;
 
     const int lane = threadIdx.x;
-    float v0 = tv[lane], v1 = tv[lane + 64];
-    int i0 = ti[lane], i1 = ti[lane + 64];
-    bool s0 = false, s1 = false;                   // repetition penalty, once per distinct id
-    for (int p = 0; p < n_prev; ++p) {
-        const int q = pv[p];
-        s0 |= q == i0;
-        s1 |= q == i1;
-    }
-    const float r = sp.repetition_penalty;
-    if (s0) v0 = v0 > 0.f ? v0 / r : v0 * r;
-    if (s1) v1 = v1 > 0.f ? v1 / r : v1 * r;
-    sp_sort128(v0, i0, v1, i1);
+    float v0 = tv[lane];
+    int i0 = ti[lane];
+    sp_sort64(v0, i0);
 
     // lanes 0..k-1 now hold the top k, best first
     const bool in_k = lane < k;
@@ -319,13 +316,15 @@ using namespace k2;
 
 static int sp_slices(int n) { return (n + SP_SLICE - 1) / SP_SLICE; }
 
-// per slice up to SP_MAX_KK (value, id) survivors
+// per slice up to SP_MAX_KK (value, id) survivors: the first round's, then
+// the second round's
 static size_t sp_half_bytes(int vocab) { return k2_align256((size_t)sp_slices(vocab) * SP_MAX_KK * 4); }
+static size_t sp_half2_bytes() { return k2_align256((size_t)SP_MAX_SLICES2 * SP_MAX_KK * 4); }
 
 extern "C" size_t k2_sample_workspace_bytes(int vocab)
 {
     if (vocab <= 0 || sp_slices(vocab) > SP_MAX_SLICES) return 0;
-    return 2 * sp_half_bytes(vocab);
+    return 2 * sp_half_bytes(vocab) + 2 * sp_half2_bytes();
 }
 
 extern "C" int k2_sample(const float *logits, int vocab, const k2_sampling *sp, const int32_t *prev,
@@ -343,12 +342,19 @@ extern "C" int k2_sample(const float *logits, int vocab, const k2_sampling *sp, 
     hipStream_t st = k2_stream(stream);
     const int k = sp->top_k < vocab ? sp->top_k : vocab;
     const int kk = sp->top_k + n_prev < vocab ? sp->top_k + n_prev : vocab;
-    float *cv = (float *)ws;
-    int *ci = (int *)((char *)ws + sp_half_bytes(vocab));
-    const int slices = sp_slices(vocab);
-    hipLaunchKernelGGL(sample_sel_kernel, dim3(slices), dim3(SP_NT), 0, st, logits, vocab, kk, cv, ci);
+    char *w = (char *)ws;
+    float *cv = (float *)w;
+    int *ci = (int *)(w + sp_half_bytes(vocab));
+    float *cv2 = (float *)(w + 2 * sp_half_bytes(vocab));
+    int *ci2 = (int *)(w + 2 * sp_half_bytes(vocab) + sp_half2_bytes());
+    const int slices = sp_slices(vocab), n1 = slices * kk;
+    hipLaunchKernelGGL(sample_sel_kernel, dim3(slices), dim3(SP_NT), 0, st, logits, nullptr, vocab, kk, cv, ci);
     K2_CHECK_LAUNCH();
-    hipLaunchKernelGGL(sample_final_kernel, dim3(1), dim3(SP_FINAL_NT), 0, st, cv, ci, slices * kk, kk, k, *sp,
+    // a second round over the survivors: at most SP_MAX_SLICES2 blocks
+    const int slices2 = sp_slices(n1);
+    hipLaunchKernelGGL(sample_sel_kernel, dim3(slices2), dim3(SP_NT), 0, st, cv, ci, n1, kk, cv2, ci2);
+    K2_CHECK_LAUNCH();
+    hipLaunchKernelGGL(sample_final_kernel, dim3(1), dim3(SP_FINAL_NT), 0, st, cv2, ci2, slices2 * kk, k, *sp,
                        prev, n_prev, seed, counter, out_token);
     K2_CHECK_LAUNCH();
     return K2_OK;
