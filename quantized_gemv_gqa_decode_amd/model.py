@@ -232,6 +232,36 @@ class DecodeModel:
         k2.check(k2.k2_decode_step_dev(self.model, d_token, pos, lg, d_next, d_err, stream))
         return lg
 
+    def generate_sampled(self, prompt, n_decode: int, sampling, seed: int, window: int = 64):
+        """Seeded sampling on the device.  The prompt positions go through
+        k2_decode_step; from the last one on, each position's logits go to
+        k2_sample (counter = that position), which writes the token into a
+        device history buffer that the next k2_decode_step_dev reads, so no
+        token makes a host round trip.  The repetition penalty sees the last
+        ``window`` (<= 64) tokens of prompt and output.  Returns the tokens."""
+        cfg = self.cfg
+        P = len(prompt)
+        n_decode = min(n_decode, cfg.cap - P)
+        window = max(0, min(int(window), 64))
+        hist = torch.zeros(P + n_decode, dtype=torch.int32, device=self.device)
+        hist[:P] = torch.tensor([int(t) for t in prompt], dtype=torch.int32)
+        wsb = k2.k2_sample_workspace_bytes(cfg.vocab)
+        if wsb == 0:
+            raise k2.K2Error(k2.K2_EUNSUPPORTED)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device=self.device)
+        greedy = torch.zeros(1, dtype=torch.int32, device=self.device)
+        for p, t in enumerate(prompt):
+            self.step(int(t), p, want_logits=p == P - 1)
+        for i in range(n_decode):
+            n = P + i                                  # the new token goes to hist[n]
+            if i > 0:
+                self.step_dev(hist[n - 1:n], n - 1, greedy)
+            lo = max(0, n - window)
+            k2.check(k2.k2_sample(self.logits, cfg.vocab, sampling, hist[lo:n] if n > lo else None,
+                                  n - lo, seed, n - 1, hist[n:n + 1], ws, wsb))
+        torch.cuda.synchronize()
+        return hist[P:].cpu().tolist()
+
     def generate(self, prompt, n_decode: int, teacher=None, collect_logits: bool = True):
         """Greedy run on the device: the prompt positions skip the head, the
         last prompt position and every decode position emit an argmax.  With

@@ -402,3 +402,37 @@ def test_verify_refusals():
     assert k2.k2_verify(gm.model, [1] * 8, 8, 60, None, nx, ws, b) == k2.K2_ERANGE
     assert k2.k2_verify(gm.model, [1] * 8, 8, 0, None, nx, ws, b - 256) == k2.K2_EINVAL
     assert k2.k2_verify(gm.model, [1], 1, 0, None, nx, ws, b) == k2.K2_EUNSUPPORTED
+
+
+def test_generate_sampled_matches_oracle():
+    """Device-side sampled generation (k2_decode_step_dev + k2_sample, no host
+    round trip per token) against the oracle decoder fed the same tokens and
+    the sampling oracle: every token equal, except where the sampling oracle's
+    decision margin is below 1e-4 (fp32 weights and cache: the logits agree
+    to ~1e-6)."""
+    from oracle import sampling as S
+    cfg = synth.TINY.replace(wdt="f32", kvdt="f32")
+    prompt = list(synth.prompt(cfg))
+    P = len(prompt)
+    sp = k2.k2_sampling(temperature=0.8, top_k=20, top_p=0.95, min_p=0.02, repetition_penalty=1.3)
+    gm = DecodeModel(cfg, DEV)
+    n_dec = min(12, cfg.cap - P)
+    toks = gm.generate_sampled(prompt, n_dec, sp, seed=11, window=16)
+    assert len(toks) == n_dec
+    dec = oracle.Decoder.from_synth(cfg)
+    lg = None
+    for p, t in enumerate(prompt):
+        _, lg = dec.step(int(t), p, want_logits=p == P - 1)
+    seq = list(prompt)
+    near = 0
+    for i, tok in enumerate(toks):
+        n = P + i
+        if i > 0:
+            _, lg = dec.step(seq[-1], n - 1)
+        want, margin = S.sample(lg, 0.8, 20, 0.95, 0.02, 1.3, seq[max(0, n - 16):n], 11, n - 1)
+        if tok != want:
+            assert margin < 1e-4, (i, tok, want, margin)
+            near += 1
+        seq.append(tok)
+    assert near <= 1, near
+    say(f"sampled {toks}")
