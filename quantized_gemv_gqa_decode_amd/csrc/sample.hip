@@ -25,7 +25,7 @@
 namespace k2 {
 
 constexpr int SP_SLICE = 2048;             // logits per selection block
-constexpr int SP_NT = 256, SP_PER = SP_SLICE / SP_NT;
+constexpr int SP_NT = 1024, SP_PER = SP_SLICE / SP_NT;
 constexpr int SP_FINAL_NT = 1024, SP_FINAL_PER = 1;
 constexpr int SP_MAX_SLICES = 128;         // vocab <= 262144: <= 128 * 128 survivors of the first round
 constexpr int SP_MAX_K = 64, SP_MAX_PREV = 64, SP_MAX_KK = 128;
