@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define K2_ABI_VERSION 1
+#define K2_ABI_VERSION 2
 
 typedef enum {
     K2_OK = 0,
@@ -361,20 +361,29 @@ int k2_verify(const k2_model *m, const int32_t *tokens, int T, int pos0, float *
  * fp32 (nullable: prefill positions skip the head); next_token: device int32
  * (nullable), the first-maximum argmax.  K2_ERANGE if token is outside
  * [0, vocab) or pos outside [0, cap): refuse rather than clamp ([k3_run.c]
- * main()), nothing enqueued.  With the environment variable K2_PERSISTENT=1
- * the position runs as one cooperative persistent kernel (head_dim 16 or
- * 128, n_qh / n_kv 2 or 4; other shapes keep the multi-kernel form). */
+ * main()), nothing enqueued. */
 int k2_decode_step(const k2_model *m, int token, int pos, float *logits, int32_t *next_token,
                    void *stream);
 
-/* Same step with the token read from device memory (d_token), so that a
- * greedy loop can feed next_token back without a host round trip
- * (d_token may equal the previous step's next_token).  A token outside
- * [0, vocab) is caught on the device: *d_err (device int32, nullable) is set
- * to K2_ERANGE, and the step runs on token 0 so that every kernel still
- * completes; the caller must check d_err before trusting the outputs
- * ([k3_run.c] forward(): the caller must check). */
-int k2_decode_step_dev(const k2_model *m, const int32_t *d_token, int pos, float *logits,
+/* Same step with the token AND the position read from device memory, so
+ * that a greedy loop runs without a host round trip and one captured step
+ * (or a captured loop of steps) replays at every position:
+ *   d_token (device int32, required): the token to embed; it may be the
+ *     previous step's next_token.
+ *   d_pos (device int32, required): the position; the step's last kernel
+ *     advances it by one, so consecutive calls walk pos, pos + 1, ...
+ * The launch grids do not depend on the position (the attention grid covers
+ * the most splits the capacity allows; blocks past the position's split
+ * count leave at once).  Range errors are caught on the device, where no
+ * refusal before launch is possible ([k3_run.c] forward(): the caller must
+ * check): a token outside [0, vocab) sets *d_err (device int32, nullable)
+ * to K2_ERANGE and the step runs on token 0; a position outside [0, cap)
+ * sets *d_err to K2_ERANGE, no cache slot is written, *d_pos is not
+ * advanced, and logits / next_token are then undefined.  The caller must
+ * read d_err before trusting the outputs.  K2_EINVAL (nothing enqueued) if
+ * d_token or d_pos is NULL; otherwise the host-side refusals of
+ * k2_decode_step. */
+int k2_decode_step_dev(const k2_model *m, const int32_t *d_token, int32_t *d_pos, float *logits,
                        int32_t *next_token, int32_t *d_err, void *stream);
 
 /* ------------------------------------------------------------------------
@@ -451,6 +460,20 @@ size_t k2_moe_layer_workspace_bytes(const k2_moe_config *cfg, int T);
 int k2_moe_layer(const k2_moe_layer_weights *w, const float *x, int T, float *y,
                  int32_t *topk_idx_out, float *topk_w_out, int32_t *d_err, void *ws,
                  size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement utility (not a step of the path)
+ * ---------------------------------------------------------------------- */
+
+/* Streaming read of buf[0, bytes) split into `blocks` contiguous slabs of
+ * floor(bytes / 16 / blocks) 16-byte words (one 256-thread block each), with
+ * the decode GEMVs' load policy (non-temporal 128-bit loads, 8 in flight per
+ * thread); the tail past blocks * slab is not read.  sink: device uint32
+ * [blocks], receives one word per block.  Timing repeated launches over a
+ * buffer far larger than the memory-side cache gives the read bandwidth the
+ * weight stream can reach ("achievable" beside the 8 TB/s peak).  K2_EINVAL
+ * for null / misaligned pointers or bytes < 16 * blocks. */
+int k2_read_probe(const void *buf, size_t bytes, int blocks, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

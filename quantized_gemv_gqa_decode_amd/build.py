@@ -13,8 +13,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libk2.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["gemv.hip", "gemv_f32.hip", "gemv_bf16.hip", "gemv_fp8.hip", "gemv_mxfp4.hip", "gemv_q4s.hip",
-           "attn.hip", "misc.hip", "decode.hip", "moe.hip", "dense_mfma.hip", "fused.hip",
-           "step_f32.hip", "step_bf16.hip", "step_fp8.hip", "step_mxfp4.hip", "prefill.hip", "attn_rows.hip", "sample.hip"]
+           "attn.hip", "attn_o.hip", "misc.hip", "decode.hip", "moe.hip", "dense_mfma.hip", "prefill.hip",
+           "attn_rows.hip", "sample.hip"]
 ARCH = "gfx950"
 
 

@@ -1,9 +1,6 @@
 // attn.hip -- split-K GQA decode attention for gfx950, with the RoPE and
 // KV-cache append of the new position fused in: launchers and C ABI (the
 // device code is in attn_impl.h).
-#include <stdlib.h>
-#include <string.h>
-
 #include "attn_impl.h"
 
 namespace k2 {
@@ -27,20 +24,6 @@ int attn_max_splits(int n_kv, int cap)
     if (target < 1) target = 1;
     const int by_chunk = (cap + K2_ATTN_MAX_CHUNK - 1) / K2_ATTN_MAX_CHUNK;
     return target > by_chunk ? target : by_chunk;
-}
-
-// Finer splits for the persistent step kernel, whose attention items share
-// the grid with idle blocks: about 32 positions per block, at most the
-// workspace's split count.
-int attn_splits_fine(int n_kv, int cap, int len, int *chunk)
-{
-    const int max_s = attn_max_splits(n_kv, cap);
-    int S = (len + 31) / 32;
-    if (S > max_s) S = max_s;
-    if (S < 1) S = 1;
-    const int c = (len + S - 1) / S;
-    *chunk = c;
-    return (len + c - 1) / c;
 }
 
 size_t attn_ws_bytes(int n_qh, int n_kv, int hd, int cap)
@@ -274,12 +257,6 @@ extern "C" int k2_rope_append_attn(k2_dtype kvdt, const float *qkv, const float 
     return attn_launch(kvdt, head_dim, n_qh / n_kv, true, a, k2_stream(stream));
 }
 
-static bool env_off(const char *name)
-{
-    const char *e = getenv(name);
-    return e && strcmp(e, "0") == 0;
-}
-
 static int64_t weight_code_bytes(int wdt, int64_t N, int64_t K)
 {
     switch (wdt) {
@@ -298,14 +275,14 @@ int k2::attn_then_o(int wdt, int kvdt, int hd, int rep, AttnArgs at, const GemvA
     // KV, ctx 4096) the one launch was 1.6 % (MXFP4) and 2.3 % (Q4S) slower
     // per decode step and even with fp8 weights, while with a bf16 cache it
     // is 1.8 % faster
-    if (kvdt != K2_I8 && !env_off("K2_ATTN_O")) {
+    if (kvdt != K2_I8) {
         rc = attn_o_launch(wdt, kvdt, hd, rep, at, o, d_err, st);
         if (rc != K2_EUNSUPPORTED) return rc;
     }
-    if (!env_off("K2_PREFETCH")) {
-        at.pf = o.W;
-        at.pf_bytes = weight_code_bytes(wdt, o.N, o.K);
-    }
+    // the attention launch's idle compute units read the O weights once so
+    // that they sit in the memory-side cache when the GEMV streams them
+    at.pf = o.W;
+    at.pf_bytes = weight_code_bytes(wdt, o.N, o.K);
     if ((rc = attn_launch(kvdt, hd, rep, true, at, st))) return rc;
     return gemv_dispatch(wdt, o, PRO_NONE, EPI_PLAIN, st);
 }

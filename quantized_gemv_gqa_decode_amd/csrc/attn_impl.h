@@ -1,5 +1,6 @@
 // attn_impl.h -- device code of the split-K GQA decode attention (included
-// by attn.hip for the standalone kernels and by the persistent step kernel).
+// by attn.hip for the stand-alone kernels, by attn_rows.hip for a prefill
+// chunk's queries and by attn_o_impl.h for the attention + O launch).
 //
 // Semantics ([k2-burn] "Model shape": GQA with 4x KV repeat; "Limitations":
 // plain SDPA, softmax in fp32; "KV cache storage": fp32 / bf16 / symmetric
@@ -7,17 +8,18 @@
 //   out[h] = softmax_j(q_h . K_hat[g][j] * scale) V_hat[g][j],  g = h / rep,
 // over positions j in [0, len).
 //
-// Grid: (S splits, n_kv heads); block = 256 threads.  Block (s, g) handles
-// positions [s*chunk, min(len, (s+1)*chunk)) for the rep query heads of kv
-// head g:
+// Grid: (S splits, n_kv heads); block = ATT_NT threads (8 waves, the
+// StreamWide shape below).  Block (s, g) handles positions
+// [s*chunk, min(len, (s+1)*chunk)) for the rep query heads of kv head g:
 //   1. the rep query heads are rotated (fused form) and scaled into LDS;
-//   2. each wave streams its positions: a K (and V) row of head_dim values is
-//      split over LPP lanes that each load 16 bytes, so one wave instruction
-//      covers 64/LPP positions; the K and V loads of NL such slots are issued
-//      together before any arithmetic; the int8 per-position scale multiplies
-//      the finished dot product and is folded into the probability for V;
+//   2. K and V rows stream through a ring of LDS stages filled by LDS-DMA
+//      (global_load_lds), two tiles in flight while one is computed; a row
+//      of head_dim values is split over LPP lanes (16 bytes each), so one
+//      wave covers 64/LPP positions per slot; the int8 per-position scale
+//      multiplies the finished dot product and is folded into the
+//      probability for V;
 //   3. each wave keeps an online fp32 softmax (running max, rescaled sum and
-//      accumulator); the four waves are merged through LDS;
+//      accumulator); the waves are merged through LDS;
 //   4. with one split the normalised output is written directly; otherwise
 //      every block publishes (max, sum, unnormalised o) at device scope, and
 //      the last block of the kv head to finish combines the S partials in
@@ -619,18 +621,9 @@ __device__ __forceinline__ bool block_wait_count(const unsigned *p, unsigned nee
 // so that no wait inside the block (a barrier, or the wait the compiler
 // places before LDS writes that could race an LDS-DMA) waits for its
 // store.  Returns whether this block holds the new position.
-struct NoWait {
-    __device__ void operator()() const {}
-};
-
-// QSYNC (fused layer kernel): q, k and v are written by other blocks of the
-// same launch; the block first issues its tile copies, then calls
-// wait_qkv() (every thread; it returns once they are stored), then reads
-// q/k/v at device scope.
-template <int KVDT, int HD, int REP, bool FUSED, bool COH, class C = StreamWide, bool QSYNC = false,
-          class W = NoWait>
+template <int KVDT, int HD, int REP, bool FUSED, bool COH, class C = StreamWide>
 __device__ __forceinline__ bool attn_stream_block(const AttnArgs &a, int g, int s, int S, float *smem,
-                                                  uint32_t &kv_bits, float &kv_scale, W wait_qkv = W())
+                                                  uint32_t &kv_bits, float &kv_scale)
 {
     using G = StreamGeom<KVDT, HD, C>;
     using T = typename G::T;
@@ -661,8 +654,7 @@ __device__ __forceinline__ bool attn_stream_block(const AttnArgs &a, int g, int 
     K2_ATRACE(0);
 
     // q (and the new k, v): loaded first, so that waiting for them never
-    // waits for the tile copies issued after them -- except under QSYNC,
-    // where they exist only once the QKV blocks of this launch have counted
+    // waits for the tile copies issued after them
     constexpr int QV = (REP * HD + NT - 1) / NT;
     constexpr int HALF = HD / 2;
     float qx0[QV], qx1[QV], qc[QV], qsn[QV];
@@ -675,8 +667,8 @@ __device__ __forceinline__ bool attn_stream_block(const AttnArgs &a, int g, int 
             const int hl = tt / HD, d = tt % HD, h = g * REP + hl;
             if constexpr (FUSED) {
                 const float *u = a.qkv + (int64_t)h * HD;
-                qx0[v] = ld1<QSYNC>(u + d % HALF);
-                qx1[v] = ld1<QSYNC>(u + d % HALF + HALF);
+                qx0[v] = ld1<false>(u + d % HALF);
+                qx1[v] = ld1<false>(u + d % HALF + HALF);
                 qc[v] = a.cos_sin[((int64_t)a.pos * HALF + d % HALF) * 2];
                 qsn[v] = a.cos_sin[((int64_t)a.pos * HALF + d % HALF) * 2 + 1];
             } else {
@@ -688,17 +680,17 @@ __device__ __forceinline__ bool attn_stream_block(const AttnArgs &a, int g, int 
             if (holds_new) {
                 if (tid < HD) {
                     const float *u = a.qkv + (int64_t)(a.n_qh + g) * HD;
-                    nk0 = ld1<QSYNC>(u + tid % HALF);
-                    nk1 = ld1<QSYNC>(u + tid % HALF + HALF);
+                    nk0 = ld1<false>(u + tid % HALF);
+                    nk1 = ld1<false>(u + tid % HALF + HALF);
                     kc0 = a.cos_sin[((int64_t)a.pos * HALF + tid % HALF) * 2];
                     ks0 = a.cos_sin[((int64_t)a.pos * HALF + tid % HALF) * 2 + 1];
                 } else if (tid < 2 * HD) {
-                    nk0 = ld1<QSYNC>(a.qkv + (int64_t)(a.n_qh + a.n_kv + g) * HD + (tid - HD));
+                    nk0 = ld1<false>(a.qkv + (int64_t)(a.n_qh + a.n_kv + g) * HD + (tid - HD));
                 }
             }
         }
     };
-    if constexpr (!QSYNC) load_qkv();
+    load_qkv();
 
     // tile t -> stage t % NST: K rows, V rows, then the int8 scales
     auto issue_tile = [&](int t) {
@@ -730,10 +722,6 @@ __device__ __forceinline__ bool attn_stream_block(const AttnArgs &a, int g, int 
 #pragma unroll
     for (int t = 0; t < NST; ++t)
         if (t < n_tiles) issue_tile(t);
-    if constexpr (QSYNC) {
-        wait_qkv();
-        load_qkv();
-    }
 
     // 1. query heads of this kv head, rotated (fused) and pre-scaled
 #pragma unroll
@@ -1074,6 +1062,33 @@ __device__ __forceinline__ void attn_combine_block(const AttnArgs &a, int g, flo
     }
 }
 
+// Position taken from device memory (a.d_pos set): pos, len, chunk and the
+// split count S follow from *d_pos by the rule of attn_splits on the host
+// (chunk = ceil(len / target) clamped to [K2_ATTN_MIN_CHUNK,
+// K2_ATTN_MAX_CHUNK], target = K2_ATTN_TARGET_BLOCKS / n_kv), so S never
+// exceeds the grid's split extent (attn_max_splits of the capacity).
+// Returns false for a position outside [0, cap): the first block reports
+// K2_ERANGE in d_err and every block leaves without writing.
+__device__ __forceinline__ bool attn_resolve_pos(AttnArgs &a)
+{
+    if (!a.d_pos) return true;
+    const int p = *a.d_pos;            // written by an earlier kernel of the stream
+    if (p < 0 || p >= a.cap) {
+        if (a.d_err && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) coh_store_i(a.d_err, K2_ERANGE);
+        return false;
+    }
+    a.pos = p;
+    a.len = p + 1;
+    int target = K2_ATTN_TARGET_BLOCKS / a.n_kv;
+    if (target < 1) target = 1;
+    int c = (a.len + target - 1) / target;
+    c = c < K2_ATTN_MIN_CHUNK ? K2_ATTN_MIN_CHUNK : c;
+    c = c > K2_ATTN_MAX_CHUNK ? K2_ATTN_MAX_CHUNK : c;
+    a.chunk = c;
+    a.S = (a.len + c - 1) / c;
+    return true;
+}
+
 // Blocks with blockIdx.y >= n_kv read the weight range pf, split evenly over
 // them in 16-byte units, with plain loads (which allocate in the memory-side
 // cache), and exit.  They share no state with the attention blocks; the
@@ -1105,18 +1120,21 @@ __device__ __forceinline__ void attn_prefetch_block(const AttnArgs &a)
 // last block of each kv head to finish (an arrival counter, reset by that
 // block) combines the partials of the head.  No block waits for another.
 template <int KVDT, int HD, int REP, bool FUSED>
-__global__ __launch_bounds__(ATT_NT) void attn_kernel(const AttnArgs a)
+__global__ __launch_bounds__(ATT_NT) void attn_kernel(const AttnArgs a0)
 {
     constexpr int NA = attn_stream_lds_floats<KVDT, HD, REP, StreamWide>(), NC = combine_lds_floats<REP, ATT_NT>();
     extern __shared__ float4 lds4[];
     float *smem = reinterpret_cast<float *>(lds4);
     static_assert(NA >= NC, "combine fits the attention LDS");
     __shared__ int last;
-    if ((int)blockIdx.y >= a.n_kv) {
-        attn_prefetch_block(a);
+    if ((int)blockIdx.y >= a0.n_kv) {
+        attn_prefetch_block(a0);
         return;
     }
-    const int g = blockIdx.y, S = gridDim.x;
+    AttnArgs a = a0;
+    if (!attn_resolve_pos(a)) return;
+    if ((int)blockIdx.x >= a.S) return;            // device split count below the grid's
+    const int g = blockIdx.y, S = a.S;
     K2_ATRACE_CLEAR();
     uint32_t kv_bits = 0u;
     float kv_scale = 0.f;

@@ -337,7 +337,7 @@ __device__ __forceinline__ void gemv_units(const GemvArgs &a, const float *xs, i
                 for (int r = 0; r < R; ++r) {
                     if (lane == (b * R + r) % K2_WAVE && cur_ok[r]) {
                         float v = acc[b][r];
-                        if (a.residual) v += a.residual[(int64_t)b * a.N + cur_rows[r]];
+                        if (a.residual) v += ld1<COH>(a.residual + (int64_t)b * a.N + cur_rows[r]);
                         st1<COH>(a.y + (int64_t)b * a.N + cur_rows[r], v);
                     }
                 }

@@ -33,6 +33,11 @@ struct ArgmaxArgs {
     int *part_i;
     int32_t *out_idx;
     int n_blocks;
+    // nullable: the final reduction also advances a device position held
+    // there by one when it lies in [0, adv_cap) (the last kernel of a decode
+    // step whose position is read from device memory)
+    int32_t *adv_pos;
+    int adv_cap;
 };
 
 struct GemvArgs {
@@ -68,6 +73,14 @@ struct AttnArgs {
     unsigned *ao_sync;         // attention + O launch: AO_SYNC_WORDS (zero between calls)
     int n_qh, n_kv, cap, len, pos, chunk, S;
     float scale;
+    // Position read from device memory (nullable): when set, pos, len,
+    // chunk and S are derived on the device from *d_pos by the rule of
+    // attn_splits, the grid covers the most splits the cache capacity
+    // allows (S above is that grid extent), and blocks past the device split
+    // count exit at once.  A position outside [0, cap) sets *d_err (nullable)
+    // to K2_ERANGE and the launch writes nothing.
+    const int32_t *d_pos;
+    int32_t *d_err;
     // Weight bytes of the phase that follows (optional): blocks of the
     // launch beyond the attention grid read this range once so that it sits
     // in the memory-side cache when the next GEMV streams it.  Read only;
@@ -78,7 +91,6 @@ struct AttnArgs {
 
 size_t attn_ws_bytes(int n_qh, int n_kv, int hd, int cap);
 int attn_splits(int n_kv, int len, int *chunk);
-int attn_splits_fine(int n_kv, int cap, int len, int *chunk);
 int attn_max_splits(int n_kv, int cap);
 int attn_launch(int kvdt, int hd, int rep, bool fused, const AttnArgs &a, hipStream_t st);
 int device_cus();
@@ -109,9 +121,9 @@ int attn_o_launch(int wdt, int kvdt, int hd, int rep, const AttnArgs &at, const 
                   int32_t *d_err, hipStream_t st);
 
 // Fused-form attention (at) and then the O GEMV + residual (o, B = 1): one
-// launch where attn_o_launch has one and the cache is fp32 or bf16 (unless
-// K2_ATTN_O=0), else the two kernels, the attention launch's idle compute
-// units prefetching the O weights (unless K2_PREFETCH=0).
+// launch where attn_o_launch has one and the cache is fp32 or bf16, else the
+// two kernels, the attention launch's idle compute units prefetching the O
+// weights.
 int attn_then_o(int wdt, int kvdt, int hd, int rep, AttnArgs at, const GemvArgs &o, int32_t *d_err,
                 hipStream_t st);
 void attn_ws_carve(void *ws, int n_qh, int n_kv, int hd, int cap, AttnArgs &a);
@@ -129,6 +141,8 @@ int embed_launch(int embdt, const void *E, int H, int vocab, int token, const in
 int rmsnorm_rows_launch(const float *x, const float *gamma, float *y, int rows, int hidden, int groups,
                         float eps, hipStream_t st);
 int argmax_final_launch(const ArgmaxArgs &am, int n_blocks, hipStream_t st);
+// Advance a device position by one when it lies in [0, cap) (one thread).
+int pos_advance_launch(int32_t *d_pos, int cap, hipStream_t st);
 
 // ------------------------------------------------------ device functions --
 

@@ -193,7 +193,28 @@ __global__ __launch_bounds__(K2_BLOCK) void argmax_final_kernel(ArgmaxArgs am, i
     int bi = 0x7FFFFFFF;
     for (int b = threadIdx.x; b < n_blocks; b += K2_BLOCK) argmax_pair_max(bv, bi, am.part_v[b], am.part_i[b]);
     argmax_block(bv, bi);
-    if (threadIdx.x == 0) *am.out_idx = bi;
+    if (threadIdx.x == 0) {
+        *am.out_idx = bi;
+        if (am.adv_pos) {
+            const int p = *am.adv_pos;
+            if (p >= 0 && p < am.adv_cap) *am.adv_pos = p + 1;
+        }
+    }
+}
+
+__global__ void pos_advance_kernel(int32_t *d_pos, int cap)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        const int p = *d_pos;
+        if (p >= 0 && p < cap) *d_pos = p + 1;
+    }
+}
+
+int pos_advance_launch(int32_t *d_pos, int cap, hipStream_t st)
+{
+    hipLaunchKernelGGL(pos_advance_kernel, dim3(1), dim3(64), 0, st, d_pos, cap);
+    K2_CHECK_LAUNCH();
+    return K2_OK;
 }
 
 int argmax_final_launch(const ArgmaxArgs &am, int n_blocks, hipStream_t st)
@@ -201,6 +222,29 @@ int argmax_final_launch(const ArgmaxArgs &am, int n_blocks, hipStream_t st)
     hipLaunchKernelGGL(argmax_final_kernel, dim3(1), dim3(K2_BLOCK), 0, st, am, n_blocks);
     K2_CHECK_LAUNCH();
     return K2_OK;
+}
+
+// Streaming read of `blocks` contiguous slabs of n16 16-byte words each,
+// with the decode GEMVs' load policy (non-temporal 128-bit loads, UNR loads
+// per thread in flight, every address in range); one word per block goes to
+// sink so that no load is dropped.
+constexpr int READ_UNR = 8;
+__global__ __launch_bounds__(K2_BLOCK) void read_probe_kernel(const k2_u4 *p, int64_t n16, uint32_t *sink)
+{
+    const k2_u4 *b = p + (int64_t)blockIdx.x * n16;
+    uint32_t acc = 0u;
+    for (int64_t i = threadIdx.x; i < n16; i += (int64_t)READ_UNR * K2_BLOCK) {
+        k2_u4 v[READ_UNR];
+#pragma unroll
+        for (int d = 0; d < READ_UNR; ++d) {
+            const int64_t j = i + (int64_t)d * K2_BLOCK;
+            v[d] = __builtin_nontemporal_load(b + (j < n16 ? j : n16 - 1));
+        }
+#pragma unroll
+        for (int d = 0; d < READ_UNR; ++d) acc ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
+    }
+    acc = __builtin_amdgcn_readfirstlane(acc) ^ acc;
+    if (threadIdx.x == 0) sink[blockIdx.x] = acc;
 }
 
 size_t argmax_ws_bytes()
@@ -335,4 +379,15 @@ extern "C" int k2_argmax(const float *x, int n, int32_t *out_idx, void *ws, size
     hipLaunchKernelGGL(argmax_kernel, dim3(blocks), dim3(K2_BLOCK), 0, k2_stream(stream), x, n, am);
     K2_CHECK_LAUNCH();
     return argmax_final_launch(am, blocks, k2_stream(stream));
+}
+
+extern "C" int k2_read_probe(const void *buf, size_t bytes, int blocks, uint32_t *sink, void *stream)
+{
+    if (!k2_ptr_ok(buf) || !k2_ptr_ok(sink)) return K2_EINVAL;
+    if (blocks <= 0 || bytes < (size_t)blocks * 16) return K2_EINVAL;
+    const int64_t n16 = (int64_t)(bytes / 16 / (size_t)blocks);
+    hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(K2_BLOCK), 0, k2_stream(stream),
+                       (const k2_u4 *)buf, n16, sink);
+    K2_CHECK_LAUNCH();
+    return K2_OK;
 }

@@ -131,13 +131,6 @@ static int pf_shape_ok(const k2_config *c, bool verify = false)
     return K2_OK;
 }
 
-// K2_PREFILL_ROWS=0 runs the chunk's attention one position per launch
-static bool chunk_attn_off()
-{
-    const char *e = getenv("K2_PREFILL_ROWS");
-    return e && strcmp(e, "0") == 0;
-}
-
 // verify: logits [T][vocab] (nullable: kept in the workspace) and next [T]
 // (required) for every row; else logits [vocab] and next of the last row.
 static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos0, float *logits,
@@ -170,7 +163,6 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
     K2_CHECK_LAUNCH();
 
     // the chunk's attention as one launch (hd 128), else per position
-    const bool rows_ok = !chunk_attn_off();
     AttnArgs at{};
     attn_ws_carve(w.attn, c->n_qh, c->n_kv, hd, c->cap, at);
     at.cos_sin = m->rope;
@@ -188,9 +180,8 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
         at.vc = L->vc;
         at.ks = L->ks;
         at.vs = L->vs;
-        rc = rows_ok ? attn_rows_launch(c->kvdt, w.qkv, m->rope, w.qrot, w.o, L->kc, L->vc, L->ks, L->vs,
-                                        c->n_qh, c->n_kv, hd, c->cap, pos0, T, w.rows, st)
-                     : K2_EUNSUPPORTED;
+        rc = attn_rows_launch(c->kvdt, w.qkv, m->rope, w.qrot, w.o, L->kc, L->vc, L->ks, L->vs, c->n_qh,
+                              c->n_kv, hd, c->cap, pos0, T, w.rows, st);
         if (rc && rc != K2_EUNSUPPORTED) return rc;
         const bool per_position = rc == K2_EUNSUPPORTED;
         for (int t = 0; per_position && t < T; ++t) {

@@ -87,7 +87,8 @@ SIGNATURES = {
     "k2_prefill": (_i, [_vp, _vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "k2_verify_workspace_bytes": (_sz, [_vp, _i]),
     "k2_verify": (_i, [_vp, _vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
-    "k2_decode_step_dev": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp]),
+    "k2_decode_step_dev": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "k2_read_probe": (_i, [_vp, _sz, _i, _vp, _vp]),
     "k2_moe_route_workspace_bytes": (_sz, [_i, _i]),
     "k2_moe_route": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "k2_moe_workspace_bytes": (_sz, [_i, _i, _i, _i]),
@@ -280,9 +281,9 @@ def k2_decode_step(model: k2_model, token: int, pos: int, logits, next_token, st
                                  ptr(next_token), stream_handle(stream))
 
 
-def k2_decode_step_dev(model: k2_model, d_token, pos: int, logits, next_token, d_err,
+def k2_decode_step_dev(model: k2_model, d_token, d_pos, logits, next_token, d_err,
                        stream=None):
-    return load().k2_decode_step_dev(C.addressof(model), ptr(d_token), int(pos), ptr(logits),
+    return load().k2_decode_step_dev(C.addressof(model), ptr(d_token), ptr(d_pos), ptr(logits),
                                      ptr(next_token), ptr(d_err), stream_handle(stream))
 
 
@@ -367,3 +368,10 @@ def k2_sample(logits, vocab, sp: "k2_sampling", prev, n_prev, seed, counter, out
               stream=None):
     return load().k2_sample(ptr(logits), vocab, C.addressof(sp), ptr(prev), n_prev, int(seed),
                             int(counter), ptr(out_token), ptr(ws), ws_bytes, stream_handle(stream))
+
+
+# -------------------------------------------------------------- measurement --
+
+def k2_read_probe(buf, nbytes: int, blocks: int, sink, stream=None):
+    return load().k2_read_probe(ptr(buf), int(nbytes), int(blocks), ptr(sink),
+                                stream_handle(stream))

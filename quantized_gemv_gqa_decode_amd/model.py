@@ -122,6 +122,8 @@ class DecodeModel:
         k2.check(k2.k2_model_check(self.model))
         self.logits = torch.zeros(cfg.vocab, dtype=torch.float32, device=self.device)
         self.next = torch.zeros(1, dtype=torch.int32, device=self.device)
+        # the position k2_decode_step_dev reads and advances
+        self.d_pos = torch.zeros(1, dtype=torch.int32, device=self.device)
 
     # ------------------------------------------------------------------
     def load_int8_prefix(self, length: int):
@@ -226,10 +228,16 @@ class DecodeModel:
             toks.extend(new[:n_decode - len(toks)])
         return toks, rounds
 
-    def step_dev(self, d_token: torch.Tensor, pos: int, d_next: torch.Tensor,
+    def set_pos(self, pos: int):
+        """Set the device position that the next k2_decode_step_dev reads."""
+        self.d_pos.fill_(int(pos))
+
+    def step_dev(self, d_token: torch.Tensor, d_next: torch.Tensor,
                  d_err: Optional[torch.Tensor] = None, want_logits: bool = True, stream=None):
+        """Enqueue one position with the token (d_token) and the position
+        (self.d_pos, advanced by the step) read on the device."""
         lg = self.logits if want_logits else None
-        k2.check(k2.k2_decode_step_dev(self.model, d_token, pos, lg, d_next, d_err, stream))
+        k2.check(k2.k2_decode_step_dev(self.model, d_token, self.d_pos, lg, d_next, d_err, stream))
         return lg
 
     def generate_sampled(self, prompt, n_decode: int, sampling, seed: int, window: int = 64):
@@ -252,10 +260,11 @@ class DecodeModel:
         greedy = torch.zeros(1, dtype=torch.int32, device=self.device)
         for p, t in enumerate(prompt):
             self.step(int(t), p, want_logits=p == P - 1)
+        self.set_pos(P)                                # the first decode position
         for i in range(n_decode):
             n = P + i                                  # the new token goes to hist[n]
             if i > 0:
-                self.step_dev(hist[n - 1:n], n - 1, greedy)
+                self.step_dev(hist[n - 1:n], greedy)   # position n - 1
             lo = max(0, n - window)
             k2.check(k2.k2_sample(self.logits, cfg.vocab, sampling, hist[lo:n] if n > lo else None,
                                   n - lo, seed, n - 1, hist[n:n + 1], ws, wsb))

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert k2.k2_abi_version() == 1
+    assert k2.k2_abi_version() == 2
     for rc in (0, -1, -2, -3, -4):
         assert k2.k2_status_str(rc)
     assert "unknown" in k2.k2_status_str(7)
@@ -138,7 +138,8 @@ def test_decode_step_refuses_before_launch():
     assert L.k2_decode_step(adr, 0, 32, FAKE, FAKE, None) == k2.K2_ERANGE
     assert L.k2_decode_step(adr, 0, -1, FAKE, FAKE, None) == k2.K2_ERANGE
     assert L.k2_decode_step(adr, 0, 0, FAKE + 4, FAKE, None) == k2.K2_EINVAL
-    assert L.k2_decode_step_dev(adr, None, 0, FAKE, FAKE, None, None) == k2.K2_EINVAL
+    assert L.k2_decode_step_dev(adr, None, FAKE, FAKE, FAKE, None, None) == k2.K2_EINVAL
+    assert L.k2_decode_step_dev(adr, FAKE, None, FAKE, FAKE, None, None) == k2.K2_EINVAL
     m.ws_bytes -= 256
     assert L.k2_decode_step(adr, 0, 0, FAKE, FAKE, None) == k2.K2_EINVAL
     assert L.k2_decode_step(None, 0, 0, FAKE, FAKE, None) == k2.K2_EINVAL

@@ -68,62 +68,64 @@ def test_tiny_decoder(wdt, kvdt):
     run_parity(cfg, synth.prompt(cfg), cfg.n_decode)
 
 
-@pytest.mark.parametrize("wdt,kvdt", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "i8"),
-                                      ("fp8", "i8"), ("mxfp4", "bf16")])
-def test_tiny_decoder_persistent_path(wdt, kvdt, monkeypatch):
-    """The same decode as one persistent cooperative kernel per position
-    (opt-in with K2_PERSISTENT=1): grid barriers, device-scope activation
-    hand-off, last-block attention combine and argmax."""
-    monkeypatch.setenv("K2_PERSISTENT", "1")
-    cfg = synth.TINY.replace(wdt=wdt, kvdt=kvdt)
-    run_parity(cfg, synth.prompt(cfg), cfg.n_decode)
-
-
-def test_tiny_decoder_persistent_n_kv1(monkeypatch):
-    monkeypatch.setenv("K2_PERSISTENT", "1")
-    cfg = synth.TINY.replace(n_kv=1)
-    run_parity(cfg, synth.prompt(cfg), 8)
-
-
-# head_dim 128 with 4 query heads per kv head: the shape of the fused
-# QKV + attention + O layer kernel, small enough for a quick oracle
+# head_dim 128 with 4 query heads per kv head (the attention + O launch's
+# shape), small enough for a quick oracle
 HEAD128 = synth.TINY.replace(name="head128-small", hidden=512, n_qh=8, n_kv=2, head_dim=128,
                              inter=1024, vocab=1024, cap=512, n_decode=4)
 
 
-@pytest.mark.parametrize("fused", ["1", "0"])
 @pytest.mark.parametrize("wdt,kvdt", [("bf16", "bf16"), ("bf16", "i8"), ("fp8", "i8"),
                                       ("mxfp4", "i8"), ("f32", "f32"), ("q4s", "i8")])
 @pytest.mark.parametrize("P", [20, 200])
-def test_head128_fused_layer_front(wdt, kvdt, P, fused, monkeypatch):
-    """QKV, attention and O as one dataflow launch (opt-in, K2_FUSED=1) and
-    as three launches (the default); 200 prompt positions give several
+def test_head128_decoder(wdt, kvdt, P):
+    """Decode at the head-128 shape; 200 prompt positions give several
     attention splits per kv head, 20 give one."""
-    monkeypatch.setenv("K2_FUSED", fused)
     cfg = HEAD128.replace(wdt=wdt, kvdt=kvdt)
     run_parity(cfg, synth.prompt(cfg, P), cfg.n_decode)
+
+
+def _generate_dev(gm, prompt, n_decode, teacher=None):
+    """Greedy run whose decode positions go through k2_decode_step_dev (token
+    and position read on the device; the position advances itself)."""
+    P = len(prompt)
+    for p, t in enumerate(prompt):
+        gm.step(int(t), p, want_logits=p == P - 1)
+    hist = torch.zeros(n_decode + 1, dtype=torch.int32, device=DEV)
+    hist[0:1].copy_(gm.next)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gm.set_pos(P)
+    torch.cuda.synchronize()
+    toks = [int(hist[0].item())]
+    lgs = [to_host(gm.logits).copy()]
+    for i in range(n_decode - 1):
+        if teacher is not None:
+            hist[i:i + 1].fill_(int(teacher[i]))
+        gm.step_dev(hist[i:i + 1], hist[i + 1:i + 2], err)
+        torch.cuda.synchronize()
+        toks.append(int(hist[i + 1].item()))
+        lgs.append(to_host(gm.logits).copy())
+    assert int(err.item()) == 0
+    assert int(gm.d_pos.item()) == P + n_decode - 1
+    return toks, lgs
 
 
 @pytest.mark.parametrize("wdt,kvdt", [("bf16", "bf16"), ("bf16", "i8"), ("fp8", "i8"),
                                       ("mxfp4", "i8"), ("f32", "f32"), ("f32", "bf16"),
                                       ("q4s", "i8")])
 @pytest.mark.parametrize("P", [3, 200])
-def test_head128_attention_o_one_launch_bit_identical(wdt, kvdt, P, monkeypatch):
-    """Attention and the O projection as one launch (the default where both
-    grids fit on the chip) against the two-kernel form (K2_ATTN_O=0): the O
-    rows are summed in the same order, so every logit and token is the same
-    bit for bit.  3 prompt positions give one attention split per kv head,
-    200 give several (the combine runs before the heads are counted)."""
+def test_head128_device_position_bit_identical(wdt, kvdt, P):
+    """k2_decode_step_dev (position read on the device, grids sized for the
+    capacity, blocks past the position's split count leaving at once) against
+    k2_decode_step (host position, grids sized for it): the same splits do
+    the same arithmetic, so every logit and token is the same bit for bit.
+    3 prompt positions give one attention split per kv head, 200 give
+    several."""
     cfg = HEAD128.replace(wdt=wdt, kvdt=kvdt)
     prompt = synth.prompt(cfg, P)
-    out = {}
-    for ao in ("1", "0"):
-        monkeypatch.setenv("K2_ATTN_O", ao)
-        gm = DecodeModel(cfg, DEV)
-        out[ao] = gm.generate(prompt, cfg.n_decode)
-    (t1, l1), (t0, l0) = out["1"], out["0"]
-    assert t1 == t0
-    for i, (a, b) in enumerate(zip(l1, l0)):
+    t_host, l_host = DecodeModel(cfg, DEV).generate(prompt, cfg.n_decode)
+    t_dev, l_dev = _generate_dev(DecodeModel(cfg, DEV), prompt, cfg.n_decode, teacher=t_host)
+    assert t_dev == t_host
+    for i, (a, b) in enumerate(zip(l_dev, l_host)):
         assert np.array_equal(a, b), (i, float(np.abs(a - b).max()))
 
 
@@ -170,15 +172,42 @@ def test_decode_step_dev_token_feedback_and_error_flag():
     hist = torch.zeros(8, dtype=torch.int32, device=DEV)
     hist[0] = int(pr[-1])
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gm.set_pos(len(pr) - 1)
     for i in range(6):
-        gm.step_dev(hist[i:i + 1], len(pr) - 1 + i, hist[i + 1:i + 2], err)
+        gm.step_dev(hist[i:i + 1], hist[i + 1:i + 2], err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     assert to_host(hist[1:7]).tolist() == ref_toks
+    assert int(gm.d_pos.item()) == len(pr) + 5            # advanced once per step
+    # a token outside the vocabulary: flagged, the step runs on token 0
     bad = torch.full((1,), cfg.vocab + 5, dtype=torch.int32, device=DEV)
-    gm.step_dev(bad, 0, hist[7:8], err)
+    gm.set_pos(0)
+    gm.step_dev(bad, hist[7:8], err)
     torch.cuda.synchronize()
     assert int(err.item()) == k2.K2_ERANGE
+
+
+@pytest.mark.parametrize("bad_pos", [-1, "cap"])
+def test_decode_step_dev_position_out_of_range(bad_pos):
+    """A device position outside [0, cap): d_err is set, no cache slot is
+    written and the position is not advanced."""
+    cfg = synth.TINY
+    gm = DecodeModel(cfg, DEV)
+    for p, t in enumerate(synth.prompt(cfg, 5)):
+        gm.step(int(t), p, want_logits=False)
+    torch.cuda.synchronize()
+    caches = [(L["kc"].clone(), L["vc"].clone()) for L in gm.layers]
+    pos = cfg.cap if bad_pos == "cap" else bad_pos
+    gm.set_pos(pos)
+    tok = torch.zeros(1, dtype=torch.int32, device=DEV)
+    nxt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gm.step_dev(tok, nxt, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == k2.K2_ERANGE
+    assert int(gm.d_pos.item()) == pos
+    for L, (kc, vc) in zip(gm.layers, caches):
+        assert torch.equal(L["kc"], kc) and torch.equal(L["vc"], vc)
 
 
 @pytest.mark.slow
@@ -273,15 +302,6 @@ def test_head128_prefill_matches_oracle(kvdt, P):
     of the workspace zeroed)."""
     cfg = HEAD128.replace(wdt="bf16", kvdt=kvdt, cap=128)
     _prefill_parity(cfg, P, 3)
-
-
-@pytest.mark.parametrize("kvdt", ["bf16", "i8"])
-def test_head128_prefill_per_position_attention(kvdt, monkeypatch):
-    """The chunk's attention one position per launch (K2_PREFILL_ROWS=0),
-    the form used before the one-launch chunk attention: same parity bar."""
-    monkeypatch.setenv("K2_PREFILL_ROWS", "0")
-    cfg = HEAD128.replace(wdt="bf16", kvdt=kvdt, cap=128)
-    _prefill_parity(cfg, 70, 2)
 
 
 def test_prefill_equals_decode_steps_on_cache():
