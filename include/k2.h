@@ -208,6 +208,23 @@ int k2_gqa_decode_attn(k2_dtype kvdt, const float *q, const void *kc, const void
                        int head_dim, int cap, int len, float scale, void *ws, size_t ws_bytes,
                        void *stream);
 
+/* k2_gqa_decode_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and the same kernels, with the
+ * workspace in a file-scope device array of the library
+ * (k2_gqa_decode_attn_scratch_limit() bytes, 4 MiB; one copy per device,
+ * held until the process ends) instead of a caller buffer.  The call
+ * allocates nothing.  K2_EUNSUPPORTED when k2_attn_workspace_bytes(n_qh,
+ * n_kv, head_dim, cap) exceeds the limit (nothing enqueued); otherwise the
+ * refusals of k2_gqa_decode_attn, and K2_EHIP if the array's device address
+ * cannot be obtained.  Every call on one device shares that device's array:
+ * calls that overlap in time on one device (other streams, other host
+ * threads) race and must be serialized by the caller. */
+size_t k2_gqa_decode_attn_scratch_limit(void);
+int k2_gqa_decode_attn_noalloc(k2_dtype kvdt, const float *q, const void *kc, const void *vc,
+                               const float *ks, const float *vs, float *out, int n_qh, int n_kv,
+                               int head_dim, int cap, int len, float scale, void *stream);
+
 /* Fused step used by k2_decode_step: from the raw QKV projection
  * qkv = [q (n_qh*hd); k (n_kv*hd); v (n_kv*hd)], rotate q and k at `pos`,
  * store k and v at slot `pos` of the cache (kvdt as above), then attend over

@@ -1,6 +1,8 @@
 // attn.hip -- split-K GQA decode attention for gfx950, with the RoPE and
 // KV-cache append of the new position fused in: launchers and C ABI (the
 // device code is in attn_impl.h).
+#include <atomic>
+
 #include "attn_impl.h"
 
 namespace k2 {
@@ -213,6 +215,78 @@ extern "C" int k2_gqa_decode_attn(k2_dtype kvdt, const float *q, const void *kc,
     if (len < 1 || len > cap) return K2_ERANGE;
     AttnArgs a{};
     attn_ws_carve(ws, n_qh, n_kv, head_dim, cap, a);
+    a.q = q;
+    a.kc = const_cast<void *>(kc);
+    a.vc = const_cast<void *>(vc);
+    a.ks = const_cast<float *>(ks);
+    a.vs = const_cast<float *>(vs);
+    a.out = out;
+    a.n_qh = n_qh;
+    a.n_kv = n_kv;
+    a.cap = cap;
+    a.len = len;
+    a.pos = len - 1;
+    a.scale = scale;
+    a.S = attn_splits(n_kv, len, &a.chunk);
+    return attn_launch(kvdt, head_dim, n_qh / n_kv, false, a, k2_stream(stream));
+}
+
+// ------------------------------------------------ no-allocation variant --
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc): k2_gqa_decode_attn with
+// its workspace (split partials, their (max, sum) pairs and the per-kv-head
+// arrival counters) in this file-scope device array instead of a caller
+// buffer.  Each device holds its own copy until the process ends; its
+// address comes from hipGetSymbolAddress on the first call on that device
+// (in host code the array's name is not a device address).
+constexpr size_t K2_SCRATCH_BYTES = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[K2_SCRATCH_BYTES];
+static std::atomic<void *> g_scratch_dev[64];
+
+// This device's address of `scratch` (set up once per device, with that
+// device current), or nullptr on a runtime error.
+static void *scratch_ptr()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void *p = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+        g_scratch_dev[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
+}
+
+__global__ void zero_u32_kernel(unsigned *p, int n)
+{
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+extern "C" size_t k2_gqa_decode_attn_scratch_limit(void) { return K2_SCRATCH_BYTES; }
+
+extern "C" int k2_gqa_decode_attn_noalloc(k2_dtype kvdt, const float *q, const void *kc, const void *vc,
+                                          const float *ks, const float *vs, float *out, int n_qh,
+                                          int n_kv, int head_dim, int cap, int len, float scale,
+                                          void *stream)
+{
+    if (n_qh <= 0 || n_kv <= 0 || head_dim <= 0 || cap <= 0 || n_qh % n_kv) return K2_EINVAL;
+    const size_t need = attn_ws_bytes(n_qh, n_kv, head_dim, cap);
+    if (need > K2_SCRATCH_BYTES) return K2_EUNSUPPORTED;   // beyond the scratch array
+    void *ws = scratch_ptr();
+    if (!ws) return K2_EHIP;
+    int rc = attn_common_check(kvdt, kc, vc, ks, vs, out, n_qh, n_kv, head_dim, cap, ws, need);
+    if (rc) return rc;
+    if (!k2_ptr_ok(q)) return K2_EINVAL;
+    if (len < 1 || len > cap) return K2_ERANGE;
+    AttnArgs a{};
+    attn_ws_carve(ws, n_qh, n_kv, head_dim, cap, a);
+    // the arrival counters must start at zero: the array keeps whatever the
+    // last call on this device left (a fill kernel, not a memset node, so
+    // that the call can sit inside a captured graph)
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, k2_stream(stream), a.head_cnt, n_kv);
+    K2_CHECK_LAUNCH();
     a.q = q;
     a.kc = const_cast<void *>(kc);
     a.vc = const_cast<void *>(vc);

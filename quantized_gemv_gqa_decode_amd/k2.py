@@ -72,6 +72,9 @@ SIGNATURES = {
     "k2_attn_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "k2_gqa_decode_attn": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp,
                                 _sz, _vp]),
+    "k2_gqa_decode_attn_scratch_limit": (_sz, []),
+    "k2_gqa_decode_attn_noalloc": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
+                                        _vp]),
     "k2_rope_append_attn": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
                                  _sz, _vp]),
     "k2_rope_append_attn_o": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
@@ -223,6 +226,17 @@ def k2_gqa_decode_attn(kvdt, q, kc, vc, ks, vs, out, n_qh, n_kv, head_dim, cap, 
     return load().k2_gqa_decode_attn(kvdt, ptr(q), ptr(kc), ptr(vc), ptr(ks), ptr(vs), ptr(out),
                                      n_qh, n_kv, head_dim, cap, length, float(scale), ptr(ws),
                                      ws_bytes, stream_handle(stream))
+
+
+def k2_gqa_decode_attn_scratch_limit() -> int:
+    return load().k2_gqa_decode_attn_scratch_limit()
+
+
+def k2_gqa_decode_attn_noalloc(kvdt, q, kc, vc, ks, vs, out, n_qh, n_kv, head_dim, cap, length,
+                               scale, stream=None):
+    return load().k2_gqa_decode_attn_noalloc(kvdt, ptr(q), ptr(kc), ptr(vc), ptr(ks), ptr(vs),
+                                             ptr(out), n_qh, n_kv, head_dim, cap, length,
+                                             float(scale), stream_handle(stream))
 
 
 def k2_rope_append_attn(kvdt, qkv, cos_sin, kc, vc, ks, vs, out, n_qh, n_kv, head_dim, cap, pos,
