@@ -551,14 +551,24 @@ static __shared__ unsigned long long k2_attn_trs[12];
 #endif
 
 // Block shape of the streaming attention: waves per block, tiles in flight,
-// bytes per K (or V) tile.  The stand-alone kernel uses 8 waves, 3 stages of
-// 16 KiB; the fused layer kernel (fused_impl.h) a leaner 4 waves, 2 stages
-// of 8 KiB, to share one LDS budget with its GEMV blocks.
+// bytes per K (or V) tile.  Every attention kernel uses 8 waves and, by
+// default, 2 stages of 16 KiB K + 16 KiB V tiles (K2_ATT_NST, K2_ATT_TILE):
+// ~66 KiB of LDS, so two blocks fit a compute unit.  Measured at the 3.7B
+// shape against 3 stages (~98 KiB, one block per unit): decode step with the
+// position on the device 2.155 against 2.204 ms (bf16 cache, L 520-776),
+// int8 attention at 32k positions 31.7 against 33.8 us; 8 KiB tiles (3 or 4
+// stages) were slower at 32k (35.7-36.9 us).
 template <int WPB_, int NST_, int TILE_>
 struct StreamCfg {
     static constexpr int WPB = WPB_, NT = WPB_ * K2_WAVE, NST = NST_, TILE = TILE_;
 };
-using StreamWide = StreamCfg<8, 3, 16384>;
+#ifndef K2_ATT_NST
+#define K2_ATT_NST 2
+#endif
+#ifndef K2_ATT_TILE
+#define K2_ATT_TILE 16384
+#endif
+using StreamWide = StreamCfg<8, K2_ATT_NST, K2_ATT_TILE>;
 constexpr int ATT_NT = StreamWide::NT;     // threads per stand-alone attention block
 
 template <int KVDT, int HD, class C = StreamWide>

@@ -9,7 +9,10 @@ namespace k2 {
 
 // O rows per wave; chunks per lane cover one 4096-wide row of each format in
 // one pass (f32 16, bf16 8, fp8 4, MXFP4 and Q4S 2)
-constexpr int AO_R = 2;
+#ifndef K2_AO_R
+#define K2_AO_R 2
+#endif
+constexpr int AO_R = K2_AO_R;
 template <int WDT> struct AoTile { static constexpr int U = 4096 / (K2_WAVE * WT<WDT>::EPC); };
 
 template <int WDT, int KVDT>
@@ -21,20 +24,29 @@ static int attn_o_go(const AttnOArgs &f0, hipStream_t st)
     f.o.n_units = (f.o.N + AO_R - 1) / AO_R;
     f.na = f.at.S * f.at.n_kv;
     const int no = (int)((f.o.n_units + WPB - 1) / WPB);
-    const int cus = device_cus();
-    // with a host position: only when both grids fit at once (else the two
-    // kernels); with a device position the split count is not known here
-    // and the one launch is always taken (correct whatever fits, see
-    // attn_o_impl.h)
-    if (cus <= 0 || (!f.at.d_pos && f.na + no > cus)) return K2_EUNSUPPORTED;
     size_t lds = attn_stream_lds_floats<KVDT, HD, REP>();
     const size_t lc = combine_lds_floats<REP, ATT_NT>();
     const size_t lo = (size_t)EPC * xs_plane(f.o.K / EPC);
     lds = lds > lc ? lds : lc;
     lds = lds > lo ? lds : lo;
     if (lds * sizeof(float) > 160 * 1024) return K2_EUNSUPPORTED;
-    hipLaunchKernelGGL((attn_o_kernel<WDT, KVDT, HD, REP, AO_R, U>), dim3(f.na + no), dim3(ATT_NT),
-                       lds * sizeof(float), st, f);
+    auto kern = attn_o_kernel<WDT, KVDT, HD, REP, AO_R, U>;
+    // blocks of this launch one compute unit holds at once (LDS, waves,
+    // registers), asked once per instantiation
+    static const int per_cu = [&] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(kern), ATT_NT,
+                                                         lds * sizeof(float)) != hipSuccess)
+            n = 1;
+        return n < 1 ? 1 : n;
+    }();
+    const int cus = device_cus();
+    // with a host position: only when both grids fit at once (else the two
+    // kernels); with a device position the split count is not known here
+    // and the one launch is always taken (correct whatever fits, see
+    // attn_o_impl.h)
+    if (cus <= 0 || (!f.at.d_pos && f.na + no > cus * per_cu)) return K2_EUNSUPPORTED;
+    hipLaunchKernelGGL(kern, dim3(f.na + no), dim3(ATT_NT), lds * sizeof(float), st, f);
     K2_CHECK_LAUNCH();
     return K2_OK;
 }
@@ -69,3 +81,12 @@ int attn_o_launch(int wdt, int kvdt, int hd, int rep, const AttnArgs &at, const 
 }
 
 }  // namespace k2
+
+#ifdef K2_ATTN_TRACE
+// per-block stage timestamps of the last attention + O launch (trace builds)
+extern "C" int k2_attn_o_trace_read(unsigned long long *out, int n)
+{
+    return hipMemcpyFromSymbol(out, HIP_SYMBOL(k2::k2_attn_trace), sizeof(unsigned long long) * n) ==
+                   hipSuccess ? 0 : -4;
+}
+#endif

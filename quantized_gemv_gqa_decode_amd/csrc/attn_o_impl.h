@@ -25,7 +25,8 @@ namespace k2 {
 // while the attention ran.
 //   * the block that completes kv head g (its combiner, or the only split)
 //     stores the head's output at device scope, waits for the stores and
-//     counts the head; the last head raises every ready copy;
+//     raises head g's flag in every copy of the flag line; an O block waits
+//     until its copy shows every head's flag (one wave polls one line);
 //   * every O block counts itself when done; the last one clears the
 //     counters and flags, so the sync words are zero between launches.
 // Blocks start in index order and an O block waits only for attention
@@ -53,6 +54,12 @@ struct AttnOArgs {
 // lets those go first and still lands the O rows well before the attention
 // ends (3.7B shape: ~2 % faster per decode step than no hold-back).
 constexpr int AO_O_DELAY_TICKS = 120;
+#ifndef K2_AO_HEADFLAGS
+#define K2_AO_HEADFLAGS 1
+#endif
+#ifndef K2_AO_RESPRE
+#define K2_AO_RESPRE 1
+#endif
 
 template <int KVDT, int HD, int REP>
 __device__ __forceinline__ void ao_attn_role(const AttnOArgs &f, int ab, float *smem)
@@ -70,6 +77,7 @@ __device__ __forceinline__ void ao_attn_role(const AttnOArgs &f, int ab, float *
     if (S > 1) {
         __builtin_amdgcn_s_waitcnt(0);             // this thread's partial stores completed
         __syncthreads();
+        K2_ATRACE(4);
         if (threadIdx.x == 0) {
             const unsigned old = __hip_atomic_fetch_add(a.head_cnt + g, 1u, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT);
@@ -77,25 +85,37 @@ __device__ __forceinline__ void ao_attn_role(const AttnOArgs &f, int ab, float *
             if (complete) __hip_atomic_store(a.head_cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
-        if (complete) attn_combine_block<HD, REP, true, ATT_NT>(a, g, smem);
+        K2_ATRACE(5);
+        if (complete) {
+            attn_combine_block<HD, REP, true, ATT_NT>(a, g, smem);
+            K2_ATRACE(6);
+        }
     } else {
         if (threadIdx.x == 0) complete = 1;
         __syncthreads();
     }
-    if (complete) {                                // the head's output is stored: count it
+    if (complete) {                                // the head's output is stored: raise its flags
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+#if K2_AO_HEADFLAGS
+        if (threadIdx.x < AO_READY_COPIES)
+            __hip_atomic_store(sync + AO_SYNC_READY + threadIdx.x * 64 + g, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+#else
         if (threadIdx.x == 0) {
-            const unsigned done = __hip_atomic_fetch_add(sync + AO_SYNC_HEADS, 1u, __ATOMIC_RELAXED,
+            const unsigned done = __hip_atomic_fetch_add(sync + AO_SYNC_ODONE - 32, 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
             if (done == (unsigned)a.n_kv - 1)
                 for (int c = 0; c < AO_READY_COPIES; ++c)
-                    __hip_atomic_store(sync + AO_SYNC_READY + c * 64, 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+                    for (int h = 0; h < a.n_kv; ++h)
+                        __hip_atomic_store(sync + AO_SYNC_READY + c * 64 + h, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
         }
+#endif
     }
     // the new position's K/V: no block of this launch reads slot pos
     if (holder) kv_write_head<KVDT, HD>(kv_bits, kv_scale, a.kc, a.vc, a.ks, a.vs, g, a.cap, a.pos);
+    K2_ATRACE(11);
 }
 
 template <int WDT, int R, int U>
@@ -115,29 +135,65 @@ __device__ __forceinline__ void ao_o_role(const AttnOArgs &f, int ob, float *xs)
     bool ok[R];
     k2_u4 w[U][R];
     float sc[U][R];
+    K2_ATRACE(0);
     {
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         while (__builtin_amdgcn_s_memrealtime() - t0 < (uint64_t)AO_O_DELAY_TICKS) __builtin_amdgcn_s_sleep(2);
     }
+    K2_ATRACE(1);
     gemv_prefetch<WDT, R, U, EPI_PLAIN>(a, unit, rows, ok, w, sc);   // weights before the wait
-    block_wait_count(sync + AO_SYNC_READY + (ob % AO_READY_COPIES) * 64, 1u, f.d_err);
+    // the residual of this wave's first unit does not depend on the
+    // attention either: lane r loads row r's now
+    const int lane = threadIdx.x & 63;
+#if K2_AO_RESPRE
+    const float res0 = (lane < R && ok[lane < R ? lane : 0]) ? a.residual[rows[lane < R ? lane : 0]] : 0.f;
+    const float *res0p = &res0;
+#else
+    const float *res0p = nullptr;
+#endif
+    K2_ATRACE(2);
+    // every kv head's ready flag, in this block's copy of the flag line
+    {
+        __shared__ int ok_s;
+        const unsigned *fl = sync + AO_SYNC_READY + (ob % AO_READY_COPIES) * 64;
+        const int nkv = f.at.n_kv;
+        if (threadIdx.x < K2_WAVE) {
+            int spins = 0;
+            bool all;
+            do {
+                const unsigned v = lane < nkv ? coh_load_u(fl + lane) : 1u;
+                all = __all(v != 0u);
+                if (!all) __builtin_amdgcn_s_sleep(K2_WAIT_SLEEP);
+            } while (!all && ++spins < K2_WAIT_SPIN_LIMIT);
+            if (lane == 0) ok_s = all;
+            if (!all && lane == 0 && f.d_err) coh_store_i(f.d_err, K2_EHIP);
+        }
+        __syncthreads();
+    }
+    K2_ATRACE(3);
     // the attention output (B = 1), device scope, into the GEMV's LDS planes
     for (int i = threadIdx.x * 4; i < a.K; i += ATT_NT * 4)
         *reinterpret_cast<float4 *>(xs + xs_offset<EPC>(i, S)) = ld4<true>(a.x, i);
     __syncthreads();
-    gemv_units<WDT, R, U, 1, EPI_PLAIN, false>(a, xs, S, unit, stride, rows, ok, w, sc, best_v, best_i);
+    K2_ATRACE(4);
+    gemv_units<WDT, R, U, 1, EPI_PLAIN, false>(a, xs, S, unit, stride, rows, ok, w, sc, best_v, best_i, res0p);
     __syncthreads();                               // every wave of the block is past its wait
+    K2_ATRACE(5);
     if (threadIdx.x == 0) {
         const unsigned d = __hip_atomic_fetch_add(sync + AO_SYNC_ODONE, 1u, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
         if (d == (unsigned)nob - 1) {              // the last O block: clear for the next launch
-            __hip_atomic_store(sync + AO_SYNC_HEADS, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#if !K2_AO_HEADFLAGS
+            __hip_atomic_store(sync + AO_SYNC_ODONE - 32, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#endif
             for (int c = 0; c < AO_READY_COPIES; ++c)
-                __hip_atomic_store(sync + AO_SYNC_READY + c * 64, 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                for (int h = 0; h < f.at.n_kv; ++h)
+                    __hip_atomic_store(sync + AO_SYNC_READY + c * 64 + h, 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(sync + AO_SYNC_ODONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+    K2_ATRACE(11);
 }
 
 template <int WDT, int KVDT, int HD, int REP, int R, int U>
@@ -147,9 +203,11 @@ __global__ __launch_bounds__(ATT_NT) void attn_o_kernel(const AttnOArgs f0)
     float *smem = reinterpret_cast<float *>(lds4);
     AttnOArgs f = f0;
     if (!attn_resolve_pos(f.at)) return;           // nothing is written
+    K2_ATRACE_CLEAR();
     const int b = blockIdx.x;
     if (b < f.na) ao_attn_role<KVDT, HD, REP>(f, b, smem);
     else ao_o_role<WDT, R, U>(f, b - f.na, smem);
+    K2_ATRACE_FLUSH();
 }
 
 }  // namespace k2

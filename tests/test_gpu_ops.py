@@ -173,7 +173,7 @@ def test_q4s_decode_every_nibble_via_gemv():
                                    (70, 4096, 1), (33, 10240, 1), (45, 320, 2), (19, 1024, 4),
                                    (23, 1536, 8),
                                    # rows split over 2 or 4 waves (long rows), ragged row counts
-                                   (2561, 10240, 1), (1001, 5632, 1), (3, 3072, 1)])
+                                   (2561, 10240, 1), (1001, 5632, 1), (3, 3072, 1), (7, 12288, 1)])
 def test_gemv_matches_oracle(wdt, N, K, B):
     if wdt == "q4s" and K % 64:
         pytest.skip("Q4S blocks are 64 columns")
@@ -391,12 +391,15 @@ def test_rope_append_attn_matches_oracle(kvdt, hd, n_qh, n_kv, pos):
 @pytest.mark.parametrize("pos", [0, 200, 700, 3000])
 def test_rope_append_attn_o(wdt, kvdt, pos):
     """Attention then the O projection + residual at the 3.7B head shape (32 q /
-    8 kv heads, hd 128, hidden 2560).  With a bf16 cache up to ~770 positions
-    it is one launch (O blocks beside the attention blocks), otherwise the
-    attention kernel and the GEMV; either way out, h and the cache are bit-identical to
-    k2_rope_append_attn followed by the GEMV, and h matches the oracle
-    (fp64 attention, then the dequantized O matvec) within the attention's
-    error carried through |W_o| plus the fp32 summation bound."""
+    8 kv heads, hd 128, hidden 2560).  With a bf16 cache while both grids fit
+    the chip (about 2.8k positions at two blocks per compute unit) it is one
+    launch (O blocks beside the attention blocks), otherwise the
+    attention kernel and the GEMV; either way out and the cache are
+    bit-identical to k2_rope_append_attn followed by the GEMV, h agrees with
+    that pair within the fp32 summation bound (the stand-alone GEMV sums a
+    4096-wide row over four waves), and both match the oracle (fp64
+    attention, then the dequantized O matvec) within the attention's error
+    carried through |W_o| plus the fp32 summation bound."""
     n_qh, n_kv, hd, H = 32, 8, 128, 2560
     K = n_qh * hd
     say(f"attn+O {wdt} {kvdt} pos={pos}")
@@ -437,8 +440,13 @@ def test_rope_append_attn_o(wdt, kvdt, pos):
         assert not torch.any(ws[-(256 + 4608):] != 0), "counters left zeroed"
         res.append((to_host(out), to_host(h), to_host(kc, view), to_host(vc, view), to_host(ks),
                     to_host(vs)))
-    for a, b in zip(res[0], res[1]):
-        assert np.array_equal(a, b)
+    # out and the caches are the same bytes; h is the same product summed in
+    # another order where the stand-alone GEMV splits a row over four waves
+    for i, (a, b) in enumerate(zip(res[0], res[1])):
+        if i != 1:
+            assert np.array_equal(a, b)
+    hd_diff = np.abs(res[0][1].astype(np.float64) - res[1][1].astype(np.float64))
+    assert np.all(hd_diff <= 2 * sumabs_bound(dense, to_host(out).astype(np.float64)) + 1e-6), hd_diff.max()
     q = oracle.rope(qkv[:K].astype(np.float64), n_qh, hd, pos, 1e4)
     k = oracle.rope(qkv[K:K + n_kv * hd].astype(np.float64), n_kv, hd, pos, 1e4)
     v = qkv[K + n_kv * hd:].astype(np.float64)
@@ -449,8 +457,8 @@ def test_rope_append_attn_o(wdt, kvdt, pos):
     step = (np.abs(v).max() / 127) if kvdt == "i8" else 0.0
     att_tol = 5e-5 * vmax + 2 * step + 1e-5
     bound = np.abs(dense) @ np.full(K, att_tol) + sumabs_bound(dense, att) + 1e-5
-    got = res[0][1].astype(np.float64)
-    assert np.all(np.abs(got - href) <= bound), float(np.abs(got - href).max())
+    for got in (res[0][1].astype(np.float64), res[1][1].astype(np.float64)):
+        assert np.all(np.abs(got - href) <= bound), float(np.abs(got - href).max())
 
 
 # ------------------------------------------------------------------ argmax ---
