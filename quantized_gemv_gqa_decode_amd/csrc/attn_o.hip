@@ -9,10 +9,7 @@ namespace k2 {
 
 // O rows per wave; chunks per lane cover one 4096-wide row of each format in
 // one pass (f32 16, bf16 8, fp8 4, MXFP4 and Q4S 2)
-#ifndef K2_AO_R
-#define K2_AO_R 2
-#endif
-constexpr int AO_R = K2_AO_R;
+constexpr int AO_R = 2;        // 1 measured slower (19.1 against 17.6 us at 776 positions)
 template <int WDT> struct AoTile { static constexpr int U = 4096 / (K2_WAVE * WT<WDT>::EPC); };
 
 template <int WDT, int KVDT>

@@ -54,12 +54,7 @@ struct AttnOArgs {
 // lets those go first and still lands the O rows well before the attention
 // ends (3.7B shape: ~2 % faster per decode step than no hold-back).
 constexpr int AO_O_DELAY_TICKS = 120;
-#ifndef K2_AO_HEADFLAGS
-#define K2_AO_HEADFLAGS 1
-#endif
-#ifndef K2_AO_RESPRE
-#define K2_AO_RESPRE 1
-#endif
+
 
 template <int KVDT, int HD, int REP>
 __device__ __forceinline__ void ao_attn_role(const AttnOArgs &f, int ab, float *smem)
@@ -97,21 +92,9 @@ __device__ __forceinline__ void ao_attn_role(const AttnOArgs &f, int ab, float *
     if (complete) {                                // the head's output is stored: raise its flags
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-#if K2_AO_HEADFLAGS
         if (threadIdx.x < AO_READY_COPIES)
             __hip_atomic_store(sync + AO_SYNC_READY + threadIdx.x * 64 + g, 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-#else
-        if (threadIdx.x == 0) {
-            const unsigned done = __hip_atomic_fetch_add(sync + AO_SYNC_ODONE - 32, 1u, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            if (done == (unsigned)a.n_kv - 1)
-                for (int c = 0; c < AO_READY_COPIES; ++c)
-                    for (int h = 0; h < a.n_kv; ++h)
-                        __hip_atomic_store(sync + AO_SYNC_READY + c * 64 + h, 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-        }
-#endif
     }
     // the new position's K/V: no block of this launch reads slot pos
     if (holder) kv_write_head<KVDT, HD>(kv_bits, kv_scale, a.kc, a.vc, a.ks, a.vs, g, a.cap, a.pos);
@@ -145,12 +128,7 @@ __device__ __forceinline__ void ao_o_role(const AttnOArgs &f, int ob, float *xs)
     // the residual of this wave's first unit does not depend on the
     // attention either: lane r loads row r's now
     const int lane = threadIdx.x & 63;
-#if K2_AO_RESPRE
     const float res0 = (lane < R && ok[lane < R ? lane : 0]) ? a.residual[rows[lane < R ? lane : 0]] : 0.f;
-    const float *res0p = &res0;
-#else
-    const float *res0p = nullptr;
-#endif
     K2_ATRACE(2);
     // every kv head's ready flag, in this block's copy of the flag line
     {
@@ -176,16 +154,13 @@ __device__ __forceinline__ void ao_o_role(const AttnOArgs &f, int ob, float *xs)
         *reinterpret_cast<float4 *>(xs + xs_offset<EPC>(i, S)) = ld4<true>(a.x, i);
     __syncthreads();
     K2_ATRACE(4);
-    gemv_units<WDT, R, U, 1, EPI_PLAIN, false>(a, xs, S, unit, stride, rows, ok, w, sc, best_v, best_i, res0p);
+    gemv_units<WDT, R, U, 1, EPI_PLAIN, false>(a, xs, S, unit, stride, rows, ok, w, sc, best_v, best_i, &res0);
     __syncthreads();                               // every wave of the block is past its wait
     K2_ATRACE(5);
     if (threadIdx.x == 0) {
         const unsigned d = __hip_atomic_fetch_add(sync + AO_SYNC_ODONE, 1u, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
         if (d == (unsigned)nob - 1) {              // the last O block: clear for the next launch
-#if !K2_AO_HEADFLAGS
-            __hip_atomic_store(sync + AO_SYNC_ODONE - 32, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#endif
             for (int c = 0; c < AO_READY_COPIES; ++c)
                 for (int h = 0; h < f.at.n_kv; ++h)
                     __hip_atomic_store(sync + AO_SYNC_READY + c * 64 + h, 0u, __ATOMIC_RELAXED,
