@@ -459,6 +459,52 @@ def bench_verify(cfg, gm, P, args, stream):
     print(json.dumps(out), flush=True)
 
 
+def bench_spec(cfg, gm, P, args, stream):
+    """Speculative greedy decode with the n-gram drafter (draft.py): the
+    512-token prompt, then N greedy tokens as draft-and-verify rounds
+    (k2_verify of [last token, drafts]; a round without a draft is one
+    k2_decode_step), wall-clock timed with the host loop it needs.  The same
+    N tokens by plain greedy decode are timed first and must be equal."""
+    import numpy as np
+    import torch
+    import synth
+    prompt = synth.prompt(cfg, P)
+    N = args.steps
+    gm.prefill(prompt, 0)
+    hist = torch.zeros(N + 1, dtype=torch.int32, device=gm.device)
+    hist[0:1].copy_(gm.next)
+    gm.set_pos(P)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(N - 1):
+        gm.step_dev(hist[j:j + 1], hist[j + 1:j + 2])
+    torch.cuda.synchronize()
+    plain_s = time.perf_counter() - t0
+    plain = hist[:N].cpu().numpy().tolist()
+    gm.generate_speculative(prompt, 8, None, args.spec)           # warm (also the verify workspace)
+    gm.prefill(prompt, 0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    toks, rounds = gm.generate_speculative(prompt, N, None, args.spec, prefilled=True)
+    torch.cuda.synchronize()
+    spec_s = time.perf_counter() - t0
+    st = gm.spec_stats
+    out = {
+        "metric": "speculative greedy decode tokens/s (n-gram drafter, batched verification)",
+        "value": round(N / spec_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": N, "warmup": 1,
+        "ms_per_step": round(spec_s / N * 1000, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "prompt_len": P, "max_drafts": args.spec,
+                   "weights": cfg.wdt, "kv_cache": cfg.kvdt},
+        "plain_greedy_tokens_per_s": round(N / plain_s, 1),
+        "rounds": rounds, "drafted": st["drafted"], "accepted": st["accepted"],
+        "acceptance": round(st["accepted"] / st["drafted"], 4) if st["drafted"] else None,
+        "tokens_equal_plain_greedy": toks == plain,
+        "note": "wall clock of the host loops after the prompt's prefill, both ways",
+    }
+    print(json.dumps(out), flush=True)
+
+
 def synth_config(name):
     import synth
     return synth.CONFIGS[name]
@@ -599,6 +645,10 @@ def main():
     ap.add_argument("--verify-chunk", type=int, default=0, metavar="T",
                     help="instead of the decode bench: time k2_verify of T positions (2..32; "
                          "bf16 weights) after the prompt, i.e. one draft-and-verify round")
+    ap.add_argument("--spec", type=int, default=0, metavar="K",
+                    help="instead of the decode bench: greedy decode of --steps tokens as "
+                         "draft-and-verify rounds with the n-gram drafter (up to K drafts), "
+                         "against plain greedy decode of the same tokens")
     ap.add_argument("--sample", action="store_true",
                     help="instead of the decode bench: time k2_sample over the config's vocabulary "
                          "(temperature 0.8, top-k 40, top-p 0.9, min-p 0.05, penalty 1.2 on 32 ids)")
@@ -655,6 +705,8 @@ def main():
         return bench_prefill(cfg, gm, P, args, stream)
     if args.verify_chunk:
         return bench_verify(cfg, gm, P, args, stream)
+    if args.spec:
+        return bench_spec(cfg, gm, P, args, stream)
 
     if args.prefix:
         if cfg.kvdt != "i8":

@@ -196,36 +196,47 @@ class DecodeModel:
                               self._vf_ws.numel(), stream))
         return self._vf_next[:T]
 
-    def generate_speculative(self, prompt, n_decode: int, draft, k: int):
+    def generate_speculative(self, prompt, n_decode: int, draft=None, k: int = 8,
+                             prefilled: bool = False):
         """Greedy decode with draft-and-verify: after the prompt (prefill),
-        each round feeds [last token, k drafted tokens] to k2_verify and keeps
-        the greedy tokens up to the first draft that disagrees.  draft(history,
-        k) returns k proposed tokens.  Returns (tokens, rounds); the tokens are
-        those of plain greedy decode."""
+        each round feeds [last token, drafted tokens] to k2_verify and keeps
+        the greedy tokens up to the first draft that disagrees; a round with
+        no draft is one plain decode step.  draft(history, k) returns up to k
+        proposed tokens (default: the n-gram drafter of ``draft.py``).
+        Returns (tokens, rounds); the tokens are those of plain greedy
+        decode.  self.spec_stats counts rounds, drafted and accepted tokens.
+        prefilled: the caches already hold the prompt and self.next its
+        greedy token (the prompt is then only the drafter's history)."""
+        from .draft import ngram_draft
+        if draft is None:
+            draft = ngram_draft
         P = len(prompt)
         n_decode = min(n_decode, self.cfg.cap - P)
-        self.prefill(prompt, 0)
+        if not prefilled:
+            self.prefill(prompt, 0)
         torch.cuda.synchronize()
         toks = [int(self.next.item())]
-        rounds = 0
+        rounds = drafted = accepted = 0
         while len(toks) < n_decode:
             pos = P + len(toks) - 1                   # where the last token goes
             kk = min(k, self.cfg.cap - 1 - pos, 31)
-            if kk < 1:
+            d = [int(t) for t in draft(list(prompt) + toks, kk)][:kk] if kk >= 1 else []
+            rounds += 1
+            if not d:
                 lg, nx = self.step(toks[-1], pos)
                 torch.cuda.synchronize()
                 toks.append(int(nx.item()))
-                rounds += 1
                 continue
-            d = [int(t) for t in draft(list(prompt) + toks, kk)]
             g = self.verify([toks[-1]] + d, pos).cpu().numpy().tolist()
-            rounds += 1
+            drafted += len(d)
             new = [g[0]]
-            for i in range(1, kk + 1):
+            for i in range(1, len(d) + 1):
                 if d[i - 1] != new[-1]:
                     break
                 new.append(g[i])
+            accepted += len(new) - 1
             toks.extend(new[:n_decode - len(toks)])
+        self.spec_stats = {"rounds": rounds, "drafted": drafted, "accepted": accepted}
         return toks, rounds
 
     def set_pos(self, pos: int):

@@ -449,14 +449,17 @@ def test_head128_verify_every_row_matches_oracle():
 
 
 @pytest.mark.parametrize("kvdt", ["bf16", "i8"])
-@pytest.mark.parametrize("mode", ["exact", "wrong", "half"])
+@pytest.mark.parametrize("mode", ["exact", "wrong", "half", "ngram"])
 def test_head128_speculative_decode_equals_greedy(kvdt, mode):
     """Draft-and-verify greedy decode gives the oracle's greedy tokens
     whatever the drafts: all right (every draft accepted), all wrong (one
-    token per round), or right every other round."""
+    token per round), right every other round, or the n-gram drafter's
+    (draft.py) on a prompt that repeats a stretch, so that its drafts fire."""
     cfg = HEAD128.replace(wdt="bf16", kvdt=kvdt, cap=128)
     P, n = 16, 40
     prompt = synth.prompt(cfg, P)
+    if mode == "ngram":                      # a repeated stretch the drafter can match
+        prompt = np.concatenate([prompt[:8], prompt[:8]])
     dec = oracle.Decoder.from_synth(cfg)
     ref_toks, ref_lg = dec.generate(prompt, n + 8)
     calls = [0]
@@ -470,7 +473,8 @@ def test_head128_speculative_decode_equals_greedy(kvdt, mode):
         return [(t + 1) % cfg.vocab for t in true]
 
     gm = DecodeModel(cfg, DEV)
-    toks, rounds = gm.generate_speculative(prompt, n, draft, 7)
+    toks, rounds = gm.generate_speculative(prompt, n, None if mode == "ngram" else draft,
+                                           8 if mode == "ngram" else 7)
     for i, (a, b) in enumerate(zip(toks, ref_toks)):
         if a != b:
             assert near_tie_ok(a, ref_lg[i], 1e-3), (i, a, b)
@@ -481,7 +485,7 @@ def test_head128_speculative_decode_equals_greedy(kvdt, mode):
         assert rounds <= (n + 7) // 8 + 1
     if mode == "wrong":
         assert rounds == n - 1
-    say(f"{mode}: {n} tokens in {rounds} rounds")
+    say(f"{mode}: {n} tokens in {rounds} rounds, {gm.spec_stats}")
 
 
 def test_verify_refusals():
