@@ -527,10 +527,12 @@ def cpu_baseline_sample(lg, prev, params, seed, budget_s: float = 5.0):
                       f"consecutive counters, after one untimed call; {dt:.1f} s"}
 
 
-def bench_sample(cfg, cpu: bool = True):
+def bench_sample(cfg, cpu: bool = True, top_k: int = 40, n_prev: int = 32):
     """k2_sample on seeded N(0, 1.5) logits of the config's vocabulary: one
     call per decode position, 200 calls with consecutive counters timed with
-    HIP events (parity with the sampling oracle is the tests' job)."""
+    HIP events (parity with the sampling oracle is the tests' job).  top_k 0
+    (off) or above 64, or more than 64 previous ids, time the
+    whole-vocabulary path."""
     import numpy as np
     import torch
     from quantized_gemv_gqa_decode_amd import k2
@@ -539,8 +541,8 @@ def bench_sample(cfg, cpu: bool = True):
     V = cfg.vocab
     rng = np.random.default_rng(3)
     lg = (rng.standard_normal(V) * 1.5).astype(np.float32)
-    prev = rng.integers(0, V, 32).astype(np.int32)
-    params = (0.8, 40, 0.9, 0.05, 1.2)                   # temperature, top-k, top-p, min-p, penalty
+    prev = rng.integers(0, V, n_prev).astype(np.int32)
+    params = (0.8, top_k, 0.9, 0.05, 1.2)                # temperature, top-k, top-p, min-p, penalty
     X = torch.from_numpy(lg).to(dev)
     P = torch.from_numpy(prev).to(dev)
     sp = k2.k2_sampling(temperature=params[0], top_k=params[1], top_p=params[2], min_p=params[3],
@@ -550,13 +552,13 @@ def bench_sample(cfg, cpu: bool = True):
     n = 200
     out = torch.zeros(n, dtype=torch.int32, device=dev)
     for c in range(8):
-        k2.check(k2.k2_sample(X, V, sp, P, 32, 5, c, out[c:c + 1], ws, wsb))
+        k2.check(k2.k2_sample(X, V, sp, P, n_prev, 5, c, out[c:c + 1], ws, wsb))
     torch.cuda.synchronize()
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
     s.record()
     for c in range(n):
-        k2.check(k2.k2_sample(X, V, sp, P, 32, 5, c, out[c:c + 1], ws, wsb))
+        k2.check(k2.k2_sample(X, V, sp, P, n_prev, 5, c, out[c:c + 1], ws, wsb))
     e.record()
     e.synchronize()
     us = s.elapsed_time(e) / n * 1000
@@ -565,7 +567,9 @@ def bench_sample(cfg, cpu: bool = True):
             "ms_per_step": round(us / 1000, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic", "config": {"workload": cfg.name, "vocab": V,
-                                            "top_k": 40, "n_prev": 32},
+                                            "top_k": top_k, "n_prev": n_prev,
+                                            "path": "one-wave sort" if 1 <= top_k <= 64 and n_prev <= 64
+                                            else "whole vocabulary"},
             "us_per_call": round(us, 1), "tokens_head": out[:8].cpu().tolist()}
     if cpu:
         line["cpu_baseline"] = cpu_baseline_sample(lg, prev, params, 5)
@@ -604,6 +608,58 @@ def read_ceiling(dev, gib: int = 2, reps: int = 10):
     return {"GBps": round(best, 1), "frac_of_peak": round(best / PEAK_HBM_GBPS, 4),
             "kernel": "k2_read_probe (non-temporal 128-bit loads, one slab per block)",
             "bytes": nbytes, "by_blocks": table}
+
+
+def gemv_launches(fmts):
+    """Ten launches each of the 3.7B shape's gate/up (norm + SwiGLU,
+    20480 x 2560) and lm_head (norm + argmax, 250624 x 2560) GEMVs per weight
+    format, on random weights quantized by the library: a fixed workload for
+    profiler counter runs (rocprofv3 --pmc ... -- python3 bench.py
+    --gemv-launches bf16,fp8,mxfp4,q4s)."""
+    import torch
+    from quantized_gemv_gqa_decode_amd import k2
+    k2.load(build_if_missing=False)
+    dev = torch.device("cuda:0")
+    H, I, V = 2560, 10240, 250624
+
+    def mat(wdt, N, K):
+        src = (torch.randn(N, K, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
+        if wdt == "bf16":
+            return src, None
+        if wdt == "fp8":
+            w = torch.empty(N, K, dtype=torch.uint8, device=dev)
+            s = torch.empty(N, device=dev)
+            k2.check(k2.k2_quantize_fp8_rows(src, w, s, N, K))
+        elif wdt == "mxfp4":
+            w = torch.empty(N, K // 2, dtype=torch.uint8, device=dev)
+            s = torch.empty(N, K // 32, dtype=torch.uint8, device=dev)
+            k2.check(k2.k2_quantize_mxfp4(src, w, s, N, K))
+        else:
+            w = torch.empty(N, K // 2, dtype=torch.uint8, device=dev)
+            s = torch.empty(N, K // 64, device=dev)
+            k2.check(k2.k2_quantize_q4s(src, w, s, N, K))
+        torch.cuda.synchronize()
+        return w, s
+
+    h = torch.randn(H, device=dev)
+    g = torch.ones(H, device=dev)
+    act = torch.empty(I, device=dev)
+    lg = torch.empty(V, device=dev)
+    nx = torch.zeros(1, dtype=torch.int32, device=dev)
+    amb = k2.k2_argmax_workspace_bytes(V)
+    amws = torch.zeros(amb, dtype=torch.uint8, device=dev)
+    for f in fmts:
+        dt = k2.DTYPES[f]
+        gu, gus = mat(f, 2 * I, H)
+        lm, lms = mat(f, V, H)
+        for _ in range(10):
+            k2.check(k2.k2_norm_gemv_swiglu(dt, gu, gus, h, g, 2, 1e-6, act, I, H))
+        for _ in range(10):
+            k2.check(k2.k2_norm_gemv_argmax(dt, lm, lms, h, g, 2, 1e-6, lg, V, H, nx, amws, amb))
+        torch.cuda.synchronize()
+        del gu, gus, lm, lms
+        torch.cuda.empty_cache()
+    print(json.dumps({"gemv_launches": fmts, "per_kernel": 10}))
 
 
 def copy_probe(mib: int):
@@ -652,8 +708,14 @@ def main():
     ap.add_argument("--sample", action="store_true",
                     help="instead of the decode bench: time k2_sample over the config's vocabulary "
                          "(temperature 0.8, top-k 40, top-p 0.9, min-p 0.05, penalty 1.2 on 32 ids)")
+    ap.add_argument("--sample-top-k", type=int, default=40, help="--sample: top-k (0 = off)")
+    ap.add_argument("--sample-prev", type=int, default=32, help="--sample: previous ids")
     ap.add_argument("--prefill-steps", action="store_true",
                     help="consume the prompt one decode step per position instead of k2_prefill")
+    ap.add_argument("--gemv-launches", default=None, metavar="FMTS",
+                    help="instead of the decode bench: 10 launches each of the gate/up and "
+                         "lm_head GEMVs per weight format (comma list of bf16, fp8, mxfp4, q4s), "
+                         "a fixed workload for profiler counter runs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the decode bench: launch a plain fp32 copy kernel over "
                          "MIB MiB five times (the known-size reference that scales the HBM "
@@ -671,8 +733,11 @@ def main():
 
     if args.copy_probe:
         return copy_probe(args.copy_probe)
+    if args.gemv_launches:
+        return gemv_launches(args.gemv_launches.split(","))
     if args.sample:
-        return bench_sample(synth_config(args.config), cpu=not args.no_cpu_baseline)
+        return bench_sample(synth_config(args.config), cpu=not args.no_cpu_baseline,
+                            top_k=args.sample_top_k, n_prev=args.sample_prev)
 
     import synth
     from quantized_gemv_gqa_decode_amd import k2

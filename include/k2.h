@@ -258,19 +258,25 @@ int k2_rope_append_attn_o(k2_dtype kvdt, const float *qkv, const float *cos_sin,
                           int32_t *d_err, void *stream);
 
 /* Seeded sampling of one token from logits [vocab] ([k2-burn] "Project
- * layout": sampling.rs -- temperature / top-k / top-p / min-p / repetition
- * penalty; the order is the conventional one, the pages give none):
+ * layout": sampling.rs; "Usage": --top-k / --top-p / --min-p as separate
+ * truncation filters, --repetition-penalty on already-seen tokens; the order
+ * is the conventional one, the pages give none):
  * repetition penalty r on the distinct ids of prev (l > 0 -> l / r, else
- * l * r), temperature, top-k (ties: lower id first), softmax, top-p (the
- * shortest prefix whose probability reaches top_p), min-p (keep p >=
- * min_p * max p), then the first kept token whose cumulative probability
- * exceeds u * the kept total, u = (word 0 of Philox4x32-10(counter = (counter
- * lo, counter hi, 0, 0), key = (seed lo, seed hi))) >> 8) * 2^-24.
- * logits: device float [vocab], vocab <= 262144, read only; prev: device
- * int32 [n_prev] (nullable when n_prev = 0); out_token: device int32.
- * sp (host): 0 < temperature, 1 <= top_k <= 64, 0 < top_p <= 1,
- * 0 <= min_p < 1, repetition_penalty >= 1 (K2_EINVAL / K2_EUNSUPPORTED
- * otherwise); n_prev <= 64.  Greedy decoding is k2_argmax.  ws: device,
+ * l * r), temperature, top-k (ties: lower id first; top_k = 0: off, every
+ * token stays a candidate), softmax, top-p (the shortest prefix whose
+ * probability reaches top_p), min-p (keep p >= min_p * max p), then the first
+ * kept token whose cumulative probability exceeds u * the kept total,
+ * u = (word 0 of Philox4x32-10(counter = (counter lo, counter hi, 0, 0),
+ * key = (seed lo, seed hi))) >> 8) * 2^-24.
+ * logits: device float [vocab], vocab <= 2^24, read only; prev: device int32
+ * [n_prev] (nullable when n_prev = 0; any length, repeats count once, ids
+ * outside the vocabulary are ignored); out_token: device int32.
+ * sp (host): 0 < temperature, top_k >= 0, 0 < top_p <= 1, 0 <= min_p < 1,
+ * repetition_penalty >= 1 (K2_EINVAL otherwise).  1 <= top_k <= 64 with at
+ * most 64 previous ids (and vocab <= 262144) takes a selection of the
+ * k + n_prev best logits sorted by one wave; anything else the
+ * whole-vocabulary path (radix selection by exact fixed-point probability
+ * mass, no sort).  Greedy decoding is k2_argmax.  ws: device,
  * k2_sample_workspace_bytes(vocab) bytes, 256-byte aligned (no state kept
  * between calls). */
 typedef struct {

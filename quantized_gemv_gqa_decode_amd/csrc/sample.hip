@@ -321,10 +321,21 @@ static int sp_slices(int n) { return (n + SP_SLICE - 1) / SP_SLICE; }
 static size_t sp_half_bytes(int vocab) { return k2_align256((size_t)sp_slices(vocab) * SP_MAX_KK * 4); }
 static size_t sp_half2_bytes() { return k2_align256((size_t)SP_MAX_SLICES2 * SP_MAX_KK * 4); }
 
+namespace k2 {
+size_t sample_full_ws_bytes(int vocab);
+int sample_full(const float *logits, int vocab, const k2_sampling &sp, const int32_t *prev, int n_prev,
+                uint64_t seed, uint64_t counter, int32_t *out, void *ws, hipStream_t st);
+}
+
+constexpr int SP_MAX_VOCAB = 1 << 24;
+
 extern "C" size_t k2_sample_workspace_bytes(int vocab)
 {
-    if (vocab <= 0 || sp_slices(vocab) > SP_MAX_SLICES) return 0;
-    return 2 * sp_half_bytes(vocab) + 2 * sp_half2_bytes();
+    if (vocab <= 0 || vocab > SP_MAX_VOCAB) return 0;
+    const size_t full = sample_full_ws_bytes(vocab);
+    if (sp_slices(vocab) > SP_MAX_SLICES) return full;
+    const size_t fast = 2 * sp_half_bytes(vocab) + 2 * sp_half2_bytes();
+    return fast > full ? fast : full;
 }
 
 extern "C" int k2_sample(const float *logits, int vocab, const k2_sampling *sp, const int32_t *prev,
@@ -333,13 +344,17 @@ extern "C" int k2_sample(const float *logits, int vocab, const k2_sampling *sp, 
 {
     if (!k2_ptr_ok(logits) || !sp || !out_token || !ws || ((uintptr_t)ws & 255u)) return K2_EINVAL;
     if (vocab <= 0 || n_prev < 0 || (n_prev > 0 && !prev)) return K2_EINVAL;
-    if (sp_slices(vocab) > SP_MAX_SLICES || n_prev > SP_MAX_PREV) return K2_EUNSUPPORTED;
-    if (sp->top_k < 1 || sp->top_k > SP_MAX_K) return K2_EUNSUPPORTED;
+    if (vocab > SP_MAX_VOCAB) return K2_EUNSUPPORTED;
+    if (sp->top_k < 0) return K2_EINVAL;
     if (!(sp->temperature > 0.f) || !(sp->top_p > 0.f && sp->top_p <= 1.f) ||
         !(sp->min_p >= 0.f && sp->min_p < 1.f) || !(sp->repetition_penalty >= 1.f))
         return K2_EINVAL;
     if (ws_bytes < k2_sample_workspace_bytes(vocab)) return K2_EINVAL;
     hipStream_t st = k2_stream(stream);
+    // the whole-vocabulary path: top-k off or wider than one wave sorts, or
+    // more previous ids than the candidate bound k + n_prev <= 128 allows
+    if (sp->top_k == 0 || sp->top_k > SP_MAX_K || n_prev > SP_MAX_PREV || sp_slices(vocab) > SP_MAX_SLICES)
+        return sample_full(logits, vocab, *sp, prev, n_prev, seed, counter, out_token, ws, st);
     const int k = sp->top_k < vocab ? sp->top_k : vocab;
     const int kk = sp->top_k + n_prev < vocab ? sp->top_k + n_prev : vocab;
     char *w = (char *)ws;

@@ -236,7 +236,8 @@ def test_sample_validation():
     L = k2.load()
     ws = 0x100000
     b = k2.k2_sample_workspace_bytes(250624)
-    assert b > 0 and k2.k2_sample_workspace_bytes(300000) == 0
+    assert b > 0 and k2.k2_sample_workspace_bytes(300000) > 0
+    assert k2.k2_sample_workspace_bytes((1 << 24) + 1) == 0 and k2.k2_sample_workspace_bytes(0) == 0
     out = FAKE
 
     def call(vocab=1000, n_prev=0, prev=None, wsb=b, **kw):
@@ -245,13 +246,12 @@ def test_sample_validation():
         sp = k2.k2_sampling(**p)
         return L.k2_sample(FAKE, vocab, C.addressof(sp), prev, n_prev, 1, 2, out, ws, wsb, None)
     assert call(temperature=0.0) == k2.K2_EINVAL
-    assert call(top_k=0) == k2.K2_EUNSUPPORTED
-    assert call(top_k=65) == k2.K2_EUNSUPPORTED
+    assert call(top_k=-1) == k2.K2_EINVAL
     assert call(top_p=0.0) == k2.K2_EINVAL
     assert call(top_p=1.5) == k2.K2_EINVAL
     assert call(min_p=1.0) == k2.K2_EINVAL
     assert call(repetition_penalty=0.9) == k2.K2_EINVAL
     assert call(n_prev=3, prev=None) == k2.K2_EINVAL
-    assert call(n_prev=65, prev=FAKE) == k2.K2_EUNSUPPORTED
-    assert call(vocab=300000) == k2.K2_EUNSUPPORTED
+    assert call(vocab=(1 << 24) + 1) == k2.K2_EUNSUPPORTED
+    assert call(vocab=300000, wsb=b) == k2.K2_EINVAL          # workspace too small for it
     assert call(wsb=16) == k2.K2_EINVAL

@@ -521,6 +521,78 @@ def test_sample_matches_oracle(vocab, params):
         assert len(set(got)) == 1
 
 
+@pytest.mark.parametrize("vocab", [1000, 250624])
+@pytest.mark.parametrize("params", [
+    dict(temperature=0.8, top_k=0, top_p=0.9, min_p=0.05, repetition_penalty=1.2),
+    dict(temperature=1.0, top_k=0, top_p=1.0, min_p=0.0, repetition_penalty=1.0),
+    dict(temperature=0.6, top_k=200, top_p=0.95, min_p=0.0, repetition_penalty=1.3),
+    dict(temperature=0.5, top_k=0, top_p=0.5, min_p=0.01, repetition_penalty=1.1),
+    dict(temperature=0.7, top_k=40, top_p=0.9, min_p=0.0, repetition_penalty=1.4),
+])
+def test_sample_whole_vocabulary_matches_oracle(vocab, params):
+    """Top-k off (0) or above 64, and 300 previous ids (with repeats): the
+    whole-vocabulary path (sample_full.hip) against the sampling oracle.
+    Its weights are exact fixed-point sums of fp32 exp values, within
+    ~3e-7 of the oracle's fp64 masses (relative to the total), so a token may
+    differ only where the oracle's decision margin is below 2e-6."""
+    from oracle import sampling as S
+    rng = np.random.default_rng(vocab + 7 * params["top_k"] + int(100 * params["top_p"]))
+    lg = (rng.standard_normal(vocab) * 1.5).astype(np.float32)
+    lg[rng.integers(0, vocab, 5)] += 4.0
+    prev = rng.integers(0, vocab, 300).astype(np.int32)
+    prev[:4] = np.argsort(-lg)[:4]
+    prev[150:200] = prev[:50]                                # repeats count once
+    sp = k2.k2_sampling(**params)
+    wsb = k2.k2_sample_workspace_bytes(vocab)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    X, P = to_dev(lg), to_dev(prev)
+    n = 32
+    out = torch.zeros(n, dtype=torch.int32, device=DEV)
+    for rep in range(2):                                     # the workspace is reusable
+        for c in range(n):
+            check(k2.k2_sample(X, vocab, sp, P, prev.size, 4321, c, out[c:c + 1], ws, wsb))
+        sync()
+        got = to_host(out).tolist()
+        near = 0
+        for c in range(n):
+            want, margin = S.sample(lg.astype(np.float64), params["temperature"], params["top_k"],
+                                    params["top_p"], params["min_p"], params["repetition_penalty"],
+                                    prev.tolist(), 4321, c)
+            if got[c] != want:
+                assert margin < 2e-6, (c, got[c], want, margin)
+                near += 1
+        assert near <= 3, near
+
+
+@pytest.mark.parametrize("vocab", [4100, 250624])
+@pytest.mark.parametrize("top_p", [0.5, 1.0])
+def test_sample_whole_vocabulary_ties(vocab, top_p):
+    """350 tied leaders (two penalised out of the tie) with top-k off: the
+    top-p cut falls inside the tie (top_p 0.5: the lowest ids among them are
+    kept) and every draw lands on a tied token, whose weights are exactly 1
+    in fp32 and fp64: every token must match the oracle."""
+    from oracle import sampling as S
+    rng = np.random.default_rng(vocab + int(10 * top_p))
+    lg = rng.standard_normal(vocab).astype(np.float32)
+    lead = np.concatenate([np.arange(100, 400), np.arange(vocab - 60, vocab - 10)])
+    lg[lead] = 12.0
+    prev = np.array([lead[0], lead[7], 5] * 30, dtype=np.int32)
+    sp = k2.k2_sampling(temperature=1.0, top_k=0, top_p=top_p, min_p=0.0, repetition_penalty=1.5)
+    wsb = k2.k2_sample_workspace_bytes(vocab)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    X, P = to_dev(lg), to_dev(prev)
+    n = 48
+    out = torch.zeros(n, dtype=torch.int32, device=DEV)
+    for c in range(n):
+        check(k2.k2_sample(X, vocab, sp, P, prev.size, 99, c, out[c:c + 1], ws, wsb))
+    sync()
+    got = to_host(out).tolist()
+    for c in range(n):
+        want, margin = S.sample(lg.astype(np.float64), 1.0, 0, top_p, 0.0, 1.5, prev.tolist(), 99, c)
+        if got[c] != want:
+            assert margin < 2e-6, (c, got[c], want, margin)
+
+
 @pytest.mark.parametrize("vocab", [1000, 4100, 250624])
 @pytest.mark.parametrize("top_k", [1, 64])
 def test_sample_ties_take_lower_ids(vocab, top_k):
