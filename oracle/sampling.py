@@ -9,7 +9,8 @@ Reading taken here (the conventional order of those filters):
   1. repetition penalty r >= 1 on every distinct token id in `prev`:
      a logit l > 0 becomes l / r, otherwise l * r;
   2. temperature T > 0: z = l / T;
-  3. top-k: keep the k largest z (ties: the lower token id first);
+  3. top-k: keep the k largest z (ties: the lower token id first); k = 0
+     means no truncation (every token stays a candidate);
   4. softmax over the kept tokens;
   5. top-p: in that order, keep the shortest prefix whose cumulative
      probability reaches top_p (at least one token);
@@ -53,40 +54,52 @@ def uniform(seed: int, counter: int) -> float:
 
 def sample(logits, temperature: float, top_k: int, top_p: float, min_p: float,
            penalty: float, prev, seed: int, counter: int):
-    """Returns (token, margin): margin is the smallest distance, in kept
-    probability mass, between u * total and a cumulative boundary or between
-    a filter threshold and a kept/dropped probability -- where it is tiny, a
+    """Returns (token, margin): margin is the smallest distance at which a
+    decision of this draw is taken -- in z between the two tokens on either
+    side of the top-k cut, in kept probability mass between top_p and the
+    cumulative sums on either side of the top-p cut, between the min-p
+    threshold and a probability it compares, between u * total and the
+    cumulative sums on either side of the drawn token, and in z between the
+    drawn token and its neighbours in the order -- where it is tiny, a
     computation in another precision may pick a neighbour."""
     l = np.asarray(logits, dtype=np.float64).copy()
     for t in sorted(set(int(x) for x in prev)):
         l[t] = l[t] / penalty if l[t] > 0 else l[t] * penalty
     z = l / temperature
-    order = np.lexsort((np.arange(z.size), -z))[:top_k]          # value desc, id asc
+    order = np.lexsort((np.arange(z.size), -z))                  # value desc, id asc
+    margins = []
+    if 0 < top_k < z.size:
+        margins.append(abs(z[order[top_k - 1]] - z[order[top_k]]))
+    if top_k > 0:
+        order = order[:top_k]
     zk = z[order]
     p = np.exp(zk - zk[0])
     p /= p.sum()
-    margins = [abs(zk[i] - zk[i + 1]) for i in range(len(zk) - 1)] if len(zk) > 1 else []
     cum = np.cumsum(p)
     n = int(np.searchsorted(cum, top_p - 1e-15) + 1) if top_p < 1.0 else len(p)
     n = max(1, min(n, len(p)))
-    margins += [abs(c - top_p) for c in cum[:len(p)]] if top_p < 1.0 else []
+    if top_p < 1.0:
+        margins += [abs(cum[j] - top_p) for j in (n - 2, n - 1) if 0 <= j < len(p)]
     keep = p[:n]
     ids = order[:n]
+    zkeep = zk[:n]
     if min_p > 0.0:
         thr = min_p * keep[0]
-        margins += [abs(v - thr) for v in keep]
+        margins.append(float(np.abs(keep - thr).min()))
+        if n < len(p):
+            margins.append(abs(p[n] - thr))
         sel = keep >= thr
-        keep, ids = keep[sel], ids[sel]
+        keep, ids, zkeep = keep[sel], ids[sel], zkeep[sel]
     total = keep.sum()
     u = uniform(seed, counter)
     target = u * total
-    acc = 0.0
-    pick = int(ids[-1])
-    for pi, ti in zip(keep, ids):
-        margins.append(abs(acc - target))
-        acc += pi
-        if acc > target:
-            pick = int(ti)
-            margins.append(abs(acc - target))
-            break
+    acc = np.cumsum(keep)
+    j = int(np.searchsorted(acc, target, side="right"))       # first cumulative > target
+    j = min(j, len(keep) - 1)
+    pick = int(ids[j])
+    margins.append(abs(acc[j] - target))
+    margins.append(abs((acc[j - 1] if j > 0 else 0.0) - target))
+    for jj in (j - 1, j + 1):
+        if 0 <= jj < len(zkeep):
+            margins.append(abs(zkeep[jj] - zkeep[j]))
     return pick, (min(margins) if margins else 1.0)

@@ -87,3 +87,29 @@ def test_top_k_one_is_greedy():
     for c in range(10):
         t, _ = S.sample(lg, 0.7, 1, 0.9, 0.1, 1.3, [], 1, c)
         assert t == int(np.argmax(lg))
+
+
+def test_top_k_zero_means_no_truncation():
+    # k = 0 keeps every token: the draws equal those with k = vocab for any
+    # filters, and the distribution is the plain softmax
+    rng = np.random.default_rng(5)
+    lg = rng.standard_normal(300) * 2
+    for c in range(200):
+        a = S.sample(lg, 0.7, 0, 0.9, 0.02, 1.3, [3, 7, 7, 250], 21, c)
+        b = S.sample(lg, 0.7, 300, 0.9, 0.02, 1.3, [3, 7, 7, 250], 21, c)
+        assert a == b
+    assert np.abs(_freq(LG, top_k=0) - np.array([0.1, 0.2, 0.3, 0.4])).max() < 0.015
+
+
+def test_penalty_applies_to_every_distinct_previous_id():
+    # hundreds of previous ids (duplicates counted once): each penalised
+    # logit is l / r (l > 0) or l * r, the rest untouched -- checked through
+    # a draw with top-k = 1 (the argmax of the penalised logits)
+    rng = np.random.default_rng(6)
+    lg = rng.standard_normal(2000)
+    prev = list(rng.integers(0, 2000, 700)) * 2
+    pen = lg.copy()
+    for t in set(prev):
+        pen[t] = pen[t] / 1.5 if pen[t] > 0 else pen[t] * 1.5
+    tok, _ = S.sample(lg, 1.0, 1, 1.0, 0.0, 1.5, prev, 1, 0)
+    assert tok == int(np.argmax(pen))
