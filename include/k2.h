@@ -351,11 +351,13 @@ int k2_model_check(const k2_model *m);
  * activation split into bf16 hi + lo (about 16 significant bits, fp32
  * accumulation); the caches receive every position; logits (nullable) and
  * next_token (nullable) are those of the LAST position.  tokens: HOST array
- * [T].  Needs bf16 projection weights and 2 <= T <= 32 (K2_EUNSUPPORTED
- * otherwise; a single position is k2_decode_step).  ws: device workspace of
- * k2_prefill_workspace_bytes(&m->cfg, T) bytes, 256-byte aligned,
- * zero-filled before its first use (left zeroed where it must be); calls that
- * share it must not overlap in time.  K2_ERANGE if a token is outside the
+ * [T].  Needs bf16 projection weights and 2 <= T <= 256 (K2_EUNSUPPORTED
+ * otherwise; a single position is k2_decode_step); every weight byte is read
+ * once per 64 positions (the token blocks of a row block share it through
+ * L2).  ws: device workspace of k2_prefill_workspace_bytes(&m->cfg, T) bytes
+ * (it serves every smaller T), 256-byte aligned, zero-filled before its
+ * first use (left zeroed where it must be); calls that share it must not
+ * overlap in time.  K2_ERANGE if a token is outside the
  * vocabulary or pos0 + T > cap (nothing enqueued). */
 size_t k2_prefill_workspace_bytes(const k2_config *cfg, int T);
 int k2_prefill(const k2_model *m, const int32_t *tokens, int T, int pos0, float *logits,
@@ -372,8 +374,8 @@ int k2_prefill(const k2_model *m, const int32_t *tokens, int T, int pos0, float 
  * d_i while d_i == next_tokens[i - 1]; cache slots past the accepted ones
  * are simply written again by later calls.  ws: k2_verify_workspace_bytes
  * (it includes the lm_head partials and a logits buffer), zero-filled
- * before its first use.  Same refusals as k2_prefill; K2_EINVAL without
- * next_tokens. */
+ * before its first use.  Same refusals as k2_prefill, with 2 <= T <= 32;
+ * K2_EINVAL without next_tokens. */
 size_t k2_verify_workspace_bytes(const k2_config *cfg, int T);
 int k2_verify(const k2_model *m, const int32_t *tokens, int T, int pos0, float *logits,
               int32_t *next_tokens, void *ws, size_t ws_bytes, void *stream);

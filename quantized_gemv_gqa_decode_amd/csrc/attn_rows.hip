@@ -34,13 +34,14 @@ static int attn_rows_rep(int rep, const AttnArgs &a, int T, int S_max, hipStream
 size_t attn_rows_ws_bytes(int n_qh, int n_kv, int hd, int cap, int T)
 {
     const size_t S = (size_t)attn_max_splits(n_kv, cap), rep = (size_t)(n_qh / n_kv);
-    return k2_align256((size_t)T * n_kv * S * rep * hd * 4) + k2_align256((size_t)T * n_kv * S * rep * 2 * 4) +
-           k2_align256((size_t)T * n_kv * 4);
+    return k2_align256((size_t)T * n_kv * S * rep * hd * 4) + k2_align256((size_t)T * n_kv * S * rep * 2 * 4);
 }
+
+size_t attn_rows_cnt_bytes(int n_kv, int T) { return k2_align256((size_t)T * n_kv * 4); }
 
 int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qrot, float *out, void *kc,
                      void *vc, float *ks, float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T,
-                     void *ws, hipStream_t st)
+                     void *ws, unsigned *cnt, hipStream_t st)
 {
     if (hd != 128 || T < 1) return K2_EUNSUPPORTED;
     const int rep = n_qh / n_kv;
@@ -72,8 +73,7 @@ int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qr
     a.part = (float *)p;
     p += k2_align256((size_t)T * n_kv * S * rep * hd * 4);
     a.part_ml = (float *)p;
-    p += k2_align256((size_t)T * n_kv * S * rep * 2 * 4);
-    a.head_cnt = (unsigned *)p;
+    a.head_cnt = cnt;
     a.q = qrot;
     a.kc = kc;
     a.vc = vc;

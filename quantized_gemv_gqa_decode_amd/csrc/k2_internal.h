@@ -98,13 +98,15 @@ int device_cus();
 // A prefill chunk's attention: RoPE and cache append of the T rows of qkv
 // ([T][(n_qh + 2 n_kv) hd], positions pos0 ..), then every row's query over
 // the cache up to its own position, in one launch (out [T][n_qh][hd];
-// qrot [T][n_qh][hd] scratch).  ws: attn_rows_ws_bytes, zero-filled before
-// its first use.  K2_EUNSUPPORTED (nothing enqueued) unless hd = 128 and
-// n_qh / n_kv is 1, 2, 4 or 8.
+// qrot [T][n_qh][hd] scratch).  ws: attn_rows_ws_bytes (split partials);
+// cnt: attn_rows_cnt_bytes of split counters, zero-filled before its first
+// use and left zero by every launch.  K2_EUNSUPPORTED (nothing enqueued)
+// unless hd = 128 and n_qh / n_kv is 1, 2, 4 or 8.
 size_t attn_rows_ws_bytes(int n_qh, int n_kv, int hd, int cap, int T);
+size_t attn_rows_cnt_bytes(int n_kv, int T);
 int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qrot, float *out, void *kc,
                      void *vc, float *ks, float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T,
-                     void *ws, hipStream_t st);
+                     void *ws, unsigned *cnt, hipStream_t st);
 
 // Sync words of the attention + O launch: the O-block counter on a line of
 // its own, and 16 copies (one 256-byte line each) of the per-kv-head ready
@@ -184,5 +186,17 @@ bool dense_mfma_ok(int N, int K);
 size_t dense_mfma_ws_bytes(int N, int K, int T);
 int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi, float *part,
                hipStream_t st);
+
+// The projections of a prefill chunk of 1..GM_MAX_T positions on the matrix
+// cores (gemm_mfma.hip): y [T][N] = x [T][K] W^T with the epilogue epi
+// (SwiGLU: y [T][N/2], gate rows n, up rows n + N/2).  ws:
+// gemm_mfma_ws_bytes (the activation planes and split partials; no state
+// kept between calls).  K2_EUNSUPPORTED (nothing enqueued) unless K % 128 == 0
+// and N % 4 == 0 (SwiGLU: N % 256 == 0).
+constexpr int GM_MAX_T = 256;
+bool gemm_mfma_ok(int N, int K, int epi);
+size_t gemm_mfma_ws_bytes(int N, int K, int T, int epi);
+int gemm_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi, void *ws,
+              hipStream_t st);
 
 }  // namespace k2

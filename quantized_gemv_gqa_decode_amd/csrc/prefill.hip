@@ -7,14 +7,15 @@
 // T positions at once every projection is a [N][K] x [K][T] product, so a
 // weight byte feeds 2T flops: past a few positions that is a dense
 // contraction, run here on v_mfma_f32_16x16x32_bf16 by the bf16 product of
-// dense_mfma.hip (activations split into bf16 hi + lo, fp32 accumulation).
+// gemm_mfma.hip (activations split into bf16 hi + lo, fp32 accumulation),
+// which reads the weights once for up to 256 positions.
 //
 // Per layer, for the T rows of the chunk:
 //   1. GroupedRMSNorm of every row                       (one launch)
 //   2. QKV = W_qkv X                                     (matrix cores)
-//   3. per position p = pos0 + t, in order: RoPE, KV append at p, attention
-//      over [0, p] -- position t sees the K/V rows of the earlier positions
-//      of the chunk because their launches come first on the stream
+//   3. RoPE and KV append of every row, then every row's attention over
+//      [0, pos0 + t] (one launch for head_dim 128; else per position, in
+//      order, so that position t sees the K/V rows of the earlier ones)
 //   4. H += W_o O                                        (matrix cores, add)
 //   5. GroupedRMSNorm, then ACT = silu(W_g X) * (W_u X)  (matrix cores, SwiGLU)
 //   6. H += W_d ACT                                      (matrix cores, add)
@@ -28,7 +29,8 @@
 
 namespace k2 {
 
-constexpr int PF_MAX_T = 32;               // positions per call (one matrix-core token group)
+constexpr int PF_MAX_T = GM_MAX_T;         // positions per call
+constexpr int VF_MAX_T = 32;               // positions per verification call (its lm_head keeps [T][vocab])
 
 struct PfTokens {
     int tok[PF_MAX_T];
@@ -47,6 +49,7 @@ __global__ void embed_rows_kernel(const PfTokens tk, int embdt, const void *E, i
 struct PrefillWs {
     float *h, *x, *qkv, *o, *act, *part, *qrot, *lm_part, *logits;
     void *attn, *rows, *am;
+    unsigned *rows_cnt;
     int32_t *next;
 };
 
@@ -61,14 +64,36 @@ __global__ __launch_bounds__(K2_BLOCK) void argmax_rows_kernel(const float *x, i
     if (threadIdx.x == 0) out[blockIdx.x] = bi;
 }
 
+// A projection of the chunk's T rows: up to 32 rows the small-T product
+// (dense_mfma.hip, measured faster there), above that the token-blocked
+// GEMM (gemm_mfma.hip), which reads every weight byte once per 64 rows.
+constexpr int PF_GEMM_MIN_T = 33;
+
+static size_t pf_proj_bytes(int N, int K, int T, int epi)
+{
+    return T >= PF_GEMM_MIN_T ? gemm_mfma_ws_bytes(N, K, T, epi) : dense_mfma_ws_bytes(N, K, T);
+}
+
+static int pf_proj(const void *W, const float *x, float *y, int N, int K, int T, int epi, float *ws,
+                   hipStream_t st)
+{
+    if (T >= PF_GEMM_MIN_T) return gemm_mfma((const uint16_t *)W, x, y, N, K, T, epi, ws, st);
+    return dense_mfma((const uint16_t *)W, x, y, N, K, T, epi, ws, st);
+}
+
+// the projections' scratch for any chunk of up to T rows (the split count
+// of a product, and so its partials, need not grow with T)
 static size_t pf_part_bytes(const k2_config *c, int T)
 {
     const int qkv_rows = (c->n_qh + 2 * c->n_kv) * c->head_dim, qd = c->n_qh * c->head_dim;
-    const size_t b[4] = {dense_mfma_ws_bytes(qkv_rows, c->hidden, T), dense_mfma_ws_bytes(c->hidden, qd, T),
-                         dense_mfma_ws_bytes(2 * c->inter, c->hidden, T),
-                         dense_mfma_ws_bytes(c->hidden, c->inter, T)};
     size_t m = 0;
-    for (size_t v : b) m = v > m ? v : m;
+    for (int t = 2; t <= T; ++t) {
+        const size_t b[4] = {pf_proj_bytes(qkv_rows, c->hidden, t, DM_EPI_PLAIN),
+                             pf_proj_bytes(c->hidden, qd, t, DM_EPI_ADD),
+                             pf_proj_bytes(2 * c->inter, c->hidden, t, DM_EPI_SWIGLU),
+                             pf_proj_bytes(c->hidden, c->inter, t, DM_EPI_ADD)};
+        for (size_t v : b) m = v > m ? v : m;
+    }
     return m;
 }
 
@@ -88,9 +113,10 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base, boo
     // counters, the argmax's) come first, at offsets that do not depend on T:
     // a workspace sized for one T serves every smaller T
     char *attn = take(attn_ws_bytes(c->n_qh, c->n_kv, c->head_dim, c->cap));
-    char *rows = take(attn_rows_ws_bytes(c->n_qh, c->n_kv, c->head_dim, c->cap, PF_MAX_T));
+    char *rows_cnt = take(attn_rows_cnt_bytes(c->n_kv, PF_MAX_T));
     char *am = take(argmax_ws_bytes());
     char *nx = take(4);
+    char *rows = take(attn_rows_ws_bytes(c->n_qh, c->n_kv, c->head_dim, c->cap, T));
     char *h = take((size_t)T * c->hidden * 4);
     char *x = take((size_t)T * c->hidden * 4);
     char *qkv = take((size_t)T * qkv_rows * 4);
@@ -104,6 +130,7 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base, boo
         w->lm_part = (float *)lm_part;
         w->logits = (float *)lgt;
         w->rows = rows;
+        w->rows_cnt = (unsigned *)rows_cnt;
         w->qrot = (float *)qrot;
         w->h = (float *)h;
         w->x = (float *)x;
@@ -128,6 +155,9 @@ static int pf_shape_ok(const k2_config *c, bool verify = false)
     if (!dense_mfma_ok(qkv_rows, c->hidden) || !dense_mfma_ok(c->hidden, qd) ||
         !dense_mfma_ok(2 * c->inter, c->hidden) || !dense_mfma_ok(c->hidden, c->inter))
         return K2_EUNSUPPORTED;
+    if (!gemm_mfma_ok(qkv_rows, c->hidden, DM_EPI_PLAIN) || !gemm_mfma_ok(c->hidden, qd, DM_EPI_ADD) ||
+        !gemm_mfma_ok(2 * c->inter, c->hidden, DM_EPI_SWIGLU) || !gemm_mfma_ok(c->hidden, c->inter, DM_EPI_ADD))
+        return K2_EUNSUPPORTED;
     return K2_OK;
 }
 
@@ -139,7 +169,7 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
     int rc = k2_model_check(m);
     if (rc) return rc;
     const k2_config *c = &m->cfg;
-    if (T < 2 || T > PF_MAX_T) return K2_EUNSUPPORTED;
+    if (T < 2 || T > (verify ? VF_MAX_T : PF_MAX_T)) return K2_EUNSUPPORTED;
     if (!tokens || (verify && !k2_ptr_ok(next))) return K2_EINVAL;
     if ((rc = pf_shape_ok(c, verify))) return rc;
     if (logits && !k2_aligned16(logits)) return K2_EINVAL;
@@ -174,14 +204,14 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
     for (int l = 0; l < c->n_layers; ++l) {
         const k2_layer *L = &m->layers[l];
         if ((rc = rmsnorm_rows_launch(w.h, L->g_in, w.x, T, H, c->groups, c->eps, st))) return rc;
-        if ((rc = dense_mfma((const uint16_t *)L->qkv, w.x, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, st)))
+        if ((rc = pf_proj(L->qkv, w.x, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, st)))
             return rc;
         at.kc = L->kc;
         at.vc = L->vc;
         at.ks = L->ks;
         at.vs = L->vs;
         rc = attn_rows_launch(c->kvdt, w.qkv, m->rope, w.qrot, w.o, L->kc, L->vc, L->ks, L->vs, c->n_qh,
-                              c->n_kv, hd, c->cap, pos0, T, w.rows, st);
+                              c->n_kv, hd, c->cap, pos0, T, w.rows, w.rows_cnt, st);
         if (rc && rc != K2_EUNSUPPORTED) return rc;
         const bool per_position = rc == K2_EUNSUPPORTED;
         for (int t = 0; per_position && t < T; ++t) {
@@ -192,11 +222,11 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
             at.S = attn_splits(c->n_kv, at.len, &at.chunk);
             if ((rc = attn_launch(c->kvdt, hd, rep, true, at, st))) return rc;
         }
-        if ((rc = dense_mfma((const uint16_t *)L->o, w.o, w.h, H, qd, T, DM_EPI_ADD, w.part, st))) return rc;
+        if ((rc = pf_proj(L->o, w.o, w.h, H, qd, T, DM_EPI_ADD, w.part, st))) return rc;
         if ((rc = rmsnorm_rows_launch(w.h, L->g_post, w.x, T, H, c->groups, c->eps, st))) return rc;
-        if ((rc = dense_mfma((const uint16_t *)L->gu, w.x, w.act, 2 * I, H, T, DM_EPI_SWIGLU, w.part, st)))
+        if ((rc = pf_proj(L->gu, w.x, w.act, 2 * I, H, T, DM_EPI_SWIGLU, w.part, st)))
             return rc;
-        if ((rc = dense_mfma((const uint16_t *)L->down, w.act, w.h, H, I, T, DM_EPI_ADD, w.part, st)))
+        if ((rc = pf_proj(L->down, w.act, w.h, H, I, T, DM_EPI_ADD, w.part, st)))
             return rc;
     }
 
@@ -247,7 +277,7 @@ extern "C" int k2_prefill(const k2_model *m, const int32_t *tokens, int T, int p
 
 extern "C" size_t k2_verify_workspace_bytes(const k2_config *cfg, int T)
 {
-    if (!cfg || T < 2 || T > PF_MAX_T || pf_shape_ok(cfg, true)) return 0;
+    if (!cfg || T < 2 || T > VF_MAX_T || pf_shape_ok(cfg, true)) return 0;
     if (k2_decode_workspace_bytes(cfg) == 0) return 0;
     return pf_layout(cfg, T, nullptr, nullptr, true);
 }

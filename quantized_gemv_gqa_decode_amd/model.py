@@ -155,10 +155,10 @@ class DecodeModel:
         k2.check(k2.k2_decode_step(self.model, token, pos, lg, nx, stream))
         return lg, nx
 
-    def prefill(self, tokens, pos0: int = 0, chunk: int = 32, want_logits: bool = True,
+    def prefill(self, tokens, pos0: int = 0, chunk: int = 256, want_logits: bool = True,
                 stream=None):
         """Consume prompt positions pos0 .. pos0+len(tokens)-1 with k2_prefill,
-        ``chunk`` (2..32) positions per call; a lone last position goes through
+        ``chunk`` (2..256) positions per call; a lone last position goes through
         k2_decode_step.  The logits/next of the last position land in
         self.logits / self.next when want_logits."""
         toks = [int(t) for t in tokens]

@@ -157,7 +157,12 @@ def test_prefill_refuses_unsupported_shapes():
     m = _fake_model(ok)
     assert k2.k2_prefill_workspace_bytes(m.cfg, 8) > 0
     assert k2.k2_prefill_workspace_bytes(m.cfg, 1) == 0
-    assert k2.k2_prefill_workspace_bytes(m.cfg, 33) == 0
+    assert k2.k2_prefill_workspace_bytes(m.cfg, 256) > k2.k2_prefill_workspace_bytes(m.cfg, 33) > 0
+    assert k2.k2_prefill_workspace_bytes(m.cfg, 257) == 0
+    sizes = [k2.k2_prefill_workspace_bytes(m.cfg, t) for t in range(2, 257)]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:]))       # a chunk's workspace serves smaller chunks
+    assert k2.k2_verify_workspace_bytes(m.cfg, 32) > 0
+    assert k2.k2_verify_workspace_bytes(m.cfg, 33) == 0
     wsb = k2.k2_prefill_workspace_bytes(m.cfg, 8)
     L = k2.load()
     toks = (C.c_int32 * 8)(*[1] * 8)

@@ -338,8 +338,8 @@ def test_k2h_int8_long_context(prefix):
 # ------------------------------------------------------------------ prefill ---
 
 def _prefill_parity(cfg, P, n_after, chunk=32):
-    """Prompt of P positions through k2_prefill (chunks of up to 32 rows on
-    the matrix cores), then n_after decode steps teacher-forced on the
+    """Prompt of P positions through k2_prefill (chunks of up to `chunk` rows
+    on the matrix cores), then n_after decode steps teacher-forced on the
     oracle's tokens: the last prompt position's logits and every later
     position's logits against the oracle (the later ones read the caches the
     prefill wrote)."""
@@ -377,6 +377,26 @@ def test_head128_prefill_matches_oracle(kvdt, P):
     _prefill_parity(cfg, P, 3)
 
 
+@pytest.mark.parametrize("kvdt", ["bf16", "i8"])
+@pytest.mark.parametrize("P,chunk", [(100, 64), (130, 64), (300, 256), (258, 256), (200, 48)])
+def test_head128_prefill_large_chunks(kvdt, P, chunk):
+    """Chunks above 32 positions (token blocks of 64, several per row block):
+    100 = 64 + 36 (a ragged token block), 130 = 64 + 64 + 2 (a last chunk
+    of two rows), 300 = 256 + 44, 258 = 256 + a lone position through the
+    decode step, 200 = 4 x 48 + 8 (48 rows padded to 64)."""
+    cfg = HEAD128.replace(wdt="bf16", kvdt=kvdt, cap=320)
+    _prefill_parity(cfg, P, 3, chunk=chunk)
+
+
+@pytest.mark.parametrize("P,chunk", [(40, 32), (70, 64), (150, 256)])
+def test_prefill_ragged_rows(P, chunk):
+    """Projections whose row counts are not multiples of the 256-row block
+    (qkv 384 rows, o and down 384 rows; one query head per kv head):
+    the clamped weight rows must never be stored."""
+    cfg = HEAD128.replace(hidden=384, n_qh=1, n_kv=1, inter=640, wdt="bf16", kvdt="bf16", cap=160)
+    _prefill_parity(cfg, P, 3, chunk=chunk)
+
+
 def test_prefill_equals_decode_steps_on_cache():
     """The caches a prefill writes decode the same next positions as the
     caches of position-by-position decode, within the bf16 cache's rounding:
@@ -410,7 +430,8 @@ def test_prefill_refuses_before_launch():
     assert k2.k2_prefill(gm.model, [1] * 7 + [cfg.vocab], 8, 0, gm.logits, gm.next, ws, b) == k2.K2_ERANGE
     assert k2.k2_prefill(gm.model, [1] * 8, 8, 0, gm.logits, gm.next, ws, b - 256) == k2.K2_EINVAL
     assert k2.k2_prefill(gm.model, [1], 1, 0, gm.logits, gm.next, ws, b) == k2.K2_EUNSUPPORTED
-    assert k2.k2_prefill(gm.model, [1] * 33, 33, 0, gm.logits, gm.next, ws, b) == k2.K2_EUNSUPPORTED
+    assert k2.k2_prefill(gm.model, [1] * 257, 257, 0, gm.logits, gm.next, ws, b) == k2.K2_EUNSUPPORTED
+    assert k2.k2_prefill(gm.model, [1] * 33, 33, 0, gm.logits, gm.next, ws, b) == k2.K2_EINVAL  # ws for 8
     torch.cuda.synchronize()
     assert torch.all(gm.logits == 7.0)
 
