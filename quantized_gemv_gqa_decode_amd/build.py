@@ -14,7 +14,7 @@ LIB = os.path.join(HERE, "libk2.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["gemv.hip", "gemv_f32.hip", "gemv_bf16.hip", "gemv_fp8.hip", "gemv_mxfp4.hip", "gemv_q4s.hip",
            "attn.hip", "attn_o.hip", "misc.hip", "decode.hip", "moe.hip", "dense_mfma.hip", "prefill.hip",
-           "attn_rows.hip", "sample.hip", "sample_full.hip", "gemm_mfma.hip"]
+           "attn_rows.hip", "sample.hip", "sample_full.hip", "gemm_mfma.hip", "attn_prefill.hip"]
 ARCH = "gfx950"
 
 

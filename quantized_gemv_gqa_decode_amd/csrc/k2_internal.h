@@ -104,6 +104,13 @@ int device_cus();
 // unless hd = 128 and n_qh / n_kv is 1, 2, 4 or 8.
 size_t attn_rows_ws_bytes(int n_qh, int n_kv, int hd, int cap, int T);
 size_t attn_rows_cnt_bytes(int n_kv, int T);
+// From this many rows on, attn_rows_launch runs the attention of a bf16 /
+// int8 cache through attn_prefill_launch (attn_prefill.hip): the causal
+// attention of rows pos0 .. pos0+T-1 (qrot [T][n_qh][128], already rotated,
+// K/V already appended) on the matrix cores, out [T][n_qh][128].
+constexpr int ATTN_PREFILL_MIN_T = 33;
+int attn_prefill_launch(int kvdt, const float *qrot, float *out, const void *kc, const void *vc, const float *ks,
+                        const float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T, hipStream_t st);
 int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qrot, float *out, void *kc,
                      void *vc, float *ks, float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T,
                      void *ws, unsigned *cnt, hipStream_t st);

@@ -252,28 +252,29 @@ def _golden_parity(name, cfg):
     assert np.array_equal(prompt, synth.prompt(cfg, len(prompt))), "seeded prompt changed"
     toks, ref = [int(t) for t in g["tokens"]], g["logits"].astype(np.float64)
     P = len(prompt)
-    say(f"golden {name}: prefill {P} positions")
     gm = DecodeModel(cfg, DEV)
-    gm.prefill(prompt, 0, chunk=32)
-    torch.cuda.synchronize()
-    got = [(to_host(gm.logits).astype(np.float64), int(gm.next.item()))]
-    for i in range(len(toks) - 1):
-        lg, nx = gm.step(toks[i], P + i)
-        torch.cuda.synchronize()
-        got.append((to_host(lg).astype(np.float64), int(nx.item())))
     tol = tol_for(cfg)
-    errs = []
-    for i, ((lg, t), r) in enumerate(zip(got, ref)):
-        err = float(np.abs(lg - r).max())
-        errs.append(err)
-        assert err <= tol, (i, err)
-        gap = float(g["top2_gap"][i])
-        if gap > tie_gap(err):
-            assert t == toks[i], (i, t, toks[i], err, gap)
-        else:
-            assert near_tie_ok(t, r, tie_gap(err)), (i, t, toks[i], err, gap)
-    say(f"golden {name}: max|dlogit| per position {[f'{e:.3g}' for e in errs]} (tol {tol}); "
-        f"top-2 gaps {[round(float(x), 3) for x in g['top2_gap']]}")
+    for chunk in (32, 256):                     # the small-T and the token-blocked prefill kernels
+        say(f"golden {name}: prefill {P} positions in chunks of {chunk}")
+        gm.prefill(prompt, 0, chunk=chunk)      # rewrites cache slots 0 .. P-1
+        torch.cuda.synchronize()
+        got = [(to_host(gm.logits).astype(np.float64), int(gm.next.item()))]
+        for i in range(len(toks) - 1):
+            lg, nx = gm.step(toks[i], P + i)
+            torch.cuda.synchronize()
+            got.append((to_host(lg).astype(np.float64), int(nx.item())))
+        errs = []
+        for i, ((lg, t), r) in enumerate(zip(got, ref)):
+            err = float(np.abs(lg - r).max())
+            errs.append(err)
+            assert err <= tol, (chunk, i, err)
+            gap = float(g["top2_gap"][i])
+            if gap > tie_gap(err):
+                assert t == toks[i], (chunk, i, t, toks[i], err, gap)
+            else:
+                assert near_tie_ok(t, r, tie_gap(err)), (chunk, i, t, toks[i], err, gap)
+        say(f"golden {name} chunk {chunk}: max|dlogit| per position {[f'{e:.3g}' for e in errs]} "
+            f"(tol {tol}); top-2 gaps {[round(float(x), 3) for x in g['top2_gap']]}")
 
 
 @pytest.mark.slow
@@ -386,6 +387,16 @@ def test_head128_prefill_large_chunks(kvdt, P, chunk):
     decode step, 200 = 4 x 48 + 8 (48 rows padded to 64)."""
     cfg = HEAD128.replace(wdt="bf16", kvdt=kvdt, cap=320)
     _prefill_parity(cfg, P, 3, chunk=chunk)
+
+
+@pytest.mark.parametrize("kvdt", ["bf16", "i8"])
+@pytest.mark.parametrize("n_qh,n_kv", [(8, 1), (8, 4), (4, 4)])
+def test_prefill_gqa_ratios(n_qh, n_kv, kvdt):
+    """Chunks of 64 rows on the matrix-core attention at 8, 2 and 1 query
+    heads per kv head (8, 32 and 64 chunk rows per block): 150 = 64 + 64 +
+    22 positions."""
+    cfg = HEAD128.replace(n_qh=n_qh, n_kv=n_kv, wdt="bf16", kvdt=kvdt, cap=160)
+    _prefill_parity(cfg, 150, 3, chunk=64)
 
 
 @pytest.mark.parametrize("P,chunk", [(40, 32), (70, 64), (150, 256)])
