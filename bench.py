@@ -38,7 +38,7 @@ PEAK_HBM_GBPS = 8000.0
 # taken on: if their digest differs, the traffic is reported as null.
 FETCH_SCALE = 1073741824 / (524301.8 * 1024)
 WRITE_SCALE = 1073741824 / (1048576.0 * 1024)
-GEMV_BF16_SOURCES = ("k2_dev.h", "k2_internal.h", "gemv_impl.h", "gemv.hip", "gemv_bf16.hip")
+GEMV_BF16_SOURCES = ("k2_dev.h", "gemv_impl.h", "gemv.hip", "gemv_bf16.hip")
 PMC_TRAFFIC = {
     "k2h-3.7b-bf16-kvbf16-ctx4096": {
         "sources": GEMV_BF16_SOURCES, "digest": "8fd6a2d01ae1ccef",

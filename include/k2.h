@@ -353,8 +353,8 @@ int k2_model_check(const k2_model *m);
  * next_token (nullable) are those of the LAST position.  tokens: HOST array
  * [T].  Needs bf16 projection weights and 2 <= T <= 256 (K2_EUNSUPPORTED
  * otherwise; a single position is k2_decode_step); every weight byte is read
- * once per 64 positions (the token blocks of a row block share it through
- * L2).  ws: device workspace of k2_prefill_workspace_bytes(&m->cfg, T) bytes
+ * from HBM once per call (the token blocks of a row block, 128 positions
+ * each, share it through L2).  ws: device workspace of k2_prefill_workspace_bytes(&m->cfg, T) bytes
  * (it serves every smaller T), 256-byte aligned, zero-filled before its
  * first use (left zeroed where it must be); calls that share it must not
  * overlap in time.  K2_ERANGE if a token is outside the

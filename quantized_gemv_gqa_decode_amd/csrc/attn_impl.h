@@ -514,7 +514,6 @@ __device__ __forceinline__ void attn_block(const AttnArgs &a, int g, int s, int 
 // read them from LDS with the query heads held in registers.  A block keeps
 // up to 96 KiB in flight: long contexts become bandwidth-bound.
 
-#define K2_VMCNT(n) (((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
 
 // Optional per-block stage trace for performance work (never enabled in the
 // library build): thread 0 keeps the 100 MHz real-time counter of each

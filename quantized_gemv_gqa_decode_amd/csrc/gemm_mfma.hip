@@ -9,9 +9,9 @@
 // so ~16 bits of every activation enter an fp32 accumulation (the precision
 // of dense_mfma.hip, the small-T product).
 //
-// Tiling: a block (4 waves) owns 256 weight rows x BT tokens and streams its
-// k-range in chunks of 128; a wave holds 4 row tiles of 16 rows x BT/16
-// token tiles of accumulators.  Per chunk the block copies the chunk's
+// Tiling: a block (4 waves) owns 256 weight rows x BT (32, 64 or 128)
+// tokens and streams its k-range in chunks of 128; a wave holds 4 row tiles
+// of 16 rows x BT/16 token tiles of accumulators.  Per chunk the block copies the chunk's
 // activation tile (both planes) into LDS with LDS-DMA (global_load_lds) one
 // chunk ahead (two LDS buffers), and every wave loads its own weight rows one
 // chunk ahead into registers; an activation fragment read from LDS feeds 4
@@ -46,9 +46,6 @@ constexpr int GM_BM = 4 * GM_RT * 16;      // weight rows per block (256)
 constexpr int GM_BK = 128;                 // k per chunk (16 k-chunks of 8)
 constexpr int GM_ROWB = GM_BK * 2;         // bytes of one token's chunk row in LDS
 
-#ifndef K2_GM_BT
-#define K2_GM_BT 64                        // tokens per block for chunks above 32 positions
-#endif
 
 struct GemmArgs {
     const uint16_t *W;         // [N][K] bf16
@@ -176,12 +173,16 @@ __global__ __launch_bounds__(256, BT <= 64 ? 2 : 1) void gm_kernel(const GemmArg
                 const int off = t * GM_ROWB + ((kc - t) & 15) * 16;
                 const gm_bf16x8 bh = *reinterpret_cast<const gm_bf16x8 *>(st + off);
                 const gm_bf16x8 bl = *reinterpret_cast<const gm_bf16x8 *>(st + PLANE + off);
+                // the hi products of all row tiles, then the lo ones: 4
+                // independent MFMAs between two into one accumulator
 #pragma unroll
-                for (int rt = 0; rt < GM_RT; ++rt) {
-                    const gm_bf16x8 av = __builtin_bit_cast(gm_bf16x8, wc[rt][j]);
-                    acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc[rt][tt], 0, 0, 0);
-                    acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[rt][tt], 0, 0, 0);
-                }
+                for (int rt = 0; rt < GM_RT; ++rt)
+                    acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gm_bf16x8, wc[rt][j]), bh,
+                                                                          acc[rt][tt], 0, 0, 0);
+#pragma unroll
+                for (int rt = 0; rt < GM_RT; ++rt)
+                    acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gm_bf16x8, wc[rt][j]), bl,
+                                                                          acc[rt][tt], 0, 0, 0);
             }
         }
         if (c + 1 < nch) {
@@ -269,7 +270,10 @@ __global__ __launch_bounds__(256) void gm_reduce_kernel(const float *part, int S
     else *dst = s;
 }
 
-static int gm_bt(int T) { return T <= 32 ? 32 : K2_GM_BT; }
+// tokens per block: 128 for long chunks (measured on the 512-token prompt of
+// the 3.7B-shaped model: 23.1 ms against 24.2 with 64), less for short
+// ones, whose padding would be wasted work
+static int gm_bt(int T) { return T <= 32 ? 32 : T <= 64 ? 64 : 128; }
 static int gm_tp(int T)
 {
     const int bt = gm_bt(T);

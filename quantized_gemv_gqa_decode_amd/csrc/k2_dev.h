@@ -80,6 +80,11 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations of the wave are outstanding (0 <= n <= 63), without
+// waiting on the export or LDS/scalar counters
+#define K2_VMCNT(n) (((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
+
 // ---------------------------------------------------------------- codecs --
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }

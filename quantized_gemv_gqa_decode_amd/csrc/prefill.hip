@@ -66,7 +66,7 @@ __global__ __launch_bounds__(K2_BLOCK) void argmax_rows_kernel(const float *x, i
 
 // A projection of the chunk's T rows: up to 32 rows the small-T product
 // (dense_mfma.hip, measured faster there), above that the token-blocked
-// GEMM (gemm_mfma.hip), which reads every weight byte once per 64 rows.
+// GEMM (gemm_mfma.hip), which reads every weight byte from HBM once per call.
 constexpr int PF_GEMM_MIN_T = 33;
 
 static size_t pf_proj_bytes(int N, int K, int T, int epi)
