@@ -697,7 +697,7 @@ def main():
                     help="latent-MoE workload only: comma-separated token counts")
     ap.add_argument("--prefill-chunk", type=int, default=0, metavar="T",
                     help="instead of the decode bench: time the prompt's prefill through "
-                         "k2_prefill in chunks of T positions (2..32; bf16 weights)")
+                         "k2_prefill in chunks of T positions (2..256; bf16 weights)")
     ap.add_argument("--verify-chunk", type=int, default=0, metavar="T",
                     help="instead of the decode bench: time k2_verify of T positions (2..32; "
                          "bf16 weights) after the prompt, i.e. one draft-and-verify round")

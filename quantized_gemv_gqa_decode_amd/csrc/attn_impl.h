@@ -9,11 +9,11 @@
 // over positions j in [0, len).
 //
 // Grid: (S splits, n_kv heads); block = ATT_NT threads (8 waves, the
-// StreamWide shape below).  Block (s, g) handles positions
+// StreamFor shape below).  Block (s, g) handles positions
 // [s*chunk, min(len, (s+1)*chunk)) for the rep query heads of kv head g:
 //   1. the rep query heads are rotated (fused form) and scaled into LDS;
 //   2. K and V rows stream through a ring of LDS stages filled by LDS-DMA
-//      (global_load_lds), two tiles in flight while one is computed; a row
+//      (global_load_lds), the next tiles in flight while one is computed; a row
 //      of head_dim values is split over LPP lanes (16 bytes each), so one
 //      wave covers 64/LPP positions per slot; the int8 per-position scale
 //      multiplies the finished dot product and is folded into the
@@ -550,27 +550,22 @@ static __shared__ unsigned long long k2_attn_trs[12];
 #endif
 
 // Block shape of the streaming attention: waves per block, tiles in flight,
-// bytes per K (or V) tile.  Every attention kernel uses 8 waves and, by
-// default, 2 stages of 16 KiB K + 16 KiB V tiles (K2_ATT_NST, K2_ATT_TILE):
-// ~66 KiB of LDS, so two blocks fit a compute unit.  Measured at the 3.7B
-// shape against 3 stages (~98 KiB, one block per unit): decode step with the
-// position on the device 2.155 against 2.204 ms (bf16 cache, L 520-776),
-// int8 attention at 32k positions 31.7 against 33.8 us; 8 KiB tiles (3 or 4
-// stages) were slower at 32k (35.7-36.9 us).
+// bytes per K (or V) tile.  Every attention kernel uses 8 waves and 16 KiB K
+// + 16 KiB V tiles; the ring holds 3 stages for fp32 / bf16 caches (~98 KiB
+// of LDS, one block per compute unit) and 2 for int8 (~66 KiB, two blocks
+// per unit).  Measured at the 3.7B shape: bf16 cache, decode step with the
+// position on the device 2.139 ms with 3 stages against 2.149 with 2; int8
+// attention at 32k positions 31.7 us with 2 against 33.8 with 3; 8 KiB
+// tiles (3 or 4 stages) were slower at 32k (35.7-36.9 us).
 template <int WPB_, int NST_, int TILE_>
 struct StreamCfg {
     static constexpr int WPB = WPB_, NT = WPB_ * K2_WAVE, NST = NST_, TILE = TILE_;
 };
-#ifndef K2_ATT_NST
-#define K2_ATT_NST 2
-#endif
-#ifndef K2_ATT_TILE
-#define K2_ATT_TILE 16384
-#endif
-using StreamWide = StreamCfg<8, K2_ATT_NST, K2_ATT_TILE>;
-constexpr int ATT_NT = StreamWide::NT;     // threads per stand-alone attention block
+template <int KVDT>
+using StreamFor = StreamCfg<8, KVDT == K2_I8 ? 2 : 3, 16384>;
+constexpr int ATT_NT = StreamFor<K2_BF16>::NT;   // threads per stand-alone attention block
 
-template <int KVDT, int HD, class C = StreamWide>
+template <int KVDT, int HD, class C = StreamFor<KVDT>>
 struct StreamGeom {
     using T = typename KVT<KVDT>::T;
     static constexpr int EPC = KVT<KVDT>::EPC;
@@ -589,7 +584,7 @@ struct StreamGeom {
     static_assert(NI >= 1 && NI * 16 * C::NT == TILEB, "tile copy shape");
 };
 
-template <int KVDT, int HD, int REP, class C = StreamWide>
+template <int KVDT, int HD, int REP, class C = StreamFor<KVDT>>
 __host__ __device__ constexpr int attn_stream_lds_floats()
 {
     // stages (reused for the wave merge afterwards), q, new k/v, merge (m, l)
@@ -630,7 +625,7 @@ __device__ __forceinline__ bool block_wait_count(const unsigned *p, unsigned nee
 // so that no wait inside the block (a barrier, or the wait the compiler
 // places before LDS writes that could race an LDS-DMA) waits for its
 // store.  Returns whether this block holds the new position.
-template <int KVDT, int HD, int REP, bool FUSED, bool COH, class C = StreamWide>
+template <int KVDT, int HD, int REP, bool FUSED, bool COH, class C = StreamFor<KVDT>>
 __device__ __forceinline__ bool attn_stream_block(const AttnArgs &a, int g, int s, int S, float *smem,
                                                   uint32_t &kv_bits, float &kv_scale)
 {
@@ -1074,11 +1069,12 @@ __device__ __forceinline__ void attn_combine_block(const AttnArgs &a, int g, flo
 // Position taken from device memory (a.d_pos set): pos, len, chunk and the
 // split count S follow from *d_pos by the rule of attn_splits on the host
 // (chunk = ceil(len / target) clamped to [K2_ATTN_MIN_CHUNK,
-// K2_ATTN_MAX_CHUNK], target = K2_ATTN_TARGET_BLOCKS / n_kv), so S never
-// exceeds the grid's split extent (attn_max_splits of the capacity).
+// K2_ATTN_MAX_CHUNK], target = K2_ATTN_TARGET_BLOCKS / n_kv), with the chunk
+// raised where needed so that S never exceeds Sg, the grid's split extent
+// (a longer range per block: the kernels take any chunk).
 // Returns false for a position outside [0, cap): the first block reports
 // K2_ERANGE in d_err and every block leaves without writing.
-__device__ __forceinline__ bool attn_resolve_pos(AttnArgs &a)
+__device__ __forceinline__ bool attn_resolve_pos(AttnArgs &a, int Sg)
 {
     if (!a.d_pos) return true;
     const int p = *a.d_pos;            // written by an earlier kernel of the stream
@@ -1093,6 +1089,8 @@ __device__ __forceinline__ bool attn_resolve_pos(AttnArgs &a)
     int c = (a.len + target - 1) / target;
     c = c < K2_ATTN_MIN_CHUNK ? K2_ATTN_MIN_CHUNK : c;
     c = c > K2_ATTN_MAX_CHUNK ? K2_ATTN_MAX_CHUNK : c;
+    const int cg = (a.len + Sg - 1) / Sg;
+    c = c > cg ? c : cg;
     a.chunk = c;
     a.S = (a.len + c - 1) / c;
     return true;
@@ -1131,7 +1129,7 @@ __device__ __forceinline__ void attn_prefetch_block(const AttnArgs &a)
 template <int KVDT, int HD, int REP, bool FUSED>
 __global__ __launch_bounds__(ATT_NT) void attn_kernel(const AttnArgs a0)
 {
-    constexpr int NA = attn_stream_lds_floats<KVDT, HD, REP, StreamWide>(), NC = combine_lds_floats<REP, ATT_NT>();
+    constexpr int NA = attn_stream_lds_floats<KVDT, HD, REP>(), NC = combine_lds_floats<REP, ATT_NT>();
     extern __shared__ float4 lds4[];
     float *smem = reinterpret_cast<float *>(lds4);
     static_assert(NA >= NC, "combine fits the attention LDS");
@@ -1141,7 +1139,7 @@ __global__ __launch_bounds__(ATT_NT) void attn_kernel(const AttnArgs a0)
         return;
     }
     AttnArgs a = a0;
-    if (!attn_resolve_pos(a)) return;
+    if (!attn_resolve_pos(a, gridDim.x)) return;
     if ((int)blockIdx.x >= a.S) return;            // device split count below the grid's
     const int g = blockIdx.y, S = a.S;
     K2_ATRACE_CLEAR();

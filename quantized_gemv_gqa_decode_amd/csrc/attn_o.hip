@@ -19,7 +19,6 @@ static int attn_o_go(const AttnOArgs &f0, hipStream_t st)
     constexpr int WPB = ATT_NT / K2_WAVE;
     AttnOArgs f = f0;
     f.o.n_units = (f.o.N + AO_R - 1) / AO_R;
-    f.na = f.at.S * f.at.n_kv;
     const int no = (int)((f.o.n_units + WPB - 1) / WPB);
     size_t lds = attn_stream_lds_floats<KVDT, HD, REP>();
     const size_t lc = combine_lds_floats<REP, ATT_NT>();
@@ -38,11 +37,18 @@ static int attn_o_go(const AttnOArgs &f0, hipStream_t st)
         return n < 1 ? 1 : n;
     }();
     const int cus = device_cus();
-    // with a host position: only when both grids fit at once (else the two
-    // kernels); with a device position the split count is not known here
-    // and the one launch is always taken (correct whatever fits, see
-    // attn_o_impl.h)
-    if (cus <= 0 || (!f.at.d_pos && f.na + no > cus * per_cu)) return K2_EUNSUPPORTED;
+    if (cus <= 0) return K2_EUNSUPPORTED;
+    // only when both roles fit the chip at once (else the two kernels).  A
+    // device position's split count is not known here: the grid's split
+    // extent is cut to what fits beside the O blocks, and the kernel takes
+    // longer ranges per block where the position needs more splits than that
+    if (f.at.d_pos) {
+        const int room = (cus * per_cu - no) / f.at.n_kv;
+        if (room < 1) return K2_EUNSUPPORTED;
+        f.at.S = f.at.S < room ? f.at.S : room;
+    }
+    f.na = f.at.S * f.at.n_kv;
+    if (f.na + no > cus * per_cu) return K2_EUNSUPPORTED;
     hipLaunchKernelGGL(kern, dim3(f.na + no), dim3(ATT_NT), lds * sizeof(float), st, f);
     K2_CHECK_LAUNCH();
     return K2_OK;

@@ -260,15 +260,12 @@ __device__ __forceinline__ void gemv_prefetch(const GemvArgs &a, int64_t unit, i
 // The unit loop of one wave, starting at `unit` whose pass-0 loads are in
 // rows/ok/w/sc; activations staged in xs (plane stride S).  COH: outputs are
 // stored at device scope (read by other blocks of the same grid).
-// res0 (nullable, B = 1): the residual of the first unit's rows, already
-// loaded (lane r holds row r's value).
 template <int WDT, int R, int U, int B, int EPI, bool COH>
 __device__ __forceinline__ void gemv_units(const GemvArgs &a, const float *xs, int S, int64_t unit,
                                            int64_t stride, int64_t (&rows)[R], bool (&ok)[R],
                                            k2_u4 (&w)[U][R], float (&sc)[U][R], float &best_v,
-                                           int &best_i, const float *res0 = nullptr)
+                                           int &best_i)
 {
-    bool first = true;
     constexpr int EPC = WT<WDT>::EPC;
     const int CPR = a.K / EPC;                     // 16-byte chunks per row
     const int passes = (CPR + U * K2_WAVE - 1) / (U * K2_WAVE);
@@ -340,15 +337,11 @@ __device__ __forceinline__ void gemv_units(const GemvArgs &a, const float *xs, i
                 for (int r = 0; r < R; ++r) {
                     if (lane == (b * R + r) % K2_WAVE && cur_ok[r]) {
                         float v = acc[b][r];
-                        if (a.residual) {
-                            if (res0 && first && B == 1) v += *res0;
-                            else v += ld1<COH>(a.residual + (int64_t)b * a.N + cur_rows[r]);
-                        }
+                        if (a.residual) v += a.residual[(int64_t)b * a.N + cur_rows[r]];
                         st1<COH>(a.y + (int64_t)b * a.N + cur_rows[r], v);
                     }
                 }
         }
-        first = false;
     }
 }
 

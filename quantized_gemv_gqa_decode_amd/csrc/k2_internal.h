@@ -118,11 +118,11 @@ int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qr
 // Sync words of the attention + O launch: the O-block counter on a line of
 // its own, and 16 copies (one 256-byte line each) of the per-kv-head ready
 // flags, so that the O blocks' polling spreads over memory channels.
+constexpr int AO_SYNC_HEADS = 0;           // kv heads whose output is stored
 constexpr int AO_SYNC_ODONE = 64;          // O blocks finished
 constexpr int AO_READY_COPIES = 16;
-constexpr int AO_SYNC_READY = 128;         // [copy * 64 + kv head]: that head's output is stored
+constexpr int AO_SYNC_READY = 128;         // [copy * 64]: every head's output is stored
 constexpr int AO_SYNC_WORDS = AO_SYNC_READY + AO_READY_COPIES * 64;
-constexpr int AO_MAX_KV = 64;              // head flags per copy line
 
 // Attention followed by the O projection (+ residual) in one launch when
 // the shape has an instantiation and both grids fit on the chip at once;

@@ -119,8 +119,8 @@ def _generate_dev(gm, prompt, n_decode, teacher=None):
                                       ("q4s", "i8")])
 @pytest.mark.parametrize("P", [3, 200])
 def test_head128_device_position_bit_identical(wdt, kvdt, P):
-    """k2_decode_step_dev (position read on the device, grids sized for the
-    capacity, blocks past the position's split count leaving at once) against
+    """k2_decode_step_dev (position read on the device, grids sized without
+    it, blocks past the position's split count leaving at once) against
     k2_decode_step (host position, grids sized for it): the same splits do
     the same arithmetic, so every logit and token is the same bit for bit.
     3 prompt positions give one attention split per kv head, 200 give
@@ -132,6 +132,38 @@ def test_head128_device_position_bit_identical(wdt, kvdt, P):
     assert t_dev == t_host
     for i, (a, b) in enumerate(zip(l_dev, l_host)):
         assert np.array_equal(a, b), (i, float(np.abs(a - b).max()))
+
+
+@pytest.mark.parametrize("pos", [700, 900, 1000])
+def test_device_position_more_splits_than_the_grid(pos):
+    """The 3.7B layer shape (2 layers, vocab 4096) with a bf16 cache: the
+    attention + O launch of k2_decode_step_dev fits 12 attention splits per
+    kv head beside its 160 O blocks.  Up to 768 positions the device split
+    rule gives at most 12 and the step equals the host-position step bit
+    for bit; past that each block takes a longer range than the host rule's
+    (which runs attention and O as two launches there), so the two agree to
+    fp32 rounding: logits within 1e-3, the same token."""
+    cfg = synth.K2H_BF16.replace(n_layers=2, vocab=4096, cap=1024)
+    gm = DecodeModel(cfg, DEV)
+    gm.prefill(synth.prompt(cfg, pos), 0)
+    tok = int(synth.prompt(cfg, pos + 1)[pos])
+    lg, nx = gm.step(tok, pos)                       # host position
+    torch.cuda.synchronize()
+    l_host, t_host = to_host(lg).copy(), int(nx.item())
+    gm.set_pos(pos)
+    d_tok = torch.full((1,), tok, dtype=torch.int32, device=DEV)
+    d_nx = torch.zeros(1, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gm.step_dev(d_tok, d_nx, err)                    # the same slot, written again with the same values
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and int(gm.d_pos.item()) == pos + 1
+    l_dev = to_host(gm.logits)
+    diff = float(np.abs(l_dev - l_host).max())
+    say(f"position {pos}: device vs host position max|dlogit| = {diff:.3g}")
+    if pos + 1 <= 768:
+        assert np.array_equal(l_dev, l_host), diff
+    assert diff <= 1e-3
+    assert int(d_nx.item()) == t_host or near_tie_ok(int(d_nx.item()), l_host.astype(np.float64), 2e-3)
 
 
 @pytest.mark.parametrize("change", [dict(groups=1), dict(n_kv=4), dict(n_kv=1),
