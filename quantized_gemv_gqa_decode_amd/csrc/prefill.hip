@@ -47,21 +47,43 @@ __global__ void embed_rows_kernel(const PfTokens tk, int embdt, const void *E, i
 }
 
 struct PrefillWs {
-    float *h, *x, *qkv, *o, *act, *part, *qrot, *lm_part, *logits;
+    float *h, *x, *qkv, *o, *act, *part, *qrot, *lm_part, *logits, *ar_v;
+    int *ar_i;
     void *attn, *rows, *am;
     unsigned *rows_cnt;
     int32_t *next;
 };
 
-// First maximum of every row of x [rows][n] (one block per row).
-__global__ __launch_bounds__(K2_BLOCK) void argmax_rows_kernel(const float *x, int n, int32_t *out)
+// First maximum of every row of x [rows][n] in two launches: block (b, t)
+// of the first finds the first maximum of the b-th of AR_NB contiguous
+// slices of row t; one wave per row then takes the first maximum of the
+// AR_NB candidates (ties go to the lower index at both levels, so the result
+// is the row's first maximum).
+constexpr int AR_NB = K2_WAVE;
+
+__global__ __launch_bounds__(K2_BLOCK) void argmax_rows_part_kernel(const float *x, int n, float *pv, int *pi)
 {
-    const float *r = x + (int64_t)blockIdx.x * n;
+    const int t = blockIdx.y, b = blockIdx.x;
+    const int per = (n + AR_NB - 1) / AR_NB;
+    const int lo = b * per, hi = lo + per < n ? lo + per : n;
+    const float *r = x + (int64_t)t * n;
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int i = threadIdx.x; i < n; i += K2_BLOCK) argmax_pair_max(bv, bi, r[i], i);
+    for (int i = lo + threadIdx.x; i < hi; i += K2_BLOCK) argmax_pair_max(bv, bi, r[i], i);
     argmax_block(bv, bi);
-    if (threadIdx.x == 0) out[blockIdx.x] = bi;
+    if (threadIdx.x == 0) {
+        pv[t * AR_NB + b] = bv;
+        pi[t * AR_NB + b] = bi;
+    }
+}
+
+__global__ __launch_bounds__(K2_WAVE) void argmax_rows_final_kernel(const float *pv, const int *pi, int32_t *out)
+{
+    const int t = blockIdx.x, lane = threadIdx.x;
+    float v = pv[t * AR_NB + lane];
+    int i = pi[t * AR_NB + lane];
+    argmax_wave(v, i);
+    if (lane == 0) out[t] = i;
 }
 
 // A projection of the chunk's T rows: up to 32 rows the small-T product
@@ -126,7 +148,11 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base, boo
     char *qrot = take((size_t)T * qd * 4);
     char *lm_part = verify ? take(dense_mfma_ws_bytes(c->vocab, c->hidden, T)) : nullptr;
     char *lgt = verify ? take((size_t)T * c->vocab * 4) : nullptr;
+    char *arv = verify ? take((size_t)T * AR_NB * 4) : nullptr;
+    char *ari = verify ? take((size_t)T * AR_NB * 4) : nullptr;
     if (w) {
+        w->ar_v = (float *)arv;
+        w->ar_i = (int *)ari;
         w->lm_part = (float *)lm_part;
         w->logits = (float *)lgt;
         w->rows = rows;
@@ -236,7 +262,10 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
         if ((rc = rmsnorm_rows_launch(w.h, m->g_final, w.x, T, H, c->groups, c->eps, st))) return rc;
         if ((rc = dense_mfma((const uint16_t *)m->lm, w.x, lg, c->vocab, H, T, DM_EPI_PLAIN, w.lm_part, st)))
             return rc;
-        hipLaunchKernelGGL(argmax_rows_kernel, dim3(T), dim3(K2_BLOCK), 0, st, lg, c->vocab, next);
+        hipLaunchKernelGGL(argmax_rows_part_kernel, dim3(AR_NB, T), dim3(K2_BLOCK), 0, st, lg, c->vocab, w.ar_v,
+                           w.ar_i);
+        K2_CHECK_LAUNCH();
+        hipLaunchKernelGGL(argmax_rows_final_kernel, dim3(T), dim3(K2_WAVE), 0, st, w.ar_v, w.ar_i, next);
         K2_CHECK_LAUNCH();
     } else if (logits) {
         ArgmaxArgs am{};
