@@ -787,8 +787,8 @@ def main():
         prompt = synth.prompt(cfg, P)
         t0 = time.perf_counter()
         if cfg.wdt == "bf16" and P >= 2 and not args.prefill_steps:
-            gm.prefill(prompt, 0, chunk=32)          # k2_prefill, 32 positions per call
-            how = "k2_prefill, chunks of 32"
+            gm.prefill(prompt, 0)                    # k2_prefill, 256 positions per call
+            how = "k2_prefill, chunks of 256"
         else:
             for p, t in enumerate(prompt):
                 gm.step(int(t), p, want_logits=(p == P - 1))
