@@ -173,7 +173,10 @@ def test_q4s_decode_every_nibble_via_gemv():
                                    (70, 4096, 1), (33, 10240, 1), (45, 320, 2), (19, 1024, 4),
                                    (23, 1536, 8),
                                    # rows split over 2 or 4 waves (long rows), ragged row counts
-                                   (2561, 10240, 1), (1001, 5632, 1), (3, 3072, 1), (7, 12288, 1)])
+                                   (2561, 10240, 1), (1001, 5632, 1), (3, 3072, 1), (7, 12288, 1),
+                                   # 2560 columns (80 chunks per 4-bit row: a partly empty
+                                   # second slot) with 2 and 4 rows per wave
+                                   (5123, 2560, 1), (10241, 2560, 1)])
 def test_gemv_matches_oracle(wdt, N, K, B):
     if wdt == "q4s" and K % 64:
         pytest.skip("Q4S blocks are 64 columns")
@@ -194,6 +197,56 @@ def test_gemv_matches_oracle(wdt, N, K, B):
         tol = sumabs_bound(dense, x[b].astype(np.float64))
         assert np.all(np.abs(got[b] - ref) <= tol), (b, np.abs(got[b] - ref).max())
         assert np.all(np.abs(got_r[b] - (ref + res[b])) <= tol + 2.0 ** -23 * np.abs(ref + res[b]))
+
+
+def _wdev(wdt, m):
+    return to_dev(m.w), (to_dev(m.s) if m.s is not None else None)
+
+
+@pytest.mark.parametrize("wdt", ["bf16", "fp8", "mxfp4", "q4s"])
+def test_norm_gemv_swiglu_and_argmax_2560_columns(wdt):
+    """The fused decode GEMVs at the 3.7B row length (2560 columns: 80 chunks
+    per 4-bit row, 160 per fp8 row) with 2 rows per wave and more: GroupedRMSNorm
+    prologue, then SwiGLU of gate / up row pairs (10240 rows), and the argmax
+    epilogue (10241 rows, ragged), against the oracle's norm and matvec."""
+    K, inter, G, eps = 2560, 5120, 2, 1e-6
+    rng = np.random.default_rng(7)
+    h = rng.standard_normal(K).astype(np.float32) * 3.0
+    gamma = (1.0 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    x = oracle.rmsnorm_grouped(h.astype(np.float64), gamma.astype(np.float64), G, eps)
+    wd = k2.DTYPES[wdt]
+    # SwiGLU: gate rows, then up rows
+    m, dense = _mat_and_dense(wdt, 2 * inter, K, seed=11)
+    W, S = _wdev(wdt, m)
+    act = torch.full((inter,), float("nan"), dtype=torch.float32, device=DEV)
+    check(k2.k2_norm_gemv_swiglu(wd, W, S, to_dev(h), to_dev(gamma), G, eps, act, inter, K))
+    sync()
+    ref = m.matvec(x)
+    g, u = ref[:inter], ref[inter:]
+    bound = sumabs_bound(dense, x) + 1e-5 * (np.abs(dense) @ np.abs(x))
+    sg = 1.0 / (1.0 + np.exp(-g))
+    want = g * sg * u
+    tol = 1.2 * bound[:inter] * np.abs(u) + np.abs(g * sg) * bound[inter:] + 1e-6
+    err = np.abs(to_host(act) - want)
+    say(f"{wdt} norm+gate/up+SwiGLU: max err {err.max():.3g}")
+    assert np.all(err <= tol), (int(np.argmax(err - tol)), err.max())
+    # argmax: 10241 rows (an incomplete last unit)
+    N = 10241
+    m2, dense2 = _mat_and_dense(wdt, N, K, seed=13)
+    W2, S2 = _wdev(wdt, m2)
+    logits = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+    idx = torch.zeros(1, dtype=torch.int32, device=DEV)
+    wsb = k2.k2_argmax_workspace_bytes(N)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    check(k2.k2_norm_gemv_argmax(wd, W2, S2, to_dev(h), to_dev(gamma), G, eps, logits, N, K, idx, ws, wsb))
+    sync()
+    ref2 = m2.matvec(x)
+    b2 = sumabs_bound(dense2, x) + 1e-5 * (np.abs(dense2) @ np.abs(x))
+    got = to_host(logits)
+    assert np.all(np.abs(got - ref2) <= b2), float(np.abs(got - ref2).max())
+    best = int(np.argmax(ref2))
+    t = int(idx.item())
+    assert t == best or ref2[best] - ref2[t] <= 2 * b2.max(), (t, best)
 
 
 def test_gemv_rejects_bad_args_without_writing():
