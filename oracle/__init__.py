@@ -361,9 +361,10 @@ class Decoder:
                              C.cast(arr, C.POINTER(_Layer)))
 
     @classmethod
-    def from_synth(cls, cfg, n_layers: Optional[int] = None) -> "Decoder":
+    def from_synth(cls, cfg, n_layers: Optional[int] = None, progress=None) -> "Decoder":
         """Build from the seeded draws in ``synth`` (optionally only the first
-        ``n_layers`` layers, for partial-depth checks)."""
+        ``n_layers`` layers, for partial-depth checks).  ``progress``, if
+        given, is called with a short message after each layer is drawn."""
         import synth
         if n_layers is not None:
             cfg = cfg.replace(n_layers=n_layers)
@@ -373,6 +374,8 @@ class Decoder:
                            for w in ("wqkv", "wo", "wgu", "wd")})
             gi.append(synth.norm_gain(cfg))
             gp.append(synth.norm_gain(cfg))
+            if progress is not None:
+                progress(f"oracle layer {l + 1}/{cfg.n_layers} drawn")
         lm = Mat.from_draw(cfg.wdt, synth.lm_head_weight(cfg))
         return cls(cfg, synth.embed_weight(cfg), lm, layers, gi, gp, synth.norm_gain(cfg))
 

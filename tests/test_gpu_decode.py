@@ -422,6 +422,15 @@ def test_head128_prefill_large_chunks(kvdt, P, chunk):
 
 
 @pytest.mark.parametrize("kvdt", ["bf16", "i8"])
+def test_head128_prefill_long_prompt(kvdt):
+    """A 2000-position prompt in chunks of 256: the matrix-core attention
+    streams up to 32 key tiles per block and the last chunk (208 rows)
+    starts at position 1792; then three decode steps on those caches."""
+    cfg = HEAD128.replace(wdt="bf16", kvdt=kvdt, cap=2048)
+    _prefill_parity(cfg, 2000, 3, chunk=256)
+
+
+@pytest.mark.parametrize("kvdt", ["bf16", "i8"])
 @pytest.mark.parametrize("n_qh,n_kv", [(8, 1), (8, 4), (4, 4)])
 def test_prefill_gqa_ratios(n_qh, n_kv, kvdt):
     """Chunks of 64 rows on the matrix-core attention at 8, 2 and 1 query
