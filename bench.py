@@ -703,10 +703,12 @@ def main():
                     help="latent-MoE workload only: comma-separated token counts")
     ap.add_argument("--prefill-chunk", type=int, default=0, metavar="T",
                     help="instead of the decode bench: time the prompt's prefill through "
-                         "k2_prefill in chunks of T positions (2..256; bf16 weights)")
+                         "k2_prefill in chunks of T positions (2..256; bf16, fp8, MXFP4 or Q4S "
+                         "weights)")
     ap.add_argument("--verify-chunk", type=int, default=0, metavar="T",
                     help="instead of the decode bench: time k2_verify of T positions (2..32; "
-                         "bf16 weights) after the prompt, i.e. one draft-and-verify round")
+                         "bf16, fp8, MXFP4 or Q4S weights) after the prompt, i.e. one "
+                         "draft-and-verify round")
     ap.add_argument("--spec", type=int, default=0, metavar="K",
                     help="instead of the decode bench: greedy decode of --steps tokens as "
                          "draft-and-verify rounds with the n-gram drafter (up to K drafts), "
@@ -792,7 +794,7 @@ def main():
     else:
         prompt = synth.prompt(cfg, P)
         t0 = time.perf_counter()
-        if cfg.wdt == "bf16" and P >= 2 and not args.prefill_steps:
+        if cfg.wdt != "f32" and P >= 2 and not args.prefill_steps:
             gm.prefill(prompt, 0)                    # k2_prefill, 256 positions per call
             how = "k2_prefill, chunks of 256"
         else:

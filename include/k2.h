@@ -316,7 +316,8 @@ typedef struct {
 
 /* One layer (host struct of device pointers).  qkv stacks the q rows, then k,
  * then v; gu stacks the gate rows, then the up rows.  *_s: fp32 row scales
- * (fp8), E8M0 bytes (MXFP4), NULL otherwise. */
+ * [N] (fp8), E8M0 bytes [N][K/32] (MXFP4), fp32 block scales [N][K/64]
+ * (Q4S), NULL otherwise. */
 typedef struct {
     const void *qkv, *qkv_s;    /* [(n_qh + 2 n_kv) hd][hidden] */
     const void *o, *o_s;        /* [hidden][n_qh hd] */
@@ -349,12 +350,17 @@ int k2_model_check(const k2_model *m);
  * calls of k2_decode_step at those positions, up to rounding: the
  * projections of the T rows run on the matrix cores with each fp32
  * activation split into bf16 hi + lo (about 16 significant bits, fp32
- * accumulation); the caches receive every position; logits (nullable) and
- * next_token (nullable) are those of the LAST position.  tokens: HOST array
- * [T].  Needs bf16 projection weights and 2 <= T <= 256 (K2_EUNSUPPORTED
- * otherwise; a single position is k2_decode_step); every weight byte is read
- * from HBM once per call (the token blocks of a row block, 128 positions
- * each, share it through L2).  ws: device workspace of k2_prefill_workspace_bytes(&m->cfg, T) bytes
+ * accumulation); fp8, MXFP4 and Q4S weights are decoded to exact bf16
+ * values (fp8: the code's value, row scale applied to the row's sum; MXFP4:
+ * the element times its block's 2^e; Q4S: the code, each 64-column block's
+ * sum times its scale).  The caches receive every position; logits
+ * (nullable) and next_token (nullable) are those of the LAST position.
+ * tokens: HOST array [T].  Needs bf16, fp8, MXFP4 or Q4S projection weights
+ * with hidden, n_qh * head_dim and inter multiples of 128, and 2 <= T <= 256
+ * (K2_EUNSUPPORTED otherwise; a single position is k2_decode_step; MXFP4
+ * and Q4S scale arrays 16-byte aligned, K2_EINVAL otherwise); every
+ * weight byte is read from HBM once per call (the token blocks of a row
+ * block, 32 to 128 positions each, share it through L2).  ws: device workspace of k2_prefill_workspace_bytes(&m->cfg, T) bytes
  * (it serves every smaller T), 256-byte aligned, zero-filled before its
  * first use (left zeroed where it must be); calls that share it must not
  * overlap in time.  K2_ERANGE if a token is outside the
@@ -366,7 +372,8 @@ int k2_prefill(const k2_model *m, const int32_t *tokens, int T, int pos0, float 
 /* Batched greedy verification of T positions in one sweep (speculative
  * decoding: the pages' drafter proposes tokens and one pass over the
  * weights checks them all): the k2_prefill computation, plus the final norm,
- * the lm_head (matrix cores) and the first-maximum argmax of EVERY row.
+ * the lm_head (matrix cores, any of k2_prefill's weight formats) and the
+ * first-maximum argmax of EVERY row.
  * next_tokens[t] (device int32 [T], required) is the greedy token after
  * position pos0 + t, the same as a k2_decode_step at that position would
  * give up to rounding; logits (nullable, device [T][vocab]) receives every

@@ -33,6 +33,19 @@
 // MFMA operand layout (16x16x32 bf16): lane l holds A row l % 16 and B
 // column l % 16, elements k = 8 (l / 16) + [0, 8); D holds column l % 16,
 // rows 4 (l / 16) + [0, 4).
+//
+// Quantized weights ([k2-burn] "Quantization": fp8 and int4 Q4S; [k3_run.c]
+// header: MXFP4) are decoded in registers to bf16 values that are exact:
+//   * fp8 E4M3: the code's value (3 mantissa bits); the row scale multiplies
+//     the row's sum (the epilogue, or each split's partial);
+//   * MXFP4: the E2M1 value times the block's 2^e (two significant bits);
+//   * Q4S: the int4 code / 16; each 64-column block's products go to a
+//     fresh accumulator that is added to the row's sum times 16 s[n][b].
+// Which k a lane holds is free as long as A and B agree, so the quantized
+// forms pick the k order that makes a lane's weight bytes contiguous (one
+// or two 16- or 8-byte loads per row tile and chunk) and, for Q4S, keeps
+// every MFMA inside one 64-column block; the LDS k-chunk read for B follows
+// the same order.
 #include "k2_dev.h"
 #include "k2_internal.h"
 
@@ -48,7 +61,8 @@ constexpr int GM_ROWB = GM_BK * 2;         // bytes of one token's chunk row in 
 
 
 struct GemmArgs {
-    const uint16_t *W;         // [N][K] bf16
+    const void *W;             // [N][K] of the weight format (4-bit: [N][K/2] bytes)
+    const void *Ws;            // fp8: float [N]; MXFP4: uint8 [N][K/32]; Q4S: float [N][K/64]
     const uint16_t *xh, *xl;   // [TP][K] bf16 planes (rows >= T zero)
     float *y;                  // [T][N] (SwiGLU: [T][N/2])
     float *part;               // [S][TP][N] when S > 1
@@ -92,13 +106,63 @@ __device__ __forceinline__ int gm_row(const GemmArgs &a, int b, int w, int rt, i
     return b * GM_BM + w * 64 + rt * 16 + r;
 }
 
-template <int BT>
+// two fp32 whose low 16 bits are zero (exact bf16 values) -> a bf16 pair
+__device__ __forceinline__ uint32_t gm_pack(float lo, float hi)
+{
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+// bytes of weight storage per row per 128-column chunk; 16-byte registers
+// per lane and row tile that hold a chunk's weights
+template <int WDT> struct GmW;
+template <> struct GmW<K2_BF16>    { static constexpr int CB = 256, NW = 4; };
+template <> struct GmW<K2_FP8E4M3> { static constexpr int CB = 128, NW = 2; };
+template <> struct GmW<K2_MXFP4>   { static constexpr int CB = 64,  NW = 1; };
+template <> struct GmW<K2_Q4S>     { static constexpr int CB = 64,  NW = 1; };
+
+// LDS k-chunk (8 columns) that lane quarter q multiplies in k-step j
+template <int WDT>
+__device__ __forceinline__ int gm_kchunk(int j, int q)
+{
+    if constexpr (WDT == K2_BF16) return 4 * j + q;                       // k = 32 j + 8 q
+    else if constexpr (WDT == K2_Q4S) return 8 * (j >> 1) + 2 * q + (j & 1);   // k = 64 (j/2) + 16 q + 8 (j%2)
+    else return 4 * q + j;                                                // k = 32 q + 8 j
+}
+
+// the lane's 8 weights of k-step j of one row tile, as exact bf16
+template <int WDT>
+__device__ __forceinline__ gm_bf16x8 gm_decode(const k2_u4 (&w)[GmW<WDT>::NW], int j, float sc)
+{
+    k2_u4 r;
+    if constexpr (WDT == K2_BF16) {
+        r = w[j];
+    } else if constexpr (WDT == K2_FP8E4M3) {
+        const k2_u4 u = w[j >> 1];
+        const uint32_t d0 = (j & 1) ? u.z : u.x, d1 = (j & 1) ? u.w : u.y;
+        const k2_f2 a = fp8x2_lo(d0), b = fp8x2_hi(d0), c = fp8x2_lo(d1), d = fp8x2_hi(d1);
+        r = k2_u4{gm_pack(a.x, a.y), gm_pack(b.x, b.y), gm_pack(c.x, c.y), gm_pack(d.x, d.y)};
+    } else if constexpr (WDT == K2_MXFP4) {
+        const uint32_t d = w[0][j];
+        const k2_f2 a = fp4x2<0>(d), b = fp4x2<1>(d), c = fp4x2<2>(d), e = fp4x2<3>(d);
+        r = k2_u4{gm_pack(a.x * sc, a.y * sc), gm_pack(b.x * sc, b.y * sc), gm_pack(c.x * sc, c.y * sc),
+                  gm_pack(e.x * sc, e.y * sc)};
+    } else {
+        const uint32_t d = w[0][j];
+        r = k2_u4{gm_pack(q4s_off(d), q4s_off(d >> 4)), gm_pack(q4s_off(d >> 8), q4s_off(d >> 12)),
+                  gm_pack(q4s_off(d >> 16), q4s_off(d >> 20)), gm_pack(q4s_off(d >> 24), q4s_off(d >> 28))};
+    }
+    return __builtin_bit_cast(gm_bf16x8, r);
+}
+
+template <int BT, int WDT>
 __global__ __launch_bounds__(256, BT <= 64 ? 2 : 1) void gm_kernel(const GemmArgs a)
 {
     constexpr int NT = BT / 16;                           // token tiles
     constexpr int PLANE = BT * GM_ROWB;                   // bytes of one plane's chunk tile
     constexpr int STAGE = 2 * PLANE;                      // hi + lo
     constexpr int NDMA = PLANE / 1024 / 4;                // 1 KiB wave copies per wave, plane and chunk
+    constexpr int CB = GmW<WDT>::CB, NW = GmW<WDT>::NW;
+    constexpr bool Q4 = WDT == K2_Q4S;
     extern __shared__ float4 lds4[];
     char *lds = reinterpret_cast<char *>(lds4);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -111,23 +175,57 @@ __global__ __launch_bounds__(256, BT <= 64 ? 2 : 1) void gm_kernel(const GemmArg
     const int tblk = L % a.tb, rest = L / a.tb;
     const int rb = rest % a.rb, split = rest / a.rb;
     const int t0 = tblk * BT, kbeg = split * a.KS, nch = a.KS / GM_BK;
+    const int64_t rowb = (int64_t)a.K / GM_BK * CB;       // storage bytes of one row
 
-    // this wave's row tiles; rows past N read row N-1 and are never stored
-    const uint16_t *wrow[GM_RT];
+    // this wave's row tiles (A rows: lane row c16); rows past N read row N-1
+    // and are never stored.  Byte offset of the lane's first load in chunk 0:
+    // bf16 k = 8q (then +32 per k-step), fp8 k = 32q, MXFP4 k = 32q, Q4S
+    // k = 16q (then +64 for the second block)
+    const char *wrow[GM_RT];
+    const uint32_t *erow[GM_RT];                          // MXFP4: the row's scale bytes of chunk 0
+    constexpr int QOFF = WDT == K2_BF16 ? 16 : WDT == K2_FP8E4M3 ? 32 : WDT == K2_MXFP4 ? 16 : 8;
 #pragma unroll
     for (int rt = 0; rt < GM_RT; ++rt) {
         int r = gm_row(a, rb, wave, rt, c16);
         r = r < a.N ? r : a.N - 1;
-        wrow[rt] = a.W + (int64_t)r * a.K + kbeg + q * 8;
+        wrow[rt] = (const char *)a.W + r * rowb + (int64_t)kbeg / GM_BK * CB + q * QOFF;
+        if constexpr (WDT == K2_MXFP4)
+            erow[rt] = (const uint32_t *)((const uint8_t *)a.Ws + (int64_t)r * (a.K / 32) + kbeg / 32);
     }
-    // chunk c, k-step j of row tile rt: the 16 B at column c*128 + 32j + 8q
-    // (the 4 lanes of a row read 64 contiguous bytes per instruction)
-    auto load_w = [&](int c, k2_u4 (&w)[GM_RT][4]) {
+    // Q4S: the lane's row's block scales (the product is taken transposed,
+    // so a lane's D values all belong to its own weight row c16)
+    const float *srow[GM_RT];
+    if constexpr (Q4) {
 #pragma unroll
-        for (int rt = 0; rt < GM_RT; ++rt)
+        for (int rt = 0; rt < GM_RT; ++rt) {
+            int r = gm_row(a, rb, wave, rt, c16);
+            r = r < a.N ? r : a.N - 1;
+            srow[rt] = (const float *)a.Ws + (int64_t)r * (a.K / 64) + kbeg / 64;
+        }
+    }
+    // (scales stay raw until used: converting them here would wait for the
+    // loads just issued)
+    auto load_w = [&](int c, k2_u4 (&w)[GM_RT][NW], uint32_t (&e)[GM_RT], k2_f2 (&s)[GM_RT]) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                w[rt][j] = __builtin_nontemporal_load(reinterpret_cast<const k2_u4 *>(wrow[rt] + c * GM_BK + 32 * j));
+        for (int rt = 0; rt < GM_RT; ++rt) {
+            const char *p = wrow[rt] + (int64_t)c * CB;
+            if constexpr (WDT == K2_BF16) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    w[rt][j] = __builtin_nontemporal_load(reinterpret_cast<const k2_u4 *>(p + 64 * j));
+            } else if constexpr (WDT == K2_FP8E4M3) {
+                w[rt][0] = __builtin_nontemporal_load(reinterpret_cast<const k2_u4 *>(p));
+                w[rt][1] = __builtin_nontemporal_load(reinterpret_cast<const k2_u4 *>(p + 16));
+            } else if constexpr (WDT == K2_MXFP4) {
+                w[rt][0] = __builtin_nontemporal_load(reinterpret_cast<const k2_u4 *>(p));
+                e[rt] = erow[rt][c];
+            } else {
+                const uint64_t lo = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(p));
+                const uint64_t hi = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(p + 32));
+                w[rt][0] = k2_u4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+                s[rt] = *reinterpret_cast<const k2_f2 *>(srow[rt] + 2 * c);
+            }
+        }
     };
     // the activation tile of chunk c into LDS buffer c & 1: wave copy i of a
     // plane covers tile bytes [(4i + wave) * 1024, + 1024); tile byte o is
@@ -152,8 +250,10 @@ __global__ __launch_bounds__(256, BT <= 64 ? 2 : 1) void gm_kernel(const GemmArg
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) acc[rt][tt] = gm_f32x4{0.f, 0.f, 0.f, 0.f};
 
-    k2_u4 wc[GM_RT][4], wn[GM_RT][4];
-    load_w(0, wc);
+    k2_u4 wc[GM_RT][NW], wn[GM_RT][NW];
+    uint32_t ec[GM_RT], en[GM_RT];
+    k2_f2 sc[GM_RT], sn[GM_RT];
+    load_w(0, wc, ec, sc);
     dma_x(0);
 #pragma unroll 1
     for (int c = 0; c < nch; ++c) {
@@ -161,36 +261,155 @@ __global__ __launch_bounds__(256, BT <= 64 ? 2 : 1) void gm_kernel(const GemmArg
         __syncthreads();                                  // every wave's; nobody still reads buffer (c + 1) & 1
         if (c + 1 < nch) {
             dma_x(c + 1);
-            load_w(c + 1, wn);
+            load_w(c + 1, wn, en, sn);
         }
         const char *st = lds + (c & 1) * STAGE;
+        if constexpr (!Q4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int kc = j * 4 + q;                     // this lane's k-chunk in k-step j
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                const int t = tt * 16 + c16;
-                const int off = t * GM_ROWB + ((kc - t) & 15) * 16;
-                const gm_bf16x8 bh = *reinterpret_cast<const gm_bf16x8 *>(st + off);
-                const gm_bf16x8 bl = *reinterpret_cast<const gm_bf16x8 *>(st + PLANE + off);
-                // the hi products of all row tiles, then the lo ones: 4
-                // independent MFMAs between two into one accumulator
+            for (int j = 0; j < 4; ++j) {
+                gm_bf16x8 A[GM_RT];
 #pragma unroll
                 for (int rt = 0; rt < GM_RT; ++rt)
-                    acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gm_bf16x8, wc[rt][j]), bh,
-                                                                          acc[rt][tt], 0, 0, 0);
+                    A[rt] = gm_decode<WDT>(wc[rt], j, WDT == K2_MXFP4 ? e8m0_to_f32((ec[rt] >> (8 * q)) & 0xFFu) : 0.f);
+                const int kc = gm_kchunk<WDT>(j, q);          // this lane's k-chunk in k-step j
 #pragma unroll
-                for (int rt = 0; rt < GM_RT; ++rt)
-                    acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gm_bf16x8, wc[rt][j]), bl,
-                                                                          acc[rt][tt], 0, 0, 0);
+                for (int tt = 0; tt < NT; ++tt) {
+                    const int t = tt * 16 + c16;
+                    const int off = t * GM_ROWB + ((kc - t) & 15) * 16;
+                    const gm_bf16x8 bh = *reinterpret_cast<const gm_bf16x8 *>(st + off);
+                    const gm_bf16x8 bl = *reinterpret_cast<const gm_bf16x8 *>(st + PLANE + off);
+                    // the hi products of all row tiles, then the lo ones: 4
+                    // independent MFMAs between two into one accumulator
+#pragma unroll
+                    for (int rt = 0; rt < GM_RT; ++rt)
+                        acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rt], bh, acc[rt][tt], 0, 0, 0);
+#pragma unroll
+                    for (int rt = 0; rt < GM_RT; ++rt)
+                        acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rt], bl, acc[rt][tt], 0, 0, 0);
+                }
+            }
+        } else {
+            // two 64-column blocks per chunk: each block's four MFMAs (two
+            // k-steps, hi and lo) into a fresh accumulator, then scaled in.
+            // Operands swapped (D = X W^T): lane l holds tokens 4 (l / 16) +
+            // [0, 4) of weight row l % 16, so one scale per lane and block
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                gm_bf16x8 A0[GM_RT], A1[GM_RT];
+#pragma unroll
+                for (int rt = 0; rt < GM_RT; ++rt) {
+                    A0[rt] = gm_decode<WDT>(wc[rt], 2 * h, 0.f);
+                    A1[rt] = gm_decode<WDT>(wc[rt], 2 * h + 1, 0.f);
+                }
+                const int kc0 = gm_kchunk<WDT>(2 * h, q), kc1 = gm_kchunk<WDT>(2 * h + 1, q);
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    const int t = tt * 16 + c16;
+                    const int o0 = t * GM_ROWB + ((kc0 - t) & 15) * 16, o1 = t * GM_ROWB + ((kc1 - t) & 15) * 16;
+                    const gm_bf16x8 bh0 = *reinterpret_cast<const gm_bf16x8 *>(st + o0);
+                    const gm_bf16x8 bl0 = *reinterpret_cast<const gm_bf16x8 *>(st + PLANE + o0);
+                    const gm_bf16x8 bh1 = *reinterpret_cast<const gm_bf16x8 *>(st + o1);
+                    const gm_bf16x8 bl1 = *reinterpret_cast<const gm_bf16x8 *>(st + PLANE + o1);
+                    gm_f32x4 tmp[GM_RT];
+#pragma unroll
+                    for (int rt = 0; rt < GM_RT; ++rt)
+                        tmp[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh0, A0[rt], gm_f32x4{0.f, 0.f, 0.f, 0.f}, 0,
+                                                                         0, 0);
+#pragma unroll
+                    for (int rt = 0; rt < GM_RT; ++rt)
+                        tmp[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl0, A0[rt], tmp[rt], 0, 0, 0);
+#pragma unroll
+                    for (int rt = 0; rt < GM_RT; ++rt)
+                        tmp[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh1, A1[rt], tmp[rt], 0, 0, 0);
+#pragma unroll
+                    for (int rt = 0; rt < GM_RT; ++rt)
+                        tmp[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl1, A1[rt], tmp[rt], 0, 0, 0);
+#pragma unroll
+                    for (int rt = 0; rt < GM_RT; ++rt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[rt][tt][e] += tmp[rt][e] * (16.0f * sc[rt][h]);
+                    // one token tile at a time: the scheduler would otherwise
+                    // start the next tiles' reads and chains early, past the
+                    // register budget
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
         if (c + 1 < nch) {
 #pragma unroll
-            for (int rt = 0; rt < GM_RT; ++rt)
+            for (int rt = 0; rt < GM_RT; ++rt) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) wc[rt][j] = wn[rt][j];
+                for (int j = 0; j < NW; ++j) wc[rt][j] = wn[rt][j];
+                ec[rt] = en[rt];
+                sc[rt] = sn[rt];
+            }
         }
+    }
+
+    // fp8: the row scales of the lane's D rows 4q .. 4q+3
+    if constexpr (WDT == K2_FP8E4M3) {
+#pragma unroll
+        for (int rt = 0; rt < GM_RT; ++rt) {
+            const int n0 = gm_row(a, rb, wave, rt, 4 * q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int n = n0 + e < a.N ? n0 + e : a.N - 1;
+                const float rs = ((const float *)a.Ws)[n];
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) acc[rt][tt][e] *= rs;
+            }
+        }
+    }
+
+    if constexpr (Q4) {
+        // the lane holds row c16 of each row tile for tokens 16 tt + 4q + [0, 4)
+        if (a.S > 1) {
+#pragma unroll
+            for (int rt = 0; rt < GM_RT; ++rt) {
+                const int n = gm_row(a, rb, wave, rt, c16);
+                if (n >= a.N) continue;
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = t0 + tt * 16 + 4 * q + e;
+                        a.part[((int64_t)split * a.TP + t) * a.N + n] = acc[rt][tt][e];
+                    }
+            }
+            return;
+        }
+        if (a.epi == DM_EPI_SWIGLU) {
+            const int half = a.N / 2;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const int n = gm_row(a, rb, wave, rt, c16);
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = t0 + tt * 16 + 4 * q + e;
+                        if (t >= a.T) continue;
+                        const float g = acc[rt][tt][e], u = acc[rt + 2][tt][e];
+                        a.y[(int64_t)t * half + n] = g / (1.0f + expf(-g)) * u;
+                    }
+            }
+            return;
+        }
+#pragma unroll
+        for (int rt = 0; rt < GM_RT; ++rt) {
+            const int n = gm_row(a, rb, wave, rt, c16);
+            if (n >= a.N) continue;
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = t0 + tt * 16 + 4 * q + e;
+                    if (t >= a.T) continue;
+                    float *dst = a.y + (int64_t)t * a.N + n;
+                    *dst = a.epi == DM_EPI_ADD ? *dst + acc[rt][tt][e] : acc[rt][tt][e];
+                }
+        }
+        return;
     }
 
     // the lane holds rows 4q .. 4q+3 of each row tile for token 16 tt + c16
@@ -272,11 +491,17 @@ __global__ __launch_bounds__(256) void gm_reduce_kernel(const float *part, int S
 
 // tokens per block: 128 for long chunks (measured on the 512-token prompt of
 // the 3.7B-shaped model: 23.1 ms against 24.2 with 64), less for short
-// ones, whose padding would be wasted work
-static int gm_bt(int T) { return T <= 32 ? 32 : T <= 64 ? 64 : 128; }
-static int gm_tp(int T)
+// ones, whose padding would be wasted work.  Q4S: 32 (its fresh per-block
+// accumulators and the scaled sums need registers that larger token blocks
+// would spill)
+static int gm_bt(int T, int wdt)
 {
-    const int bt = gm_bt(T);
+    if (wdt == K2_Q4S) return 32;
+    return T <= 32 ? 32 : T <= 64 ? 64 : 128;
+}
+static int gm_tp(int T, int wdt)
+{
+    const int bt = gm_bt(T, wdt);
     return (T + bt - 1) / bt * bt;
 }
 static int gm_rb(int N, int epi) { return epi == DM_EPI_SWIGLU ? N / GM_BM : (N + GM_BM - 1) / GM_BM; }
@@ -284,10 +509,10 @@ static int gm_rb(int N, int epi) { return epi == DM_EPI_SWIGLU ? N / GM_BM : (N 
 // Split-K count: one split when the row x token blocks already give a block
 // per CU; else the most splits (a divisor of the chunk count, >= 2 chunks
 // each) whose blocks still fit on the chip at once.
-static int gm_splits(int N, int K, int T, int epi)
+static int gm_splits(int N, int K, int T, int epi, int wdt)
 {
-    const int bt = gm_bt(T);
-    const int blk = gm_rb(N, epi) * (gm_tp(T) / bt);
+    const int bt = gm_bt(T, wdt);
+    const int blk = gm_rb(N, epi) * (gm_tp(T, wdt) / bt);
     const int slots = 256 * (bt <= 64 ? 2 : 1);
     if (blk >= 256) return 1;
     const int nch = K / GM_BK;
@@ -304,26 +529,41 @@ bool gemm_mfma_ok(int N, int K, int epi)
     return N % 4 == 0;
 }
 
-size_t gemm_mfma_ws_bytes(int N, int K, int T, int epi)
+size_t gemm_mfma_ws_bytes(int wdt, int N, int K, int T, int epi)
 {
     if (!gemm_mfma_ok(N, K, epi) || T < 1 || T > GM_MAX_T) return 0;
-    const int TP = gm_tp(T), S = gm_splits(N, K, T, epi);
+    const int TP = gm_tp(T, wdt), S = gm_splits(N, K, T, epi, wdt);
     return 2 * k2_align256((size_t)TP * K * 2) + (S > 1 ? k2_align256((size_t)S * TP * N * 4) : 0);
 }
 
-int gemm_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi, void *ws,
-              hipStream_t st)
+template <int WDT>
+static void gm_launch(int BT, int nblk, size_t lds, hipStream_t st, const GemmArgs &a)
+{
+    if constexpr (WDT == K2_Q4S) {
+        hipLaunchKernelGGL((gm_kernel<32, WDT>), dim3(nblk), dim3(256), lds, st, a);
+    } else {
+        if (BT == 32) hipLaunchKernelGGL((gm_kernel<32, WDT>), dim3(nblk), dim3(256), lds, st, a);
+        else if (BT == 64) hipLaunchKernelGGL((gm_kernel<64, WDT>), dim3(nblk), dim3(256), lds, st, a);
+        else hipLaunchKernelGGL((gm_kernel<128, WDT>), dim3(nblk), dim3(256), lds, st, a);
+    }
+}
+
+int gemm_mfma(int wdt, const void *W, const void *Ws, const float *x, float *y, int N, int K, int T, int epi,
+              void *ws, hipStream_t st)
 {
     if (!gemm_mfma_ok(N, K, epi) || T < 1 || T > GM_MAX_T || !ws) return K2_EUNSUPPORTED;
+    if (wdt != K2_BF16 && wdt != K2_FP8E4M3 && wdt != K2_MXFP4 && wdt != K2_Q4S) return K2_EUNSUPPORTED;
+    if (wdt != K2_BF16 && !Ws) return K2_EINVAL;
     GemmArgs a{};
-    const int BT = gm_bt(T), TP = gm_tp(T);
-    const int S = gm_splits(N, K, T, epi);
+    const int BT = gm_bt(T, wdt), TP = gm_tp(T, wdt);
+    const int S = gm_splits(N, K, T, epi, wdt);
     char *p = (char *)ws;
     uint16_t *xh = (uint16_t *)p;
     p += k2_align256((size_t)TP * K * 2);
     uint16_t *xl = (uint16_t *)p;
     p += k2_align256((size_t)TP * K * 2);
     a.W = W;
+    a.Ws = Ws;
     a.xh = xh;
     a.xl = xl;
     a.part = S > 1 ? (float *)p : nullptr;
@@ -346,9 +586,12 @@ int gemm_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, 
     hipLaunchKernelGGL(gm_split_kernel, dim3(sb), dim3(256), 0, st, x, xh, xl, T, TP, K);
     K2_CHECK_LAUNCH();
     const size_t lds = 2 * 2 * (size_t)BT * GM_ROWB;
-    if (BT == 32) hipLaunchKernelGGL((gm_kernel<32>), dim3(nblk), dim3(256), lds, st, a);
-    else if (BT == 64) hipLaunchKernelGGL((gm_kernel<64>), dim3(nblk), dim3(256), lds, st, a);
-    else hipLaunchKernelGGL((gm_kernel<128>), dim3(nblk), dim3(256), lds, st, a);
+    switch (wdt) {
+    case K2_BF16: gm_launch<K2_BF16>(BT, nblk, lds, st, a); break;
+    case K2_FP8E4M3: gm_launch<K2_FP8E4M3>(BT, nblk, lds, st, a); break;
+    case K2_MXFP4: gm_launch<K2_MXFP4>(BT, nblk, lds, st, a); break;
+    default: gm_launch<K2_Q4S>(BT, nblk, lds, st, a); break;
+    }
     K2_CHECK_LAUNCH();
     if (S > 1) {
         const int n_out = epi == DM_EPI_SWIGLU ? N / 2 : N;

@@ -36,6 +36,8 @@ int gemv_dispatch_q4s(const GemvArgs &a, int pro, int epi, hipStream_t st);
 
 int gemv_dispatch(int wdt, const GemvArgs &a, int pro, int epi, hipStream_t st)
 {
+    // a quantized format without its scales is refused here, not read at address 0
+    if (((wdt == K2_FP8E4M3 || wdt == K2_Q4S) && !a.Sf) || (wdt == K2_MXFP4 && !a.S8)) return K2_EINVAL;
     switch (wdt) {
     case K2_F32: return gemv_dispatch_f32(a, pro, epi, st);
     case K2_BF16: return gemv_dispatch_bf16(a, pro, epi, st);

@@ -196,14 +196,15 @@ int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T,
 
 // The projections of a prefill chunk of 1..GM_MAX_T positions on the matrix
 // cores (gemm_mfma.hip): y [T][N] = x [T][K] W^T with the epilogue epi
-// (SwiGLU: y [T][N/2], gate rows n, up rows n + N/2).  ws:
-// gemm_mfma_ws_bytes (the activation planes and split partials; no state
-// kept between calls).  K2_EUNSUPPORTED (nothing enqueued) unless K % 128 == 0
-// and N % 4 == 0 (SwiGLU: N % 256 == 0).
+// (SwiGLU: y [T][N/2], gate rows n, up rows n + N/2), W of format wdt
+// (K2_BF16, K2_FP8E4M3, K2_MXFP4, K2_Q4S) with its scales Ws as in a
+// k2_layer.  ws: gemm_mfma_ws_bytes (the activation planes and split
+// partials; no state kept between calls).  K2_EUNSUPPORTED (nothing
+// enqueued) unless K % 128 == 0 and N % 4 == 0 (SwiGLU: N % 256 == 0).
 constexpr int GM_MAX_T = 256;
 bool gemm_mfma_ok(int N, int K, int epi);
-size_t gemm_mfma_ws_bytes(int N, int K, int T, int epi);
-int gemm_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi, void *ws,
-              hipStream_t st);
+size_t gemm_mfma_ws_bytes(int wdt, int N, int K, int T, int epi);
+int gemm_mfma(int wdt, const void *W, const void *Ws, const float *x, float *y, int N, int K, int T, int epi,
+              void *ws, hipStream_t st);
 
 }  // namespace k2

@@ -6,9 +6,11 @@
 // position by position gives exactly the incremental (cached) result.  With
 // T positions at once every projection is a [N][K] x [K][T] product, so a
 // weight byte feeds 2T flops: past a few positions that is a dense
-// contraction, run here on v_mfma_f32_16x16x32_bf16 by the bf16 product of
-// gemm_mfma.hip (activations split into bf16 hi + lo, fp32 accumulation),
-// which reads the weights once for up to 256 positions.
+// contraction, run here on v_mfma_f32_16x16x32_bf16 by the product of
+// gemm_mfma.hip (activations split into bf16 hi + lo, fp32 accumulation;
+// fp8, MXFP4 and Q4S weights decoded in registers to exact bf16 values with
+// their scales applied to the sums), which reads the weights once for up to
+// 256 positions.
 //
 // Per layer, for the T rows of the chunk:
 //   1. GroupedRMSNorm of every row                       (one launch)
@@ -86,21 +88,24 @@ __global__ __launch_bounds__(K2_WAVE) void argmax_rows_final_kernel(const float 
     if (lane == 0) out[t] = i;
 }
 
-// A projection of the chunk's T rows: up to 32 rows the small-T product
-// (dense_mfma.hip, measured faster there), above that the token-blocked
-// GEMM (gemm_mfma.hip), which reads every weight byte from HBM once per call.
+// A projection of the chunk's T rows: for bf16 weights up to 32 rows the
+// small-T product (dense_mfma.hip, measured faster there), else the
+// token-blocked GEMM (gemm_mfma.hip), which reads every weight byte from
+// HBM once per call and decodes quantized weights in registers.
 constexpr int PF_GEMM_MIN_T = 33;
 
-static size_t pf_proj_bytes(int N, int K, int T, int epi)
+static bool pf_dense(int wdt, int T) { return wdt == K2_BF16 && T < PF_GEMM_MIN_T; }
+
+static size_t pf_proj_bytes(int wdt, int N, int K, int T, int epi)
 {
-    return T >= PF_GEMM_MIN_T ? gemm_mfma_ws_bytes(N, K, T, epi) : dense_mfma_ws_bytes(N, K, T);
+    return pf_dense(wdt, T) ? dense_mfma_ws_bytes(N, K, T) : gemm_mfma_ws_bytes(wdt, N, K, T, epi);
 }
 
-static int pf_proj(const void *W, const float *x, float *y, int N, int K, int T, int epi, float *ws,
-                   hipStream_t st)
+static int pf_proj(int wdt, const void *W, const void *Ws, const float *x, float *y, int N, int K, int T, int epi,
+                   float *ws, hipStream_t st)
 {
-    if (T >= PF_GEMM_MIN_T) return gemm_mfma((const uint16_t *)W, x, y, N, K, T, epi, ws, st);
-    return dense_mfma((const uint16_t *)W, x, y, N, K, T, epi, ws, st);
+    if (pf_dense(wdt, T)) return dense_mfma((const uint16_t *)W, x, y, N, K, T, epi, ws, st);
+    return gemm_mfma(wdt, W, Ws, x, y, N, K, T, epi, ws, st);
 }
 
 // the projections' scratch for any chunk of up to T rows (the split count
@@ -108,12 +113,13 @@ static int pf_proj(const void *W, const float *x, float *y, int N, int K, int T,
 static size_t pf_part_bytes(const k2_config *c, int T)
 {
     const int qkv_rows = (c->n_qh + 2 * c->n_kv) * c->head_dim, qd = c->n_qh * c->head_dim;
+    const int wd = c->wdt;
     size_t m = 0;
     for (int t = 2; t <= T; ++t) {
-        const size_t b[4] = {pf_proj_bytes(qkv_rows, c->hidden, t, DM_EPI_PLAIN),
-                             pf_proj_bytes(c->hidden, qd, t, DM_EPI_ADD),
-                             pf_proj_bytes(2 * c->inter, c->hidden, t, DM_EPI_SWIGLU),
-                             pf_proj_bytes(c->hidden, c->inter, t, DM_EPI_ADD)};
+        const size_t b[4] = {pf_proj_bytes(wd, qkv_rows, c->hidden, t, DM_EPI_PLAIN),
+                             pf_proj_bytes(wd, c->hidden, qd, t, DM_EPI_ADD),
+                             pf_proj_bytes(wd, 2 * c->inter, c->hidden, t, DM_EPI_SWIGLU),
+                             pf_proj_bytes(wd, c->hidden, c->inter, t, DM_EPI_ADD)};
         for (size_t v : b) m = v > m ? v : m;
     }
     return m;
@@ -146,7 +152,9 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base, boo
     char *act = take((size_t)T * c->inter * 4);
     char *part = take(pf_part_bytes(c, T));
     char *qrot = take((size_t)T * qd * 4);
-    char *lm_part = verify ? take(dense_mfma_ws_bytes(c->vocab, c->hidden, T)) : nullptr;
+    char *lm_part = verify ? take(c->wdt == K2_BF16 ? dense_mfma_ws_bytes(c->vocab, c->hidden, T)
+                                                    : gemm_mfma_ws_bytes(c->wdt, c->vocab, c->hidden, T, DM_EPI_PLAIN))
+                           : nullptr;
     char *lgt = verify ? take((size_t)T * c->vocab * 4) : nullptr;
     char *arv = verify ? take((size_t)T * AR_NB * 4) : nullptr;
     char *ari = verify ? take((size_t)T * AR_NB * 4) : nullptr;
@@ -171,20 +179,38 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base, boo
     return off;
 }
 
-// Shapes this path handles (K2_EUNSUPPORTED otherwise): bf16 projection
-// weights whose products the matrix-core kernel takes.
+// Shapes this path handles (K2_EUNSUPPORTED otherwise): bf16, fp8, MXFP4 or
+// Q4S projection weights whose products the matrix-core kernels take.
 static int pf_shape_ok(const k2_config *c, bool verify = false)
 {
-    if (c->wdt != K2_BF16) return K2_EUNSUPPORTED;
-    if (verify && !dense_mfma_ok(c->vocab, c->hidden)) return K2_EUNSUPPORTED;
+    const int wd = c->wdt;
+    if (wd != K2_BF16 && wd != K2_FP8E4M3 && wd != K2_MXFP4 && wd != K2_Q4S) return K2_EUNSUPPORTED;
+    if (verify && !(wd == K2_BF16 ? dense_mfma_ok(c->vocab, c->hidden)
+                                  : gemm_mfma_ok(c->vocab, c->hidden, DM_EPI_PLAIN)))
+        return K2_EUNSUPPORTED;
     const int qkv_rows = (c->n_qh + 2 * c->n_kv) * c->head_dim, qd = c->n_qh * c->head_dim;
-    if (!dense_mfma_ok(qkv_rows, c->hidden) || !dense_mfma_ok(c->hidden, qd) ||
-        !dense_mfma_ok(2 * c->inter, c->hidden) || !dense_mfma_ok(c->hidden, c->inter))
+    if (wd == K2_BF16 && (!dense_mfma_ok(qkv_rows, c->hidden) || !dense_mfma_ok(c->hidden, qd) ||
+                          !dense_mfma_ok(2 * c->inter, c->hidden) || !dense_mfma_ok(c->hidden, c->inter)))
         return K2_EUNSUPPORTED;
     if (!gemm_mfma_ok(qkv_rows, c->hidden, DM_EPI_PLAIN) || !gemm_mfma_ok(c->hidden, qd, DM_EPI_ADD) ||
         !gemm_mfma_ok(2 * c->inter, c->hidden, DM_EPI_SWIGLU) || !gemm_mfma_ok(c->hidden, c->inter, DM_EPI_ADD))
         return K2_EUNSUPPORTED;
     return K2_OK;
+}
+
+// The matrix-core products read MXFP4 scale bytes four at a time and Q4S
+// block scales two at a time: their scale arrays must be 16-byte aligned.
+static bool pf_scales_ok(const k2_model *m)
+{
+    const k2_config *c = &m->cfg;
+    if (c->wdt != K2_MXFP4 && c->wdt != K2_Q4S) return true;
+    if (!k2_ptr_ok(m->lm_s)) return false;
+    for (int l = 0; l < c->n_layers; ++l) {
+        const k2_layer *L = &m->layers[l];
+        if (!k2_ptr_ok(L->qkv_s) || !k2_ptr_ok(L->o_s) || !k2_ptr_ok(L->gu_s) || !k2_ptr_ok(L->down_s))
+            return false;
+    }
+    return true;
 }
 
 // verify: logits [T][vocab] (nullable: kept in the workspace) and next [T]
@@ -198,6 +224,7 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
     if (T < 2 || T > (verify ? VF_MAX_T : PF_MAX_T)) return K2_EUNSUPPORTED;
     if (!tokens || (verify && !k2_ptr_ok(next))) return K2_EINVAL;
     if ((rc = pf_shape_ok(c, verify))) return rc;
+    if (!pf_scales_ok(m)) return K2_EINVAL;
     if (logits && !k2_aligned16(logits)) return K2_EINVAL;
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pf_layout(c, T, nullptr, nullptr, verify)) return K2_EINVAL;
     if (pos0 < 0 || (int64_t)pos0 + T > c->cap) return K2_ERANGE;
@@ -230,7 +257,7 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
     for (int l = 0; l < c->n_layers; ++l) {
         const k2_layer *L = &m->layers[l];
         if ((rc = rmsnorm_rows_launch(w.h, L->g_in, w.x, T, H, c->groups, c->eps, st))) return rc;
-        if ((rc = pf_proj(L->qkv, w.x, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, st)))
+        if ((rc = pf_proj(c->wdt, L->qkv, L->qkv_s, w.x, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, st)))
             return rc;
         at.kc = L->kc;
         at.vc = L->vc;
@@ -248,11 +275,11 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
             at.S = attn_splits(c->n_kv, at.len, &at.chunk);
             if ((rc = attn_launch(c->kvdt, hd, rep, true, at, st))) return rc;
         }
-        if ((rc = pf_proj(L->o, w.o, w.h, H, qd, T, DM_EPI_ADD, w.part, st))) return rc;
+        if ((rc = pf_proj(c->wdt, L->o, L->o_s, w.o, w.h, H, qd, T, DM_EPI_ADD, w.part, st))) return rc;
         if ((rc = rmsnorm_rows_launch(w.h, L->g_post, w.x, T, H, c->groups, c->eps, st))) return rc;
-        if ((rc = pf_proj(L->gu, w.x, w.act, 2 * I, H, T, DM_EPI_SWIGLU, w.part, st)))
+        if ((rc = pf_proj(c->wdt, L->gu, L->gu_s, w.x, w.act, 2 * I, H, T, DM_EPI_SWIGLU, w.part, st)))
             return rc;
-        if ((rc = pf_proj(L->down, w.act, w.h, H, I, T, DM_EPI_ADD, w.part, st)))
+        if ((rc = pf_proj(c->wdt, L->down, L->down_s, w.act, w.h, H, I, T, DM_EPI_ADD, w.part, st)))
             return rc;
     }
 
@@ -260,8 +287,10 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
         // every row: final norm, lm_head on the matrix cores, first-maximum argmax
         float *lg = logits ? logits : w.logits;
         if ((rc = rmsnorm_rows_launch(w.h, m->g_final, w.x, T, H, c->groups, c->eps, st))) return rc;
-        if ((rc = dense_mfma((const uint16_t *)m->lm, w.x, lg, c->vocab, H, T, DM_EPI_PLAIN, w.lm_part, st)))
-            return rc;
+        rc = c->wdt == K2_BF16
+                 ? dense_mfma((const uint16_t *)m->lm, w.x, lg, c->vocab, H, T, DM_EPI_PLAIN, w.lm_part, st)
+                 : gemm_mfma(c->wdt, m->lm, m->lm_s, w.x, lg, c->vocab, H, T, DM_EPI_PLAIN, w.lm_part, st);
+        if (rc) return rc;
         hipLaunchKernelGGL(argmax_rows_part_kernel, dim3(AR_NB, T), dim3(K2_BLOCK), 0, st, lg, c->vocab, w.ar_v,
                            w.ar_i);
         K2_CHECK_LAUNCH();
@@ -272,6 +301,8 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
         argmax_ws_carve(w.am, am);
         GemvArgs lm{};
         lm.W = m->lm;
+        lm.Sf = (const float *)m->lm_s;            // fp8 row scales, Q4S block scales
+        lm.S8 = (const uint8_t *)m->lm_s;          // MXFP4 E8M0 bytes
         lm.x = w.h + (int64_t)(T - 1) * H;
         lm.gamma = m->g_final;
         lm.eps = c->eps;

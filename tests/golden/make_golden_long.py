@@ -1,7 +1,7 @@
 """Write the long-prompt expected values under tests/golden/ -- calls only the
 oracle (and the seeded input generators of ``synth``).
 
-    python tests/golden/make_golden_long.py [k2h_bf16_p512] [k2h_i8_p1024]
+    python tests/golden/make_golden_long.py [k2h_bf16_p512] [k2h_i8_p1024] [k2h_fp8_w2_p300] ...
 
 Each file holds the oracle's greedy run of the full-depth 3.7B-shaped model
 (hidden 2560, 36 layers, 32 q / 8 kv heads, head_dim 128, SwiGLU 10240, vocab
@@ -15,6 +15,13 @@ argmax:
   k2h_i8_p1024.npz    int8 KV cache, context 32768, 1024-token prompt, so
                       the cache the decode steps read is the one a real
                       prefill wrote (no synthetic history)
+
+  k2h_{fp8,mxfp4,q4s}_w2_p300.npz
+                      the quantized-weight models (fp8 E4M3 + row scale,
+                      MXFP4, Q4S; int8 KV) at their full widths but two
+                      layers and a 4096-token vocabulary, 300-token prompt
+                      (the prefill's 256 + 44 chunks at the real product
+                      shapes, with an oracle run of minutes)
 
 Arrays: ``prompt`` (int32), ``tokens`` (int32 [5]: the argmax after the last
 prompt position and after each decode step), ``logits`` (float32 [5][vocab],
@@ -38,9 +45,16 @@ import synth  # noqa: E402
 HERE = os.path.dirname(os.path.abspath(__file__))
 N_EMIT = 5
 
+def _w2(name: str):
+    return synth.CONFIGS[name].replace(n_layers=2, vocab=4096, cap=512)
+
+
 RUNS = {
     "k2h_bf16_p512": (synth.K2H_BF16, 512),
     "k2h_i8_p1024": (synth.K2H_BF16_I8_LONG, 1024),
+    "k2h_fp8_w2_p300": (_w2("k2h-3.7b-fp8-kvi8-ctx4096"), 300),
+    "k2h_mxfp4_w2_p300": (_w2("k2h-3.7b-mxfp4-kvi8-ctx4096"), 300),
+    "k2h_q4s_w2_p300": (_w2("k2h-3.7b-q4s-kvi8-ctx4096"), 300),
 }
 
 

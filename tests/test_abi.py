@@ -146,8 +146,8 @@ def test_decode_step_refuses_before_launch():
 
 
 def test_prefill_refuses_unsupported_shapes():
-    # fp32 weights, and a bf16 model whose hidden size the matrix-core product
-    # does not take (64 is not a multiple of 128): no workspace, no launch
+    # fp32 weights, and a bf16 model whose hidden size the matrix-core products
+    # do not take (64 is not a multiple of 128): no workspace, no launch
     assert k2.k2_prefill_workspace_bytes(_fake_model().cfg, 8) == 0
     m = _fake_model(dict(wdt=k2.K2_BF16))
     assert k2.k2_prefill_workspace_bytes(m.cfg, 8) == 0
@@ -171,6 +171,28 @@ def test_prefill_refuses_unsupported_shapes():
     assert L.k2_prefill(C.addressof(m), bad, 8, 0, None, None, 0x100000, wsb, None) == k2.K2_ERANGE
     assert L.k2_prefill(C.addressof(m), toks, 8, 0, None, None, 0x100000, wsb - 1, None) == k2.K2_EINVAL
     assert L.k2_prefill(C.addressof(m), None, 8, 0, None, None, 0x100000, wsb, None) == k2.K2_EINVAL
+
+
+@pytest.mark.parametrize("wdt", ["fp8", "mxfp4", "q4s"])
+def test_prefill_takes_quantized_weights(wdt):
+    # the matrix-core products decode fp8 / MXFP4 / Q4S weights: workspace
+    # sizes as for bf16 (monotone in T), verification too; MXFP4 and Q4S
+    # scale arrays that are not 16-byte aligned are refused before a launch
+    ok = dict(hidden=512, n_qh=8, n_kv=2, head_dim=128, inter=1024, vocab=1024, wdt=k2.DTYPES[wdt])
+    m = _fake_model(ok)
+    sizes = [k2.k2_prefill_workspace_bytes(m.cfg, t) for t in range(2, 257)]
+    assert sizes[0] > 0 and all(a <= b for a, b in zip(sizes, sizes[1:]))
+    assert k2.k2_prefill_workspace_bytes(m.cfg, 257) == 0
+    assert k2.k2_verify_workspace_bytes(m.cfg, 32) > 0
+    assert k2.k2_verify_workspace_bytes(m.cfg, 33) == 0
+    wsb = sizes[6]
+    L = k2.load()
+    toks = (C.c_int32 * 8)(*[1] * 8)
+    assert L.k2_prefill(C.addressof(m), toks, 8, 30, None, None, 0x100000, wsb, None) == k2.K2_ERANGE
+    if wdt != "fp8":
+        m._keep[1].gu_s = FAKE + 8
+        assert k2.k2_model_check(m) == k2.K2_OK
+        assert L.k2_prefill(C.addressof(m), toks, 8, 0, None, None, 0x100000, wsb, None) == k2.K2_EINVAL
 
 
 @pytest.mark.parametrize("change,rc", [(dict(head_dim=96), -3), (dict(n_kv=3), -3),

@@ -449,6 +449,40 @@ def test_prefill_ragged_rows(P, chunk):
     _prefill_parity(cfg, P, 3, chunk=chunk)
 
 
+@pytest.mark.parametrize("wdt", ["fp8", "mxfp4", "q4s"])
+@pytest.mark.parametrize("P,chunk", [(3, 256), (70, 32), (150, 64), (300, 256)])
+def test_head128_prefill_quantized(wdt, P, chunk):
+    """fp8, MXFP4 and Q4S weights decoded in registers by the matrix-core
+    product: 3 positions in one chunk (token block of 32, mostly padding),
+    70 = 32 + 32 + 6, 150 = 64 + 64 + 22 (blocks of 64; Q4S: 32) and 300 =
+    256 + 44 (blocks of 128 for fp8 / MXFP4, with split-K on the short
+    products); int8 cache, then three decode steps."""
+    cfg = HEAD128.replace(wdt=wdt, kvdt="i8", cap=320)
+    _prefill_parity(cfg, P, 3, chunk=chunk)
+
+
+@pytest.mark.parametrize("wdt", ["fp8", "mxfp4", "q4s"])
+def test_prefill_ragged_rows_quantized(wdt):
+    """Quantized weights with row counts that are not multiples of the
+    256-row block (384-row projections): clamped rows, their scales
+    included, must never be stored."""
+    cfg = HEAD128.replace(hidden=384, n_qh=1, n_kv=1, inter=640, wdt=wdt, kvdt="bf16", cap=160)
+    _prefill_parity(cfg, 150, 3, chunk=256)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "q4s"])
+def test_k2h_quantized_prefill_full_width_golden(fmt):
+    """The 3.7B shapes of the quantized models (hidden 2560, 32 / 8 heads,
+    inter 10240: the products' split-K counts and 10240-column rows) at two
+    layers and a 4096-token vocabulary: a 300-position prompt through
+    k2_prefill in chunks of 32 and of 256 (256 + 44), then four decode steps,
+    against the stored oracle run."""
+    cfg = synth.CONFIGS[f"k2h-3.7b-{fmt}-kvi8-ctx4096"].replace(n_layers=2, vocab=4096, cap=512)
+    _golden_parity(f"k2h_{fmt}_w2_p300", cfg)
+
+
 def test_prefill_equals_decode_steps_on_cache():
     """The caches a prefill writes decode the same next positions as the
     caches of position-by-position decode, within the bf16 cache's rounding:
@@ -499,10 +533,12 @@ def test_k2h_bf16_prefill_full_depth():
 
 # ------------------------------------------------------- batched verification ---
 
-def test_head128_verify_every_row_matches_oracle():
+@pytest.mark.parametrize("wdt,kvdt", [("bf16", "bf16"), ("fp8", "i8"), ("mxfp4", "i8"), ("q4s", "i8")])
+def test_head128_verify_every_row_matches_oracle(wdt, kvdt):
     """k2_verify of 12 positions fed the oracle's own tokens: every row's
-    logits and greedy token against the oracle at that position."""
-    cfg = HEAD128.replace(wdt="bf16", kvdt="bf16", cap=128)
+    logits and greedy token against the oracle at that position (quantized
+    weights: the lm_head of all rows on the token-blocked product too)."""
+    cfg = HEAD128.replace(wdt=wdt, kvdt=kvdt, cap=128)
     P = 20
     prompt = synth.prompt(cfg, P)
     dec = oracle.Decoder.from_synth(cfg)
