@@ -67,9 +67,12 @@ int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qr
     default: return K2_EUNSUPPORTED;
     }
     K2_CHECK_LAUNCH();
-    // long chunks of a bf16 / int8 cache: every row's attention on the
-    // matrix cores, the K/V tiles shared by the rows of a block
-    if (T >= ATTN_PREFILL_MIN_T && (kvdt == K2_BF16 || kvdt == K2_I8))
+    // long chunks of a bf16 / int8 cache (or medium ones on a short cache):
+    // every row's attention on the matrix cores, the K/V tiles shared by the
+    // rows of a block
+    const bool mc = T >= ATTN_PREFILL_MIN_T ||
+                    (T >= ATTN_PREFILL_SHORT_T && (int64_t)pos0 + T <= ATTN_PREFILL_SHORT_LEN);
+    if (mc && (kvdt == K2_BF16 || kvdt == K2_I8))
         return attn_prefill_launch(kvdt, qrot, out, kc, vc, ks, vs, n_qh, n_kv, hd, cap, pos0, T, st);
     AttnArgs a{};
     const size_t S = (size_t)attn_max_splits(n_kv, cap);

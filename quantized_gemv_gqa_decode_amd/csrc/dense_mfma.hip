@@ -14,7 +14,13 @@
 //     ahead of the MFMAs;
 //   * per-split partials [split][token][row] are summed in split order by a
 //     second kernel, which also applies the epilogue (plain, add into y, or
-//     SwiGLU of row pairs i, i + N/2).
+//     SwiGLU of row pairs i, i + N/2) -- or, given arrival counters, by the
+//     last block to finish of each row block (of each gate / up row-block
+//     pair for SwiGLU): every block stores its partials at device scope and
+//     counts itself, and the last one sums the group's partials in split
+//     order (the same order, so the same result) and applies the epilogue.
+//     That saves the second launch, whose gap and first-byte latency are
+//     most of its cost at these sizes.
 // MFMA operand layout (16x16x32 bf16): lane l holds A row l % 16 and B column
 // l % 16, elements k = 8 (l / 16) + [0, 8); D holds column l % 16, rows
 // 4 (l / 16) + [0, 4).
@@ -32,12 +38,18 @@ constexpr int DM_ROWS = DM_RT * 16 * DM_WAVES;    // rows per block
 constexpr int DM_KC = 128;                        // columns per chunk (4 MFMA k-steps)
 constexpr int DM_MAX_KS = 512;                    // columns per split
 constexpr int DM_MAX_T = 32;                      // tokens per launch
+constexpr int DM_FUSE_MAX = 128;                  // tokens x splits summed in-kernel at most
 
 struct DenseArgs {
     const uint16_t *W;       // [N][K] bf16
     const float *x;          // [T][K] fp32
     float *part;             // [splits][TP][N]
     int N, K, T, KS;
+    // in-kernel reduction (cnt non-null): arrival counters [groups], zero
+    // between launches; the epilogue and its output y [T][N or N/2]
+    unsigned *cnt;
+    float *y;
+    int epi;
 };
 
 __host__ __device__ constexpr int dm_lds_bytes(int tp, int ks) { return 2 * tp * (ks + 8) * 2; }
@@ -143,6 +155,8 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
     compute(NCH - 1, wc);
 
     // partials: the lane holds rows 4q..4q+3 of each tile for token c16 + 16 tt
+    // (device scope when another block sums them)
+    const bool fuse = a.cnt != nullptr;
 #pragma unroll
     for (int rt = 0; rt < DM_RT; ++rt) {
         if (!rok[rt]) continue;
@@ -150,9 +164,66 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
             const int t = tt * 16 + c16;
-            if (t < a.T)
-                *reinterpret_cast<float4 *>(a.part + ((int64_t)split * TP + t) * a.N + r0) =
-                    make_float4(acc[rt][tt][0], acc[rt][tt][1], acc[rt][tt][2], acc[rt][tt][3]);
+            if (t >= a.T) continue;
+            const int64_t o = ((int64_t)split * TP + t) * a.N + r0;
+            const float4 v = make_float4(acc[rt][tt][0], acc[rt][tt][1], acc[rt][tt][2], acc[rt][tt][3]);
+            if (fuse) coh_store4(a.part, (int)o, v);
+            else *reinterpret_cast<float4 *>(a.part + o) = v;
+        }
+    }
+    if (!fuse) return;
+
+    // arrival: row block b alone, or SwiGLU gate block b with up block
+    // b + rb / 2 (both counted on counter b)
+    __shared__ int last;
+    const int rb = gridDim.x, splits = gridDim.y;
+    const bool pair = a.epi == DM_EPI_SWIGLU;
+    const int grp = pair ? blockIdx.x % (rb / 2) : blockIdx.x;
+    const unsigned arrivals = (unsigned)(pair ? 2 * splits : splits);
+    __builtin_amdgcn_s_waitcnt(0);                // this thread's partial stores completed
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned old = __hip_atomic_fetch_add(a.cnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = old == arrivals - 1;
+        if (last) __hip_atomic_store(a.cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last) return;
+
+    // the group's outputs, each summed over the splits in split order: a
+    // thread owns 4 consecutive outputs (gate rows for SwiGLU) of every 4th
+    // token and loads 8 splits' partials before adding them
+    const int n_out = pair ? a.N / 2 : a.N;
+    const int n = grp * DM_ROWS + (tid & 63) * 4;
+    if (n >= n_out) return;
+    constexpr int B8 = 8;
+    for (int t = tid >> 6; t < a.T; t += 4) {
+        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f), up = sum;
+        for (int s0 = 0; s0 < splits; s0 += B8) {
+            float4 v[B8], u[B8];
+#pragma unroll
+            for (int i = 0; i < B8; ++i) {
+                if (s0 + i >= splits) break;
+                const int o = (int)(((int64_t)(s0 + i) * TP + t) * a.N + n);
+                v[i] = coh_load4(a.part, o);
+                if (pair) u[i] = coh_load4(a.part, o + n_out);
+            }
+#pragma unroll
+            for (int i = 0; i < B8; ++i) {
+                if (s0 + i >= splits) break;
+                sum.x += v[i].x; sum.y += v[i].y; sum.z += v[i].z; sum.w += v[i].w;
+                if (pair) { up.x += u[i].x; up.y += u[i].y; up.z += u[i].z; up.w += u[i].w; }
+            }
+        }
+        float4 *dst = reinterpret_cast<float4 *>(a.y + (int64_t)t * n_out + n);
+        if (pair) {
+            *dst = make_float4(sum.x / (1.0f + expf(-sum.x)) * up.x, sum.y / (1.0f + expf(-sum.y)) * up.y,
+                               sum.z / (1.0f + expf(-sum.z)) * up.z, sum.w / (1.0f + expf(-sum.w)) * up.w);
+        } else if (a.epi == DM_EPI_ADD) {
+            const float4 r = *dst;
+            *dst = make_float4(r.x + sum.x, r.y + sum.y, r.z + sum.z, r.w + sum.w);
+        } else {
+            *dst = sum;
         }
     }
 }
@@ -197,17 +268,28 @@ size_t dense_mfma_ws_bytes(int N, int K, int T)
     return (size_t)(K / dm_ks(N, K)) * tp * N * 4;
 }
 
+int dense_mfma_cnt_words(int N) { return (N + DM_ROWS - 1) / DM_ROWS; }
+
 // y = W x for T token rows (T >= 2), through per-split partials in `part`
 // (dense_mfma_ws_bytes); groups of up to 32 tokens run one after another.
+// cnt (nullable, dense_mfma_cnt_words(N) zeroed words, left zero): sum the
+// partials in the product's last blocks instead of a second launch (SwiGLU
+// only when N / 2 is a multiple of the 256-row block).
 int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi, float *part,
-               hipStream_t st)
+               hipStream_t st, unsigned *cnt)
 {
     if (!dense_mfma_ok(N, K) || T < 2) return K2_EUNSUPPORTED;
     const int KS = dm_ks(N, K), splits = K / KS;
     const int n_out = epi == DM_EPI_SWIGLU ? N / 2 : N;
+    if (epi == DM_EPI_SWIGLU && (N / 2) % DM_ROWS) cnt = nullptr;
+    // the last block of a group reads T x splits partial rows: past ~128 of
+    // them that tail costs more than the second launch (3.7B shape,
+    // verification rounds with every product fused: T = 2 3.90 against 4.23
+    // ms, T = 8 4.85 against 4.84, T = 16 5.85 against 5.12)
+    if ((int64_t)(T < DM_MAX_T ? T : DM_MAX_T) * splits > DM_FUSE_MAX) cnt = nullptr;
     for (int t0 = 0; t0 < T; t0 += DM_MAX_T) {
         const int tg = T - t0 < DM_MAX_T ? T - t0 : DM_MAX_T;
-        DenseArgs a{W, x + (int64_t)t0 * K, part, N, K, tg, KS};
+        DenseArgs a{W, x + (int64_t)t0 * K, part, N, K, tg, KS, cnt, y + (int64_t)t0 * n_out, epi};
         const dim3 grid((N + DM_ROWS - 1) / DM_ROWS, splits);
         const int tp = tg <= 16 ? 16 : 32;
         const size_t lds = dm_lds_bytes(tp, KS);
@@ -219,6 +301,7 @@ int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T,
         }
 #undef DM_GO
         K2_CHECK_LAUNCH();
+        if (cnt) continue;
         hipLaunchKernelGGL(dense_reduce_kernel, dim3((n_out + 255) / 256, tg), dim3(256), 0, st, part,
                            splits, tp, N, epi, y + (int64_t)t0 * n_out);
         K2_CHECK_LAUNCH();

@@ -187,6 +187,15 @@ __device__ __forceinline__ float4 coh_load4(const float *base, int off)
                        __uint_as_float(v[3]));
 }
 
+// base[off .. off + 4) = v at device scope (a vector store with the sc1
+// policy); base wave-uniform, off per lane, in floats
+__device__ __forceinline__ void coh_store4(float *base, int off, float4 v)
+{
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const u4 d = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(d, k2_rsrc(base), off * 4, 0, K2_SC1);
+}
+
 __device__ __forceinline__ float coh_load(const float *p)
 {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -107,8 +107,15 @@ size_t attn_rows_cnt_bytes(int n_kv, int T);
 // From this many rows on, attn_rows_launch runs the attention of a bf16 /
 // int8 cache through attn_prefill_launch (attn_prefill.hip): the causal
 // attention of rows pos0 .. pos0+T-1 (qrot [T][n_qh][128], already rotated,
-// K/V already appended) on the matrix cores, out [T][n_qh][128].
+// K/V already appended) on the matrix cores, out [T][n_qh][128].  Shorter
+// chunks of at least ATTN_PREFILL_SHORT_T rows take it too while the cache
+// holds at most ATTN_PREFILL_SHORT_LEN positions: its blocks each stream every
+// key of their kv head, which beats the split per-row kernel there and loses
+// to it on long caches (3.7B shape, 16-row verification: 5.11 against 5.58
+// ms at 528 positions, 14.56 against 11.32 ms at 8208).
 constexpr int ATTN_PREFILL_MIN_T = 33;
+constexpr int ATTN_PREFILL_SHORT_T = 12;
+constexpr int ATTN_PREFILL_SHORT_LEN = 1024;
 int attn_prefill_launch(int kvdt, const float *qrot, float *out, const void *kc, const void *vc, const float *ks,
                         const float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T, hipStream_t st);
 int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qrot, float *out, void *kc,
@@ -192,7 +199,8 @@ enum { DM_EPI_PLAIN = 0, DM_EPI_ADD = 1, DM_EPI_SWIGLU = 2 };
 bool dense_mfma_ok(int N, int K);
 size_t dense_mfma_ws_bytes(int N, int K, int T);
 int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi, float *part,
-               hipStream_t st);
+               hipStream_t st, unsigned *cnt = nullptr);
+int dense_mfma_cnt_words(int N);
 
 // The projections of a prefill chunk of 1..GM_MAX_T positions on the matrix
 // cores (gemm_mfma.hip): y [T][N] = x [T][K] W^T with the epilogue epi

@@ -52,7 +52,7 @@ struct PrefillWs {
     float *h, *x, *qkv, *o, *act, *part, *qrot, *lm_part, *logits, *ar_v;
     int *ar_i;
     void *attn, *rows, *am;
-    unsigned *rows_cnt;
+    unsigned *rows_cnt, *dm_cnt;
     int32_t *next;
 };
 
@@ -102,9 +102,9 @@ static size_t pf_proj_bytes(int wdt, int N, int K, int T, int epi)
 }
 
 static int pf_proj(int wdt, const void *W, const void *Ws, const float *x, float *y, int N, int K, int T, int epi,
-                   float *ws, hipStream_t st)
+                   float *ws, unsigned *cnt, hipStream_t st)
 {
-    if (pf_dense(wdt, T)) return dense_mfma((const uint16_t *)W, x, y, N, K, T, epi, ws, st);
+    if (pf_dense(wdt, T)) return dense_mfma((const uint16_t *)W, x, y, N, K, T, epi, ws, st, cnt);
     return gemm_mfma(wdt, W, Ws, x, y, N, K, T, epi, ws, st);
 }
 
@@ -144,6 +144,15 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base, boo
     char *rows_cnt = take(attn_rows_cnt_bytes(c->n_kv, PF_MAX_T));
     char *am = take(argmax_ws_bytes());
     char *nx = take(4);
+    // arrival counters of the small-T products' in-kernel reduction (one per
+    // 256-row block of the tallest product)
+    {
+        int rows = c->vocab;
+        const int prod[3] = {(c->n_qh + 2 * c->n_kv) * c->head_dim, 2 * c->inter, c->hidden};
+        for (int r : prod) rows = r > rows ? r : rows;
+        char *dc = take((size_t)dense_mfma_cnt_words(rows) * 4);
+        if (w) w->dm_cnt = (unsigned *)dc;
+    }
     char *rows = take(attn_rows_ws_bytes(c->n_qh, c->n_kv, c->head_dim, c->cap, T));
     char *h = take((size_t)T * c->hidden * 4);
     char *x = take((size_t)T * c->hidden * 4);
@@ -257,7 +266,7 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
     for (int l = 0; l < c->n_layers; ++l) {
         const k2_layer *L = &m->layers[l];
         if ((rc = rmsnorm_rows_launch(w.h, L->g_in, w.x, T, H, c->groups, c->eps, st))) return rc;
-        if ((rc = pf_proj(c->wdt, L->qkv, L->qkv_s, w.x, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, st)))
+        if ((rc = pf_proj(c->wdt, L->qkv, L->qkv_s, w.x, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, w.dm_cnt, st)))
             return rc;
         at.kc = L->kc;
         at.vc = L->vc;
@@ -275,11 +284,11 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
             at.S = attn_splits(c->n_kv, at.len, &at.chunk);
             if ((rc = attn_launch(c->kvdt, hd, rep, true, at, st))) return rc;
         }
-        if ((rc = pf_proj(c->wdt, L->o, L->o_s, w.o, w.h, H, qd, T, DM_EPI_ADD, w.part, st))) return rc;
+        if ((rc = pf_proj(c->wdt, L->o, L->o_s, w.o, w.h, H, qd, T, DM_EPI_ADD, w.part, w.dm_cnt, st))) return rc;
         if ((rc = rmsnorm_rows_launch(w.h, L->g_post, w.x, T, H, c->groups, c->eps, st))) return rc;
-        if ((rc = pf_proj(c->wdt, L->gu, L->gu_s, w.x, w.act, 2 * I, H, T, DM_EPI_SWIGLU, w.part, st)))
+        if ((rc = pf_proj(c->wdt, L->gu, L->gu_s, w.x, w.act, 2 * I, H, T, DM_EPI_SWIGLU, w.part, w.dm_cnt, st)))
             return rc;
-        if ((rc = pf_proj(c->wdt, L->down, L->down_s, w.act, w.h, H, I, T, DM_EPI_ADD, w.part, st)))
+        if ((rc = pf_proj(c->wdt, L->down, L->down_s, w.act, w.h, H, I, T, DM_EPI_ADD, w.part, w.dm_cnt, st)))
             return rc;
     }
 
@@ -288,7 +297,7 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
         float *lg = logits ? logits : w.logits;
         if ((rc = rmsnorm_rows_launch(w.h, m->g_final, w.x, T, H, c->groups, c->eps, st))) return rc;
         rc = c->wdt == K2_BF16
-                 ? dense_mfma((const uint16_t *)m->lm, w.x, lg, c->vocab, H, T, DM_EPI_PLAIN, w.lm_part, st)
+                 ? dense_mfma((const uint16_t *)m->lm, w.x, lg, c->vocab, H, T, DM_EPI_PLAIN, w.lm_part, st, w.dm_cnt)
                  : gemm_mfma(c->wdt, m->lm, m->lm_s, w.x, lg, c->vocab, H, T, DM_EPI_PLAIN, w.lm_part, st);
         if (rc) return rc;
         hipLaunchKernelGGL(argmax_rows_part_kernel, dim3(AR_NB, T), dim3(K2_BLOCK), 0, st, lg, c->vocab, w.ar_v,

@@ -431,6 +431,15 @@ def test_head128_prefill_long_prompt(kvdt):
 
 
 @pytest.mark.parametrize("kvdt", ["bf16", "i8"])
+def test_head128_prefill_chunks_of_32_past_1024(kvdt):
+    """Chunks of 32 rows over 1100 positions: up to position 1024 their
+    attention runs on the matrix cores (a short cache), past it through the
+    split per-row kernel; 1100 = 34 x 32 + 12."""
+    cfg = HEAD128.replace(wdt="bf16", kvdt=kvdt, cap=1152)
+    _prefill_parity(cfg, 1100, 3, chunk=32)
+
+
+@pytest.mark.parametrize("kvdt", ["bf16", "i8"])
 @pytest.mark.parametrize("n_qh,n_kv", [(8, 1), (8, 4), (4, 4)])
 def test_prefill_gqa_ratios(n_qh, n_kv, kvdt):
     """Chunks of 64 rows on the matrix-core attention at 8, 2 and 1 query
