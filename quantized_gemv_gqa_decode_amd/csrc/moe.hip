@@ -17,6 +17,8 @@
 // selected expert are streamed once for all of its tokens (in groups of TB
 // staged in LDS); the per-pair outputs are then combined in slot order.  No
 // float atomics: the result is the same from run to run.
+#include <mutex>
+
 #include "gemv_impl.h"
 
 namespace k2 {
@@ -448,7 +450,7 @@ int moe_expert_launch(const float *z, int T, int latent, int inter, const int32_
 // bf16 GEMV of T token rows, as many rows per launch as the staged
 // activations allow (1, 2, 4 or 8)
 static int gemv_rows_bf16(const uint16_t *W, const float *x, float *y, int N, int K, int T,
-                          hipStream_t st)
+                          hipStream_t st, const float *residual = nullptr)
 {
     const int bmax = K2_MAX_LDS_FLOATS / K;
     int t = 0;
@@ -462,6 +464,7 @@ static int gemv_rows_bf16(const uint16_t *W, const float *x, float *y, int N, in
         a.N = N;
         a.K = K;
         a.B = b;
+        a.residual = residual ? residual + (int64_t)t * N : nullptr;
         const int rc = gemv_dispatch(K2_BF16, a, PRO_NONE, EPI_PLAIN, st);
         if (rc) return rc;
         t += b;
@@ -489,6 +492,7 @@ static int dense_rows_bf16(const uint16_t *W, const float *x, float *y, int N, i
 {
     if (T >= 2 && dense_mfma_ok(N, K)) return dense_mfma(W, x, y, N, K, T, epi, part, st);
     if (epi == DM_EPI_PLAIN) return gemv_rows_bf16(W, x, y, N, K, T, st);
+    if (epi == DM_EPI_ADD) return gemv_rows_bf16(W, x, y, N, K, T, st, y);   // y = W x + y in one launch
     int rc = gemv_rows_bf16(W, x, tmp, N, K, T, st);
     if (rc) return rc;
     if (epi == DM_EPI_SWIGLU) {
@@ -499,6 +503,38 @@ static int dense_rows_bf16(const uint16_t *W, const float *x, float *y, int N, i
     }
     K2_CHECK_LAUNCH();
     return K2_OK;
+}
+
+// A second stream per device for the shared experts, which read only the
+// layer input: they run beside the router / latent / routed-expert chain
+// and join it before W_up adds into y.  Created once per device (default
+// priority) and kept for the life of the process, with its fork and join
+// events; calls of k2_moe_layer that overlap in time on one device would
+// share them and must not (as they must not share a workspace).
+struct MoeSide {
+    hipStream_t s;
+    hipEvent_t fork, join;
+};
+constexpr int MOE_MAX_DEVICES = 64;
+static std::mutex g_moe_side_mu;
+static MoeSide g_moe_side[MOE_MAX_DEVICES];
+static bool g_moe_side_ok[MOE_MAX_DEVICES];
+
+static MoeSide *moe_side()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MOE_MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lk(g_moe_side_mu);
+    if (!g_moe_side_ok[dev]) {
+        MoeSide m{};
+        if (hipStreamCreateWithFlags(&m.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&m.fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&m.join, hipEventDisableTiming) != hipSuccess)
+            return nullptr;
+        g_moe_side[dev] = m;
+        g_moe_side_ok[dev] = true;
+    }
+    return &g_moe_side[dev];
 }
 
 static int moe_dims_check(int T, int latent, int inter, int top_k, int n_experts)
@@ -582,7 +618,7 @@ extern "C" size_t k2_moe_layer_workspace_bytes(const k2_moe_config *c, int T)
     n += k2_align256((size_t)T * 2 * c->inter * 4);                 // shared gate/up
     n += k2_align256((size_t)T * c->inter * 4);                     // shared act
     n += k2_align256((size_t)T * c->hidden * 4);                    // shared out
-    n += k2_align256(moe_dense_part_bytes(c, T));                   // matrix-core partials
+    n += k2_align256(moe_dense_part_bytes(c, T)) * 2;               // matrix-core partials (both streams)
     n += moe_ws_layout(T, c->top_k, c->inter, c->latent, nullptr, nullptr);
     return n;
 }
@@ -615,7 +651,28 @@ extern "C" int k2_moe_layer(const k2_moe_layer_weights *w, const float *x, int T
     float *sact = (float *)take((size_t)T * c->inter * 4);
     float *sout = (float *)take((size_t)T * c->hidden * 4);
     float *part = (float *)take(moe_dense_part_bytes(c, T));
+    float *part2 = (float *)take(moe_dense_part_bytes(c, T));
     void *ews = p;
+
+    // shared experts on the hidden input, on the side stream: y = sum_s W2_s
+    // (silu(W1_s x) * (W3_s x)); W_up r is added into y after the join
+    MoeSide *side = nullptr;
+    if (c->n_shared > 0) {
+        if (!(side = moe_side())) return K2_EHIP;
+        if (hipEventRecord(side->fork, st) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+            return K2_EHIP;
+        for (int s = 0; s < c->n_shared; ++s) {
+            const uint16_t *w13 = w->sh_w13 + (int64_t)s * 2 * c->inter * c->hidden;
+            const uint16_t *w2 = w->sh_w2 + (int64_t)s * c->hidden * c->inter;
+            if ((rc = dense_rows_bf16(w13, x, sact, 2 * c->inter, c->hidden, T, DM_EPI_SWIGLU, part2, sgu,
+                                      side->s)))
+                return rc;
+            if ((rc = dense_rows_bf16(w2, sact, y, c->hidden, c->inter, T, s == 0 ? DM_EPI_PLAIN : DM_EPI_ADD,
+                                      part2, sout, side->s)))
+                return rc;
+        }
+        if (hipEventRecord(side->join, side->s) != hipSuccess) return K2_EHIP;
+    }
 
     // router on the hidden input
     if ((rc = dense_rows_bf16(w->w_router, x, logits, c->n_experts, c->hidden, T, DM_EPI_PLAIN, part,
@@ -632,18 +689,11 @@ extern "C" int k2_moe_layer(const k2_moe_layer_weights *w, const float *x, int T
     if ((rc = moe_expert_launch(z, T, c->latent, c->inter, tidx, tw, c->top_k, c->n_experts, w->w13q,
                                 w->w13s, w->w2q, w->w2s, r, d_err, ews, st)))
         return rc;
-    // y = W_up r
-    if ((rc = dense_rows_bf16(w->w_up, r, y, c->hidden, c->latent, T, DM_EPI_PLAIN, part, nullptr, st)))
+    // y (+)= W_up r: after the shared experts' join when there are any
+    if (side && hipStreamWaitEvent(st, side->join, 0) != hipSuccess) return K2_EHIP;
+    if ((rc = dense_rows_bf16(w->w_up, r, y, c->hidden, c->latent, T, side ? DM_EPI_ADD : DM_EPI_PLAIN, part,
+                              sout, st)))
         return rc;
-    // shared experts on the hidden input, added into y
-    for (int s = 0; s < c->n_shared; ++s) {
-        const uint16_t *w13 = w->sh_w13 + (int64_t)s * 2 * c->inter * c->hidden;
-        const uint16_t *w2 = w->sh_w2 + (int64_t)s * c->hidden * c->inter;
-        if ((rc = dense_rows_bf16(w13, x, sact, 2 * c->inter, c->hidden, T, DM_EPI_SWIGLU, part, sgu, st)))
-            return rc;
-        if ((rc = dense_rows_bf16(w2, sact, y, c->hidden, c->inter, T, DM_EPI_ADD, part, sout, st)))
-            return rc;
-    }
     if (topk_idx_out) {
         if (hipMemcpyAsync(topk_idx_out, tidx, (size_t)T * c->top_k * 4, hipMemcpyDeviceToDevice, st))
             return K2_EHIP;

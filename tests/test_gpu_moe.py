@@ -147,6 +147,35 @@ def test_moe_layer_repeat_is_deterministic():
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("T", [1, 8])
+def test_moe_layer_graph_replay_equals_eager(T):
+    """The layer's shared experts run on a second stream joined before W_up:
+    captured as one HIP graph (fork and join inside the capture) and replayed
+    three times, with eager launches of the layer and synchronizations in
+    between, every replay gives exactly the eager result."""
+    lay = MoeLayer(SMALL, DEV)
+    x = to_dev(synth.moe_activations(SMALL, T))
+    y_ref = lay.forward(x)[0].clone()
+    torch.cuda.synchronize()
+    y = torch.empty_like(y_ref)
+    idx = torch.empty((T, SMALL.top_k), dtype=torch.int32, device=DEV)
+    gw = torch.empty((T, SMALL.top_k), dtype=torch.float32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=cap):
+        lay.forward(x, y, idx, gw)               # the capture stream is current here
+    torch.cuda.current_stream().wait_stream(cap)
+    for _ in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref)
+        e = lay.forward(x)[0]                    # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(e, y_ref)
+
+
 def test_moe_route_standalone():
     cfg = SMALL.replace(routed_scale=2.5)
     om = OracleMoe(cfg)
