@@ -487,12 +487,14 @@ typedef struct {
  * y: [T][hidden], overwritten.  topk_idx_out / topk_w_out ([T][top_k],
  * nullable) receive the routing.  d_err as in k2_moe_expert_gemv.  Limits:
  * those of k2_moe_route and k2_moe_expert_gemv.  ws:
- * k2_moe_layer_workspace_bytes(&cfg, T) bytes, 256-byte aligned.  With
- * shared experts the library forks them onto a stream of its own (one per
- * device, created on first use, default priority) after an event recorded
- * on `stream`, and `stream` waits for them before W_up: the call stays
- * ordered on `stream` and can be captured into a graph from it; calls that
- * overlap in time on one device must not (they would share that stream). */
+ * k2_moe_layer_workspace_bytes(&cfg, T) bytes, 256-byte aligned.  The
+ * router and the shared experts (they read only x) are forked onto a stream
+ * of the library's own (one per device, created on first use, default
+ * priority) after an event recorded on `stream`, which waits for the
+ * routing before the routed experts and for the shared experts before W_up:
+ * the call stays ordered on `stream` and can be captured into a graph from
+ * it; calls that overlap in time on one device must not (they would share
+ * that stream). */
 size_t k2_moe_layer_workspace_bytes(const k2_moe_config *cfg, int T);
 int k2_moe_layer(const k2_moe_layer_weights *w, const float *x, int T, float *y,
                  int32_t *topk_idx_out, float *topk_w_out, int32_t *d_err, void *ws,

@@ -505,15 +505,15 @@ static int dense_rows_bf16(const uint16_t *W, const float *x, float *y, int N, i
     return K2_OK;
 }
 
-// A second stream per device for the shared experts, which read only the
-// layer input: they run beside the router / latent / routed-expert chain
-// and join it before W_up adds into y.  Created once per device (default
-// priority) and kept for the life of the process, with its fork and join
-// events; calls of k2_moe_layer that overlap in time on one device would
-// share them and must not (as they must not share a workspace).
+// A second stream per device for the work that reads only the layer input
+// (the router, the shared experts): it runs beside the latent / routed-expert
+// chain.  Created once per device (default priority) and kept for the life
+// of the process, with its fork, routing and join events; calls of
+// k2_moe_layer that overlap in time on one device would share them and must
+// not (as they must not share a workspace).
 struct MoeSide {
     hipStream_t s;
-    hipEvent_t fork, join;
+    hipEvent_t fork, routed, join;
 };
 constexpr int MOE_MAX_DEVICES = 64;
 static std::mutex g_moe_side_mu;
@@ -529,6 +529,7 @@ static MoeSide *moe_side()
         MoeSide m{};
         if (hipStreamCreateWithFlags(&m.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
         if (hipEventCreateWithFlags(&m.fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&m.routed, hipEventDisableTiming) != hipSuccess ||
             hipEventCreateWithFlags(&m.join, hipEventDisableTiming) != hipSuccess)
             return nullptr;
         g_moe_side[dev] = m;
@@ -654,45 +655,46 @@ extern "C" int k2_moe_layer(const k2_moe_layer_weights *w, const float *x, int T
     float *part2 = (float *)take(moe_dense_part_bytes(c, T));
     void *ews = p;
 
-    // shared experts on the hidden input, on the side stream: y = sum_s W2_s
-    // (silu(W1_s x) * (W3_s x)); W_up r is added into y after the join
-    MoeSide *side = nullptr;
-    if (c->n_shared > 0) {
-        if (!(side = moe_side())) return K2_EHIP;
-        if (hipEventRecord(side->fork, st) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
-            return K2_EHIP;
-        for (int s = 0; s < c->n_shared; ++s) {
-            const uint16_t *w13 = w->sh_w13 + (int64_t)s * 2 * c->inter * c->hidden;
-            const uint16_t *w2 = w->sh_w2 + (int64_t)s * c->hidden * c->inter;
-            if ((rc = dense_rows_bf16(w13, x, sact, 2 * c->inter, c->hidden, T, DM_EPI_SWIGLU, part2, sgu,
-                                      side->s)))
-                return rc;
-            if ((rc = dense_rows_bf16(w2, sact, y, c->hidden, c->inter, T, s == 0 ? DM_EPI_PLAIN : DM_EPI_ADD,
-                                      part2, sout, side->s)))
-                return rc;
-        }
-        if (hipEventRecord(side->join, side->s) != hipSuccess) return K2_EHIP;
-    }
-
-    // router on the hidden input
-    if ((rc = dense_rows_bf16(w->w_router, x, logits, c->n_experts, c->hidden, T, DM_EPI_PLAIN, part,
-                              nullptr, st)))
+    // Two streams.  The library's side stream takes the work that reads only
+    // the layer input: the router (its routing is waited for before the
+    // routed experts), then the shared experts, y = sum_s W2_s(silu(W1_s x) *
+    // (W3_s x)) (waited for before W_up adds into y).  The caller's stream
+    // runs W_dn, the latent norm, the routed experts and W_up.
+    MoeSide *side = moe_side();
+    if (!side) return K2_EHIP;
+    if (hipEventRecord(side->fork, st) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+        return K2_EHIP;
+    if ((rc = dense_rows_bf16(w->w_router, x, logits, c->n_experts, c->hidden, T, DM_EPI_PLAIN, part2, nullptr,
+                              side->s)))
         return rc;
-    hipLaunchKernelGGL(moe_route_kernel, dim3(T), dim3(K2_WAVE), 0, st, logits, w->router_bias,
+    hipLaunchKernelGGL(moe_route_kernel, dim3(T), dim3(K2_WAVE), 0, side->s, logits, w->router_bias,
                        c->n_experts, c->top_k, c->routed_scale, tidx, tw);
     K2_CHECK_LAUNCH();
+    if (hipEventRecord(side->routed, side->s) != hipSuccess) return K2_EHIP;
+    for (int s = 0; s < c->n_shared; ++s) {
+        const uint16_t *w13 = w->sh_w13 + (int64_t)s * 2 * c->inter * c->hidden;
+        const uint16_t *w2 = w->sh_w2 + (int64_t)s * c->hidden * c->inter;
+        if ((rc = dense_rows_bf16(w13, x, sact, 2 * c->inter, c->hidden, T, DM_EPI_SWIGLU, part2, sgu, side->s)))
+            return rc;
+        if ((rc = dense_rows_bf16(w2, sact, y, c->hidden, c->inter, T, s == 0 ? DM_EPI_PLAIN : DM_EPI_ADD, part2,
+                                  sout, side->s)))
+            return rc;
+    }
+    if (hipEventRecord(side->join, side->s) != hipSuccess) return K2_EHIP;
+
     // latent: z = RMSNorm(W_dn x)
     if ((rc = dense_rows_bf16(w->w_down, x, z, c->latent, c->hidden, T, DM_EPI_PLAIN, part, nullptr, st)))
         return rc;
     if ((rc = k2_rmsnorm_grouped(z, w->latent_gamma, z, T, c->latent, 1, c->eps, stream))) return rc;
-    // routed experts
+    // routed experts, once the routing is in
+    if (hipStreamWaitEvent(st, side->routed, 0) != hipSuccess) return K2_EHIP;
     if ((rc = moe_expert_launch(z, T, c->latent, c->inter, tidx, tw, c->top_k, c->n_experts, w->w13q,
                                 w->w13s, w->w2q, w->w2s, r, d_err, ews, st)))
         return rc;
-    // y (+)= W_up r: after the shared experts' join when there are any
-    if (side && hipStreamWaitEvent(st, side->join, 0) != hipSuccess) return K2_EHIP;
-    if ((rc = dense_rows_bf16(w->w_up, r, y, c->hidden, c->latent, T, side ? DM_EPI_ADD : DM_EPI_PLAIN, part,
-                              sout, st)))
+    // y (+)= W_up r, after the side stream's work
+    if (hipStreamWaitEvent(st, side->join, 0) != hipSuccess) return K2_EHIP;
+    if ((rc = dense_rows_bf16(w->w_up, r, y, c->hidden, c->latent, T, c->n_shared > 0 ? DM_EPI_ADD : DM_EPI_PLAIN,
+                              part, sout, st)))
         return rc;
     if (topk_idx_out) {
         if (hipMemcpyAsync(topk_idx_out, tidx, (size_t)T * c->top_k * 4, hipMemcpyDeviceToDevice, st))
