@@ -49,7 +49,8 @@ int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qr
     if (kvdt != K2_F32 && kvdt != K2_BF16 && kvdt != K2_I8) return K2_EUNSUPPORTED;
     {
         int chunk = 0;
-        if ((size_t)attn_splits(n_kv, pos0 + T, &chunk) > (size_t)attn_max_splits(n_kv, cap)) return K2_EUNSUPPORTED;
+        if ((size_t)attn_splits(n_kv * T, pos0 + T, &chunk) > (size_t)attn_max_splits(n_kv, cap))
+            return K2_EUNSUPPORTED;
     }
     switch (kvdt) {
     case K2_F32:
@@ -93,7 +94,10 @@ int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qr
     a.len = pos0 + T;                          // the last slice's length
     a.pos = a.len - 1;
     a.scale = 1.0f / sqrtf((float)hd);
-    const int S_max = attn_splits(n_kv, a.len, &a.chunk);
+    // the decode rule's block target shared by the T rows: every row gets
+    // 1/T of the splits one decode position would (8 rows at 528 positions:
+    // 4 splits of 132 instead of 9 of 64, one round of 256 blocks)
+    const int S_max = attn_splits(n_kv * T, a.len, &a.chunk);
     switch (kvdt) {
     case K2_F32: return attn_rows_rep<K2_F32>(rep, a, T, S_max, st);
     case K2_BF16: return attn_rows_rep<K2_BF16>(rep, a, T, S_max, st);
