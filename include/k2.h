@@ -493,8 +493,9 @@ typedef struct {
  * priority) after an event recorded on `stream`, which waits for the
  * routing before the routed experts and for the shared experts before W_up:
  * the call stays ordered on `stream` and can be captured into a graph from
- * it; calls that overlap in time on one device must not (they would share
- * that stream). */
+ * it (a call captured before the device's first uncaptured call runs on
+ * `stream` alone); calls that overlap in time on one device must not (they
+ * would share that stream). */
 size_t k2_moe_layer_workspace_bytes(const k2_moe_config *cfg, int T);
 int k2_moe_layer(const k2_moe_layer_weights *w, const float *x, int T, float *y,
                  int32_t *topk_idx_out, float *topk_w_out, int32_t *d_err, void *ws,

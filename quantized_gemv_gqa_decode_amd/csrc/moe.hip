@@ -520,12 +520,17 @@ static std::mutex g_moe_side_mu;
 static MoeSide g_moe_side[MOE_MAX_DEVICES];
 static bool g_moe_side_ok[MOE_MAX_DEVICES];
 
-static MoeSide *moe_side()
+// The side stream of the current device, created on first use -- but not
+// while `st` is being captured into a graph (creating a stream could end the
+// capture): the layer then runs on `st` alone.
+static MoeSide *moe_side(hipStream_t st)
 {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MOE_MAX_DEVICES) return nullptr;
     std::lock_guard<std::mutex> lk(g_moe_side_mu);
     if (!g_moe_side_ok[dev]) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
         MoeSide m{};
         if (hipStreamCreateWithFlags(&m.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
         if (hipEventCreateWithFlags(&m.fork, hipEventDisableTiming) != hipSuccess ||
@@ -659,40 +664,41 @@ extern "C" int k2_moe_layer(const k2_moe_layer_weights *w, const float *x, int T
     // the layer input: the router (its routing is waited for before the
     // routed experts), then the shared experts, y = sum_s W2_s(silu(W1_s x) *
     // (W3_s x)) (waited for before W_up adds into y).  The caller's stream
-    // runs W_dn, the latent norm, the routed experts and W_up.
-    MoeSide *side = moe_side();
-    if (!side) return K2_EHIP;
-    if (hipEventRecord(side->fork, st) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+    // runs W_dn, the latent norm, the routed experts and W_up.  Without a
+    // side stream everything runs on the caller's stream in the same order.
+    MoeSide *side = moe_side(st);
+    const hipStream_t ss = side ? side->s : st;
+    if (side && (hipEventRecord(side->fork, st) != hipSuccess || hipStreamWaitEvent(ss, side->fork, 0) != hipSuccess))
         return K2_EHIP;
     if ((rc = dense_rows_bf16(w->w_router, x, logits, c->n_experts, c->hidden, T, DM_EPI_PLAIN, part2, nullptr,
-                              side->s)))
+                              ss)))
         return rc;
-    hipLaunchKernelGGL(moe_route_kernel, dim3(T), dim3(K2_WAVE), 0, side->s, logits, w->router_bias,
+    hipLaunchKernelGGL(moe_route_kernel, dim3(T), dim3(K2_WAVE), 0, ss, logits, w->router_bias,
                        c->n_experts, c->top_k, c->routed_scale, tidx, tw);
     K2_CHECK_LAUNCH();
-    if (hipEventRecord(side->routed, side->s) != hipSuccess) return K2_EHIP;
+    if (side && hipEventRecord(side->routed, ss) != hipSuccess) return K2_EHIP;
     for (int s = 0; s < c->n_shared; ++s) {
         const uint16_t *w13 = w->sh_w13 + (int64_t)s * 2 * c->inter * c->hidden;
         const uint16_t *w2 = w->sh_w2 + (int64_t)s * c->hidden * c->inter;
-        if ((rc = dense_rows_bf16(w13, x, sact, 2 * c->inter, c->hidden, T, DM_EPI_SWIGLU, part2, sgu, side->s)))
+        if ((rc = dense_rows_bf16(w13, x, sact, 2 * c->inter, c->hidden, T, DM_EPI_SWIGLU, part2, sgu, ss)))
             return rc;
         if ((rc = dense_rows_bf16(w2, sact, y, c->hidden, c->inter, T, s == 0 ? DM_EPI_PLAIN : DM_EPI_ADD, part2,
-                                  sout, side->s)))
+                                  sout, ss)))
             return rc;
     }
-    if (hipEventRecord(side->join, side->s) != hipSuccess) return K2_EHIP;
+    if (side && hipEventRecord(side->join, ss) != hipSuccess) return K2_EHIP;
 
     // latent: z = RMSNorm(W_dn x)
     if ((rc = dense_rows_bf16(w->w_down, x, z, c->latent, c->hidden, T, DM_EPI_PLAIN, part, nullptr, st)))
         return rc;
     if ((rc = k2_rmsnorm_grouped(z, w->latent_gamma, z, T, c->latent, 1, c->eps, stream))) return rc;
     // routed experts, once the routing is in
-    if (hipStreamWaitEvent(st, side->routed, 0) != hipSuccess) return K2_EHIP;
+    if (side && hipStreamWaitEvent(st, side->routed, 0) != hipSuccess) return K2_EHIP;
     if ((rc = moe_expert_launch(z, T, c->latent, c->inter, tidx, tw, c->top_k, c->n_experts, w->w13q,
                                 w->w13s, w->w2q, w->w2s, r, d_err, ews, st)))
         return rc;
     // y (+)= W_up r, after the side stream's work
-    if (hipStreamWaitEvent(st, side->join, 0) != hipSuccess) return K2_EHIP;
+    if (side && hipStreamWaitEvent(st, side->join, 0) != hipSuccess) return K2_EHIP;
     if ((rc = dense_rows_bf16(w->w_up, r, y, c->hidden, c->latent, T, c->n_shared > 0 ? DM_EPI_ADD : DM_EPI_PLAIN,
                               part, sout, st)))
         return rc;

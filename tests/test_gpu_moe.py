@@ -176,6 +176,45 @@ def test_moe_layer_graph_replay_equals_eager(T):
         assert torch.equal(e, y_ref)
 
 
+def test_moe_layer_captured_first_runs_on_one_stream():
+    """In a fresh process whose first layer call is captured into a graph the
+    library creates no stream during the capture and runs the layer on the
+    capturing stream alone; the replays equal a later eager call (which then
+    uses the side stream)."""
+    import os
+    import subprocess
+    import sys
+    code = (
+        "import sys, torch\n"
+        "sys.path.insert(0, 'tests'); sys.path.insert(0, '.')\n"
+        "import synth\n"
+        "from test_gpu_moe import SMALL\n"
+        "from quantized_gemv_gqa_decode_amd.moe import MoeLayer\n"
+        "dev = torch.device('cuda:0')\n"
+        "lay = MoeLayer(SMALL, dev)\n"
+        "x = torch.from_numpy(synth.moe_activations(SMALL, 8)).to(dev)\n"
+        "y = torch.empty((8, SMALL.hidden), device=dev)\n"
+        "idx = torch.empty((8, SMALL.top_k), dtype=torch.int32, device=dev)\n"
+        "gw = torch.empty((8, SMALL.top_k), device=dev)\n"
+        "torch.cuda.synchronize()\n"
+        "g = torch.cuda.CUDAGraph()\n"
+        "cap = torch.cuda.Stream()\n"
+        "cap.wait_stream(torch.cuda.current_stream())\n"
+        "with torch.cuda.graph(g, stream=cap):\n"
+        "    lay.forward(x, y, idx, gw)\n"
+        "torch.cuda.current_stream().wait_stream(cap)\n"
+        "g.replay(); torch.cuda.synchronize()\n"
+        "ref = lay.forward(x)[0]; torch.cuda.synchronize()\n"
+        "assert torch.equal(y, ref), float((y - ref).abs().max())\n"
+        "g.replay(); torch.cuda.synchronize()\n"
+        "assert torch.equal(y, ref)\n"
+        "print('captured-first OK')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert "captured-first OK" in r.stdout
+
+
 def test_moe_route_standalone():
     cfg = SMALL.replace(routed_scale=2.5)
     om = OracleMoe(cfg)
