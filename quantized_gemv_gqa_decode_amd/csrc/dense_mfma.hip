@@ -8,9 +8,9 @@
 //   * each activation is split into bf16 hi + bf16 lo (x - hi rounded again),
 //     two MFMAs per weight tile, fp32 accumulation: the weights are exact in
 //     bf16 and the split keeps ~16 bits of every activation;
-//   * a block of 4 waves owns 256 rows and one k-range (split-K); it stages
+//   * a block of 4 waves owns 256, 128 or 64 rows and one k-range (split-K); it stages
 //     its slice of the activations once in LDS as the two bf16 planes, each
-//     wave streams 4 row tiles of 16 rows from HBM, one 128-column chunk
+//     wave streams its 4, 2 or 1 row tiles of 16 rows from HBM, one 128-column chunk
 //     ahead of the MFMAs;
 //   * per-split partials [split][token][row] are summed in split order by a
 //     second kernel, which also applies the epilogue (plain, add into y, or
@@ -32,9 +32,8 @@ namespace k2 {
 typedef short dm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float dm_f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int DM_RT = 4;                          // 16-row tiles per wave
 constexpr int DM_WAVES = 4;                       // waves per block
-constexpr int DM_ROWS = DM_RT * 16 * DM_WAVES;    // rows per block
+constexpr int DM_MIN_ROWS = 16 * DM_WAVES;        // rows per block with one 16-row tile per wave
 constexpr int DM_KC = 128;                        // columns per chunk (4 MFMA k-steps)
 constexpr int DM_MAX_KS = 512;                    // columns per split
 constexpr int DM_MAX_T = 32;                      // tokens per launch
@@ -54,9 +53,10 @@ struct DenseArgs {
 
 __host__ __device__ constexpr int dm_lds_bytes(int tp, int ks) { return 2 * tp * (ks + 8) * 2; }
 
-template <int NTT, int KS>
+template <int NTT, int KS, int RT>
 __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
 {
+    constexpr int ROWS = RT * 16 * DM_WAVES;      // rows per block
     constexpr int TP = 16 * NTT;
     constexpr int RS = KS + 8;                    // LDS row stride (bf16): 16 B of pad per row
     constexpr int NCH = KS / DM_KC;               // chunks per split
@@ -70,11 +70,11 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
 
     // rows of this wave's tiles (tiles past N read the last tile again and
     // are never stored)
-    int64_t rowoff[DM_RT];
-    bool rok[DM_RT];
+    int64_t rowoff[RT];
+    bool rok[RT];
 #pragma unroll
-    for (int rt = 0; rt < DM_RT; ++rt) {
-        const int r0 = blockIdx.x * DM_ROWS + (wave * DM_RT + rt) * 16;
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r0 = blockIdx.x * ROWS + (wave * RT + rt) * 16;
         rok[rt] = r0 < a.N;
         const int row = (rok[rt] ? r0 : a.N - 16) + c16;
         rowoff[rt] = (int64_t)row * a.K + k0 + q * 8;
@@ -82,14 +82,14 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
     const dm_bf16x8 *Wv = reinterpret_cast<const dm_bf16x8 *>(a.W);
     // chunk c of tile rt, k-step j: the 16 B at element rowoff + c*128 + 32j
     // (the 4 lanes of a row read 64 contiguous bytes per instruction)
-    auto load_chunk = [&](int c, dm_bf16x8 (&w)[DM_RT][4]) {
+    auto load_chunk = [&](int c, dm_bf16x8 (&w)[RT][4]) {
 #pragma unroll
-        for (int rt = 0; rt < DM_RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 w[rt][j] = __builtin_nontemporal_load(Wv + (rowoff[rt] + c * DM_KC + 32 * j) / 8);
     };
-    dm_bf16x8 wc[DM_RT][4];
+    dm_bf16x8 wc[RT][4];
     load_chunk(0, wc);                            // weights first: their latency covers the staging
 
     // stage the activation slice as bf16 hi / lo planes (tokens >= T are 0):
@@ -119,12 +119,12 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
     }
     __syncthreads();
 
-    dm_f32x4 acc[DM_RT][NTT];
+    dm_f32x4 acc[RT][NTT];
 #pragma unroll
-    for (int rt = 0; rt < DM_RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) acc[rt][tt] = dm_f32x4{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](int c, const dm_bf16x8 (&w)[DM_RT][4]) {
+    auto compute = [&](int c, const dm_bf16x8 (&w)[RT][4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int kk = c * DM_KC + 32 * j + q * 8;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
                 const dm_bf16x8 bh = *reinterpret_cast<const dm_bf16x8 *>(xh + t * RS + kk);
                 const dm_bf16x8 bl = *reinterpret_cast<const dm_bf16x8 *>(xl + t * RS + kk);
 #pragma unroll
-                for (int rt = 0; rt < DM_RT; ++rt) {
+                for (int rt = 0; rt < RT; ++rt) {
                     acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[rt][j], bh, acc[rt][tt], 0, 0, 0);
                     acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[rt][j], bl, acc[rt][tt], 0, 0, 0);
                 }
@@ -144,11 +144,11 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
     // one chunk ahead of the MFMAs; the last chunk without a next one
 #pragma unroll 1
     for (int c = 0; c + 1 < NCH; ++c) {
-        dm_bf16x8 wn[DM_RT][4];
+        dm_bf16x8 wn[RT][4];
         load_chunk(c + 1, wn);
         compute(c, wc);
 #pragma unroll
-        for (int rt = 0; rt < DM_RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) wc[rt][j] = wn[rt][j];
     }
@@ -158,9 +158,9 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
     // (device scope when another block sums them)
     const bool fuse = a.cnt != nullptr;
 #pragma unroll
-    for (int rt = 0; rt < DM_RT; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
         if (!rok[rt]) continue;
-        const int r0 = blockIdx.x * DM_ROWS + (wave * DM_RT + rt) * 16 + 4 * q;
+        const int r0 = blockIdx.x * ROWS + (wave * RT + rt) * 16 + 4 * q;
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
             const int t = tt * 16 + c16;
@@ -191,13 +191,14 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
     if (!last) return;
 
     // the group's outputs, each summed over the splits in split order: a
-    // thread owns 4 consecutive outputs (gate rows for SwiGLU) of every 4th
-    // token and loads 8 splits' partials before adding them
+    // thread owns 4 consecutive outputs (gate rows for SwiGLU) of every
+    // TSTEP-th token and loads 8 splits' partials before adding them
+    constexpr int QUADS = ROWS / 4, TSTEP = 256 / QUADS;
     const int n_out = pair ? a.N / 2 : a.N;
-    const int n = grp * DM_ROWS + (tid & 63) * 4;
+    const int n = grp * ROWS + (tid % QUADS) * 4;
     if (n >= n_out) return;
     constexpr int B8 = 8;
-    for (int t = tid >> 6; t < a.T; t += 4) {
+    for (int t = tid / QUADS; t < a.T; t += TSTEP) {
         float4 sum = make_float4(0.f, 0.f, 0.f, 0.f), up = sum;
         for (int s0 = 0; s0 < splits; s0 += B8) {
             float4 v[B8], u[B8];
@@ -249,14 +250,21 @@ __global__ __launch_bounds__(256) void dense_reduce_kernel(const float *part, in
     else *dst = s;
 }
 
-// Columns per split: the largest of 512, 256, 128 dividing K that still
-// gives at least 256 blocks (else 128).
-static int dm_ks(int N, int K)
+// Tile shape: 16-row tiles per wave (RT: 256, 128 or 64 rows per block) and
+// columns per split (KS), the first of (4, 512), (2, 512), (1, 512),
+// (1, 256), (1, 128) that divides K and gives at least 256 blocks (else the
+// last): the longest splits first (their chunks stream one ahead of the
+// matrix cores, and fewer splits leave fewer partials), then the largest row
+// blocks (an activation fragment read from LDS feeds RT row tiles).
+struct DmTile { int rt, ks; };
+static DmTile dm_tile(int N, int K)
 {
-    const int rb = (N + DM_ROWS - 1) / DM_ROWS;
-    for (int ks = DM_MAX_KS; ks >= DM_KC; ks >>= 1)
-        if (K % ks == 0 && (int64_t)rb * (K / ks) >= 256) return ks;
-    return DM_KC;
+    static const DmTile cand[] = {{4, 512}, {2, 512}, {1, 512}, {1, 256}, {1, 128}};
+    for (const DmTile &c : cand) {
+        const int64_t rb = (N + c.rt * DM_MIN_ROWS - 1) / (c.rt * DM_MIN_ROWS);
+        if (K % c.ks == 0 && rb * (K / c.ks) >= 256) return c;
+    }
+    return {1, DM_KC};
 }
 
 bool dense_mfma_ok(int N, int K) { return N >= 16 && N % 16 == 0 && K % DM_KC == 0; }
@@ -265,23 +273,32 @@ size_t dense_mfma_ws_bytes(int N, int K, int T)
 {
     if (!dense_mfma_ok(N, K) || T < 2) return 0;
     const int tp = (T < DM_MAX_T ? T : DM_MAX_T) <= 16 ? 16 : 32;
-    return (size_t)(K / dm_ks(N, K)) * tp * N * 4;
+    return (size_t)(K / dm_tile(N, K).ks) * tp * N * 4;
 }
 
-int dense_mfma_cnt_words(int N) { return (N + DM_ROWS - 1) / DM_ROWS; }
+int dense_mfma_cnt_words(int N) { return (N + DM_MIN_ROWS - 1) / DM_MIN_ROWS; }
+
+template <int NTT, int KS>
+static void dm_go(int rt, dim3 grid, size_t lds, hipStream_t st, const DenseArgs &a)
+{
+    if (rt == 4) hipLaunchKernelGGL((dense_mfma_kernel<NTT, KS, 4>), grid, dim3(256), lds, st, a);
+    else if (rt == 2) hipLaunchKernelGGL((dense_mfma_kernel<NTT, KS, 2>), grid, dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((dense_mfma_kernel<NTT, KS, 1>), grid, dim3(256), lds, st, a);
+}
 
 // y = W x for T token rows (T >= 2), through per-split partials in `part`
 // (dense_mfma_ws_bytes); groups of up to 32 tokens run one after another.
 // cnt (nullable, dense_mfma_cnt_words(N) zeroed words, left zero): sum the
 // partials in the product's last blocks instead of a second launch (SwiGLU
-// only when N / 2 is a multiple of the 256-row block).
+// only when N / 2 is a multiple of the row block).
 int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi, float *part,
                hipStream_t st, unsigned *cnt)
 {
     if (!dense_mfma_ok(N, K) || T < 2) return K2_EUNSUPPORTED;
-    const int KS = dm_ks(N, K), splits = K / KS;
+    const DmTile tile = dm_tile(N, K);
+    const int KS = tile.ks, splits = K / KS, rows = tile.rt * DM_MIN_ROWS;
     const int n_out = epi == DM_EPI_SWIGLU ? N / 2 : N;
-    if (epi == DM_EPI_SWIGLU && (N / 2) % DM_ROWS) cnt = nullptr;
+    if (epi == DM_EPI_SWIGLU && (N / 2) % rows) cnt = nullptr;
     // the last block of a group reads T x splits partial rows: past ~128 of
     // them that tail costs more than the second launch (3.7B shape,
     // verification rounds with every product fused: T = 2 3.90 against 4.23
@@ -290,16 +307,18 @@ int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T,
     for (int t0 = 0; t0 < T; t0 += DM_MAX_T) {
         const int tg = T - t0 < DM_MAX_T ? T - t0 : DM_MAX_T;
         DenseArgs a{W, x + (int64_t)t0 * K, part, N, K, tg, KS, cnt, y + (int64_t)t0 * n_out, epi};
-        const dim3 grid((N + DM_ROWS - 1) / DM_ROWS, splits);
+        const dim3 grid((N + rows - 1) / rows, splits);
         const int tp = tg <= 16 ? 16 : 32;
         const size_t lds = dm_lds_bytes(tp, KS);
-#define DM_GO(NTT, KSV) hipLaunchKernelGGL((dense_mfma_kernel<NTT, KSV>), grid, dim3(256), lds, st, a)
         if (tp == 16) {
-            if (KS == 512) DM_GO(1, 512); else if (KS == 256) DM_GO(1, 256); else DM_GO(1, 128);
+            if (KS == 512) dm_go<1, 512>(tile.rt, grid, lds, st, a);
+            else if (KS == 256) dm_go<1, 256>(tile.rt, grid, lds, st, a);
+            else dm_go<1, 128>(tile.rt, grid, lds, st, a);
         } else {
-            if (KS == 512) DM_GO(2, 512); else if (KS == 256) DM_GO(2, 256); else DM_GO(2, 128);
+            if (KS == 512) dm_go<2, 512>(tile.rt, grid, lds, st, a);
+            else if (KS == 256) dm_go<2, 256>(tile.rt, grid, lds, st, a);
+            else dm_go<2, 128>(tile.rt, grid, lds, st, a);
         }
-#undef DM_GO
         K2_CHECK_LAUNCH();
         if (cnt) continue;
         hipLaunchKernelGGL(dense_reduce_kernel, dim3((n_out + 255) / 256, tg), dim3(256), 0, st, part,
