@@ -35,7 +35,6 @@ typedef float dm_f32x4 __attribute__((ext_vector_type(4)));
 constexpr int DM_WAVES = 4;                       // waves per block
 constexpr int DM_MIN_ROWS = 16 * DM_WAVES;        // rows per block with one 16-row tile per wave
 constexpr int DM_KC = 128;                        // columns per chunk (4 MFMA k-steps)
-constexpr int DM_MAX_KS = 512;                    // columns per split
 constexpr int DM_MAX_T = 32;                      // tokens per launch
 constexpr int DM_FUSE_MAX = 128;                  // tokens x splits summed in-kernel at most
 
@@ -251,16 +250,21 @@ __global__ __launch_bounds__(256) void dense_reduce_kernel(const float *part, in
 }
 
 // Tile shape: 16-row tiles per wave (RT: 256, 128 or 64 rows per block) and
-// columns per split (KS), the first of (4, 512), (2, 512), (1, 512),
-// (1, 256), (1, 128) that divides K and gives at least 256 blocks (else the
-// last): the longest splits first (their chunks stream one ahead of the
+// columns per split (KS), the first of (4, 1024), (2, 1024), (1, 1024) (up
+// to 16 tokens: with 32 their activation slice fills the LDS of a compute
+// unit, and measured slower), (4, 512), (2, 512), (1, 512), (1, 256),
+// (1, 128) that divides K and gives at least 256 blocks (else the last): the
+// longest splits first (their chunks stream one ahead of the
 // matrix cores, and fewer splits leave fewer partials), then the largest row
 // blocks (an activation fragment read from LDS feeds RT row tiles).
 struct DmTile { int rt, ks; };
-static DmTile dm_tile(int N, int K)
+static DmTile dm_tile(int N, int K, int T)
 {
-    static const DmTile cand[] = {{4, 512}, {2, 512}, {1, 512}, {1, 256}, {1, 128}};
+    static const DmTile cand[] = {{4, 1024}, {2, 1024}, {1, 1024}, {4, 512}, {2, 512},
+                                  {1, 512},  {1, 256},  {1, 128}};
+    const int tp = (T < DM_MAX_T ? T : DM_MAX_T) <= 16 ? 16 : 32;
     for (const DmTile &c : cand) {
+        if (c.ks == 1024 && tp > 16) continue;
         const int64_t rb = (N + c.rt * DM_MIN_ROWS - 1) / (c.rt * DM_MIN_ROWS);
         if (K % c.ks == 0 && rb * (K / c.ks) >= 256) return c;
     }
@@ -273,7 +277,7 @@ size_t dense_mfma_ws_bytes(int N, int K, int T)
 {
     if (!dense_mfma_ok(N, K) || T < 2) return 0;
     const int tp = (T < DM_MAX_T ? T : DM_MAX_T) <= 16 ? 16 : 32;
-    return (size_t)(K / dm_tile(N, K).ks) * tp * N * 4;
+    return (size_t)(K / dm_tile(N, K, T).ks) * tp * N * 4;
 }
 
 int dense_mfma_cnt_words(int N) { return (N + DM_MIN_ROWS - 1) / DM_MIN_ROWS; }
@@ -295,7 +299,7 @@ int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T,
                hipStream_t st, unsigned *cnt)
 {
     if (!dense_mfma_ok(N, K) || T < 2) return K2_EUNSUPPORTED;
-    const DmTile tile = dm_tile(N, K);
+    const DmTile tile = dm_tile(N, K, T);
     const int KS = tile.ks, splits = K / KS, rows = tile.rt * DM_MIN_ROWS;
     const int n_out = epi == DM_EPI_SWIGLU ? N / 2 : N;
     if (epi == DM_EPI_SWIGLU && (N / 2) % rows) cnt = nullptr;
@@ -311,11 +315,13 @@ int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T,
         const int tp = tg <= 16 ? 16 : 32;
         const size_t lds = dm_lds_bytes(tp, KS);
         if (tp == 16) {
-            if (KS == 512) dm_go<1, 512>(tile.rt, grid, lds, st, a);
+            if (KS == 1024) dm_go<1, 1024>(tile.rt, grid, lds, st, a);
+            else if (KS == 512) dm_go<1, 512>(tile.rt, grid, lds, st, a);
             else if (KS == 256) dm_go<1, 256>(tile.rt, grid, lds, st, a);
             else dm_go<1, 128>(tile.rt, grid, lds, st, a);
         } else {
-            if (KS == 512) dm_go<2, 512>(tile.rt, grid, lds, st, a);
+            if (KS == 1024) dm_go<2, 1024>(tile.rt, grid, lds, st, a);
+            else if (KS == 512) dm_go<2, 512>(tile.rt, grid, lds, st, a);
             else if (KS == 256) dm_go<2, 256>(tile.rt, grid, lds, st, a);
             else dm_go<2, 128>(tile.rt, grid, lds, st, a);
         }
