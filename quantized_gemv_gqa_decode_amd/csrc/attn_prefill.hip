@@ -40,6 +40,7 @@ constexpr int AP_HD = 128;
 constexpr int AP_KT = 64;                  // keys per tile
 constexpr int AP_Q = 64;                   // queries per block
 constexpr int AP_VTS = AP_KT * 2 + 8;      // bytes per V^T row in LDS
+constexpr int AP_MAX_SPLITS = 64;          // key splits (their per-query weights fill the K tile's LDS)
 
 struct ApArgs {
     const float *q;                        // rotated queries [T][n_qh][128]
@@ -48,6 +49,11 @@ struct ApArgs {
     float *out;                            // [T][n_qh][128]
     int n_qh, n_kv, cap, pos0, T;
     float qscale;                          // softmax scale * log2(e)
+    // key splits (gridDim.z > 1): unnormalised partials [split][T][n_qh][128],
+    // their (max, sum) [split][T][n_qh][2], and one arrival counter per
+    // (query block, kv head), zero between launches
+    float *part, *part_ml;
+    unsigned *cnt;
 };
 
 __device__ __forceinline__ float ap_xmax(float x)
@@ -88,6 +94,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const ApArgs a)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int q4 = lane >> 4, c16 = lane & 15;
     const int g = blockIdx.y, t0 = blockIdx.x * PPB;
+    const int z = blockIdx.z, NS = gridDim.z;             // key split of this block, splits
 
     // this lane's query: the column of its S^T and O^T tiles
     const int qi = wave * 16 + c16;
@@ -99,6 +106,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const ApArgs a)
     const int tlast = (t0 + PPB < a.T ? t0 + PPB : a.T) - 1;
     const int kmax = a.pos0 + tlast;                      // the last key a query of the block sees
     const int ntiles = kmax / AP_KT + 1;
+    // this split's tiles [tz0, tz1) (empty for a split past the block's keys)
+    const int per = (ntiles + NS - 1) / NS;
+    const int tz0 = z * per < ntiles ? z * per : ntiles;
+    const int tz1 = tz0 + per < ntiles ? tz0 + per : ntiles;
 
     // the query as B operand of the 4 k-steps of S^T: dims 32j + 8 q4 + [0, 8)
     ap_bf16x8 qh[4], ql[4];
@@ -212,13 +223,13 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const ApArgs a)
     for (int dt = 0; dt < 8; ++dt) o[dt] = ap_f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
 
-    load_tile(0);
+    if (tz0 < tz1) load_tile(tz0);
 #pragma unroll 1
-    for (int tile = 0; tile < ntiles; ++tile) {
+    for (int tile = tz0; tile < tz1; ++tile) {
         __syncthreads();                                  // every wave is done with the previous tile
         store_tile();
         __syncthreads();
-        if (tile + 1 < ntiles) load_tile(tile + 1);
+        if (tile + 1 < tz1) load_tile(tile + 1);
         const int kb0 = tile * AP_KT;
 
         // S^T for the 4 subtiles of 16 keys: s[u][e] is key 16u + 4 q4 + e
@@ -296,20 +307,96 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const ApArgs a)
     // 16 dt + 4 q4 + [0, 4) of the lane's query)
     l = xor16_add(l);
     l = xor32_add(l);
-    if (!qvalid) return;
-    const float inv = 1.0f / l;
-    float *dst = a.out + ((int64_t)t * a.n_qh + h) * AP_HD + 4 * q4;
+    const int64_t qrow = (int64_t)t * a.n_qh + h;
+    if (NS == 1) {
+        if (!qvalid) return;
+        const float inv = 1.0f / l;
+        float *dst = a.out + qrow * AP_HD + 4 * q4;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<float4 *>(dst + dt * 16) =
-            make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+        for (int dt = 0; dt < 8; ++dt)
+            *reinterpret_cast<float4 *>(dst + dt * 16) =
+                make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+        return;
+    }
+
+    // key splits: publish this split's partial (device scope), count the
+    // block in; the last block of the (query block, kv head) combines
+    const int64_t prow = (int64_t)z * a.T * a.n_qh + qrow;
+    if (qvalid) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+            coh_store4(a.part, (int)(prow * AP_HD + dt * 16 + 4 * q4),
+                       make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]));
+        if (q4 == 0) {
+            coh_store(a.part_ml + prow * 2, m);
+            coh_store(a.part_ml + prow * 2 + 1, l);
+        }
+    }
+    __shared__ int last;
+    __builtin_amdgcn_s_waitcnt(0);                        // this thread's partial stores completed
+    __syncthreads();
+    if (tid == 0) {
+        unsigned *c = a.cnt + blockIdx.y * gridDim.x + blockIdx.x;
+        const unsigned old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = old == (unsigned)NS - 1;
+        if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last) return;
+
+    // weights of the splits per query, w_z = 2^(m_z - M) / sum_z l_z 2^(m_z - M),
+    // in LDS (the K tile's space; every wave is past its last use), then
+    // out = sum_z w_z o_z in split order
+    float *wz = reinterpret_cast<float *>(k_lds);         // [AP_Q][NS], NS <= AP_MAX_SPLITS
+    if (tid < AP_Q) {
+        const int tq = t0 + tid / REP, hq = g * REP + tid % REP;
+        if (tq < a.T) {
+            const int64_t r0 = (int64_t)tq * a.n_qh + hq, stride = (int64_t)a.T * a.n_qh;
+            float M = -INFINITY;
+            for (int zz = 0; zz < NS; ++zz) M = fmaxf(M, coh_load(a.part_ml + (zz * stride + r0) * 2));
+            float L = 0.f;
+            for (int zz = 0; zz < NS; ++zz) {
+                const float mz = coh_load(a.part_ml + (zz * stride + r0) * 2);
+                const float f = mz == -INFINITY ? 0.f : k2_exp2(mz - M);
+                wz[tid * NS + zz] = f;
+                L += f * coh_load(a.part_ml + (zz * stride + r0) * 2 + 1);
+            }
+            const float inv = 1.0f / L;
+            for (int zz = 0; zz < NS; ++zz) wz[tid * NS + zz] *= inv;
+        }
+    }
+    __syncthreads();
+    constexpr int DQ = AP_HD / 4;                         // float4 columns of a query
+    for (int it = tid; it < AP_Q * DQ; it += 256) {
+        const int qq = it / DQ, dq = it % DQ;
+        const int tq = t0 + qq / REP, hq = g * REP + qq % REP;
+        if (tq >= a.T) continue;
+        const int64_t r0 = (int64_t)tq * a.n_qh + hq, stride = (int64_t)a.T * a.n_qh;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int z0 = 0; z0 < NS; z0 += 8) {
+            float4 v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (z0 + i < NS) v[i] = coh_load4(a.part, (int)(((z0 + i) * stride + r0) * AP_HD + dq * 4));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (z0 + i >= NS) break;
+                const float f = wz[qq * NS + z0 + i];
+                acc.x += f * v[i].x;
+                acc.y += f * v[i].y;
+                acc.z += f * v[i].z;
+                acc.w += f * v[i].w;
+            }
+        }
+        *reinterpret_cast<float4 *>(a.out + r0 * AP_HD + dq * 4) = acc;
+    }
 }
 
 template <int KVDT>
-static int attn_prefill_rep(int rep, const ApArgs &a, hipStream_t st)
+static int attn_prefill_rep(int rep, const ApArgs &a, int ns, hipStream_t st)
 {
     const int ppb = AP_Q / rep;
-    const dim3 grid((a.T + ppb - 1) / ppb, a.n_kv);
+    const dim3 grid((a.T + ppb - 1) / ppb, a.n_kv, ns);
     switch (rep) {
     case 1: hipLaunchKernelGGL((attn_prefill_kernel<KVDT, 1>), grid, dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL((attn_prefill_kernel<KVDT, 2>), grid, dim3(256), 0, st, a); break;
@@ -321,13 +408,35 @@ static int attn_prefill_rep(int rep, const ApArgs &a, hipStream_t st)
     return K2_OK;
 }
 
+// Key splits: none while the query blocks alone give a block per compute
+// unit or the keys are few; else enough for ~2 blocks per compute unit, each
+// split at least 4 tiles (256 keys), at most AP_MAX_SPLITS and what the
+// workspace holds (max_splits).
+static int ap_splits(int T, int rep, int n_kv, int pos0, int max_splits)
+{
+    const int qb = (T + AP_Q / rep - 1) / (AP_Q / rep);
+    const int blocks = qb * n_kv;
+    const int ntiles = (pos0 + T - 1) / AP_KT + 1;
+    if (blocks >= 256 || ntiles < 8) return 1;
+    int ns = (512 + blocks - 1) / blocks;
+    ns = ns < ntiles / 4 ? ns : ntiles / 4;
+    ns = ns < AP_MAX_SPLITS ? ns : AP_MAX_SPLITS;
+    ns = ns < max_splits ? ns : max_splits;
+    return ns > 1 ? ns : 1;
+}
+
 int attn_prefill_launch(int kvdt, const float *qrot, float *out, const void *kc, const void *vc, const float *ks,
-                        const float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T, hipStream_t st)
+                        const float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T, float *part,
+                        float *part_ml, int max_splits, unsigned *cnt, hipStream_t st)
 {
     if (hd != AP_HD || T < 1 || n_kv < 1 || n_qh % n_kv) return K2_EUNSUPPORTED;
     if (kvdt != K2_BF16 && kvdt != K2_I8) return K2_EUNSUPPORTED;
     if (pos0 < 0 || (int64_t)pos0 + T > cap) return K2_ERANGE;
+    const int ns = (part && part_ml && cnt) ? ap_splits(T, n_qh / n_kv, n_kv, pos0, max_splits) : 1;
     ApArgs a{};
+    a.part = part;
+    a.part_ml = part_ml;
+    a.cnt = cnt;
     a.q = qrot;
     a.kc = kc;
     a.vc = vc;
@@ -340,7 +449,8 @@ int attn_prefill_launch(int kvdt, const float *qrot, float *out, const void *kc,
     a.pos0 = pos0;
     a.T = T;
     a.qscale = K2_LOG2E / sqrtf((float)hd);
-    return kvdt == K2_I8 ? attn_prefill_rep<K2_I8>(n_qh / n_kv, a, st) : attn_prefill_rep<K2_BF16>(n_qh / n_kv, a, st);
+    return kvdt == K2_I8 ? attn_prefill_rep<K2_I8>(n_qh / n_kv, a, ns, st)
+                         : attn_prefill_rep<K2_BF16>(n_qh / n_kv, a, ns, st);
 }
 
 }  // namespace k2

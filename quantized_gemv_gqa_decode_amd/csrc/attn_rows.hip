@@ -68,19 +68,21 @@ int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qr
     default: return K2_EUNSUPPORTED;
     }
     K2_CHECK_LAUNCH();
-    // long chunks of a bf16 / int8 cache (or medium ones on a short cache):
-    // every row's attention on the matrix cores, the K/V tiles shared by the
-    // rows of a block
+    // chunks of a bf16 / int8 cache with enough rows: every row's attention
+    // on the matrix cores, the K/V tiles shared by the rows of a block
     const bool mc = T >= ATTN_PREFILL_MIN_T ||
-                    (T >= ATTN_PREFILL_SHORT_T && (int64_t)pos0 + T <= ATTN_PREFILL_SHORT_LEN);
-    if (mc && (kvdt == K2_BF16 || kvdt == K2_I8))
-        return attn_prefill_launch(kvdt, qrot, out, kc, vc, ks, vs, n_qh, n_kv, hd, cap, pos0, T, st);
-    AttnArgs a{};
+                    (T >= ATTN_PREFILL_LONG_MIN_T && (int64_t)pos0 + T > ATTN_PREFILL_LONG_LEN);
     const size_t S = (size_t)attn_max_splits(n_kv, cap);
     char *p = (char *)ws;
-    a.part = (float *)p;
+    float *part = (float *)p;
     p += k2_align256((size_t)T * n_kv * S * rep * hd * 4);
-    a.part_ml = (float *)p;
+    float *part_ml = (float *)p;
+    if (mc && (kvdt == K2_BF16 || kvdt == K2_I8))
+        return attn_prefill_launch(kvdt, qrot, out, kc, vc, ks, vs, n_qh, n_kv, hd, cap, pos0, T, part, part_ml,
+                                   (int)S, cnt, st);
+    AttnArgs a{};
+    a.part = part;
+    a.part_ml = part_ml;
     a.head_cnt = cnt;
     a.q = qrot;
     a.kc = kc;

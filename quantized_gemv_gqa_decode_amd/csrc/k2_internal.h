@@ -104,20 +104,22 @@ int device_cus();
 // unless hd = 128 and n_qh / n_kv is 1, 2, 4 or 8.
 size_t attn_rows_ws_bytes(int n_qh, int n_kv, int hd, int cap, int T);
 size_t attn_rows_cnt_bytes(int n_kv, int T);
-// From this many rows on, attn_rows_launch runs the attention of a bf16 /
-// int8 cache through attn_prefill_launch (attn_prefill.hip): the causal
-// attention of rows pos0 .. pos0+T-1 (qrot [T][n_qh][128], already rotated,
-// K/V already appended) on the matrix cores, out [T][n_qh][128].  Shorter
-// chunks of at least ATTN_PREFILL_SHORT_T rows take it too while the cache
-// holds at most ATTN_PREFILL_SHORT_LEN positions: its blocks each stream every
-// key of their kv head, which beats the split per-row kernel there and loses
-// to it on long caches (3.7B shape, 16-row verification: 5.11 against 5.58
-// ms at 528 positions, 14.56 against 11.32 ms at 8208).
-constexpr int ATTN_PREFILL_MIN_T = 33;
-constexpr int ATTN_PREFILL_SHORT_T = 12;
-constexpr int ATTN_PREFILL_SHORT_LEN = 1024;
+// From ATTN_PREFILL_MIN_T rows on (from ATTN_PREFILL_LONG_MIN_T rows once
+// the cache holds more than ATTN_PREFILL_LONG_LEN positions), attn_rows_launch
+// runs the attention of a bf16 / int8 cache through attn_prefill_launch
+// (attn_prefill.hip): the causal attention of rows pos0 .. pos0+T-1 (qrot
+// [T][n_qh][128], already rotated, K/V already appended) on the matrix
+// cores, out [T][n_qh][128]; fewer rows take the split per-row kernel.
+// Measured on 3.7B-shaped verification rounds (matrix cores against the
+// per-row kernel): 2 rows 3.88 against 3.63 ms at 528 positions and 4.51
+// against 4.19 at 8192; 8 rows 4.10 against 3.89 at 528 and 5.05 against
+// 6.14 at 8192; 12-32 rows faster at every length measured.
+constexpr int ATTN_PREFILL_MIN_T = 12;
+constexpr int ATTN_PREFILL_LONG_MIN_T = 8;
+constexpr int ATTN_PREFILL_LONG_LEN = 1024;
 int attn_prefill_launch(int kvdt, const float *qrot, float *out, const void *kc, const void *vc, const float *ks,
-                        const float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T, hipStream_t st);
+                        const float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T, float *part,
+                        float *part_ml, int max_splits, unsigned *cnt, hipStream_t st);
 int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qrot, float *out, void *kc,
                      void *vc, float *ks, float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T,
                      void *ws, unsigned *cnt, hipStream_t st);

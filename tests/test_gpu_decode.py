@@ -431,12 +431,13 @@ def test_head128_prefill_long_prompt(kvdt):
 
 
 @pytest.mark.parametrize("kvdt", ["bf16", "i8"])
-def test_head128_prefill_chunks_of_32_past_1024(kvdt):
-    """Chunks of 32 rows over 1100 positions: up to position 1024 their
-    attention runs on the matrix cores (a short cache), past it through the
-    split per-row kernel; 1100 = 34 x 32 + 12."""
+@pytest.mark.parametrize("chunk", [10, 32])
+def test_head128_prefill_chunks_past_1024(kvdt, chunk):
+    """Chunks of 10 rows over 1100 positions take the split per-row attention
+    up to position 1024 and the matrix-core attention (with key splits) past
+    it; chunks of 32 take the matrix cores throughout (1100 = 34 x 32 + 12)."""
     cfg = HEAD128.replace(wdt="bf16", kvdt=kvdt, cap=1152)
-    _prefill_parity(cfg, 1100, 3, chunk=32)
+    _prefill_parity(cfg, 1100, 3, chunk=chunk)
 
 
 @pytest.mark.parametrize("kvdt", ["bf16", "i8"])
