@@ -54,7 +54,27 @@ struct ApArgs {
     // (query block, kv head), zero between launches
     float *part, *part_ml;
     unsigned *cnt;
+    // the output as bf16 hi / lo planes [T][n_qh * 128] instead of out (nullable)
+    uint16_t *oh, *ol;
 };
+
+// out[i .. i+3] = v, or its bf16 hi / lo planes
+__device__ __forceinline__ void ap_out4(const ApArgs &a, int64_t i, float4 v)
+{
+    if (a.oh) {
+        const float f[4] = {v.x, v.y, v.z, v.w};
+        uint16_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = f32_to_bf16_rne(f[e]);
+            l[e] = f32_to_bf16_rne(f[e] - bf16_to_f32(h[e]));
+        }
+        *reinterpret_cast<uint2 *>(a.oh + i) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+        *reinterpret_cast<uint2 *>(a.ol + i) = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+    } else {
+        *reinterpret_cast<float4 *>(a.out + i) = v;
+    }
+}
 
 __device__ __forceinline__ float ap_xmax(float x)
 {
@@ -311,11 +331,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const ApArgs a)
     if (NS == 1) {
         if (!qvalid) return;
         const float inv = 1.0f / l;
-        float *dst = a.out + qrow * AP_HD + 4 * q4;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
-            *reinterpret_cast<float4 *>(dst + dt * 16) =
-                make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+            ap_out4(a, qrow * AP_HD + 4 * q4 + dt * 16,
+                    make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv));
         return;
     }
 
@@ -388,7 +407,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const ApArgs a)
                 acc.w += f * v[i].w;
             }
         }
-        *reinterpret_cast<float4 *>(a.out + r0 * AP_HD + dq * 4) = acc;
+        ap_out4(a, r0 * AP_HD + dq * 4, acc);
     }
 }
 
@@ -427,13 +446,16 @@ static int ap_splits(int T, int rep, int n_kv, int pos0, int max_splits)
 
 int attn_prefill_launch(int kvdt, const float *qrot, float *out, const void *kc, const void *vc, const float *ks,
                         const float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T, float *part,
-                        float *part_ml, int max_splits, unsigned *cnt, hipStream_t st)
+                        float *part_ml, int max_splits, unsigned *cnt, uint16_t *oh, uint16_t *ol,
+                        hipStream_t st)
 {
     if (hd != AP_HD || T < 1 || n_kv < 1 || n_qh % n_kv) return K2_EUNSUPPORTED;
     if (kvdt != K2_BF16 && kvdt != K2_I8) return K2_EUNSUPPORTED;
     if (pos0 < 0 || (int64_t)pos0 + T > cap) return K2_ERANGE;
     const int ns = (part && part_ml && cnt) ? ap_splits(T, n_qh / n_kv, n_kv, pos0, max_splits) : 1;
     ApArgs a{};
+    a.oh = oh;
+    a.ol = ol;
     a.part = part;
     a.part_ml = part_ml;
     a.cnt = cnt;

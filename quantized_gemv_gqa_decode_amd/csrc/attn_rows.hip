@@ -41,8 +41,9 @@ size_t attn_rows_cnt_bytes(int n_kv, int T) { return k2_align256((size_t)T * n_k
 
 int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qrot, float *out, void *kc,
                      void *vc, float *ks, float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T,
-                     void *ws, unsigned *cnt, hipStream_t st)
+                     void *ws, unsigned *cnt, hipStream_t st, uint16_t *oh, uint16_t *ol, bool *planes)
 {
+    if (planes) *planes = false;
     if (hd != 128 || T < 1) return K2_EUNSUPPORTED;
     const int rep = n_qh / n_kv;
     if (rep != 1 && rep != 2 && rep != 4 && rep != 8) return K2_EUNSUPPORTED;
@@ -77,9 +78,12 @@ int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qr
     float *part = (float *)p;
     p += k2_align256((size_t)T * n_kv * S * rep * hd * 4);
     float *part_ml = (float *)p;
-    if (mc && (kvdt == K2_BF16 || kvdt == K2_I8))
-        return attn_prefill_launch(kvdt, qrot, out, kc, vc, ks, vs, n_qh, n_kv, hd, cap, pos0, T, part, part_ml,
-                                   (int)S, cnt, st);
+    if (mc && (kvdt == K2_BF16 || kvdt == K2_I8)) {
+        const int rc = attn_prefill_launch(kvdt, qrot, out, kc, vc, ks, vs, n_qh, n_kv, hd, cap, pos0, T, part,
+                                           part_ml, (int)S, cnt, oh, ol, st);
+        if (rc == K2_OK && planes && oh && ol) *planes = true;
+        return rc;
+    }
     AttnArgs a{};
     a.part = part;
     a.part_ml = part_ml;

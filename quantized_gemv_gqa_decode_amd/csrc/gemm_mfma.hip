@@ -65,6 +65,7 @@ struct GemmArgs {
     const void *Ws;            // fp8: float [N]; MXFP4: uint8 [N][K/32]; Q4S: float [N][K/64]
     const uint16_t *xh, *xl;   // [TP][K] bf16 planes (rows >= T zero)
     float *y;                  // [T][N] (SwiGLU: [T][N/2])
+    uint16_t *yh, *yl;         // SwiGLU into bf16 hi / lo planes [T][N/2] instead of y (nullable)
     float *part;               // [S][TP][N] when S > 1
     int N, K, T, TP, S, KS, epi, rb, tb, xcd;
 };
@@ -93,6 +94,18 @@ __global__ __launch_bounds__(256) void gm_split_kernel(const float *x, uint16_t 
         lv.y = l[2] | ((uint32_t)l[3] << 16);
         *reinterpret_cast<uint2 *>(xh + e) = hv;
         *reinterpret_cast<uint2 *>(xl + e) = lv;
+    }
+}
+
+// y, or its bf16 hi / lo planes, at element i
+__device__ __forceinline__ void gm_out(const GemmArgs &a, int64_t i, float v)
+{
+    if (a.yh) {
+        const uint16_t h = f32_to_bf16_rne(v);
+        a.yh[i] = h;
+        a.yl[i] = f32_to_bf16_rne(v - bf16_to_f32(h));
+    } else {
+        a.y[i] = v;
     }
 }
 
@@ -390,7 +403,7 @@ __global__ __launch_bounds__(256, BT <= 64 ? 2 : 1) void gm_kernel(const GemmArg
                         const int t = t0 + tt * 16 + 4 * q + e;
                         if (t >= a.T) continue;
                         const float g = acc[rt][tt][e], u = acc[rt + 2][tt][e];
-                        a.y[(int64_t)t * half + n] = g / (1.0f + expf(-g)) * u;
+                        gm_out(a, (int64_t)t * half + n, g / (1.0f + expf(-g)) * u);
                     }
             }
             return;
@@ -442,7 +455,21 @@ __global__ __launch_bounds__(256, BT <= 64 ? 2 : 1) void gm_kernel(const GemmArg
                     const float g = acc[rt][tt][e], u = acc[rt + 2][tt][e];
                     o[e] = g / (1.0f + expf(-g)) * u;
                 }
-                *reinterpret_cast<float4 *>(a.y + (int64_t)t * half + n0) = make_float4(o[0], o[1], o[2], o[3]);
+                const int64_t i0 = (int64_t)t * half + n0;
+                if (a.yh) {
+                    uint16_t h[4], l[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        h[e] = f32_to_bf16_rne(o[e]);
+                        l[e] = f32_to_bf16_rne(o[e] - bf16_to_f32(h[e]));
+                    }
+                    *reinterpret_cast<uint2 *>(a.yh + i0) =
+                        make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+                    *reinterpret_cast<uint2 *>(a.yl + i0) =
+                        make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+                } else {
+                    *reinterpret_cast<float4 *>(a.y + i0) = make_float4(o[0], o[1], o[2], o[3]);
+                }
             }
         }
         return;
@@ -471,7 +498,7 @@ __global__ __launch_bounds__(256, BT <= 64 ? 2 : 1) void gm_kernel(const GemmArg
 
 // y[t][n] (+)= the sum over splits in split order (SwiGLU: rows n and n + N/2)
 __global__ __launch_bounds__(256) void gm_reduce_kernel(const float *part, int S, int TP, int N, int epi,
-                                                        float *y)
+                                                        float *y, uint16_t *yh, uint16_t *yl)
 {
     const int t = blockIdx.y;
     const int n = blockIdx.x * 256 + threadIdx.x;
@@ -483,10 +510,21 @@ __global__ __launch_bounds__(256) void gm_reduce_kernel(const float *part, int S
         s += p[n];
         if (epi == DM_EPI_SWIGLU) u += p[n + n_out];
     }
-    float *dst = y + (int64_t)t * n_out + n;
-    if (epi == DM_EPI_SWIGLU) *dst = s / (1.0f + expf(-s)) * u;
-    else if (epi == DM_EPI_ADD) *dst += s;
-    else *dst = s;
+    const int64_t i = (int64_t)t * n_out + n;
+    if (epi == DM_EPI_SWIGLU) {
+        const float v = s / (1.0f + expf(-s)) * u;
+        if (yh) {
+            const uint16_t h = f32_to_bf16_rne(v);
+            yh[i] = h;
+            yl[i] = f32_to_bf16_rne(v - bf16_to_f32(h));
+        } else {
+            y[i] = v;
+        }
+    } else if (epi == DM_EPI_ADD) {
+        y[i] += s;
+    } else {
+        y[i] = s;
+    }
 }
 
 // tokens per block: 128 for long chunks (measured on the 512-token prompt of
@@ -548,26 +586,25 @@ static void gm_launch(int BT, int nblk, size_t lds, hipStream_t st, const GemmAr
     }
 }
 
-int gemm_mfma(int wdt, const void *W, const void *Ws, const float *x, float *y, int N, int K, int T, int epi,
-              void *ws, hipStream_t st)
+// The product from activation planes xh / xl [>= TP rows][K] (rows past T
+// may hold anything: a token's outputs depend on its own row only, and rows
+// past T are neither stored nor summed).  ws: gemm_mfma_ws_bytes (its
+// plane part unused here).
+static int gm_core(int wdt, const void *W, const void *Ws, const uint16_t *xh, const uint16_t *xl, float *y,
+                   uint16_t *yh, uint16_t *yl, int N, int K, int T, int epi, void *ws, hipStream_t st)
 {
-    if (!gemm_mfma_ok(N, K, epi) || T < 1 || T > GM_MAX_T || !ws) return K2_EUNSUPPORTED;
-    if (wdt != K2_BF16 && wdt != K2_FP8E4M3 && wdt != K2_MXFP4 && wdt != K2_Q4S) return K2_EUNSUPPORTED;
-    if (wdt != K2_BF16 && !Ws) return K2_EINVAL;
     GemmArgs a{};
     const int BT = gm_bt(T, wdt), TP = gm_tp(T, wdt);
     const int S = gm_splits(N, K, T, epi, wdt);
-    char *p = (char *)ws;
-    uint16_t *xh = (uint16_t *)p;
-    p += k2_align256((size_t)TP * K * 2);
-    uint16_t *xl = (uint16_t *)p;
-    p += k2_align256((size_t)TP * K * 2);
+    char *p = (char *)ws + 2 * k2_align256((size_t)TP * K * 2);
     a.W = W;
     a.Ws = Ws;
     a.xh = xh;
     a.xl = xl;
     a.part = S > 1 ? (float *)p : nullptr;
     a.y = y;
+    a.yh = yh;
+    a.yl = yl;
     a.N = N;
     a.K = K;
     a.T = T;
@@ -579,12 +616,6 @@ int gemm_mfma(int wdt, const void *W, const void *Ws, const float *x, float *y, 
     a.tb = TP / BT;
     const int nblk = a.rb * a.tb * S;
     a.xcd = nblk % 8 == 0;
-
-    const int64_t n4 = (int64_t)TP * K / 4;
-    int sb = (int)((n4 + 255) / 256);
-    sb = sb < 2048 ? sb : 2048;
-    hipLaunchKernelGGL(gm_split_kernel, dim3(sb), dim3(256), 0, st, x, xh, xl, T, TP, K);
-    K2_CHECK_LAUNCH();
     const size_t lds = 2 * 2 * (size_t)BT * GM_ROWB;
     switch (wdt) {
     case K2_BF16: gm_launch<K2_BF16>(BT, nblk, lds, st, a); break;
@@ -596,10 +627,45 @@ int gemm_mfma(int wdt, const void *W, const void *Ws, const float *x, float *y, 
     if (S > 1) {
         const int n_out = epi == DM_EPI_SWIGLU ? N / 2 : N;
         hipLaunchKernelGGL(gm_reduce_kernel, dim3((n_out + 255) / 256, T), dim3(256), 0, st, a.part, S, TP, N,
-                           epi, y);
+                           epi, y, yh, yl);
         K2_CHECK_LAUNCH();
     }
     return K2_OK;
 }
+
+static int gm_check(int wdt, const void *Ws, int N, int K, int T, int epi, const void *ws)
+{
+    if (!gemm_mfma_ok(N, K, epi) || T < 1 || T > GM_MAX_T || !ws) return K2_EUNSUPPORTED;
+    if (wdt != K2_BF16 && wdt != K2_FP8E4M3 && wdt != K2_MXFP4 && wdt != K2_Q4S) return K2_EUNSUPPORTED;
+    if (wdt != K2_BF16 && !Ws) return K2_EINVAL;
+    return K2_OK;
+}
+
+int gemm_mfma(int wdt, const void *W, const void *Ws, const float *x, float *y, int N, int K, int T, int epi,
+              void *ws, hipStream_t st)
+{
+    int rc = gm_check(wdt, Ws, N, K, T, epi, ws);
+    if (rc) return rc;
+    const int TP = gm_tp(T, wdt);
+    uint16_t *xh = (uint16_t *)ws;
+    uint16_t *xl = (uint16_t *)((char *)ws + k2_align256((size_t)TP * K * 2));
+    const int64_t n4 = (int64_t)TP * K / 4;
+    int sb = (int)((n4 + 255) / 256);
+    sb = sb < 2048 ? sb : 2048;
+    hipLaunchKernelGGL(gm_split_kernel, dim3(sb), dim3(256), 0, st, x, xh, xl, T, TP, K);
+    K2_CHECK_LAUNCH();
+    return gm_core(wdt, W, Ws, xh, xl, y, nullptr, nullptr, N, K, T, epi, ws, st);
+}
+
+int gemm_mfma_planes(int wdt, const void *W, const void *Ws, const uint16_t *xh, const uint16_t *xl, float *y,
+                     uint16_t *yh, uint16_t *yl, int N, int K, int T, int epi, void *ws, hipStream_t st)
+{
+    int rc = gm_check(wdt, Ws, N, K, T, epi, ws);
+    if (rc) return rc;
+    if (!xh || !xl || ((yh || yl) && (epi != DM_EPI_SWIGLU || !yh || !yl))) return K2_EINVAL;
+    return gm_core(wdt, W, Ws, xh, xl, y, yh, yl, N, K, T, epi, ws, st);
+}
+
+int gemm_mfma_rows(int T, int wdt) { return gm_tp(T, wdt); }
 
 }  // namespace k2

@@ -117,12 +117,22 @@ size_t attn_rows_cnt_bytes(int n_kv, int T);
 constexpr int ATTN_PREFILL_MIN_T = 12;
 constexpr int ATTN_PREFILL_LONG_MIN_T = 8;
 constexpr int ATTN_PREFILL_LONG_LEN = 1024;
+// part / part_ml / cnt (nullable): room for max_splits key splits of the T
+// rows ([split][T][n_qh][hd] and [split][T][n_qh][2] floats) and one zeroed
+// counter per (64-query block, kv head), left zero; with them a chunk whose
+// query blocks leave compute units idle also splits its keys.  oh / ol
+// (nullable): the output as bf16 hi / lo planes [T][n_qh hd] instead of out.
 int attn_prefill_launch(int kvdt, const float *qrot, float *out, const void *kc, const void *vc, const float *ks,
                         const float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T, float *part,
-                        float *part_ml, int max_splits, unsigned *cnt, hipStream_t st);
+                        float *part_ml, int max_splits, unsigned *cnt, uint16_t *oh, uint16_t *ol,
+                        hipStream_t st);
+// oh / ol (nullable): where the matrix-core attention runs, its output goes
+// to these bf16 hi / lo planes instead of out, and *planes (nullable) says
+// whether it did.
 int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qrot, float *out, void *kc,
                      void *vc, float *ks, float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T,
-                     void *ws, unsigned *cnt, hipStream_t st);
+                     void *ws, unsigned *cnt, hipStream_t st, uint16_t *oh = nullptr, uint16_t *ol = nullptr,
+                     bool *planes = nullptr);
 
 // Sync words of the attention + O launch: the O-block counter on a line of
 // its own, and 16 copies (one 256-byte line each) of the per-kv-head ready
@@ -159,6 +169,10 @@ int embed_launch(int embdt, const void *E, int H, int vocab, int token, const in
 // GroupedRMSNorm of `rows` rows (one block per row and group)
 int rmsnorm_rows_launch(const float *x, const float *gamma, float *y, int rows, int hidden, int groups,
                         float eps, hipStream_t st);
+// the same norm written as bf16 hi / lo planes [rows][hidden] (hi = bf16(y),
+// lo = bf16(y - hi)): the input form of gemm_mfma_planes
+int rmsnorm_rows_planes_launch(const float *x, const float *gamma, uint16_t *yh, uint16_t *yl, int rows,
+                               int hidden, int groups, float eps, hipStream_t st);
 int argmax_final_launch(const ArgmaxArgs &am, int n_blocks, hipStream_t st);
 // Advance a device position by one when it lies in [0, cap) (one thread).
 int pos_advance_launch(int32_t *d_pos, int cap, hipStream_t st);
@@ -216,5 +230,12 @@ bool gemm_mfma_ok(int N, int K, int epi);
 size_t gemm_mfma_ws_bytes(int wdt, int N, int K, int T, int epi);
 int gemm_mfma(int wdt, const void *W, const void *Ws, const float *x, float *y, int N, int K, int T, int epi,
               void *ws, hipStream_t st);
+// The same product with the activations given as bf16 hi / lo planes
+// [gemm_mfma_rows(T, wdt)][K] (rows past T may hold anything), and for
+// SwiGLU optionally its output written as planes yh / yl [T][N/2] instead
+// of y: the forms the producers of a prefill chunk's activations write.
+int gemm_mfma_planes(int wdt, const void *W, const void *Ws, const uint16_t *xh, const uint16_t *xl, float *y,
+                     uint16_t *yh, uint16_t *yl, int N, int K, int T, int epi, void *ws, hipStream_t st);
+int gemm_mfma_rows(int T, int wdt);
 
 }  // namespace k2

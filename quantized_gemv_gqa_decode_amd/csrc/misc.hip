@@ -30,6 +30,34 @@ __global__ __launch_bounds__(K2_BLOCK) void rmsnorm_grouped_kernel(const float *
     for (int i = threadIdx.x; i < gs; i += K2_BLOCK) yr[i] = xr[i] * r * gm[i];
 }
 
+// The same rows written as bf16 hi / lo planes (hi = bf16(y), lo = bf16(y -
+// hi)), the form the matrix-core products of a prefill chunk read.
+__global__ __launch_bounds__(K2_BLOCK) void rmsnorm_planes_kernel(const float *x, const float *gamma,
+                                                                  uint16_t *yh, uint16_t *yl, int hidden,
+                                                                  int groups, float eps)
+{
+    __shared__ float red[K2_WAVES_PER_BLOCK];
+    const int row = blockIdx.x / groups, g = blockIdx.x % groups, gs = hidden / groups;
+    const float *xr = x + (int64_t)row * hidden + (int64_t)g * gs;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < gs; i += K2_BLOCK) ss += xr[i] * xr[i];
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < K2_WAVES_PER_BLOCK; ++w) t += red[w];
+    const float r = 1.0f / sqrtf(t / (float)gs + eps);
+    const int64_t o = (int64_t)row * hidden + (int64_t)g * gs;
+    const float *gm = gamma + (int64_t)g * gs;
+    for (int i = threadIdx.x; i < gs; i += K2_BLOCK) {
+        const float v = xr[i] * r * gm[i];
+        const uint16_t h = f32_to_bf16_rne(v);
+        yh[o + i] = h;
+        yl[o + i] = f32_to_bf16_rne(v - bf16_to_f32(h));
+    }
+}
+
 // ------------------------------------------------------------------- RoPE --
 // cos/sin of pos * theta^(-2i/hd), computed in fp64 and stored as fp32.
 __global__ void rope_table_kernel(float *cs, int cap, int hd, double theta)
@@ -284,6 +312,15 @@ int k2::rmsnorm_rows_launch(const float *x, const float *gamma, float *y, int ro
                             int groups, float eps, hipStream_t st)
 {
     hipLaunchKernelGGL(rmsnorm_grouped_kernel, dim3(rows * groups), dim3(K2_BLOCK), 0, st, x, gamma, y,
+                       hidden, groups, eps);
+    K2_CHECK_LAUNCH();
+    return K2_OK;
+}
+
+int k2::rmsnorm_rows_planes_launch(const float *x, const float *gamma, uint16_t *yh, uint16_t *yl, int rows,
+                                   int hidden, int groups, float eps, hipStream_t st)
+{
+    hipLaunchKernelGGL(rmsnorm_planes_kernel, dim3(rows * groups), dim3(K2_BLOCK), 0, st, x, gamma, yh, yl,
                        hidden, groups, eps);
     K2_CHECK_LAUNCH();
     return K2_OK;

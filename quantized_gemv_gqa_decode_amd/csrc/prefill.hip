@@ -50,6 +50,7 @@ __global__ void embed_rows_kernel(const PfTokens tk, int embdt, const void *E, i
 
 struct PrefillWs {
     float *h, *x, *qkv, *o, *act, *part, *qrot, *lm_part, *logits, *ar_v;
+    uint16_t *xh, *xl, *ah, *al;   // bf16 hi / lo planes: norm / attention outputs, SwiGLU output
     int *ar_i;
     void *attn, *rows, *am;
     unsigned *rows_cnt, *dm_cnt;
@@ -161,6 +162,14 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base, boo
     char *act = take((size_t)T * c->inter * 4);
     char *part = take(pf_part_bytes(c, T));
     char *qrot = take((size_t)T * qd * 4);
+    // activation planes for the token-blocked products: every row a token
+    // block may read (T rounded up to 128)
+    const size_t prow = (size_t)(T + 127) / 128 * 128;
+    const size_t xw = (size_t)c->hidden > qd ? (size_t)c->hidden : qd;
+    char *xh = take(prow * xw * 2);
+    char *xl = take(prow * xw * 2);
+    char *ah = take(prow * (size_t)c->inter * 2);
+    char *al = take(prow * (size_t)c->inter * 2);
     char *lm_part = verify ? take(c->wdt == K2_BF16 ? dense_mfma_ws_bytes(c->vocab, c->hidden, T)
                                                     : gemm_mfma_ws_bytes(c->wdt, c->vocab, c->hidden, T, DM_EPI_PLAIN))
                            : nullptr;
@@ -175,6 +184,10 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base, boo
         w->rows = rows;
         w->rows_cnt = (unsigned *)rows_cnt;
         w->qrot = (float *)qrot;
+        w->xh = (uint16_t *)xh;
+        w->xl = (uint16_t *)xl;
+        w->ah = (uint16_t *)ah;
+        w->al = (uint16_t *)al;
         w->h = (float *)h;
         w->x = (float *)x;
         w->qkv = (float *)qkv;
@@ -263,17 +276,32 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
     at.cap = c->cap;
     at.scale = 1.0f / sqrtf((float)hd);
 
+    // Token-blocked products (above 32 bf16 rows, and every quantized
+    // format) read their activations as bf16 hi / lo planes: the row norms,
+    // the matrix-core attention and the SwiGLU epilogue write them directly,
+    // so no split launch runs before those products.
+    const bool planes = !pf_dense(c->wdt, T);
     for (int l = 0; l < c->n_layers; ++l) {
         const k2_layer *L = &m->layers[l];
-        if ((rc = rmsnorm_rows_launch(w.h, L->g_in, w.x, T, H, c->groups, c->eps, st))) return rc;
-        if ((rc = pf_proj(c->wdt, L->qkv, L->qkv_s, w.x, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, w.dm_cnt, st)))
-            return rc;
+        if (planes) {
+            if ((rc = rmsnorm_rows_planes_launch(w.h, L->g_in, w.xh, w.xl, T, H, c->groups, c->eps, st))) return rc;
+            if ((rc = gemm_mfma_planes(c->wdt, L->qkv, L->qkv_s, w.xh, w.xl, w.qkv, nullptr, nullptr, qkv_rows, H,
+                                       T, DM_EPI_PLAIN, w.part, st)))
+                return rc;
+        } else {
+            if ((rc = rmsnorm_rows_launch(w.h, L->g_in, w.x, T, H, c->groups, c->eps, st))) return rc;
+            if ((rc = pf_proj(c->wdt, L->qkv, L->qkv_s, w.x, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, w.dm_cnt,
+                              st)))
+                return rc;
+        }
         at.kc = L->kc;
         at.vc = L->vc;
         at.ks = L->ks;
         at.vs = L->vs;
+        bool o_planes = false;                       // the attention wrote its output as planes (w.xh / w.xl)
         rc = attn_rows_launch(c->kvdt, w.qkv, m->rope, w.qrot, w.o, L->kc, L->vc, L->ks, L->vs, c->n_qh,
-                              c->n_kv, hd, c->cap, pos0, T, w.rows, w.rows_cnt, st);
+                              c->n_kv, hd, c->cap, pos0, T, w.rows, w.rows_cnt, st, planes ? w.xh : nullptr,
+                              planes ? w.xl : nullptr, &o_planes);
         if (rc && rc != K2_EUNSUPPORTED) return rc;
         const bool per_position = rc == K2_EUNSUPPORTED;
         for (int t = 0; per_position && t < T; ++t) {
@@ -284,12 +312,29 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
             at.S = attn_splits(c->n_kv, at.len, &at.chunk);
             if ((rc = attn_launch(c->kvdt, hd, rep, true, at, st))) return rc;
         }
-        if ((rc = pf_proj(c->wdt, L->o, L->o_s, w.o, w.h, H, qd, T, DM_EPI_ADD, w.part, w.dm_cnt, st))) return rc;
-        if ((rc = rmsnorm_rows_launch(w.h, L->g_post, w.x, T, H, c->groups, c->eps, st))) return rc;
-        if ((rc = pf_proj(c->wdt, L->gu, L->gu_s, w.x, w.act, 2 * I, H, T, DM_EPI_SWIGLU, w.part, w.dm_cnt, st)))
-            return rc;
-        if ((rc = pf_proj(c->wdt, L->down, L->down_s, w.act, w.h, H, I, T, DM_EPI_ADD, w.part, w.dm_cnt, st)))
-            return rc;
+        if (o_planes)
+            rc = gemm_mfma_planes(c->wdt, L->o, L->o_s, w.xh, w.xl, w.h, nullptr, nullptr, H, qd, T, DM_EPI_ADD,
+                                  w.part, st);
+        else
+            rc = pf_proj(c->wdt, L->o, L->o_s, w.o, w.h, H, qd, T, DM_EPI_ADD, w.part, w.dm_cnt, st);
+        if (rc) return rc;
+        if (planes) {
+            if ((rc = rmsnorm_rows_planes_launch(w.h, L->g_post, w.xh, w.xl, T, H, c->groups, c->eps, st)))
+                return rc;
+            if ((rc = gemm_mfma_planes(c->wdt, L->gu, L->gu_s, w.xh, w.xl, nullptr, w.ah, w.al, 2 * I, H, T,
+                                       DM_EPI_SWIGLU, w.part, st)))
+                return rc;
+            if ((rc = gemm_mfma_planes(c->wdt, L->down, L->down_s, w.ah, w.al, w.h, nullptr, nullptr, H, I, T,
+                                       DM_EPI_ADD, w.part, st)))
+                return rc;
+        } else {
+            if ((rc = rmsnorm_rows_launch(w.h, L->g_post, w.x, T, H, c->groups, c->eps, st))) return rc;
+            if ((rc = pf_proj(c->wdt, L->gu, L->gu_s, w.x, w.act, 2 * I, H, T, DM_EPI_SWIGLU, w.part, w.dm_cnt,
+                              st)))
+                return rc;
+            if ((rc = pf_proj(c->wdt, L->down, L->down_s, w.act, w.h, H, I, T, DM_EPI_ADD, w.part, w.dm_cnt, st)))
+                return rc;
+        }
     }
 
     if (verify) {
