@@ -21,6 +21,13 @@
 //     order (the same order, so the same result) and applies the epilogue.
 //     That saves the second launch, whose gap and first-byte latency are
 //     most of its cost at these sizes.
+// Up to 16 tokens with K a multiple of 512 the weights take another route
+// (dense_mfma_t_kernel): the operand layout puts 16 rows in every load
+// instruction (64 bytes of each), which streams at ~3.6 TB/s where one row's
+// contiguous 1 KiB per instruction streams at ~5.2 (same footprint, same
+// loads in flight).  So each wave loads its 16 rows x 512 columns as 16 such
+// row slices into registers and moves them into the operand layout through
+// a 4 KiB LDS buffer, a quarter of the columns at a time.
 // MFMA operand layout (16x16x32 bf16): lane l holds A row l % 16 and B column
 // l % 16, elements k = 8 (l / 16) + [0, 8); D holds column l % 16, rows
 // 4 (l / 16) + [0, 4).
@@ -52,6 +59,99 @@ struct DenseArgs {
 
 __host__ __device__ constexpr int dm_lds_bytes(int tp, int ks) { return 2 * tp * (ks + 8) * 2; }
 
+// Stage rows [0, NROW) of the activation slice x[.][k0, k0 + KS) in LDS as
+// bf16 hi / lo planes of row stride RS (rows >= T are 0); every load is
+// issued before any is converted.
+template <int NROW, int KS, int RS>
+__device__ __forceinline__ void dm_stage_x(const DenseArgs &a, uint16_t *xh, uint16_t *xl, int k0, int tid)
+{
+    constexpr int NG = NROW * KS / 4 / 256;       // activation float4s per thread
+    float4 xv[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int i = g * 256 + tid, t = i / (KS / 4), k = (i % (KS / 4)) * 4;
+        xv[g] = t < a.T ? *reinterpret_cast<const float4 *>(a.x + (int64_t)t * a.K + k0 + k)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int i = g * 256 + tid, t = i / (KS / 4), k = (i % (KS / 4)) * 4;
+        const float f[4] = {xv[g].x, xv[g].y, xv[g].z, xv[g].w};
+        uint16_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = f32_to_bf16_rne(f[e]);
+            l[e] = f32_to_bf16_rne(f[e] - bf16_to_f32(h[e]));
+        }
+        uint2 hv, lv;
+        hv.x = h[0] | ((uint32_t)h[1] << 16); hv.y = h[2] | ((uint32_t)h[3] << 16);
+        lv.x = l[0] | ((uint32_t)l[1] << 16); lv.y = l[2] | ((uint32_t)l[3] << 16);
+        *reinterpret_cast<uint2 *>(xh + t * RS + k) = hv;
+        *reinterpret_cast<uint2 *>(xl + t * RS + k) = lv;
+    }
+}
+
+// After a block has stored its partials (at device scope): count its
+// arrival; the last block of its group sums the group's partials in split
+// order and applies the epilogue.  Row block b is a group alone, or for
+// SwiGLU gate block b with up block b + rb / 2 (both counted on counter b).
+template <int ROWS, int TP>
+__device__ __forceinline__ void dm_reduce_last(const DenseArgs &a, int tid)
+{
+    __shared__ int last;
+    const int rb = gridDim.x, splits = gridDim.y;
+    const bool pair = a.epi == DM_EPI_SWIGLU;
+    const int grp = pair ? blockIdx.x % (rb / 2) : blockIdx.x;
+    const unsigned arrivals = (unsigned)(pair ? 2 * splits : splits);
+    __builtin_amdgcn_s_waitcnt(0);                // this thread's partial stores completed
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned old = __hip_atomic_fetch_add(a.cnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = old == arrivals - 1;
+        if (last) __hip_atomic_store(a.cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last) return;
+
+    // the group's outputs, each summed over the splits in split order: a
+    // thread owns 4 consecutive outputs (gate rows for SwiGLU) of every
+    // TSTEP-th token and loads 8 splits' partials before adding them
+    constexpr int QUADS = ROWS / 4, TSTEP = 256 / QUADS;
+    const int n_out = pair ? a.N / 2 : a.N;
+    const int n = grp * ROWS + (tid % QUADS) * 4;
+    if (n >= n_out) return;
+    constexpr int B8 = 8;
+    for (int t = tid / QUADS; t < a.T; t += TSTEP) {
+        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f), up = sum;
+        for (int s0 = 0; s0 < splits; s0 += B8) {
+            float4 v[B8], u[B8];
+#pragma unroll
+            for (int i = 0; i < B8; ++i) {
+                if (s0 + i >= splits) break;
+                const int o = (int)(((int64_t)(s0 + i) * TP + t) * a.N + n);
+                v[i] = coh_load4(a.part, o);
+                if (pair) u[i] = coh_load4(a.part, o + n_out);
+            }
+#pragma unroll
+            for (int i = 0; i < B8; ++i) {
+                if (s0 + i >= splits) break;
+                sum.x += v[i].x; sum.y += v[i].y; sum.z += v[i].z; sum.w += v[i].w;
+                if (pair) { up.x += u[i].x; up.y += u[i].y; up.z += u[i].z; up.w += u[i].w; }
+            }
+        }
+        float4 *dst = reinterpret_cast<float4 *>(a.y + (int64_t)t * n_out + n);
+        if (pair) {
+            *dst = make_float4(sum.x / (1.0f + expf(-sum.x)) * up.x, sum.y / (1.0f + expf(-sum.y)) * up.y,
+                               sum.z / (1.0f + expf(-sum.z)) * up.z, sum.w / (1.0f + expf(-sum.w)) * up.w);
+        } else if (a.epi == DM_EPI_ADD) {
+            const float4 r = *dst;
+            *dst = make_float4(r.x + sum.x, r.y + sum.y, r.z + sum.z, r.w + sum.w);
+        } else {
+            *dst = sum;
+        }
+    }
+}
+
 template <int NTT, int KS, int RT>
 __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
 {
@@ -59,7 +159,6 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
     constexpr int TP = 16 * NTT;
     constexpr int RS = KS + 8;                    // LDS row stride (bf16): 16 B of pad per row
     constexpr int NCH = KS / DM_KC;               // chunks per split
-    constexpr int NG = TP * KS / 4 / 256;         // activation float4s per thread
     extern __shared__ float4 lds4[];
     uint16_t *xh = reinterpret_cast<uint16_t *>(lds4);
     uint16_t *xl = xh + TP * RS;
@@ -91,31 +190,7 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
     dm_bf16x8 wc[RT][4];
     load_chunk(0, wc);                            // weights first: their latency covers the staging
 
-    // stage the activation slice as bf16 hi / lo planes (tokens >= T are 0):
-    // every load is issued before any is converted
-    float4 xv[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const int i = g * 256 + tid, t = i / (KS / 4), k = (i % (KS / 4)) * 4;
-        xv[g] = t < a.T ? *reinterpret_cast<const float4 *>(a.x + (int64_t)t * a.K + k0 + k)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const int i = g * 256 + tid, t = i / (KS / 4), k = (i % (KS / 4)) * 4;
-        const float f[4] = {xv[g].x, xv[g].y, xv[g].z, xv[g].w};
-        uint16_t h[4], l[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            h[e] = f32_to_bf16_rne(f[e]);
-            l[e] = f32_to_bf16_rne(f[e] - bf16_to_f32(h[e]));
-        }
-        uint2 hv, lv;
-        hv.x = h[0] | ((uint32_t)h[1] << 16); hv.y = h[2] | ((uint32_t)h[3] << 16);
-        lv.x = l[0] | ((uint32_t)l[1] << 16); lv.y = l[2] | ((uint32_t)l[3] << 16);
-        *reinterpret_cast<uint2 *>(xh + t * RS + k) = hv;
-        *reinterpret_cast<uint2 *>(xl + t * RS + k) = lv;
-    }
+    dm_stage_x<TP, KS, RS>(a, xh, xl, k0, tid);   // the activation slice as bf16 hi / lo planes
     __syncthreads();
 
     dm_f32x4 acc[RT][NTT];
@@ -171,61 +246,80 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
         }
     }
     if (!fuse) return;
+    dm_reduce_last<ROWS, TP>(a, tid);
+}
 
-    // arrival: row block b alone, or SwiGLU gate block b with up block
-    // b + rb / 2 (both counted on counter b)
-    __shared__ int last;
-    const int rb = gridDim.x, splits = gridDim.y;
-    const bool pair = a.epi == DM_EPI_SWIGLU;
-    const int grp = pair ? blockIdx.x % (rb / 2) : blockIdx.x;
-    const unsigned arrivals = (unsigned)(pair ? 2 * splits : splits);
-    __builtin_amdgcn_s_waitcnt(0);                // this thread's partial stores completed
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned old = __hip_atomic_fetch_add(a.cnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = old == arrivals - 1;
-        if (last) __hip_atomic_store(a.cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!last) return;
+// Up to 16 tokens, K % 512 == 0: a block of 4 waves owns 64 rows and one
+// 512-column split; wave w loads rows 16w .. 16w+15 one contiguous 1 KiB row
+// slice per instruction (lane l: the row's 16-byte chunk l), then for each
+// quarter p of the columns the lanes holding them (lanes 16p .. 16p+15)
+// write their 16 rows into the wave's LDS buffer and the MFMAs read it back
+// in the operand layout.  In the buffer, slot (c + r) % 16 of row r holds
+// the quarter's chunk c, so that both the writes and the operand reads of
+// 16 rows hit 16 different bank groups.  TM activation rows are staged (the
+// operand's other token columns are zero).
+constexpr int DT_KS = 512;
+constexpr int DT_ROWS = 64;
+__host__ __device__ constexpr int dt_lds_bytes(int tm) { return 2 * tm * (DT_KS + 8) * 2 + DM_WAVES * 4096; }
 
-    // the group's outputs, each summed over the splits in split order: a
-    // thread owns 4 consecutive outputs (gate rows for SwiGLU) of every
-    // TSTEP-th token and loads 8 splits' partials before adding them
-    constexpr int QUADS = ROWS / 4, TSTEP = 256 / QUADS;
-    const int n_out = pair ? a.N / 2 : a.N;
-    const int n = grp * ROWS + (tid % QUADS) * 4;
-    if (n >= n_out) return;
-    constexpr int B8 = 8;
-    for (int t = tid / QUADS; t < a.T; t += TSTEP) {
-        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f), up = sum;
-        for (int s0 = 0; s0 < splits; s0 += B8) {
-            float4 v[B8], u[B8];
+template <int TM>
+__global__ __launch_bounds__(256) void dense_mfma_t_kernel(const DenseArgs a)
+{
+    constexpr int RS = DT_KS + 8;                 // activation row stride (bf16)
+    extern __shared__ float4 lds4[];
+    uint16_t *xh = reinterpret_cast<uint16_t *>(lds4);
+    uint16_t *xl = xh + TM * RS;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int q = lane >> 4, c16 = lane & 15;
+    char *tb = reinterpret_cast<char *>(xl + TM * RS) + wave * 4096;
+    const int split = blockIdx.y, k0 = split * DT_KS;
+    const int r0 = blockIdx.x * DT_ROWS + wave * 16;
+    const bool rok = r0 < a.N;                    // a tile past N reads the last tile and stores nothing
+    const int rl = rok ? r0 : a.N - 16;
+
+    k2_u4 w[16];
 #pragma unroll
-            for (int i = 0; i < B8; ++i) {
-                if (s0 + i >= splits) break;
-                const int o = (int)(((int64_t)(s0 + i) * TP + t) * a.N + n);
-                v[i] = coh_load4(a.part, o);
-                if (pair) u[i] = coh_load4(a.part, o + n_out);
-            }
+    for (int r = 0; r < 16; ++r)
+        w[r] = __builtin_nontemporal_load(reinterpret_cast<const k2_u4 *>(a.W + (int64_t)(rl + r) * a.K + k0) + lane);
+    dm_stage_x<TM, DT_KS, RS>(a, xh, xl, k0, tid);
+    __syncthreads();
+
+    dm_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const dm_bf16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-            for (int i = 0; i < B8; ++i) {
-                if (s0 + i >= splits) break;
-                sum.x += v[i].x; sum.y += v[i].y; sum.z += v[i].z; sum.w += v[i].w;
-                if (pair) { up.x += u[i].x; up.y += u[i].y; up.z += u[i].z; up.w += u[i].w; }
+    for (int p = 0; p < 4; ++p) {
+        if (p > 0) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the last quarter's reads are done
+        if (q == p) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) *reinterpret_cast<k2_u4 *>(tb + r * 256 + ((c16 + r) & 15) * 16) = w[r];
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 4 * j + q;                  // the quarter's chunk of this lane's k group
+            const dm_bf16x8 A = *reinterpret_cast<const dm_bf16x8 *>(tb + c16 * 256 + ((c + c16) & 15) * 16);
+            dm_bf16x8 bh = zero, bl = zero;
+            if (c16 < TM) {
+                const int kk = (16 * p + c) * 8;
+                bh = *reinterpret_cast<const dm_bf16x8 *>(xh + c16 * RS + kk);
+                bl = *reinterpret_cast<const dm_bf16x8 *>(xl + c16 * RS + kk);
             }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bl, acc, 0, 0, 0);
         }
-        float4 *dst = reinterpret_cast<float4 *>(a.y + (int64_t)t * n_out + n);
-        if (pair) {
-            *dst = make_float4(sum.x / (1.0f + expf(-sum.x)) * up.x, sum.y / (1.0f + expf(-sum.y)) * up.y,
-                               sum.z / (1.0f + expf(-sum.z)) * up.z, sum.w / (1.0f + expf(-sum.w)) * up.w);
-        } else if (a.epi == DM_EPI_ADD) {
-            const float4 r = *dst;
-            *dst = make_float4(r.x + sum.x, r.y + sum.y, r.z + sum.z, r.w + sum.w);
-        } else {
-            *dst = sum;
-        }
+        __builtin_amdgcn_wave_barrier();
     }
+
+    // partials [split][16][N]: the lane holds rows 4q .. 4q+3 for token c16
+    const bool fuse = a.cnt != nullptr;
+    if (rok && c16 < a.T) {
+        const int64_t o = ((int64_t)split * 16 + c16) * a.N + r0 + 4 * q;
+        const float4 v = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        if (fuse) coh_store4(a.part, (int)o, v);
+        else *reinterpret_cast<float4 *>(a.part + o) = v;
+    }
+    if (!fuse) return;
+    dm_reduce_last<DT_ROWS, 16>(a, tid);
 }
 
 // y[t][n] (+)= sum over splits in split order; SwiGLU: n < N/2 pairs rows n
@@ -273,9 +367,23 @@ static DmTile dm_tile(int N, int K, int T)
 
 bool dense_mfma_ok(int N, int K) { return N >= 16 && N % 16 == 0 && K % DM_KC == 0; }
 
+// The row-slice form: up to 16 tokens and K a multiple of 512, for tall
+// products (16384 rows and more) and for those of 2^24 weights and more
+// whose T x splits partial rows are summed in the last blocks.  Measured per
+// launch in 8-token verification rounds at the 3.7B shape: gate/up (20480 x
+// 2560) 26.4 against 32.6 us, lm_head 208 against 292 us; but QKV (6144 x
+// 2560) 13.5 against 12.0, O (2560 x 4096) 13.2 against 10.6, and down
+// (2560 x 10240, 20 splits: a second launch sums them) 23.8 against 18.9.
+static bool dt_ok(int N, int K, int T)
+{
+    if (T > 16 || K % DT_KS) return false;
+    return N >= 16384 || ((int64_t)N * K >= (int64_t)1 << 24 && (int64_t)T * (K / DT_KS) <= DM_FUSE_MAX);
+}
+
 size_t dense_mfma_ws_bytes(int N, int K, int T)
 {
     if (!dense_mfma_ok(N, K) || T < 2) return 0;
+    if (dt_ok(N, K, T)) return (size_t)(K / DT_KS) * 16 * N * 4;
     const int tp = (T < DM_MAX_T ? T : DM_MAX_T) <= 16 ? 16 : 32;
     return (size_t)(K / dm_tile(N, K, T).ks) * tp * N * 4;
 }
@@ -299,6 +407,23 @@ int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T,
                hipStream_t st, unsigned *cnt)
 {
     if (!dense_mfma_ok(N, K) || T < 2) return K2_EUNSUPPORTED;
+    const int n_out_all = epi == DM_EPI_SWIGLU ? N / 2 : N;
+    if (dt_ok(N, K, T)) {
+        const int splits = K / DT_KS;
+        if (epi == DM_EPI_SWIGLU && (N / 2) % DT_ROWS) cnt = nullptr;
+        if ((int64_t)T * splits > DM_FUSE_MAX) cnt = nullptr;
+        DenseArgs a{W, x, part, N, K, T, DT_KS, cnt, y, epi};
+        const dim3 grid((N + DT_ROWS - 1) / DT_ROWS, splits);
+        if (T <= 4) hipLaunchKernelGGL(dense_mfma_t_kernel<4>, grid, dim3(256), dt_lds_bytes(4), st, a);
+        else if (T <= 8) hipLaunchKernelGGL(dense_mfma_t_kernel<8>, grid, dim3(256), dt_lds_bytes(8), st, a);
+        else hipLaunchKernelGGL(dense_mfma_t_kernel<16>, grid, dim3(256), dt_lds_bytes(16), st, a);
+        K2_CHECK_LAUNCH();
+        if (cnt) return K2_OK;
+        hipLaunchKernelGGL(dense_reduce_kernel, dim3((n_out_all + 255) / 256, T), dim3(256), 0, st, part, splits,
+                           16, N, epi, y);
+        K2_CHECK_LAUNCH();
+        return K2_OK;
+    }
     const DmTile tile = dm_tile(N, K, T);
     const int KS = tile.ks, splits = K / KS, rows = tile.rt * DM_MIN_ROWS;
     const int n_out = epi == DM_EPI_SWIGLU ? N / 2 : N;

@@ -146,7 +146,7 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base, boo
     char *am = take(argmax_ws_bytes());
     char *nx = take(4);
     // arrival counters of the small-T products' in-kernel reduction (one per
-    // 256-row block of the tallest product)
+    // 64-row block of the tallest product)
     {
         int rows = c->vocab;
         const int prod[3] = {(c->n_qh + 2 * c->n_kv) * c->head_dim, 2 * c->inter, c->hidden};

@@ -307,6 +307,23 @@ def _golden_parity(name, cfg):
                 assert near_tie_ok(t, r, tie_gap(err)), (chunk, i, t, toks[i], err, gap)
         say(f"golden {name} chunk {chunk}: max|dlogit| per position {[f'{e:.3g}' for e in errs]} "
             f"(tol {tol}); top-2 gaps {[round(float(x), 3) for x in g['top2_gap']]}")
+    # the same 5 emitting positions as one k2_verify round of 5 rows after the
+    # prompt's first P - 1 positions (full-width verification products,
+    # every row's logits and greedy token)
+    say(f"golden {name}: verify 5 rows at {P - 1}")
+    gm.prefill(prompt[:-1], 0, chunk=256)
+    feed = [int(prompt[-1])] + toks[:4]
+    lg = torch.empty((5, cfg.vocab), dtype=torch.float32, device=DEV)
+    nxt = gm.verify(feed, P - 1, lg)
+    torch.cuda.synchronize()
+    got, nx = to_host(lg).astype(np.float64), to_host(nxt).tolist()
+    errs = []
+    for i in range(5):
+        err = float(np.abs(got[i] - ref[i]).max())
+        errs.append(err)
+        assert err <= tol, ("verify", i, err)
+        assert near_tie_ok(nx[i], ref[i], tie_gap(err)), ("verify", i, nx[i], toks[i], err)
+    say(f"golden {name} verify: max|dlogit| per row {[f'{e:.3g}' for e in errs]}")
 
 
 @pytest.mark.slow
