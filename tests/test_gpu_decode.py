@@ -584,6 +584,32 @@ def test_head128_verify_every_row_matches_oracle(wdt, kvdt):
         assert near_tie_ok(nx[i], ref_lg[i], tie_gap(err)), (i, nx[i], int(np.argmax(ref_lg[i])))
 
 
+@pytest.mark.parametrize("T", [3, 7, 12])
+def test_head128_verify_tall_ragged_lm_head(T):
+    """A 16,400-token vocabulary: the lm_head of a verification round is tall
+    enough for the row-slice product (1 KiB row slices moved into the
+    operand layout through LDS) and its last 64-row block holds 16 rows;
+    T = 3, 7 and 12 stage 4, 8 and 16 activation rows.  Every row's logits
+    and greedy token against the oracle."""
+    cfg = HEAD128.replace(name="head128-vocab16400", wdt="bf16", kvdt="bf16", vocab=16400, cap=128)
+    P = 20
+    prompt = synth.prompt(cfg, P)
+    dec = oracle.Decoder.from_synth(cfg)
+    ref_toks, ref_lg = dec.generate(prompt, T)
+    gm = DecodeModel(cfg, DEV)
+    gm.prefill(prompt[:-1], 0)
+    feed = [int(prompt[-1])] + ref_toks[:T - 1]
+    lg = torch.empty((T, cfg.vocab), dtype=torch.float32, device=DEV)
+    nxt = gm.verify(feed, P - 1, lg)
+    torch.cuda.synchronize()
+    got = to_host(lg).astype(np.float64)
+    nx = to_host(nxt).tolist()
+    for i in range(T):
+        err = float(np.abs(got[i] - ref_lg[i]).max())
+        assert err <= tol_for(cfg), (i, err)
+        assert near_tie_ok(nx[i], ref_lg[i], tie_gap(err)), (i, nx[i], int(np.argmax(ref_lg[i])))
+
+
 @pytest.mark.parametrize("kvdt", ["bf16", "i8"])
 @pytest.mark.parametrize("mode", ["exact", "wrong", "half", "ngram"])
 def test_head128_speculative_decode_equals_greedy(kvdt, mode):
