@@ -55,28 +55,94 @@ struct DenseArgs {
     unsigned *cnt;
     float *y;
     int epi;
+    // optional grouped-RMSNorm prologue: x holds the residual stream h and
+    // the product reads gamma * h / rms, the group's sum of squares given as
+    // nsq [T][K / 64] partial sums over 64 consecutive elements
+    const float *gamma, *nsq;
+    int groups;
+    float eps;
+    // optional output osq [T][N / 64]: the partial sums of squares of the
+    // final y rows (an epilogue that adds into the residual stream), the
+    // nsq of the next product
+    float *osq;
 };
+
 
 __host__ __device__ constexpr int dm_lds_bytes(int tp, int ks) { return 2 * tp * (ks + 8) * 2; }
 
 // Stage rows [0, NROW) of the activation slice x[.][k0, k0 + KS) in LDS as
-// bf16 hi / lo planes of row stride RS (rows >= T are 0); every load is
-// issued before any is converted.
-template <int NROW, int KS, int RS>
-__device__ __forceinline__ void dm_stage_x(const DenseArgs &a, uint16_t *xh, uint16_t *xl, int k0, int tid)
-{
-    constexpr int NG = NROW * KS / 4 / 256;       // activation float4s per thread
+// bf16 hi / lo planes of row stride RS (rows >= T are 0), in two steps: the
+// loads (x, and for the norm prologue gamma and the sums of squares) are
+// issued before the weight loads, so that the conversion waits for them
+// alone (a wave's loads return in order) and overlaps the weights in flight.
+template <int NROW, int KS>
+struct DmX {
+    static constexpr int NG = NROW * KS / 4 / 256;   // activation float4s per thread
     float4 xv[NG];
+    float4 gm;                                    // gamma of the thread's 4 columns (the same in every g)
+    float4 sq[2];                                 // float4s tid and tid + 256 of the (token, group) partials
+};
+
+template <int NROW, int KS>
+__device__ __forceinline__ void dm_x_issue(const DenseArgs &a, DmX<NROW, KS> &s, int k0, int tid)
+{
+    constexpr int NG = DmX<NROW, KS>::NG;
+    static_assert(256 % (KS / 4) == 0, "a thread's columns are the same in every row it stages");
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const int i = g * 256 + tid, t = i / (KS / 4), k = (i % (KS / 4)) * 4;
-        xv[g] = t < a.T ? *reinterpret_cast<const float4 *>(a.x + (int64_t)t * a.K + k0 + k)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        s.xv[g] = t < a.T ? *reinterpret_cast<const float4 *>(a.x + (int64_t)t * a.K + k0 + k)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (a.gamma) {
+        s.gm = *reinterpret_cast<const float4 *>(a.gamma + k0 + (tid % (KS / 4)) * 4);
+        // float4 j of the partials: (token, group) j / per4, its float4 j % per4
+        const int per4 = a.K / a.groups / 256;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int j = tid + 256 * h, tg = j / per4, t = tg / a.groups;
+            s.sq[h] = j < NROW * a.groups * per4 && t < a.T
+                          ? reinterpret_cast<const float4 *>(a.nsq + (int64_t)t * (a.K / 64))[(tg % a.groups) * per4 +
+                                                                                             j % per4]
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+}
+
+template <int NROW, int KS, int RS>
+__device__ __forceinline__ void dm_x_finish(const DenseArgs &a, DmX<NROW, KS> &s, uint16_t *xh, uint16_t *xl,
+                                            int k0, int tid)
+{
+    constexpr int NG = DmX<NROW, KS>::NG;
+    if (a.gamma) {
+        // 1 / rms of every (token, norm group) from its partials in order (the
+        // same in every block), then h * r * gamma
+        __shared__ float part4[512];
+        __shared__ float rs[DM_MAX_T][K2_MAX_GROUPS];
+        const int gs = a.K / a.groups, per4 = gs / 256;
+        part4[tid] = (s.sq[0].x + s.sq[0].y) + (s.sq[0].z + s.sq[0].w);
+        part4[tid + 256] = (s.sq[1].x + s.sq[1].y) + (s.sq[1].z + s.sq[1].w);
+        __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): the LDS store is done (weights stay in flight)
+        __builtin_amdgcn_s_barrier();
+        if (tid < NROW * a.groups) {
+            float ss = 0.f;
+            for (int i = 0; i < per4; ++i) ss += part4[tid * per4 + i];
+            rs[tid / a.groups][tid % a.groups] = 1.0f / sqrtf(ss / (float)gs + a.eps);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const int i = g * 256 + tid, t = i / (KS / 4), k = (i % (KS / 4)) * 4;
+            const float r = rs[t][(k0 + k) / gs];
+            s.xv[g] = make_float4(s.xv[g].x * r * s.gm.x, s.xv[g].y * r * s.gm.y, s.xv[g].z * r * s.gm.z,
+                                  s.xv[g].w * r * s.gm.w);
+        }
     }
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const int i = g * 256 + tid, t = i / (KS / 4), k = (i % (KS / 4)) * 4;
-        const float f[4] = {xv[g].x, xv[g].y, xv[g].z, xv[g].w};
+        const float f[4] = {s.xv[g].x, s.xv[g].y, s.xv[g].z, s.xv[g].w};
         uint16_t h[4], l[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -119,11 +185,14 @@ __device__ __forceinline__ void dm_reduce_last(const DenseArgs &a, int tid)
     constexpr int QUADS = ROWS / 4, TSTEP = 256 / QUADS;
     const int n_out = pair ? a.N / 2 : a.N;
     const int n = grp * ROWS + (tid % QUADS) * 4;
-    if (n >= n_out) return;
+    // (with osq every thread stays to the end: the 16 threads holding 64
+    // rows of a token add their squares across lanes)
+    const bool have = n < n_out;
+    if (!have && !a.osq) return;
     constexpr int B8 = 8;
     for (int t = tid / QUADS; t < a.T; t += TSTEP) {
         float4 sum = make_float4(0.f, 0.f, 0.f, 0.f), up = sum;
-        for (int s0 = 0; s0 < splits; s0 += B8) {
+        for (int s0 = 0; have && s0 < splits; s0 += B8) {
             float4 v[B8], u[B8];
 #pragma unroll
             for (int i = 0; i < B8; ++i) {
@@ -140,7 +209,20 @@ __device__ __forceinline__ void dm_reduce_last(const DenseArgs &a, int tid)
             }
         }
         float4 *dst = reinterpret_cast<float4 *>(a.y + (int64_t)t * n_out + n);
-        if (pair) {
+        if (a.osq) {
+            // the residual-stream form (ADD, N % 64 == 0): the new y and its
+            // sum of squares over each 64 rows
+            float ss = 0.f;
+            if (have) {
+                const float4 r = *dst;
+                const float4 o = make_float4(r.x + sum.x, r.y + sum.y, r.z + sum.z, r.w + sum.w);
+                *dst = o;
+                ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+            }
+#pragma unroll
+            for (int d = 1; d < 16; d <<= 1) ss += __shfl_xor(ss, d);
+            if ((tid & 15) == 0 && have) a.osq[(int64_t)t * (a.N / 64) + n / 64] = ss;
+        } else if (pair) {
             *dst = make_float4(sum.x / (1.0f + expf(-sum.x)) * up.x, sum.y / (1.0f + expf(-sum.y)) * up.y,
                                sum.z / (1.0f + expf(-sum.z)) * up.z, sum.w / (1.0f + expf(-sum.w)) * up.w);
         } else if (a.epi == DM_EPI_ADD) {
@@ -187,10 +269,11 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
             for (int j = 0; j < 4; ++j)
                 w[rt][j] = __builtin_nontemporal_load(Wv + (rowoff[rt] + c * DM_KC + 32 * j) / 8);
     };
+    DmX<TP, KS> xs;
+    dm_x_issue<TP, KS>(a, xs, k0, tid);           // the activation slice's loads, then the weights'
     dm_bf16x8 wc[RT][4];
-    load_chunk(0, wc);                            // weights first: their latency covers the staging
-
-    dm_stage_x<TP, KS, RS>(a, xh, xl, k0, tid);   // the activation slice as bf16 hi / lo planes
+    load_chunk(0, wc);
+    dm_x_finish<TP, KS, RS>(a, xs, xh, xl, k0, tid);   // as bf16 hi / lo planes, weights in flight
     __syncthreads();
 
     dm_f32x4 acc[RT][NTT];
@@ -277,11 +360,13 @@ __global__ __launch_bounds__(256) void dense_mfma_t_kernel(const DenseArgs a)
     const bool rok = r0 < a.N;                    // a tile past N reads the last tile and stores nothing
     const int rl = rok ? r0 : a.N - 16;
 
+    DmX<TM, DT_KS> xs;
+    dm_x_issue<TM, DT_KS>(a, xs, k0, tid);        // the activation slice's loads, then the weights'
     k2_u4 w[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r)
         w[r] = __builtin_nontemporal_load(reinterpret_cast<const k2_u4 *>(a.W + (int64_t)(rl + r) * a.K + k0) + lane);
-    dm_stage_x<TM, DT_KS, RS>(a, xh, xl, k0, tid);
+    dm_x_finish<TM, DT_KS, RS>(a, xs, xh, xl, k0, tid);
     __syncthreads();
 
     dm_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -324,12 +409,28 @@ __global__ __launch_bounds__(256) void dense_mfma_t_kernel(const DenseArgs a)
 
 // y[t][n] (+)= sum over splits in split order; SwiGLU: n < N/2 pairs rows n
 // (gate) and n + N/2 (up) and y has N/2 columns.
+// osq (ADD only, N % 64 == 0): the sums of squares of the new y over each
+// 64 rows, one wave's worth.
 __global__ __launch_bounds__(256) void dense_reduce_kernel(const float *part, int splits, int TP, int N,
-                                                           int epi, float *y)
+                                                           int epi, float *y, float *osq)
 {
     const int t = blockIdx.y;
     const int n = blockIdx.x * 256 + threadIdx.x;
     const int n_out = epi == DM_EPI_SWIGLU ? N / 2 : N;
+    if (osq) {
+        float ss = 0.f;
+        if (n < n_out) {
+            float s = 0.f;
+            for (int sp = 0; sp < splits; ++sp) s += part[((int64_t)sp * TP + t) * N + n];
+            float *dst = y + (int64_t)t * n_out + n;
+            const float o = *dst + s;
+            *dst = o;
+            ss = o * o;
+        }
+        ss = wave_sum(ss);
+        if ((threadIdx.x & 63) == 0 && n < n_out) osq[(int64_t)t * (N / 64) + n / 64] = ss;
+        return;
+    }
     if (n >= n_out) return;
     float s = 0.f, u = 0.f;
     for (int sp = 0; sp < splits; ++sp) {
@@ -402,17 +503,28 @@ static void dm_go(int rt, dim3 grid, size_t lds, hipStream_t st, const DenseArgs
 // (dense_mfma_ws_bytes); groups of up to 32 tokens run one after another.
 // cnt (nullable, dense_mfma_cnt_words(N) zeroed words, left zero): sum the
 // partials in the product's last blocks instead of a second launch (SwiGLU
-// only when N / 2 is a multiple of the row block).
+// only when N / 2 is a multiple of the row block).  nrm: the grouped
+// RMSNorm applied to x on the way in (x the residual stream, nrm.nsq its
+// 64-element sums of squares); osq (ADD only): those sums of the new y.
+bool dense_norm_ok(int hidden, int groups)
+{
+    // whole float4s of 64-element partials per group, at most two per thread of a block
+    return groups >= 1 && groups <= K2_MAX_GROUPS && hidden % groups == 0 && (hidden / groups) % 256 == 0 &&
+           (int64_t)DM_MAX_T * hidden / 256 <= 512;
+}
+
 int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi, float *part,
-               hipStream_t st, unsigned *cnt)
+               hipStream_t st, unsigned *cnt, const DmNorm &nrm, float *osq)
 {
     if (!dense_mfma_ok(N, K) || T < 2) return K2_EUNSUPPORTED;
+    if (nrm.gamma && (!nrm.nsq || !dense_norm_ok(K, nrm.groups))) return K2_EINVAL;
+    if (osq && (epi != DM_EPI_ADD || N % 64)) return K2_EINVAL;
     const int n_out_all = epi == DM_EPI_SWIGLU ? N / 2 : N;
     if (dt_ok(N, K, T)) {
         const int splits = K / DT_KS;
         if (epi == DM_EPI_SWIGLU && (N / 2) % DT_ROWS) cnt = nullptr;
         if ((int64_t)T * splits > DM_FUSE_MAX) cnt = nullptr;
-        DenseArgs a{W, x, part, N, K, T, DT_KS, cnt, y, epi};
+        DenseArgs a{W, x, part, N, K, T, DT_KS, cnt, y, epi, nrm.gamma, nrm.nsq, nrm.groups, nrm.eps, osq};
         const dim3 grid((N + DT_ROWS - 1) / DT_ROWS, splits);
         if (T <= 4) hipLaunchKernelGGL(dense_mfma_t_kernel<4>, grid, dim3(256), dt_lds_bytes(4), st, a);
         else if (T <= 8) hipLaunchKernelGGL(dense_mfma_t_kernel<8>, grid, dim3(256), dt_lds_bytes(8), st, a);
@@ -420,7 +532,7 @@ int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T,
         K2_CHECK_LAUNCH();
         if (cnt) return K2_OK;
         hipLaunchKernelGGL(dense_reduce_kernel, dim3((n_out_all + 255) / 256, T), dim3(256), 0, st, part, splits,
-                           16, N, epi, y);
+                           16, N, epi, y, osq);
         K2_CHECK_LAUNCH();
         return K2_OK;
     }
@@ -435,7 +547,9 @@ int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T,
     if ((int64_t)(T < DM_MAX_T ? T : DM_MAX_T) * splits > DM_FUSE_MAX) cnt = nullptr;
     for (int t0 = 0; t0 < T; t0 += DM_MAX_T) {
         const int tg = T - t0 < DM_MAX_T ? T - t0 : DM_MAX_T;
-        DenseArgs a{W, x + (int64_t)t0 * K, part, N, K, tg, KS, cnt, y + (int64_t)t0 * n_out, epi};
+        DenseArgs a{W, x + (int64_t)t0 * K, part, N, K, tg, KS, cnt, y + (int64_t)t0 * n_out, epi, nrm.gamma,
+                    nrm.nsq ? nrm.nsq + (int64_t)t0 * (K / 64) : nullptr, nrm.groups, nrm.eps,
+                    osq ? osq + (int64_t)t0 * (N / 64) : nullptr};
         const dim3 grid((N + rows - 1) / rows, splits);
         const int tp = tg <= 16 ? 16 : 32;
         const size_t lds = dm_lds_bytes(tp, KS);
@@ -453,7 +567,7 @@ int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T,
         K2_CHECK_LAUNCH();
         if (cnt) continue;
         hipLaunchKernelGGL(dense_reduce_kernel, dim3((n_out + 255) / 256, tg), dim3(256), 0, st, part,
-                           splits, tp, N, epi, y + (int64_t)t0 * n_out);
+                           splits, tp, N, epi, y + (int64_t)t0 * n_out, a.osq);
         K2_CHECK_LAUNCH();
     }
     return K2_OK;

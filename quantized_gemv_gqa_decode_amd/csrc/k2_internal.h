@@ -214,8 +214,18 @@ __device__ __forceinline__ void argmax_block(float &v, int &i)
 enum { DM_EPI_PLAIN = 0, DM_EPI_ADD = 1, DM_EPI_SWIGLU = 2 };
 bool dense_mfma_ok(int N, int K);
 size_t dense_mfma_ws_bytes(int N, int K, int T);
+// A small-T product's optional grouped-RMSNorm prologue: x is the residual
+// stream h and the product multiplies gamma * h / rms(group); nsq [T][K / 64]
+// holds the partial sums of squares over 64 consecutive elements that the
+// product which last added into h wrote through its osq (gamma null: none).
+struct DmNorm {
+    const float *gamma = nullptr, *nsq = nullptr;
+    int groups = 1;
+    float eps = 0.f;
+};
+bool dense_norm_ok(int hidden, int groups);
 int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi, float *part,
-               hipStream_t st, unsigned *cnt = nullptr);
+               hipStream_t st, unsigned *cnt = nullptr, const DmNorm &nrm = DmNorm{}, float *osq = nullptr);
 int dense_mfma_cnt_words(int N);
 
 // The projections of a prefill chunk of 1..GM_MAX_T positions on the matrix

@@ -50,6 +50,7 @@ __global__ void embed_rows_kernel(const PfTokens tk, int embdt, const void *E, i
 
 struct PrefillWs {
     float *h, *x, *qkv, *o, *act, *part, *qrot, *lm_part, *logits, *ar_v;
+    float *sq;                     // [T][hidden / 64] sums of squares of the residual stream
     uint16_t *xh, *xl, *ah, *al;   // bf16 hi / lo planes: norm / attention outputs, SwiGLU output
     int *ar_i;
     void *attn, *rows, *am;
@@ -103,9 +104,10 @@ static size_t pf_proj_bytes(int wdt, int N, int K, int T, int epi)
 }
 
 static int pf_proj(int wdt, const void *W, const void *Ws, const float *x, float *y, int N, int K, int T, int epi,
-                   float *ws, unsigned *cnt, hipStream_t st)
+                   float *ws, unsigned *cnt, hipStream_t st, const DmNorm &nrm = DmNorm{}, float *osq = nullptr)
 {
-    if (pf_dense(wdt, T)) return dense_mfma((const uint16_t *)W, x, y, N, K, T, epi, ws, st, cnt);
+    if (pf_dense(wdt, T)) return dense_mfma((const uint16_t *)W, x, y, N, K, T, epi, ws, st, cnt, nrm, osq);
+    if (nrm.gamma || osq) return K2_EINVAL;     // the norm travels in the small-T product only
     return gemm_mfma(wdt, W, Ws, x, y, N, K, T, epi, ws, st);
 }
 
@@ -162,6 +164,7 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base, boo
     char *act = take((size_t)T * c->inter * 4);
     char *part = take(pf_part_bytes(c, T));
     char *qrot = take((size_t)T * qd * 4);
+    char *sq = take((size_t)T * (c->hidden / 64 + 1) * 4);
     // activation planes for the token-blocked products: every row a token
     // block may read (T rounded up to 128)
     const size_t prow = (size_t)(T + 127) / 128 * 128;
@@ -184,6 +187,7 @@ static size_t pf_layout(const k2_config *c, int T, PrefillWs *w, void *base, boo
         w->rows = rows;
         w->rows_cnt = (unsigned *)rows_cnt;
         w->qrot = (float *)qrot;
+        w->sq = (float *)sq;
         w->xh = (uint16_t *)xh;
         w->xl = (uint16_t *)xl;
         w->ah = (uint16_t *)ah;
@@ -281,12 +285,31 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
     // the matrix-core attention and the SwiGLU epilogue write them directly,
     // so no split launch runs before those products.
     const bool planes = !pf_dense(c->wdt, T);
+    // Small-T products (bf16, up to 32 rows) take the row norms in their
+    // activation staging: every product that adds into the residual stream
+    // (O, down) also writes its 64-row sums of squares, from which the next
+    // product (gate/up, the next layer's QKV, the lm_head) scales h.  Only
+    // the first layer's input norm, after the embedding, runs on its own.
+    const bool fnorm = !planes && dense_norm_ok(H, c->groups);
+    auto norm_of = [&](const float *gamma) {
+        DmNorm n;
+        n.gamma = gamma;
+        n.nsq = w.sq;
+        n.groups = c->groups;
+        n.eps = c->eps;
+        return n;
+    };
+    float *osq = fnorm ? w.sq : nullptr;
     for (int l = 0; l < c->n_layers; ++l) {
         const k2_layer *L = &m->layers[l];
         if (planes) {
             if ((rc = rmsnorm_rows_planes_launch(w.h, L->g_in, w.xh, w.xl, T, H, c->groups, c->eps, st))) return rc;
             if ((rc = gemm_mfma_planes(c->wdt, L->qkv, L->qkv_s, w.xh, w.xl, w.qkv, nullptr, nullptr, qkv_rows, H,
                                        T, DM_EPI_PLAIN, w.part, st)))
+                return rc;
+        } else if (fnorm && l > 0) {
+            if ((rc = pf_proj(c->wdt, L->qkv, L->qkv_s, w.h, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, w.dm_cnt,
+                              st, norm_of(L->g_in))))
                 return rc;
         } else {
             if ((rc = rmsnorm_rows_launch(w.h, L->g_in, w.x, T, H, c->groups, c->eps, st))) return rc;
@@ -316,7 +339,7 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
             rc = gemm_mfma_planes(c->wdt, L->o, L->o_s, w.xh, w.xl, w.h, nullptr, nullptr, H, qd, T, DM_EPI_ADD,
                                   w.part, st);
         else
-            rc = pf_proj(c->wdt, L->o, L->o_s, w.o, w.h, H, qd, T, DM_EPI_ADD, w.part, w.dm_cnt, st);
+            rc = pf_proj(c->wdt, L->o, L->o_s, w.o, w.h, H, qd, T, DM_EPI_ADD, w.part, w.dm_cnt, st, DmNorm{}, osq);
         if (rc) return rc;
         if (planes) {
             if ((rc = rmsnorm_rows_planes_launch(w.h, L->g_post, w.xh, w.xl, T, H, c->groups, c->eps, st)))
@@ -326,6 +349,13 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
                 return rc;
             if ((rc = gemm_mfma_planes(c->wdt, L->down, L->down_s, w.ah, w.al, w.h, nullptr, nullptr, H, I, T,
                                        DM_EPI_ADD, w.part, st)))
+                return rc;
+        } else if (fnorm) {
+            if ((rc = pf_proj(c->wdt, L->gu, L->gu_s, w.h, w.act, 2 * I, H, T, DM_EPI_SWIGLU, w.part, w.dm_cnt,
+                              st, norm_of(L->g_post))))
+                return rc;
+            if ((rc = pf_proj(c->wdt, L->down, L->down_s, w.act, w.h, H, I, T, DM_EPI_ADD, w.part, w.dm_cnt, st,
+                              DmNorm{}, osq)))
                 return rc;
         } else {
             if ((rc = rmsnorm_rows_launch(w.h, L->g_post, w.x, T, H, c->groups, c->eps, st))) return rc;
@@ -340,10 +370,16 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
     if (verify) {
         // every row: final norm, lm_head on the matrix cores, first-maximum argmax
         float *lg = logits ? logits : w.logits;
-        if ((rc = rmsnorm_rows_launch(w.h, m->g_final, w.x, T, H, c->groups, c->eps, st))) return rc;
-        rc = c->wdt == K2_BF16
-                 ? dense_mfma((const uint16_t *)m->lm, w.x, lg, c->vocab, H, T, DM_EPI_PLAIN, w.lm_part, st, w.dm_cnt)
-                 : gemm_mfma(c->wdt, m->lm, m->lm_s, w.x, lg, c->vocab, H, T, DM_EPI_PLAIN, w.lm_part, st);
+        if (fnorm) {
+            rc = dense_mfma((const uint16_t *)m->lm, w.h, lg, c->vocab, H, T, DM_EPI_PLAIN, w.lm_part, st, w.dm_cnt,
+                            norm_of(m->g_final));
+        } else {
+            if ((rc = rmsnorm_rows_launch(w.h, m->g_final, w.x, T, H, c->groups, c->eps, st))) return rc;
+            rc = c->wdt == K2_BF16 ? dense_mfma((const uint16_t *)m->lm, w.x, lg, c->vocab, H, T, DM_EPI_PLAIN,
+                                                w.lm_part, st, w.dm_cnt)
+                                   : gemm_mfma(c->wdt, m->lm, m->lm_s, w.x, lg, c->vocab, H, T, DM_EPI_PLAIN,
+                                               w.lm_part, st);
+        }
         if (rc) return rc;
         hipLaunchKernelGGL(argmax_rows_part_kernel, dim3(AR_NB, T), dim3(K2_BLOCK), 0, st, lg, c->vocab, w.ar_v,
                            w.ar_i);
