@@ -39,21 +39,26 @@ size_t attn_rows_ws_bytes(int n_qh, int n_kv, int hd, int cap, int T)
 
 size_t attn_rows_cnt_bytes(int n_kv, int T) { return k2_align256((size_t)T * n_kv * 4); }
 
+bool attn_rows_ok(int kvdt, int n_qh, int n_kv, int hd, int cap, int pos0, int T)
+{
+    if (hd != 128 || T < 1 || n_kv < 1 || n_qh % n_kv) return false;
+    const int rep = n_qh / n_kv;
+    if (rep != 1 && rep != 2 && rep != 4 && rep != 8) return false;
+    if (kvdt != K2_F32 && kvdt != K2_BF16 && kvdt != K2_I8) return false;
+    int chunk = 0;
+    return (size_t)attn_splits(n_kv * T, pos0 + T, &chunk) <= (size_t)attn_max_splits(n_kv, cap);
+}
+
 int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qrot, float *out, void *kc,
                      void *vc, float *ks, float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T,
-                     void *ws, unsigned *cnt, hipStream_t st, uint16_t *oh, uint16_t *ol, bool *planes)
+                     void *ws, unsigned *cnt, hipStream_t st, uint16_t *oh, uint16_t *ol, bool *planes,
+                     bool appended)
 {
     if (planes) *planes = false;
-    if (hd != 128 || T < 1) return K2_EUNSUPPORTED;
+    if (!attn_rows_ok(kvdt, n_qh, n_kv, hd, cap, pos0, T)) return K2_EUNSUPPORTED;
     const int rep = n_qh / n_kv;
-    if (rep != 1 && rep != 2 && rep != 4 && rep != 8) return K2_EUNSUPPORTED;
-    if (kvdt != K2_F32 && kvdt != K2_BF16 && kvdt != K2_I8) return K2_EUNSUPPORTED;
-    {
-        int chunk = 0;
-        if ((size_t)attn_splits(n_kv * T, pos0 + T, &chunk) > (size_t)attn_max_splits(n_kv, cap))
-            return K2_EUNSUPPORTED;
-    }
-    switch (kvdt) {
+    switch (appended ? -1 : kvdt) {
+    case -1: break;                            // q rotated and the rows appended by the QKV product
     case K2_F32:
         hipLaunchKernelGGL((rope_append_rows_kernel<K2_F32, 128>), dim3(n_kv, T), dim3(K2_BLOCK), 0, st, qkv,
                            cos_sin, qrot, kc, vc, ks, vs, n_qh, n_kv, cap, pos0);

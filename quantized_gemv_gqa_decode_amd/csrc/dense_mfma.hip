@@ -65,6 +65,8 @@ struct DenseArgs {
     // final y rows (an epilogue that adds into the residual stream), the
     // nsq of the next product
     float *osq;
+    // optional QKV epilogue (rope.qrot non-null): RoPE and the cache append
+    DmRope rope;
 };
 
 
@@ -154,6 +156,96 @@ __device__ __forceinline__ void dm_x_finish(const DenseArgs &a, DmX<NROW, KS> &s
         lv.x = l[0] | ((uint32_t)l[1] << 16); lv.y = l[2] | ((uint32_t)l[3] << 16);
         *reinterpret_cast<uint2 *>(xh + t * RS + k) = hv;
         *reinterpret_cast<uint2 *>(xl + t * RS + k) = lv;
+    }
+}
+
+// The QKV product's last-block epilogue for a prefill chunk: the rows are
+// heads of 128 (n_qh query heads, then n_kv keys, then n_kv values), two
+// 64-row blocks each, counted together on counter h.  The last of the 2 x
+// splits blocks of head h sums the head's partials in split order, rotates
+// q and k by split-half RoPE at position pos0 + t (element d pairs with d +
+// 64, held 16 lanes away), and writes q to qrot [T][n_qh][128] or k / v into
+// the cache slot pos0 + t of their kv head in the cache format (int8: the
+// head's absolute maximum / 127 as the scale, codes rounded to nearest even
+// and clamped to +-127, the encoding of every other append).
+template <int TP>
+__device__ __forceinline__ void dm_reduce_rope(const DenseArgs &a, int tid)
+{
+    __shared__ int last;
+    const int splits = gridDim.y, head = blockIdx.x / 2;
+    __builtin_amdgcn_s_waitcnt(0);                // this thread's partial stores completed
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned arrivals = 2u * (unsigned)splits;
+        const unsigned old = __hip_atomic_fetch_add(a.cnt + head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = old == arrivals - 1;
+        if (last) __hip_atomic_store(a.cnt + head, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last) return;
+
+    const DmRope &r = a.rope;
+    const int j = tid & 31;                       // rows 4j .. 4j+3 of the head
+    const int n = head * 128 + 4 * j;
+    const bool isq = head < r.n_qh, isk = !isq && head < r.n_qh + r.n_kv;
+    const int g = isq ? 0 : isk ? head - r.n_qh : head - r.n_qh - r.n_kv;
+    constexpr int B8 = 8;
+    for (int t = tid / 32; t < a.T; t += 8) {
+        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s0 = 0; s0 < splits; s0 += B8) {
+            float4 v[B8];
+#pragma unroll
+            for (int i = 0; i < B8; ++i)
+                if (s0 + i < splits) v[i] = coh_load4(a.part, (int)(((int64_t)(s0 + i) * TP + t) * a.N + n));
+#pragma unroll
+            for (int i = 0; i < B8; ++i)
+                if (s0 + i < splits) { sum.x += v[i].x; sum.y += v[i].y; sum.z += v[i].z; sum.w += v[i].w; }
+        }
+        float x[4] = {sum.x, sum.y, sum.z, sum.w};
+        const int pos = r.pos0 + t;
+        if (isq || isk) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = __shfl_xor(x[e], 16);   // element d + 64 (d < 64) or d - 64
+            const bool lo = j < 16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = (4 * j + e) & 63;
+                const float c = r.cs[((int64_t)pos * 64 + i) * 2], sn = r.cs[((int64_t)pos * 64 + i) * 2 + 1];
+                x[e] = lo ? x[e] * c - o[e] * sn : o[e] * sn + x[e] * c;
+            }
+        }
+        if (isq) {
+            *reinterpret_cast<float4 *>(r.qrot + ((int64_t)t * r.n_qh + head) * 128 + 4 * j) =
+                make_float4(x[0], x[1], x[2], x[3]);
+            continue;
+        }
+        const int64_t idx = ((int64_t)g * r.cap + pos) * 128 + 4 * j;
+        if (r.kvdt == K2_F32) {
+            *reinterpret_cast<float4 *>((float *)(isk ? r.kc : r.vc) + idx) = make_float4(x[0], x[1], x[2], x[3]);
+        } else if (r.kvdt == K2_BF16) {
+            uint2 b;
+            b.x = f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16);
+            b.y = f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16);
+            *reinterpret_cast<uint2 *>((uint16_t *)(isk ? r.kc : r.vc) + idx) = b;
+        } else {
+            float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+            const float sc = amax / 127.0f;
+            uint32_t bits = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float q = 0.f;
+                if (amax != 0.f) {
+                    q = rintf(x[e] / sc);
+                    q = fminf(fmaxf(q, -127.f), 127.f);
+                }
+                bits |= (uint32_t)(uint8_t)(int8_t)(int)q << (8 * e);
+            }
+            *reinterpret_cast<uint32_t *>((uint8_t *)(isk ? r.kc : r.vc) + idx) = bits;
+            if (j == 0) (isk ? r.ks : r.vs)[(int64_t)g * r.cap + pos] = amax != 0.f ? sc : 0.f;
+        }
     }
 }
 
@@ -329,6 +421,12 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const DenseArgs a)
         }
     }
     if (!fuse) return;
+    if constexpr (ROWS == 64) {
+        if (a.rope.qrot) {
+            dm_reduce_rope<TP>(a, tid);
+            return;
+        }
+    }
     dm_reduce_last<ROWS, TP>(a, tid);
 }
 
@@ -404,6 +502,10 @@ __global__ __launch_bounds__(256) void dense_mfma_t_kernel(const DenseArgs a)
         else *reinterpret_cast<float4 *>(a.part + o) = v;
     }
     if (!fuse) return;
+    if (a.rope.qrot) {
+        dm_reduce_rope<16>(a, tid);
+        return;
+    }
     dm_reduce_last<DT_ROWS, 16>(a, tid);
 }
 
@@ -514,17 +616,26 @@ bool dense_norm_ok(int hidden, int groups)
 }
 
 int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi, float *part,
-               hipStream_t st, unsigned *cnt, const DmNorm &nrm, float *osq)
+               hipStream_t st, unsigned *cnt, const DmNorm &nrm, float *osq, const DmRope *rope)
 {
     if (!dense_mfma_ok(N, K) || T < 2) return K2_EUNSUPPORTED;
     if (nrm.gamma && (!nrm.nsq || !dense_norm_ok(K, nrm.groups))) return K2_EINVAL;
     if (osq && (epi != DM_EPI_ADD || N % 64)) return K2_EINVAL;
+    if (rope) {
+        // the QKV epilogue runs in the last blocks of 64-row blocks only:
+        // refused (nothing enqueued) where the product would take another form
+        if (epi != DM_EPI_PLAIN || !cnt || N % 128 || N != (rope->n_qh + 2 * rope->n_kv) * 128) return K2_EINVAL;
+        const int splits = dt_ok(N, K, T) ? K / DT_KS : K / dm_tile(N, K, T).ks;
+        if (T > DM_MAX_T || (!dt_ok(N, K, T) && dm_tile(N, K, T).rt != 1) || (int64_t)T * splits > DM_FUSE_MAX)
+            return K2_EUNSUPPORTED;
+    }
+    const DmRope rp = rope ? *rope : DmRope{};
     const int n_out_all = epi == DM_EPI_SWIGLU ? N / 2 : N;
     if (dt_ok(N, K, T)) {
         const int splits = K / DT_KS;
         if (epi == DM_EPI_SWIGLU && (N / 2) % DT_ROWS) cnt = nullptr;
         if ((int64_t)T * splits > DM_FUSE_MAX) cnt = nullptr;
-        DenseArgs a{W, x, part, N, K, T, DT_KS, cnt, y, epi, nrm.gamma, nrm.nsq, nrm.groups, nrm.eps, osq};
+        DenseArgs a{W, x, part, N, K, T, DT_KS, cnt, y, epi, nrm.gamma, nrm.nsq, nrm.groups, nrm.eps, osq, rp};
         const dim3 grid((N + DT_ROWS - 1) / DT_ROWS, splits);
         if (T <= 4) hipLaunchKernelGGL(dense_mfma_t_kernel<4>, grid, dim3(256), dt_lds_bytes(4), st, a);
         else if (T <= 8) hipLaunchKernelGGL(dense_mfma_t_kernel<8>, grid, dim3(256), dt_lds_bytes(8), st, a);
@@ -549,7 +660,7 @@ int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T,
         const int tg = T - t0 < DM_MAX_T ? T - t0 : DM_MAX_T;
         DenseArgs a{W, x + (int64_t)t0 * K, part, N, K, tg, KS, cnt, y + (int64_t)t0 * n_out, epi, nrm.gamma,
                     nrm.nsq ? nrm.nsq + (int64_t)t0 * (K / 64) : nullptr, nrm.groups, nrm.eps,
-                    osq ? osq + (int64_t)t0 * (N / 64) : nullptr};
+                    osq ? osq + (int64_t)t0 * (N / 64) : nullptr, rp};
         const dim3 grid((N + rows - 1) / rows, splits);
         const int tp = tg <= 16 ? 16 : 32;
         const size_t lds = dm_lds_bytes(tp, KS);

@@ -129,10 +129,12 @@ int attn_prefill_launch(int kvdt, const float *qrot, float *out, const void *kc,
 // oh / ol (nullable): where the matrix-core attention runs, its output goes
 // to these bf16 hi / lo planes instead of out, and *planes (nullable) says
 // whether it did.
+// whether attn_rows_launch takes this chunk (else K2_EUNSUPPORTED)
+bool attn_rows_ok(int kvdt, int n_qh, int n_kv, int hd, int cap, int pos0, int T);
 int attn_rows_launch(int kvdt, const float *qkv, const float *cos_sin, float *qrot, float *out, void *kc,
                      void *vc, float *ks, float *vs, int n_qh, int n_kv, int hd, int cap, int pos0, int T,
                      void *ws, unsigned *cnt, hipStream_t st, uint16_t *oh = nullptr, uint16_t *ol = nullptr,
-                     bool *planes = nullptr);
+                     bool *planes = nullptr, bool appended = false);
 
 // Sync words of the attention + O launch: the O-block counter on a line of
 // its own, and 16 copies (one 256-byte line each) of the per-kv-head ready
@@ -224,8 +226,22 @@ struct DmNorm {
     float eps = 0.f;
 };
 bool dense_norm_ok(int hidden, int groups);
+// The QKV product's optional epilogue in a prefill chunk: split-half RoPE of
+// q and k (head_dim 128) at positions pos0 + t, q into qrot [T][n_qh][128],
+// k and v appended to the cache (format kvdt) at those slots.  dense_mfma
+// takes it only where the product's last blocks sum the partials (cnt
+// given, tokens x splits small); it returns K2_EUNSUPPORTED, nothing
+// enqueued, where it would not, and the caller appends separately.
+struct DmRope {
+    const float *cs = nullptr;                 // [cap][64][2] cos, sin
+    float *qrot = nullptr;
+    void *kc = nullptr, *vc = nullptr;
+    float *ks = nullptr, *vs = nullptr;
+    int n_qh = 0, n_kv = 0, cap = 0, pos0 = 0, kvdt = 0;
+};
 int dense_mfma(const uint16_t *W, const float *x, float *y, int N, int K, int T, int epi, float *part,
-               hipStream_t st, unsigned *cnt = nullptr, const DmNorm &nrm = DmNorm{}, float *osq = nullptr);
+               hipStream_t st, unsigned *cnt = nullptr, const DmNorm &nrm = DmNorm{}, float *osq = nullptr,
+               const DmRope *rope = nullptr);
 int dense_mfma_cnt_words(int N);
 
 // The projections of a prefill chunk of 1..GM_MAX_T positions on the matrix

@@ -302,20 +302,45 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
     float *osq = fnorm ? w.sq : nullptr;
     for (int l = 0; l < c->n_layers; ++l) {
         const k2_layer *L = &m->layers[l];
+        bool appended = false;                   // the QKV product rotated q and appended the rows
         if (planes) {
             if ((rc = rmsnorm_rows_planes_launch(w.h, L->g_in, w.xh, w.xl, T, H, c->groups, c->eps, st))) return rc;
             if ((rc = gemm_mfma_planes(c->wdt, L->qkv, L->qkv_s, w.xh, w.xl, w.qkv, nullptr, nullptr, qkv_rows, H,
                                        T, DM_EPI_PLAIN, w.part, st)))
                 return rc;
-        } else if (fnorm && l > 0) {
-            if ((rc = pf_proj(c->wdt, L->qkv, L->qkv_s, w.h, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, w.dm_cnt,
-                              st, norm_of(L->g_in))))
-                return rc;
         } else {
-            if ((rc = rmsnorm_rows_launch(w.h, L->g_in, w.x, T, H, c->groups, c->eps, st))) return rc;
-            if ((rc = pf_proj(c->wdt, L->qkv, L->qkv_s, w.x, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, w.dm_cnt,
-                              st)))
+            // small-T bf16: the product's last blocks also rotate q and k and
+            // append the chunk's rows to the cache where they sum the partials
+            // (head_dim 128), else the attention launch does
+            DmNorm nrm;
+            const float *xin = w.x;
+            if (fnorm && l > 0) {
+                nrm = norm_of(L->g_in);
+                xin = w.h;
+            } else if ((rc = rmsnorm_rows_launch(w.h, L->g_in, w.x, T, H, c->groups, c->eps, st))) {
                 return rc;
+            }
+            DmRope rp;
+            rp.cs = m->rope;
+            rp.qrot = w.qrot;
+            rp.kc = L->kc;
+            rp.vc = L->vc;
+            rp.ks = L->ks;
+            rp.vs = L->vs;
+            rp.n_qh = c->n_qh;
+            rp.n_kv = c->n_kv;
+            rp.cap = c->cap;
+            rp.pos0 = pos0;
+            rp.kvdt = c->kvdt;
+            rc = attn_rows_ok(c->kvdt, c->n_qh, c->n_kv, hd, c->cap, pos0, T)
+                     ? dense_mfma((const uint16_t *)L->qkv, xin, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, st,
+                                  w.dm_cnt, nrm, nullptr, &rp)
+                     : K2_EUNSUPPORTED;
+            appended = rc == K2_OK;
+            if (rc == K2_EUNSUPPORTED)
+                rc = pf_proj(c->wdt, L->qkv, L->qkv_s, xin, w.qkv, qkv_rows, H, T, DM_EPI_PLAIN, w.part, w.dm_cnt,
+                             st, nrm);
+            if (rc) return rc;
         }
         at.kc = L->kc;
         at.vc = L->vc;
@@ -324,7 +349,7 @@ static int prefill_impl(const k2_model *m, const int32_t *tokens, int T, int pos
         bool o_planes = false;                       // the attention wrote its output as planes (w.xh / w.xl)
         rc = attn_rows_launch(c->kvdt, w.qkv, m->rope, w.qrot, w.o, L->kc, L->vc, L->ks, L->vs, c->n_qh,
                               c->n_kv, hd, c->cap, pos0, T, w.rows, w.rows_cnt, st, planes ? w.xh : nullptr,
-                              planes ? w.xl : nullptr, &o_planes);
+                              planes ? w.xl : nullptr, &o_planes, appended);
         if (rc && rc != K2_EUNSUPPORTED) return rc;
         const bool per_position = rc == K2_EUNSUPPORTED;
         for (int t = 0; per_position && t < T; ++t) {
