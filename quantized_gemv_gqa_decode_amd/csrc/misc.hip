@@ -8,26 +8,78 @@ namespace k2 {
 
 // ---------------------------------------------------------------- RMSNorm --
 // GroupedRMSNorm ([k2-burn] "Model shape": layernorm_num_groups): one block per
-// (row, group); y = x / sqrt(mean(x^2) + eps) * gamma.
-__global__ __launch_bounds__(K2_BLOCK) void rmsnorm_grouped_kernel(const float *x, const float *gamma,
-                                                                   float *y, int hidden, int groups,
-                                                                   float eps)
+// (row, group); y = x / sqrt(mean(x^2) + eps) * gamma.  Groups of up to
+// RMS_V * 1024 elements (float4-aligned) are held in registers: every load of
+// the group and of gamma is issued before the first is used, so the kernel
+// pays one memory round trip instead of one per loop step; other groups take
+// the strided loop.
+constexpr int RMS_V = 8;                        // float4s per thread held in registers
+
+__device__ __forceinline__ bool rms_vec_ok(int gs, const float *xr, const float *gm)
+{
+    return gs % 4 == 0 && gs <= RMS_V * 4 * K2_BLOCK && ((uintptr_t)xr & 15u) == 0 && ((uintptr_t)gm & 15u) == 0;
+}
+
+// the block's sum of x^2 over its group -> 1 / rms (every thread)
+__device__ __forceinline__ float rms_scale(float ss, int gs, float eps)
 {
     __shared__ float red[K2_WAVES_PER_BLOCK];
-    const int row = blockIdx.x / groups, g = blockIdx.x % groups, gs = hidden / groups;
-    const float *xr = x + (int64_t)row * hidden + (int64_t)g * gs;
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < gs; i += K2_BLOCK) ss += xr[i] * xr[i];
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
     float t = 0.f;
 #pragma unroll
     for (int w = 0; w < K2_WAVES_PER_BLOCK; ++w) t += red[w];
-    const float r = 1.0f / sqrtf(t / (float)gs + eps);
-    float *yr = y + (int64_t)row * hidden + (int64_t)g * gs;
-    const float *gm = gamma + (int64_t)g * gs;
-    for (int i = threadIdx.x; i < gs; i += K2_BLOCK) yr[i] = xr[i] * r * gm[i];
+    return 1.0f / sqrtf(t / (float)gs + eps);
+}
+
+// y (or its bf16 hi / lo planes) for the block's group; OUT(i, value) stores
+// element i of the group
+template <class Out>
+__device__ __forceinline__ void rms_group(const float *xr, const float *gm, int gs, float eps, Out out)
+{
+    if (rms_vec_ok(gs, xr, gm)) {
+        const int n4 = gs / 4;
+        float4 xv[RMS_V], gv[RMS_V];
+#pragma unroll
+        for (int v = 0; v < RMS_V; ++v) {
+            const int i = v * K2_BLOCK + threadIdx.x;
+            const int ii = i < n4 ? i : 0;
+            xv[v] = reinterpret_cast<const float4 *>(xr)[ii];
+            gv[v] = reinterpret_cast<const float4 *>(gm)[ii];
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int v = 0; v < RMS_V; ++v)
+            if (v * K2_BLOCK + (int)threadIdx.x < n4)
+                ss += xv[v].x * xv[v].x + xv[v].y * xv[v].y + xv[v].z * xv[v].z + xv[v].w * xv[v].w;
+        const float r = rms_scale(ss, gs, eps);
+#pragma unroll
+        for (int v = 0; v < RMS_V; ++v) {
+            const int i = v * K2_BLOCK + threadIdx.x;
+            if (i < n4) {
+                out(4 * i, xv[v].x * r * gv[v].x);
+                out(4 * i + 1, xv[v].y * r * gv[v].y);
+                out(4 * i + 2, xv[v].z * r * gv[v].z);
+                out(4 * i + 3, xv[v].w * r * gv[v].w);
+            }
+        }
+    } else {
+        float ss = 0.f;
+        for (int i = threadIdx.x; i < gs; i += K2_BLOCK) ss += xr[i] * xr[i];
+        const float r = rms_scale(ss, gs, eps);
+        for (int i = threadIdx.x; i < gs; i += K2_BLOCK) out(i, xr[i] * r * gm[i]);
+    }
+}
+
+__global__ __launch_bounds__(K2_BLOCK) void rmsnorm_grouped_kernel(const float *x, const float *gamma,
+                                                                   float *y, int hidden, int groups,
+                                                                   float eps)
+{
+    const int row = blockIdx.x / groups, g = blockIdx.x % groups, gs = hidden / groups;
+    const int64_t o = (int64_t)row * hidden + (int64_t)g * gs;
+    float *yr = y + o;
+    rms_group(x + o, gamma + (int64_t)g * gs, gs, eps, [&](int i, float v) { yr[i] = v; });
 }
 
 // The same rows written as bf16 hi / lo planes (hi = bf16(y), lo = bf16(y -
@@ -36,26 +88,13 @@ __global__ __launch_bounds__(K2_BLOCK) void rmsnorm_planes_kernel(const float *x
                                                                   uint16_t *yh, uint16_t *yl, int hidden,
                                                                   int groups, float eps)
 {
-    __shared__ float red[K2_WAVES_PER_BLOCK];
     const int row = blockIdx.x / groups, g = blockIdx.x % groups, gs = hidden / groups;
-    const float *xr = x + (int64_t)row * hidden + (int64_t)g * gs;
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < gs; i += K2_BLOCK) ss += xr[i] * xr[i];
-    ss = wave_sum(ss);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    float t = 0.f;
-#pragma unroll
-    for (int w = 0; w < K2_WAVES_PER_BLOCK; ++w) t += red[w];
-    const float r = 1.0f / sqrtf(t / (float)gs + eps);
     const int64_t o = (int64_t)row * hidden + (int64_t)g * gs;
-    const float *gm = gamma + (int64_t)g * gs;
-    for (int i = threadIdx.x; i < gs; i += K2_BLOCK) {
-        const float v = xr[i] * r * gm[i];
+    rms_group(x + o, gamma + (int64_t)g * gs, gs, eps, [&](int i, float v) {
         const uint16_t h = f32_to_bf16_rne(v);
         yh[o + i] = h;
         yl[o + i] = f32_to_bf16_rne(v - bf16_to_f32(h));
-    }
+    });
 }
 
 // ------------------------------------------------------------------- RoPE --

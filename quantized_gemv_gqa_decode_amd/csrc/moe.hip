@@ -368,15 +368,28 @@ void moe_expert_kernel(const float *xsrc, const uint8_t *wq, const uint8_t *ws, 
 }
 
 // r[t][j] = sum over slots s in order of topk_w[t][s] * out[pair_index[t][s]][j]
+// (the slots' indices, weights and rows are loaded 16 at a time before the
+// first is added: one memory round trip per 16 slots)
 __global__ void moe_combine_kernel(const float *topk_w, int top_k, int latent, MoeWs w, float *r)
 {
     const int t = blockIdx.y;
     const int j = blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= latent) return;
+    constexpr int SB = 16;
     float acc = 0.f;
-    for (int s = 0; s < top_k; ++s) {
-        const int idx = w.pair_index[t * top_k + s];
-        if (idx >= 0) acc += topk_w[t * top_k + s] * w.out[(int64_t)idx * latent + j];
+    for (int s0 = 0; s0 < top_k; s0 += SB) {
+        int idx[SB];
+        float wt[SB], v[SB];
+#pragma unroll
+        for (int i = 0; i < SB; ++i) {
+            idx[i] = s0 + i < top_k ? w.pair_index[t * top_k + s0 + i] : -1;
+            wt[i] = s0 + i < top_k ? topk_w[t * top_k + s0 + i] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < SB; ++i) v[i] = idx[i] >= 0 ? w.out[(int64_t)idx[i] * latent + j] : 0.f;
+#pragma unroll
+        for (int i = 0; i < SB; ++i)
+            if (idx[i] >= 0) acc += wt[i] * v[i];
     }
     r[(int64_t)t * latent + j] = acc;
 }
