@@ -256,9 +256,24 @@ __global__ __launch_bounds__(K2_BLOCK) void argmax_kernel(const float *x, int n,
 // First maximum over the per-block candidates (value, then lowest index).
 __global__ __launch_bounds__(K2_BLOCK) void argmax_final_kernel(ArgmaxArgs am, int n_blocks)
 {
+    // 16 candidates per thread loaded before the first comparison (one memory
+    // round trip per 4096 blocks); the (greater value, then lower index) rule
+    // gives the same winner in any order
+    constexpr int AB = 16;
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int b = threadIdx.x; b < n_blocks; b += K2_BLOCK) argmax_pair_max(bv, bi, am.part_v[b], am.part_i[b]);
+    for (int b0 = 0; b0 < n_blocks; b0 += AB * K2_BLOCK) {
+        float v[AB];
+        int ix[AB];
+#pragma unroll
+        for (int u = 0; u < AB; ++u) {
+            const int b = b0 + u * K2_BLOCK + (int)threadIdx.x;
+            v[u] = b < n_blocks ? am.part_v[b] : -INFINITY;
+            ix[u] = b < n_blocks ? am.part_i[b] : 0x7FFFFFFF;
+        }
+#pragma unroll
+        for (int u = 0; u < AB; ++u) argmax_pair_max(bv, bi, v[u], ix[u]);
+    }
     argmax_block(bv, bi);
     if (threadIdx.x == 0) {
         *am.out_idx = bi;

@@ -73,7 +73,22 @@ __global__ __launch_bounds__(K2_BLOCK) void argmax_rows_part_kernel(const float 
     const float *r = x + (int64_t)t * n;
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int i = lo + threadIdx.x; i < hi; i += K2_BLOCK) argmax_pair_max(bv, bi, r[i], i);
+    // 16 elements per thread loaded before the first comparison (one memory
+    // round trip per 4096 of the slice; the winner does not depend on order)
+    constexpr int AB = 16;
+    for (int i0 = lo; i0 < hi; i0 += AB * K2_BLOCK) {
+        float v[AB];
+#pragma unroll
+        for (int u = 0; u < AB; ++u) {
+            const int i = i0 + u * K2_BLOCK + (int)threadIdx.x;
+            v[u] = i < hi ? r[i] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < AB; ++u) {
+            const int i = i0 + u * K2_BLOCK + (int)threadIdx.x;
+            if (i < hi) argmax_pair_max(bv, bi, v[u], i);
+        }
+    }
     argmax_block(bv, bi);
     if (threadIdx.x == 0) {
         pv[t * AR_NB + b] = bv;
