@@ -88,8 +88,8 @@ def time_kernel(fn, n_launch: int, stream) -> float:
     """Average duration (ms) of `n_launch` back-to-back launches issued by fn(i).
 
     The launches are captured once into a HIP graph so that host issue cost
-    does not enter the measurement; the replay is bracketed by HIP events on
-    the stream it runs on."""
+    does not enter the measurement; each of 5 replays is bracketed by HIP
+    events on the stream it runs on, and the median replay is reported."""
     import torch
     g = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
@@ -98,16 +98,19 @@ def time_kernel(fn, n_launch: int, stream) -> float:
         for i in range(n_launch):
             fn(i)
     stream.wait_stream(cap)
+    times = []
     with torch.cuda.stream(stream):
         g.replay()                                   # warm
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        s.record(stream)
-        g.replay()
-        e.record(stream)
-    e.synchronize()
-    return s.elapsed_time(e) / n_launch
+        for _ in range(5):
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            g.replay()
+            e.record(stream)
+            e.synchronize()
+            times.append(s.elapsed_time(e) / n_launch)
+    return sorted(times)[len(times) // 2]
 
 
 def kernel_table(gm, stream, reps: int):
