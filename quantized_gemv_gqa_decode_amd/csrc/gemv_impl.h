@@ -396,6 +396,9 @@ void gemv_kernel(const GemvArgs a)
     float4 gr[XV];
     issue_x<XV>(a, xr);                            // activations (and gamma) first ...
     if constexpr (EG) issue_gamma<XV>(a, gr);
+    // (kept ahead of the weight loads: the scheduler would otherwise sink the
+    // gamma loads below them, and its use would then wait for every weight)
+    __builtin_amdgcn_sched_barrier(0);
     // ... then weights (unconditionally: a wave without a unit reads a clamped
     // row it never uses, which keeps the issue path free of branches)
     gemv_prefetch<WDT, R, U, EPI>(a, unit, rows, ok, w, sc);
