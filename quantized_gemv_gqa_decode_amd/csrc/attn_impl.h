@@ -42,6 +42,9 @@ template <int KVDT> __device__ __forceinline__ void kv_decode(const k2_u4 w, flo
 
 constexpr float K2_LOG2E = 1.4426950408889634f;
 constexpr float K2_LN2 = 0.6931471805599453f;
+// Slack of the streaming blocks' lazily moved softmax reference (base 2):
+// every weight stays <= 2^8, far from the fp32 range.
+constexpr float ATT_SLACK = 8.0f;
 
 // 2^x with the hardware exponential (x <= 0 here; -inf gives 0)
 __device__ __forceinline__ float k2_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -827,8 +830,12 @@ __device__ __forceinline__ bool attn_stream_block(const AttnArgs &a, int g, int 
             float mx = sc[0][h];
 #pragma unroll
             for (int n = 1; n < NSLOT; ++n) mx = fmaxf(mx, sc[n][h]);
-            mx = wave_max(mx);
-            if (mx > m[h]) {                         // uniform: rescale only when the maximum moves
+            // lazy rescaling: the reference m (wave-uniform) moves only when
+            // a score passes it by more than ATT_SLACK (base 2), so a tile
+            // mostly skips the wave maximum; the weights 2^(s - m) stay
+            // <= 2^ATT_SLACK, and any reference gives the same softmax
+            if (__builtin_amdgcn_ballot_w64(mx > m[h] + ATT_SLACK) != 0) {   // uniform
+                mx = wave_max(mx);
                 const float corr = k2_exp2(m[h] - mx);   // m = -inf gives 0
                 l[h] *= corr;
                 wsum[h] *= corr;
