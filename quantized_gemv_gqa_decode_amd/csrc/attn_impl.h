@@ -261,262 +261,14 @@ __device__ __forceinline__ float kv_store_head(float val, void *kc, void *vc, fl
     return stored;
 }
 
-// LDS of attn_block, carved from a float buffer of attn_lds_floats<...>()
-template <int HD, int REP, int WPB>
-__host__ __device__ constexpr int attn_lds_floats()
-{
-    return REP * HD + 2 * HD + WPB * REP * HD + WPB * REP * 2 + WPB;
-}
-
-// One block of the attention: kv head g, split s of S (positions
-// [s*chunk, min(len, (s+1)*chunk))).  Every thread of the block calls it.
-// COH: partials and outputs go to other blocks of the same grid: they are
-// stored at device scope, and the combine reads partials at device scope
-// (the partial buffer is reused by every layer, so a plain load could hit a
-// stale L2 line).  LEAN: fewer registers (half the slots in flight, q read
-// from LDS) for kernels whose other phases set the register budget.
-template <int KVDT, int HD, int REP, bool FUSED, int WPB, bool COH, bool LEAN = false>
-__device__ __forceinline__ void attn_block(const AttnArgs &a, int g, int s, int S, float *smem)
-{
-    using T = typename KVT<KVDT>::T;
-    constexpr int EPC = KVT<KVDT>::EPC;
-    constexpr int LPP = HD / EPC;                  // lanes per position
-    constexpr int PPI = K2_WAVE / LPP;             // positions per wave slot
-    constexpr int NL = LEAN ? (EPC >= 16 ? 1 : 2) : (EPC >= 16 ? 2 : 4);   // slots per wave per iteration
-    constexpr int NT = WPB * K2_WAVE;              // threads per block
-    static_assert(LPP >= 1 && LPP <= K2_WAVE, "head_dim / dtype");
-
-    auto qs = reinterpret_cast<float (*)[HD]>(smem);                         // [REP][HD]
-    auto newkv = reinterpret_cast<float (*)[HD]>(smem + REP * HD);           // [2][HD]
-    auto red_o = reinterpret_cast<float (*)[REP][HD]>(smem + REP * HD + 2 * HD);  // [WPB][REP][HD]
-    auto red_ml = reinterpret_cast<float (*)[REP][2]>(smem + REP * HD + 2 * HD + WPB * REP * HD);
-    float *tmp4 = smem + REP * HD + 2 * HD + WPB * REP * HD + WPB * REP * 2;
-    const int len = a.len;
-    const int j0 = s * a.chunk;
-    const int j1 = min(len, j0 + a.chunk);
-    const bool holds_new = FUSED && (j1 == len);
-    const int jc = holds_new ? j1 - 1 : j1;        // positions read from the cache
-    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int sub = lane / LPP, cl = lane % LPP;
-
-    const T *__restrict__ kbase = reinterpret_cast<const T *>(a.kc) + (int64_t)g * a.cap * HD;
-    const T *__restrict__ vbase = reinterpret_cast<const T *>(a.vc) + (int64_t)g * a.cap * HD;
-    // The K and V rows of the first iteration do not depend on q: issue them
-    // first (unconditionally, at a clamped valid position) so that they are in
-    // flight while q is rotated and the new position is appended.
-    k2_u4 kw[NL], vw[NL];
-    int jn[NL];
-    auto issue_kv = [&](int base) {
-#pragma unroll
-        for (int n = 0; n < NL; ++n) {
-            const int j = base + (n * WPB + wave) * PPI + sub;
-            jn[n] = j;
-            const int jj = j < jc ? j : j0;
-            kw[n] = *reinterpret_cast<const k2_u4 *>(kbase + (int64_t)jj * HD + cl * EPC);
-            vw[n] = *reinterpret_cast<const k2_u4 *>(vbase + (int64_t)jj * HD + cl * EPC);
-        }
-    };
-    issue_kv(j0);
-
-    // 1. query heads of this kv head, rotated (fused) and pre-scaled
-    for (int t = tid; t < REP * HD; t += NT) {
-        const int hl = t / HD, d = t % HD, h = g * REP + hl;
-        float val;
-        if constexpr (FUSED) {
-            constexpr int half = HD / 2;
-            const float *u = a.qkv + (int64_t)h * HD;
-            const int i = d % half;
-            const float c = a.cos_sin[((int64_t)a.pos * half + i) * 2];
-            const float sn = a.cos_sin[((int64_t)a.pos * half + i) * 2 + 1];
-            const float x0 = u[i], x1 = u[i + half];
-            val = d < half ? x0 * c - x1 * sn : x0 * sn + x1 * c;
-        } else {
-            val = a.q[(int64_t)h * HD + d];
-        }
-        qs[hl][d] = val * a.scale;
-    }
-    // 2. fused: rotate k, store k and v at slot pos (block-uniform branch)
-    if constexpr (FUSED) {
-        if (holds_new) {
-            constexpr int half = HD / 2;
-            float val = 0.f;
-            if (tid < HD) {
-                const float *u = a.qkv + (int64_t)(a.n_qh + g) * HD;
-                const int d = tid, i = d % half;
-                const float c = a.cos_sin[((int64_t)a.pos * half + i) * 2];
-                const float sn = a.cos_sin[((int64_t)a.pos * half + i) * 2 + 1];
-                const float x0 = u[i], x1 = u[i + half];
-                val = d < half ? x0 * c - x1 * sn : x0 * sn + x1 * c;
-            } else if (tid < 2 * HD) {
-                val = a.qkv[(int64_t)(a.n_qh + a.n_kv + g) * HD + (tid - HD)];
-            }
-            const float st = kv_store_head<KVDT, HD>(val, a.kc, a.vc, a.ks, a.vs, g, a.cap, a.pos, tmp4);
-            if (tid < 2 * HD) newkv[tid / HD][tid % HD] = st;
-        }
-    }
-    __syncthreads();
-
-    const float *__restrict__ ksb = a.ks + (int64_t)g * a.cap;
-    const float *__restrict__ vsb = a.vs + (int64_t)g * a.cap;
-
-    // q slice of this lane: in registers when small, else read from LDS at use
-    constexpr bool QREG = !LEAN && REP * EPC <= 32;
-    float qv[QREG ? REP : 1][QREG ? EPC : 1];
-    if constexpr (QREG) {
-#pragma unroll
-        for (int h = 0; h < REP; ++h)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) qv[h][e] = qs[h][cl * EPC + e];
-    }
-
-    // 3. per-wave online softmax over the slots of this wave: slot n of
-    //    iteration it covers positions j0 + ((it*NL + n)*WPB + wave)*PPI + [0, PPI)
-    float m[REP], l[REP], acc[REP][EPC];
-#pragma unroll
-    for (int h = 0; h < REP; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
-    }
-    for (int base = j0; base < jc; base += NL * WPB * PPI) {
-        // take this iteration's rows, then put the next iteration's loads in
-        // flight before any arithmetic (double buffering)
-        k2_u4 kcur[NL], vcur[NL];
-        int jcur[NL];
-#pragma unroll
-        for (int n = 0; n < NL; ++n) { kcur[n] = kw[n]; vcur[n] = vw[n]; jcur[n] = jn[n]; }
-        if (base + NL * WPB * PPI < jc) issue_kv(base + NL * WPB * PPI);
-        float sc[NL][REP];
-#pragma unroll
-        for (int n = 0; n < NL; ++n) {
-            float kv[EPC];
-            kv_decode<KVDT>(kcur[n], kv);
-            const bool valid = jcur[n] < jc;
-            const float ksc = (KVDT == K2_I8 && valid) ? ksb[jcur[n]] : 1.0f;
-#pragma unroll
-            for (int h = 0; h < REP; ++h) {
-                float p = 0.f;
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) {
-                    if constexpr (QREG) p += qv[h][e] * kv[e];
-                    else p += qs[h][cl * EPC + e] * kv[e];
-                }
-                p = group_sum<LPP>(p) * ksc;
-                sc[n][h] = valid ? p : -INFINITY;
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < REP; ++h) {
-            float mx = sc[0][h];
-#pragma unroll
-            for (int n = 1; n < NL; ++n) mx = fmaxf(mx, sc[n][h]);
-            mx = wave_max(mx);
-            const float mn = fmaxf(m[h], mx);
-            // mn is finite here: the first iteration of every wave that runs
-            // holds at least one valid position (base < jc for slot 0 of wave 0;
-            // other waves may see none, handled below)
-            const float corr = (mn == -INFINITY) ? 1.0f : expf(m[h] - mn);
-            l[h] *= corr;
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[h][e] *= corr;
-            m[h] = mn;
-        }
-#pragma unroll
-        for (int n = 0; n < NL; ++n) {
-            if (jcur[n] < jc) {
-                float vv[EPC];
-                kv_decode<KVDT>(vcur[n], vv);
-                const float vsc = (KVDT == K2_I8) ? vsb[jcur[n]] : 1.0f;
-#pragma unroll
-                for (int h = 0; h < REP; ++h) {
-                    const float p = expf(sc[n][h] - m[h]);
-                    l[h] += p;
-                    const float pv = p * vsc;
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e) acc[h][e] += pv * vv[e];
-                }
-            }
-        }
-    }
-    // the new position (fused): wave 0, values from LDS
-    if (holds_new && wave == 0) {
-#pragma unroll
-        for (int h = 0; h < REP; ++h) {
-            float p = 0.f;
-            for (int d = lane; d < HD; d += K2_WAVE) p += qs[h][d] * newkv[0][d];
-            const float snew = wave_sum(p);
-            const float mn = fmaxf(m[h], snew);
-            const float corr = expf(m[h] - mn);          // m = -inf gives 0
-            const float pn = expf(snew - mn);
-            l[h] = l[h] * corr + (sub == 0 ? pn : 0.f);
-#pragma unroll
-            for (int e = 0; e < EPC; ++e)
-                acc[h][e] = acc[h][e] * corr + (sub == 0 ? pn * newkv[1][cl * EPC + e] : 0.f);
-            m[h] = mn;
-        }
-    }
-    // 4. sum over the position sub-groups of the wave (same m across the wave)
-#pragma unroll
-    for (int h = 0; h < REP; ++h) {
-#pragma unroll
-        for (int o = LPP; o < K2_WAVE; o <<= 1) l[h] += __shfl_xor(l[h], o, K2_WAVE);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-            float v = acc[h][e];
-#pragma unroll
-            for (int o = LPP; o < K2_WAVE; o <<= 1) v += __shfl_xor(v, o, K2_WAVE);
-            acc[h][e] = v;
-        }
-    }
-    if (sub == 0) {
-#pragma unroll
-        for (int h = 0; h < REP; ++h)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) red_o[wave][h][cl * EPC + e] = acc[h][e];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < REP; ++h) { red_ml[wave][h][0] = m[h]; red_ml[wave][h][1] = l[h]; }
-    }
-    __syncthreads();
-
-    // 5. combine the waves; output directly (one split) or publish a partial
-    const int64_t pbase = ((int64_t)g * S + s) * REP;
-    for (int t = tid; t < REP * HD; t += NT) {
-        const int h = t / HD, d = t % HD;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < WPB; ++w) M = fmaxf(M, red_ml[w][h][0]);
-        float L = 0.f, o = 0.f;
-#pragma unroll
-        for (int w = 0; w < WPB; ++w) {
-            const float mw = red_ml[w][h][0];
-            const float f = (mw == -INFINITY) ? 0.f : expf(mw - M);
-            L += f * red_ml[w][h][1];
-            o += f * red_o[w][h][d];
-        }
-        if (S == 1) {
-            st1<COH>(a.out + (int64_t)(g * REP + h) * HD + d, o / L);
-        } else {
-            st1<COH>(a.part + (pbase + h) * HD + d, o);
-            if (d == 0) {
-                st1<COH>(a.part_ml + (pbase + h) * 2, M);
-                st1<COH>(a.part_ml + (pbase + h) * 2 + 1, L);
-            }
-        }
-    }
-}
-
 // ------------------------------------------------- streaming attention --
-// The same attention with K and V (and the int8 scales) streamed through
-// LDS by blocks of C::WPB waves: the block's positions are cut into tiles
-// of TP positions (16 KiB of K and 16 KiB of V for head_dim 128); tiles are
+// The attention of one kv head and split, with K and V (and the int8
+// scales) streamed through LDS by blocks of C::WPB waves: the block's
+// positions are cut into tiles of TP positions (16 KiB of K and 16 KiB of V for head_dim 128); tiles are
 // copied from HBM straight into LDS with LDS-DMA loads (global_load_lds, 16
 // bytes per lane, no registers), C::NST tiles in flight, and the waves
 // read them from LDS with the query heads held in registers.  A block keeps
 // up to 96 KiB in flight: long contexts become bandwidth-bound.
-
 
 // Optional per-block stage trace for performance work (never enabled in the
 // library build): thread 0 keeps the 100 MHz real-time counter of each
@@ -558,7 +310,7 @@ static __shared__ unsigned long long k2_attn_trs[12];
 // of LDS, one block per compute unit) and 2 for int8 (~66 KiB, two blocks
 // per unit).  Measured at the 3.7B shape: bf16 cache, decode step with the
 // position on the device 2.139 ms with 3 stages against 2.149 with 2; int8
-// attention at 32k positions 31.7 us with 2 against 33.8 with 3; 8 KiB
+// attention at 32k positions 28.7 us with 2 against 30.8 with 3; 8 KiB
 // tiles (3 or 4 stages) were slower at 32k (35.7-36.9 us).
 template <int WPB_, int NST_, int TILE_>
 struct StreamCfg {
